@@ -1,0 +1,144 @@
+"""Activation / weight quantization after the block Hadamard transform.
+
+Test infrastructure only (see oracle/__init__.py).
+
+[gist] §2.A: a stable block runs its linears with NVFP4 activations, a
+volatile one with INT8; [yly] §一 says the same (NVFP4 = "small fire", INT8 =
+"big fire").  Neither page defines the encodings; the readings below are the
+ones this project adopts (listed in the design doc), and the GPU path is bound to
+them bit for bit.
+
+NVFP4 (per tensor Y [M, K], K % 16 == 0):
+  1. amax_T = max |Y| over the whole tensor (or a value the caller supplies).
+     If amax_T is not finite or below 2^-100 the tensor is quantized to zero:
+     gs = 1, every scale byte 0, every code 0.  (Below that level fp32 scales
+     would turn subnormal; no bf16 activation of interest lives there.)
+  2. gs = RN(amax_T / 2688)       (2688 = 6 * 448: largest E2M1 * largest E4M3)
+  3. d  = RN(6 * gs)
+  4. per 16-element group g:  a_g = max |y|;  s_raw = RN(a_g / d);
+     s8 = E4M3(s_raw) (nearest-even, saturating at 448);
+     s_dec = RN(e4m3(s8) * gs)
+  5. s_dec == 0 -> the group's codes are 0.  Otherwise inv = RN(1 / s_dec)
+     and each code is E2M1(RN(y * inv)) with y's sign bit.
+  Codes are packed two per byte (even element in the low nibble), scales are
+  one E4M3 byte per group in row-major [M, K/16] order, and the tensor scale
+  pair is (amax_T, gs).  Dequantized value: e2m1(code) * e4m3(s8) * gs.
+  (All "RN" are fp32 round-to-nearest-even.  Step 5 multiplies by the
+  reciprocal of the group scale instead of dividing every element: one
+  correctly rounded division per group, the same count as the scale itself.)
+
+INT8 (per token row):
+  a_m = max_k |y[m, k]|; rows with a_m not finite or below 2^-100 store
+  scale 0 and all-zero codes.  Otherwise s_m = RN(a_m / 127),
+  inv = RN(1 / s_m), q = clamp(rint_even(RN(y * inv)), -127, 127).
+  Dequantized value: q * s_m.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .formats import (e2m1_to_float, e4m3_to_float, float_to_e2m1,
+                      float_to_e4m3, pack_nibbles, unpack_nibbles, bf16_to_f32)
+from .hadamard import block_hadamard_f32
+
+F32 = np.float32
+GROUP = 16
+ZERO_LIMIT = F32(2.0 ** -100)
+
+
+def _amax_ok(a) -> bool:
+    a = F32(a)
+    return bool(np.isfinite(a) and a >= ZERO_LIMIT)
+
+
+def nvfp4_quantize(y: np.ndarray, amax=None):
+    """y: fp32 [M, K].  Returns (packed codes u8 [M, K/2], scales u8
+    [M, K/16], (amax_T, gs) as float32)."""
+    y = np.ascontiguousarray(y, dtype=np.float32)
+    M, K = y.shape
+    assert K % GROUP == 0
+    if amax is None:
+        amax_t = F32(np.max(np.abs(y))) if y.size else F32(0.0)
+    else:
+        amax_t = F32(amax)
+    if M == 0 or not _amax_ok(amax_t):
+        return (np.zeros((M, K // 2), np.uint8), np.zeros((M, K // GROUP), np.uint8),
+                (amax_t, F32(1.0)))
+    gs = F32(amax_t / F32(2688.0))
+    d = F32(F32(6.0) * gs)
+    yg = y.reshape(M, K // GROUP, GROUP)
+    a_g = np.max(np.abs(yg), axis=-1)                       # exact
+    s_raw = (a_g / d).astype(np.float32)                    # RN
+    s8 = float_to_e4m3(s_raw)
+    s_dec = (e4m3_to_float(s8).astype(np.float32) * gs).astype(np.float32)
+    nz = s_dec != 0
+    inv = np.where(nz, F32(1.0) / np.where(nz, s_dec, F32(1.0)), F32(0.0)).astype(np.float32)
+    v = (yg * inv[..., None]).astype(np.float32)             # RN
+    codes = float_to_e2m1(v)
+    codes = np.where(nz[..., None], codes, np.uint8(0)).astype(np.uint8)
+    return pack_nibbles(codes.reshape(M, K)), s8, (amax_t, gs)
+
+
+def nvfp4_dequantize(packed: np.ndarray, scales: np.ndarray, gs=1.0) -> np.ndarray:
+    """float64 [R, K] = e2m1(code) * e4m3(scale) * gs (exact in float64)."""
+    codes = unpack_nibbles(packed)
+    R, K = codes.shape
+    vals = e2m1_to_float(codes).reshape(R, K // GROUP, GROUP)
+    return (vals * e4m3_to_float(scales)[..., None]).reshape(R, K) * float(gs)
+
+
+def int8_quantize(y: np.ndarray):
+    """y: fp32 [M, K] -> (int8 codes [M, K], fp32 scales [M])."""
+    y = np.ascontiguousarray(y, dtype=np.float32)
+    M, K = y.shape
+    a = np.max(np.abs(y), axis=1) if K else np.zeros(M, np.float32)
+    ok = np.isfinite(a) & (a >= ZERO_LIMIT)
+    s = np.where(ok, (a / F32(127.0)).astype(np.float32), F32(0.0)).astype(np.float32)
+    inv = np.where(ok, F32(1.0) / np.where(ok, s, F32(1.0)), F32(0.0)).astype(np.float32)
+    v = (y * inv[:, None]).astype(np.float32)
+    q = np.clip(np.rint(v), -127, 127).astype(np.int8)
+    q[~ok] = 0
+    return q, s
+
+
+def int8_dequantize(q: np.ndarray, s: np.ndarray) -> np.ndarray:
+    return q.astype(np.float64) * s.astype(np.float64)[:, None]
+
+
+def activation_stats(x_bits: np.ndarray, y: np.ndarray) -> np.ndarray:
+    """The outlier statistics fused into the quantize pass, in float64:
+    [max|x|, sum|x|, max|y|, sum|y|] with x the bf16 input before the
+    Hadamard transform and y after it.  The outlier ratio of [yly] §三 is
+    max / (sum / n)."""
+    x = np.abs(bf16_to_f32(x_bits).astype(np.float64))
+    ya = np.abs(y.astype(np.float64))
+    if x.size == 0:
+        return np.zeros(4)
+    return np.array([x.max(), x.sum(), ya.max(), ya.sum()])
+
+
+def hadamard_quantize(x_bits: np.ndarray, had_block: int, fmt: str, amax=None):
+    """The full per-linear activation pass: block Hadamard of bf16 rows, then
+    NVFP4 or INT8 quantization, plus the fused outlier statistics.
+    fmt is "nvfp4" or "int8".  Returns a dict."""
+    x = bf16_to_f32(x_bits)
+    y = block_hadamard_f32(x, had_block)
+    out = {"y": y, "stats": activation_stats(x_bits, y)}
+    if fmt == "nvfp4":
+        q, s, ts = nvfp4_quantize(y, amax)
+        out.update(q=q, scales=s, amax=ts[0], gs=ts[1])
+    elif fmt == "int8":
+        q, s = int8_quantize(y)
+        out.update(q=q, scales=s)
+    else:
+        raise ValueError(fmt)
+    return out
+
+
+def prepare_weight(w_bits: np.ndarray, had_block: int):
+    """Offline weight preparation: W [N, K] is rotated along K by the same
+    block Hadamard transform as the activations (so that the product of the
+    two rotated operands equals X W^T, H being orthonormal and symmetric) and
+    quantized to NVFP4 with its own tensor scale."""
+    r = hadamard_quantize(w_bits, had_block, "nvfp4")
+    return r["q"], r["scales"], r["gs"]
