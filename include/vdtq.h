@@ -1,0 +1,246 @@
+/*
+ * vdtq.h -- C ABI of the MI355X (gfx950) hot path of 6Bit-Diffusion's
+ * inference-time mixed-precision quantization for video diffusion
+ * transformers (DMPQ + temporal delta cache + purified delta refresh).
+ *
+ * Pages cited by title and section:
+ *   [gist] gist.science, "6Bit-Diffusion: Inference-Time Mixed-Precision
+ *          Quantization for Video Diffusion Models", §2.A DMPQ, §2.B TDC,
+ *          §2.C PDR, §4 results.
+ *   [yly]  youleyou.com, "清华大学6Bit-Diffusion技术实现视频生成AI模型3倍压缩与速度翻倍",
+ *          §一 DMPQ, §二 TDC, §三 PDR, §四 engineering, §七 limitations.
+ *
+ * Conventions shared by every call:
+ *   - Every function returns VDTQ_OK (0) or an error code.  Arguments are
+ *     validated before anything is enqueued: a non-zero return means no work
+ *     was launched and no output was touched.  vdtq_last_error() returns a
+ *     thread-local message for the last failing call on this thread.
+ *   - Pointers named *_dev are device pointers (HBM of the current HIP
+ *     device); all others are host pointers.  The caller allocates and frees
+ *     every buffer; the library allocates nothing.
+ *   - GPU work is asynchronous on `stream` (a hipStream_t; NULL = the null
+ *     stream).  Device faults surface at the caller's next synchronisation.
+ *   - Device pointers must be 16-byte aligned.  Matrices are row-major.
+ *   - Inputs must be finite; non-finite inputs give unspecified (but memory
+ *     safe) outputs.
+ *   - Calls on the same stream that share a workspace run in stream order;
+ *     concurrent calls on different streams need distinct workspaces.
+ *
+ * Element formats:
+ *   bf16    activations/weights/deltas, raw uint16 bit patterns.
+ *   NVFP4   codes: 4-bit E2M1 (OCP MX FP4; 1 sign, 2 exponent, 1 mantissa,
+ *           magnitudes 0,.5,1,1.5,2,3,4,6), two per byte, element 2j in the
+ *           low nibble of byte j, rows of K/2 bytes.  Scales: one OCP E4M3
+ *           ("fn": bias 7, max 448, no inf) byte per 16 consecutive elements
+ *           of a row, rows of K/16 bytes.  Tensor scale: fp32 pair
+ *           {amax_T, gs}; value = e2m1(code) * e4m3(scale) * gs.
+ *   INT8    codes int8 [M][K] in [-127, 127], per-row fp32 scale s_m;
+ *           value = q * s_m.
+ */
+#ifndef VDTQ_H
+#define VDTQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ------------------------------------------------------------ status codes */
+#define VDTQ_OK 0
+#define VDTQ_EINVAL 1        /* null pointer, bad shape/alignment/flag       */
+#define VDTQ_EUNSUPPORTED 2  /* valid but outside what this build handles    */
+#define VDTQ_EHIP 3          /* a HIP runtime call or launch failed          */
+
+/* ------------------------------------------------------------ enums */
+#define VDTQ_FMT_NVFP4 0
+#define VDTQ_FMT_INT8 1
+
+#define VDTQ_OUT_BF16 0
+#define VDTQ_OUT_F32 1
+
+/* hadamard_quantize flags */
+#define VDTQ_AMAX_GIVEN 1u   /* tensor_scale_dev[0] holds amax_T on entry    */
+#define VDTQ_STATS 2u        /* write the four outlier statistics            */
+
+/* scheduler actions */
+#define VDTQ_ACT_SKIP 0
+#define VDTQ_ACT_NVFP4 1
+#define VDTQ_ACT_INT8 2
+#define VDTQ_ACT_BF16 3
+
+/* vdtq_workspace_bytes op ids */
+#define VDTQ_OP_HADAMARD_QUANTIZE 0
+#define VDTQ_OP_BLOCK_STATS 1
+
+const char* vdtq_last_error(void);
+const char* vdtq_version(void);
+
+/* Bytes of workspace a call needs for the given problem size (0 if none). */
+size_t vdtq_workspace_bytes(int op, int64_t M, int64_t K);
+
+/*
+ * hadamard_quantize -- online block Hadamard transform of bf16 activations
+ * followed by NVFP4 or per-token INT8 quantization, with the outlier
+ * statistics fused in.
+ *
+ * Defined by: [gist] §2.A (block Hadamard before quantization; NVFP4 for
+ * stable blocks, INT8 for volatile ones), [yly] §一 (same), [yly] §三 (the
+ * max/mean outlier ratio of the input), [yly] §四 / [gist] §4 (quantization
+ * fused with the Hadamard transform in one kernel).
+ *
+ * Computes, per row of X and per block of `had_block` consecutive elements,
+ * y = x * H_b / sqrt(b) (Sylvester H_b, butterflies h = 1, 2, ..., b/2 in
+ * fp32 round-to-nearest-even), then:
+ *   NVFP4: amax_T = max|Y| (computed, or read from tensor_scale_dev[0] when
+ *     flags has VDTQ_AMAX_GIVEN); amax_T non-finite or < 2^-100 => all codes
+ *     and scales 0, gs = 1.  Else gs = RN(amax_T / 2688), d = RN(6 gs); per
+ *     16-group s8 = E4M3(RN(max|y| / d)) (nearest-even, saturating),
+ *     s_dec = RN(e4m3(s8) * gs); code = E2M1(RN(y * RN(1 / s_dec)))
+ *     (nearest-even, saturating, sign copied), 0 if s_dec == 0.
+ *   INT8: per row a = max|y|; a non-finite or < 2^-100 => scale 0, codes 0;
+ *     else s = RN(a / 127), q = rint_even(RN(y * RN(1 / s))), |q| <= 127.
+ *
+ * x_dev          bf16 [M][ldx], ldx >= K (elements)
+ * M              rows (tokens), >= 0; M == 0 is a no-op (NVFP4 still writes
+ *                the tensor scale {0, 1} unless AMAX_GIVEN)
+ * K              columns, > 0, multiple of 16 and of had_block; for INT8,
+ *                K <= 16384
+ * had_block      16, 32, 64, 128 or 256
+ * fmt            VDTQ_FMT_NVFP4 or VDTQ_FMT_INT8
+ * flags          VDTQ_AMAX_GIVEN (NVFP4 only) | VDTQ_STATS
+ * q_dev          NVFP4: uint8 [M][K/2]; INT8: int8 [M][K]
+ * scales_dev     NVFP4: uint8 E4M3 [M][K/16]; INT8: float [M]
+ * tensor_scale_dev  NVFP4: float[2] {amax_T, gs} (amax_T is read when
+ *                AMAX_GIVEN, else written); INT8: ignored, may be NULL
+ * stats_dev      double[4] {max|x|, sum|x|, max|y|, sum|y|} when
+ *                VDTQ_STATS (x before, y after the transform), else ignored
+ * ws_dev/ws_bytes  workspace of vdtq_workspace_bytes(VDTQ_OP_HADAMARD_QUANTIZE,
+ *                M, K) bytes (needed for NVFP4 without AMAX_GIVEN or with
+ *                VDTQ_STATS)
+ * Errors: VDTQ_EINVAL for null pointers, misalignment, bad sizes/flags or a
+ * short workspace; VDTQ_EUNSUPPORTED for INT8 with K > 16384.
+ */
+int hadamard_quantize(const void* x_dev, int64_t M, int64_t K, int64_t ldx,
+                      int had_block, int fmt, unsigned flags, void* q_dev,
+                      void* scales_dev, float* tensor_scale_dev,
+                      double* stats_dev, void* ws_dev, size_t ws_bytes,
+                      void* stream);
+
+/*
+ * qgemm_w4a4 -- Y = gs_a * gs_w * (A_hat W_hat^T) + bias with NVFP4
+ * activations A [M][K] and NVFP4 weights W [N][K] (both rotated by the same
+ * block Hadamard transform along K, so Y is the linear layer's output).
+ *
+ * Defined by: [gist] §2.A and §3.1 (NVFP4 activations for stable blocks),
+ * [gist] §4 / [yly] §四 (4-bit weights throughout: W4A4 ... W4A8).
+ *
+ * A_hat = e2m1(code) * e4m3(scale) per element (exact), W_hat likewise;
+ * products and sums in fp32 (any order), result rounded to out_dtype.
+ *
+ * a_q_dev  uint8 [M][K/2]   a_s_dev uint8 [M][K/16]   a_ts_dev float[2] {amax, gs}
+ * w_q_dev  uint8 [N][K/2]   w_s_dev uint8 [N][K/16]   w_ts_dev float[2] {amax, gs}
+ * bias_dev float [N] or NULL
+ * y_dev    out_dtype [M][ldy], ldy >= N (elements)
+ * M, N >= 0 (0 is a no-op); K > 0, multiple of 16.
+ */
+int qgemm_w4a4(const uint8_t* a_q_dev, const uint8_t* a_s_dev,
+               const float* a_ts_dev, const uint8_t* w_q_dev,
+               const uint8_t* w_s_dev, const float* w_ts_dev,
+               const float* bias_dev, void* y_dev, int64_t ldy, int out_dtype,
+               int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
+ * qgemm_w4a8 -- Y[m][n] = s_a[m] * gs_w * sum_k q_a[m][k] W_hat[n][k] + bias
+ * with per-token INT8 activations and NVFP4 weights.
+ *
+ * Defined by: [gist] §2.A (INT8 for volatile blocks), [yly] §三 (INT8 for
+ * the first recompute after a skip), [gist] §4 (W4A8 operating point).
+ *
+ * Every product q * W_hat is exact and accumulated in fp32; with all weight
+ * scales 1 (E4M3 byte 0x38), gs_w = 1 and s_a = 1 the result equals the
+ * integer sum_k q_a * e2m1(w) exactly while partial sums stay below 2^24.
+ *
+ * a_q_dev int8 [M][K]   a_s_dev float [M]   weights as in qgemm_w4a4.
+ */
+int qgemm_w4a8(const int8_t* a_q_dev, const float* a_s_dev,
+               const uint8_t* w_q_dev, const uint8_t* w_s_dev,
+               const float* w_ts_dev, const float* bias_dev, void* y_dev,
+               int64_t ldy, int out_dtype, int64_t M, int64_t N, int64_t K,
+               void* stream);
+
+/*
+ * block_stats -- one pass over a block's input, output and cached delta.
+ *
+ * Defined by: [gist] §2.A (Gamma_{t-1}: relative input-output difference of
+ * the block), [gist] §2.B (similarity of Delta_{t-1} and Delta_{t-2}; the
+ * cached residual delta), [yly] §三 (max/mean outlier ratio), [yly] §七
+ * (the online metrics cost a pass; keep it cheap).
+ *
+ * d = RN_fp32(out - in); dnew = bf16_RNE(d) (written when dnew_dev != NULL).
+ * stats_dev double[8] = {sum d^2, sum in^2, sum (dnew - dprev)^2,
+ *   sum dprev^2, max|in|, sum|in|, max|out|, sum|out|}; entries 2 and 3 are
+ *   0 when dprev_dev == NULL.  Sums are accumulated in fp64 in a fixed
+ *   order (bit-identical across runs).
+ * in_dev, out_dev, dprev_dev, dnew_dev: bf16 [n] (dnew may not alias dprev)
+ * n >= 0 (n == 0 writes zeros).
+ * ws_dev: vdtq_workspace_bytes(VDTQ_OP_BLOCK_STATS, n, 1) bytes.
+ */
+int block_stats(const void* in_dev, const void* out_dev,
+                const void* dprev_dev, void* dnew_dev, int64_t n,
+                double* stats_dev, void* ws_dev, size_t ws_bytes,
+                void* stream);
+
+/* ------------------------------------------------------------ scheduler */
+
+typedef struct {
+  double gamma;    /* Gamma threshold: NVFP4 below, INT8 at or above        */
+  double tau;      /* skip only when r < tau ...                            */
+  double tau_acc;  /* ... and acc + r < tau_acc (error accumulator)         */
+  double rho;      /* BF16 when the input outlier ratio exceeds rho         */
+  double tau_u;    /* BF16 when r exceeds tau_u (+inf disables)             */
+  int32_t warmup;  /* no skip before this step index                        */
+  int32_t pad_;
+} vdtq_dmpq_params;
+
+typedef struct {
+  int64_t step;
+  int32_t has_d1, has_d2, skipped_last, has_gamma;
+  double gamma_prev, r_last, acc;
+} vdtq_dmpq_state;
+
+/* Fresh state (step 0, no history, r_last = +inf). */
+void dmpq_state_init(vdtq_dmpq_state* s);
+
+/*
+ * dmpq_step -- host-side per-block decision for one denoising step.
+ *
+ * Defined by: [gist] §2.A (low Gamma -> NVFP4, high -> INT8), [gist] §2.B
+ * (skip on Delta similarity; error-guided switching refreshes the cache),
+ * [gist] §2.C and [yly] §三 (outliers or temporal uncertainty -> full
+ * precision before a cache write), [yly] §三 (restart after a skip -> INT8).
+ *
+ * last_stats: host double[8] from block_stats of the previous step if that
+ *   step was computed, NULL otherwise.  in_ratio: outlier ratio
+ *   max|x| / mean|x| of the block input at this step.
+ * 1. If last_stats: Gamma_prev = sqrt(s0/s1) (0 if s0 = s1 = 0, +inf if only
+ *    s1 = 0); if a delta was already cached, r_last = sqrt(s2/s3) (+inf if
+ *    s3 = 0); the delta history shifts; skipped_last = 0; acc = 0.
+ * 2. SKIP if step >= warmup, two deltas are cached, r_last < tau and
+ *    acc + r_last < tau_acc; then acc += r_last, skipped_last = 1.
+ * 3. Else BF16 if in_ratio > rho or (two deltas cached and r_last > tau_u);
+ *    else INT8 if skipped_last or no Gamma yet or Gamma_prev >= gamma;
+ *    else NVFP4.
+ * Pure host code, deterministic; *action receives VDTQ_ACT_*.
+ */
+int dmpq_step(const vdtq_dmpq_params* p, vdtq_dmpq_state* s,
+              const double* last_stats, double in_ratio, int* action);
+
+/* max / (sum / n); 1 when sum == 0 or n == 0. */
+double vdtq_outlier_ratio(double max_abs, double sum_abs, int64_t n);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* VDTQ_H */

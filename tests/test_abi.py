@@ -1,0 +1,142 @@
+"""CPU tests of the C ABI: the library loads, exports every symbol the header
+declares, rejects bad arguments before touching a device, and the host
+scheduler follows the hand-derived sequence and the oracle."""
+import ctypes
+import json
+import math
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import video_diffusion_transformer_block_amd as V
+from video_diffusion_transformer_block_amd import _lib as L
+from oracle import dmpq as D
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "vdtq.h")
+FAKE = ctypes.c_void_p(0x10000)          # aligned, never dereferenced: every call
+FAKE8 = ctypes.c_void_p(0x10008)         # below fails validation before a launch
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?(?:int|void|size_t|double|char)\s*\*?\s*(\w+)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_and_exports_agree():
+    decl = declared_functions()
+    assert sorted(L.EXPORTED) == decl
+    out = subprocess.run(["nm", "-D", "--defined-only", L.LIB_PATH], capture_output=True, text=True).stdout
+    syms = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for name in decl:
+        assert name in syms, name
+        assert getattr(V.lib(), name) is not None
+
+
+def test_version_and_workspace_sizes():
+    assert V.lib().vdtq_version().startswith(b"vdtq")
+    lib = V.lib()
+    assert lib.vdtq_workspace_bytes(L.OP_HADAMARD_QUANTIZE, 17776, 3072) >= 4 * 8 * (17776 * 48 // 256)
+    assert lib.vdtq_workspace_bytes(L.OP_BLOCK_STATS, 4446 * 1920, 1) >= 8 * 8
+    assert lib.vdtq_workspace_bytes(99, 1, 1) == 0
+
+
+def _hq(**kw):
+    a = dict(x=FAKE, M=4, K=64, ldx=64, b=64, fmt=0, flags=0, q=FAKE, s=FAKE, ts=FAKE, st=None,
+             ws=FAKE, wsb=1 << 20)
+    a.update(kw)
+    return V.lib().hadamard_quantize(a["x"], a["M"], a["K"], a["ldx"], a["b"], a["fmt"], a["flags"], a["q"],
+                                     a["s"], a["ts"], a["st"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(K=15), L.EINVAL), (dict(K=0), L.EINVAL), (dict(M=-1), L.EINVAL),
+    (dict(b=48), L.EINVAL), (dict(b=512), L.EINVAL), (dict(K=96, ldx=96, b=64), L.EINVAL),
+    (dict(ldx=60), L.EINVAL), (dict(ldx=68), L.EINVAL), (dict(fmt=2), L.EINVAL),
+    (dict(flags=4), L.EINVAL), (dict(fmt=1, flags=1), L.EINVAL),
+    (dict(fmt=1, K=16384 + 64, ldx=16448), L.EUNSUPPORTED),
+    (dict(x=None), L.EINVAL), (dict(q=None), L.EINVAL), (dict(x=FAKE8), L.EINVAL),
+    (dict(ts=None), L.EINVAL), (dict(flags=2, st=None), L.EINVAL),
+    (dict(ws=None), L.EINVAL), (dict(wsb=8), L.EINVAL),
+])
+def test_hadamard_quantize_rejects(kw, code):
+    assert _hq(**kw) == code
+    assert V.lib().vdtq_last_error()
+
+
+def _gemm(fn, **kw):
+    a = dict(aq=FAKE, as_=FAKE, ats=FAKE, wq=FAKE, ws=FAKE, wts=FAKE, bias=None, y=FAKE, ldy=64, od=0,
+             M=8, N=64, K=64)
+    a.update(kw)
+    if fn == "w4a4":
+        return V.lib().qgemm_w4a4(a["aq"], a["as_"], a["ats"], a["wq"], a["ws"], a["wts"], a["bias"], a["y"],
+                                  a["ldy"], a["od"], a["M"], a["N"], a["K"], None)
+    return V.lib().qgemm_w4a8(a["aq"], a["as_"], a["wq"], a["ws"], a["wts"], a["bias"], a["y"], a["ldy"],
+                              a["od"], a["M"], a["N"], a["K"], None)
+
+
+@pytest.mark.parametrize("fn", ["w4a4", "w4a8"])
+@pytest.mark.parametrize("kw", [dict(K=0), dict(K=40), dict(M=-2), dict(ldy=10), dict(od=3),
+                                dict(aq=None), dict(wq=None), dict(wts=None), dict(y=None),
+                                dict(aq=FAKE8), dict(M=1 << 31)])
+def test_qgemm_rejects(fn, kw):
+    assert _gemm(fn, **kw) == L.EINVAL
+
+
+def test_qgemm_empty_is_noop():
+    assert _gemm("w4a4", M=0) == L.OK
+    assert _gemm("w4a8", N=0, aq=None, y=None) == L.OK
+
+
+@pytest.mark.parametrize("kw", [dict(n=-1), dict(st=None), dict(inp=None), dict(dnew=FAKE, dprev=FAKE),
+                                dict(ws=None), dict(wsb=0), dict(inp=FAKE8)])
+def test_block_stats_rejects(kw):
+    a = dict(inp=FAKE, out=FAKE, dprev=None, dnew=None, n=64, st=FAKE, ws=FAKE, wsb=1 << 20)
+    a.update(kw)
+    rc = V.lib().block_stats(a["inp"], a["out"], a["dprev"], a["dnew"], a["n"], a["st"], a["ws"], a["wsb"], None)
+    assert rc == L.EINVAL
+
+
+def test_dmpq_step_hand_sequence():
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "dmpq_sequence.json")))
+    p = V.dmpq_params(**g["params"])
+    s = V.dmpq_state()
+    names = {L.ACT_SKIP: "skip", L.ACT_NVFP4: "nvfp4", L.ACT_INT8: "int8", L.ACT_BF16: "bf16"}
+    got = [names[V.dmpq_step(p, s, None if n is None else g["stats"][n], r)] for n, r, _ in g["calls"]]
+    assert got == [c[2] for c in g["calls"]]
+
+
+def test_dmpq_step_matches_oracle_random():
+    rng = np.random.Generator(np.random.PCG64(99))
+    for trial in range(20):
+        kw = dict(gamma=rng.uniform(0.02, 0.3), tau=rng.uniform(0.01, 0.2), tau_acc=rng.uniform(0.05, 0.6),
+                  rho=rng.uniform(2, 20), tau_u=(math.inf if trial % 2 else rng.uniform(0.2, 1.0)),
+                  warmup=int(rng.integers(0, 4)))
+        p_c, s_c = V.dmpq_params(**kw), V.dmpq_state()
+        p_o, s_o = D.Params(**kw), D.State()
+        last = None
+        for t in range(200):
+            ratio = float(rng.uniform(1, 25))
+            a_c = V.dmpq_step(p_c, s_c, last, ratio)
+            a_o = D.dmpq_step(p_o, s_o, None if last is None else np.array(last), ratio)
+            assert a_c == a_o, (trial, t)
+            if a_c == L.ACT_SKIP:
+                last = None
+            else:
+                z = rng.uniform(0, 1, 4)
+                last = [z[0] * 0.05, 1.0, (z[1] * 0.2) ** 2, 1.0 if z[2] > 0.05 else 0.0, 1, 1, 1, 1]
+        assert s_c.step == s_o.step and s_c.acc == s_o.acc and s_c.r_last == s_o.r_last
+
+
+def test_dmpq_step_null_args():
+    assert V.lib().dmpq_step(None, None, None, 1.0, None) == L.EINVAL
+
+
+def test_outlier_ratio_c():
+    assert V.outlier_ratio(4.0, 100.0, 100) == 4.0
+    assert V.outlier_ratio(0.0, 0.0, 100) == 1.0

@@ -1,0 +1,124 @@
+"""GPU parity of qgemm_w4a4 / qgemm_w4a8 against the oracle: relative
+Frobenius error <= 2e-3 (bf16 compared with the oracle's bf16 rounding; f32
+with its exact value), and the W4A8 integer accumulator bit-exact."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+import video_diffusion_transformer_block_amd as V
+from oracle import formats as F, gemm as G, quant as Q
+from helpers import bf16_values, dev_bf16, host_bits, need_gpu, rel_fro, log
+
+pytestmark = pytest.mark.gpu
+RNG = np.random.Generator(np.random.PCG64(22))
+TOL = 2e-3
+
+
+def nvfp4_dev(q, s, ts):
+    return V.NVFP4Tensor(torch.from_numpy(q).cuda(), torch.from_numpy(s).cuda(),
+                         torch.tensor(ts, dtype=torch.float32).cuda())
+
+
+def check_layer(x_bits, w_bits, b=64, bias=True, rows=None, out_dtypes=("bf16", "f32")):
+    M, K = x_bits.shape
+    N = w_bits.shape[0]
+    log(f"gemm case M={M} N={N} K={K} rows={'all' if rows is None else len(rows)}")
+    sel = np.arange(M) if rows is None else rows
+    # weights: prepared on both sides, compared bit for bit
+    wq_o, ws_o, wgs_o = Q.prepare_weight(w_bits, b)
+    wd = V.hadamard_quantize(dev_bf16(w_bits), b, "nvfp4")
+    assert np.array_equal(wd.q.cpu().numpy(), wq_o) and np.array_equal(wd.scales.cpu().numpy(), ws_o)
+    assert wd.ts.cpu().numpy()[1] == wgs_o
+    bias_h = RNG.standard_normal(N).astype(np.float32) if bias else None
+    bias_d = torch.from_numpy(bias_h).cuda() if bias else None
+    xd = dev_bf16(x_bits)
+    # oracle activations on the sampled rows (NVFP4 amax over every row)
+    amax = None
+    if rows is not None:
+        from oracle import hadamard as H
+        amax = np.float32(0)
+        for r0 in range(0, M, 4096):
+            amax = max(amax, np.float32(np.abs(H.block_hadamard_bf16(x_bits[r0:r0 + 4096], b)).max()))
+    a4 = Q.hadamard_quantize(x_bits[sel], b, "nvfp4", amax=amax)
+    a8 = Q.hadamard_quantize(x_bits[sel], b, "int8")
+    ad4 = V.hadamard_quantize(xd, b, "nvfp4")
+    ad8 = V.hadamard_quantize(xd, b, "int8")
+    for od in out_dtypes:
+        y4 = V.qgemm_w4a4(ad4, wd, bias_d, od)
+        y8 = V.qgemm_w4a8(ad8, wd, bias_d, od)
+        torch.cuda.synchronize()
+        e4, r4 = G.qgemm_w4a4(a4["q"], a4["scales"], a4["gs"], wq_o, ws_o, wgs_o, bias_h, od)
+        e8, r8 = G.qgemm_w4a8(a8["q"], a8["scales"], wq_o, ws_o, wgs_o, bias_h, od)
+        if od == "bf16":
+            g4 = bf16_values(host_bits(y4)[sel]); g8 = bf16_values(host_bits(y8)[sel])
+            w4 = bf16_values(r4); w8 = bf16_values(r8)
+        else:
+            g4 = y4.cpu().numpy()[sel]; g8 = y8.cpu().numpy()[sel]
+            w4, w8 = e4, e8
+        err4, err8 = rel_fro(g4, w4), rel_fro(g8, w8)
+        log(f"  {od}: w4a4 rel {err4:.2e}  w4a8 rel {err8:.2e}")
+        assert err4 <= TOL and err8 <= TOL, (err4, err8)
+        if od == "f32":
+            assert err4 < 1e-5 and err8 < 1e-5   # only fp32 accumulation order differs
+
+
+def test_tiny_layer():
+    need_gpu()
+    d = synth.tiny_layer()
+    check_layer(d["x"], d["w"])
+    check_layer(d["x"], d["w"], bias=False)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 64), (129, 33, 64), (300, 200, 320), (5, 130, 96),
+                                   (64, 64, 48), (200, 257, 16), (1, 640, 1920), (131, 129, 256)])
+def test_ragged(M, N, K):
+    need_gpu()
+    b = 16 if K % 64 else 64
+    x = synth.to_bf16_bits(RNG.laplace(size=(M, K)).astype(np.float32))
+    w = synth.to_bf16_bits(RNG.standard_normal((N, K)).astype(np.float32) * 0.02)
+    check_layer(x, w, b=b)
+
+
+def test_w4a8_integer_accumulator_exact():
+    """Unit weight scales, gs_w = 1, s_a = 1: Y = sum_k q * e2m1(w) exactly."""
+    need_gpu()
+    M, N, K = 192, 160, 3072
+    q = RNG.integers(-127, 128, size=(M, K)).astype(np.int8)
+    codes = RNG.integers(0, 16, size=(N, K)).astype(np.uint8)
+    wq = F.pack_nibbles(codes)
+    ws = np.full((N, K // 16), 0x38, np.uint8)
+    P = G.w4a8_integer_accumulator(q, wq)
+    # every partial sum stays below 2^24 (bound: K * 127 * 12 / 2)
+    assert K * 127 * 12 // 2 < 2 ** 24
+    a = V.INT8Tensor(torch.from_numpy(q).cuda(), torch.ones(M, dtype=torch.float32, device="cuda"))
+    w = nvfp4_dev(wq, ws, [1.0, 1.0])
+    y = V.qgemm_w4a8(a, w, None, "f32")
+    torch.cuda.synchronize()
+    assert np.array_equal(y.cpu().numpy().astype(np.float64) * 2, P.astype(np.float64))
+
+
+def test_w4a4_unit_scale_exact_products():
+    """Unit tensor scales and small exact sums: the fp32 result is exact."""
+    need_gpu()
+    M, N, K = 96, 64, 512
+    ac = RNG.integers(0, 16, size=(M, K)).astype(np.uint8)
+    wc = RNG.integers(0, 16, size=(N, K)).astype(np.uint8)
+    as_ = RNG.integers(0x30, 0x40, size=(M, K // 16)).astype(np.uint8)   # 0.5 .. 1.875
+    ws = RNG.integers(0x30, 0x40, size=(N, K // 16)).astype(np.uint8)
+    a = nvfp4_dev(F.pack_nibbles(ac), as_, [2688.0, 1.0])
+    w = nvfp4_dev(F.pack_nibbles(wc), ws, [2688.0, 1.0])
+    y = V.qgemm_w4a4(a, w, None, "f32")
+    torch.cuda.synchronize()
+    want, _ = G.qgemm_w4a4(F.pack_nibbles(ac), as_, 1.0, F.pack_nibbles(wc), ws, 1.0, None, "f32")
+    # products are multiples of 2^-8 below 2^7, sums below 2^16: all exact in fp32
+    assert np.array_equal(y.cpu().numpy().astype(np.float64), want)
+
+
+@pytest.mark.parametrize("name", ["qkv", "out", "ffn_up", "ffn_down"])
+def test_cogvideox_5b_linears_sampled(name):
+    need_gpu()
+    M = synth.TOKENS_2B_5B
+    K, N = {n: (k, nn) for n, k, nn in synth.block_linears(3072)}[name]
+    x, w = synth.layer_inputs(M, name, K, N)
+    check_layer(x, w, rows=synth.row_sample(M, 48), out_dtypes=("bf16",))

@@ -1,0 +1,149 @@
+// C ABI of the library: argument validation, status codes, the thread-local
+// error message, and dispatch to the kernel launchers.  Nothing is enqueued
+// unless every argument checks out.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "../../include/vdtq.h"
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int ok() {
+  g_err.clear();
+  return VDTQ_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(VDTQ_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+constexpr int64_t kI32 = 2147483647;
+
+}  // namespace
+
+extern "C" {
+
+const char* vdtq_last_error(void) { return g_err.c_str(); }
+
+const char* vdtq_version(void) { return "vdtq 0.1.0 gfx950"; }
+
+size_t vdtq_workspace_bytes(int op, int64_t M, int64_t K) {
+  if (op == VDTQ_OP_HADAMARD_QUANTIZE) return vdtq::hq_workspace_bytes(M, K);
+  if (op == VDTQ_OP_BLOCK_STATS) return vdtq::bs_workspace_bytes(M);
+  return 0;
+}
+
+int hadamard_quantize(const void* x_dev, int64_t M, int64_t K, int64_t ldx, int had_block, int fmt,
+                      unsigned flags, void* q_dev, void* scales_dev, float* tensor_scale_dev,
+                      double* stats_dev, void* ws_dev, size_t ws_bytes, void* stream) {
+  if (M < 0 || M > kI32) return fail(VDTQ_EINVAL, "hadamard_quantize: M=%lld out of range", (long long)M);
+  if (K <= 0 || K > kI32 || K % 16) return fail(VDTQ_EINVAL, "hadamard_quantize: K=%lld must be a positive multiple of 16", (long long)K);
+  if (had_block != 16 && had_block != 32 && had_block != 64 && had_block != 128 && had_block != 256)
+    return fail(VDTQ_EINVAL, "hadamard_quantize: had_block=%d must be 16, 32, 64, 128 or 256", had_block);
+  if (K % had_block) return fail(VDTQ_EINVAL, "hadamard_quantize: K=%lld not a multiple of had_block=%d", (long long)K, had_block);
+  if (ldx < K || ldx % 8) return fail(VDTQ_EINVAL, "hadamard_quantize: ldx=%lld must be >= K and a multiple of 8", (long long)ldx);
+  if (fmt != VDTQ_FMT_NVFP4 && fmt != VDTQ_FMT_INT8) return fail(VDTQ_EINVAL, "hadamard_quantize: fmt=%d", fmt);
+  if (flags & ~(VDTQ_AMAX_GIVEN | VDTQ_STATS)) return fail(VDTQ_EINVAL, "hadamard_quantize: unknown flags 0x%x", flags);
+  if (fmt == VDTQ_FMT_INT8 && (flags & VDTQ_AMAX_GIVEN))
+    return fail(VDTQ_EINVAL, "hadamard_quantize: VDTQ_AMAX_GIVEN applies to NVFP4 only");
+  if (fmt == VDTQ_FMT_INT8 && K > 16384)
+    return fail(VDTQ_EUNSUPPORTED, "hadamard_quantize: INT8 rows longer than 16384 (K=%lld)", (long long)K);
+  const int64_t cpr = (K + 63) / 64;
+  if (M * cpr > kI32) return fail(VDTQ_EINVAL, "hadamard_quantize: M*ceil(K/64) exceeds 2^31");
+  if (M > 0) {
+    if (!x_dev || !q_dev || !scales_dev) return fail(VDTQ_EINVAL, "hadamard_quantize: null x/q/scales");
+    if (!aligned(x_dev, 16) || !aligned(q_dev, 16) || !aligned(scales_dev, 4))
+      return fail(VDTQ_EINVAL, "hadamard_quantize: x and q must be 16-byte aligned, scales 4-byte aligned");
+  }
+  if (fmt == VDTQ_FMT_NVFP4 && (!tensor_scale_dev || !aligned(tensor_scale_dev, 4)))
+    return fail(VDTQ_EINVAL, "hadamard_quantize: NVFP4 needs an aligned tensor_scale (float[2])");
+  if ((flags & VDTQ_STATS) && (!stats_dev || !aligned(stats_dev, 8)))
+    return fail(VDTQ_EINVAL, "hadamard_quantize: VDTQ_STATS needs an aligned stats buffer (double[4])");
+  const bool need_ws = (flags & VDTQ_STATS) || (fmt == VDTQ_FMT_NVFP4 && !(flags & VDTQ_AMAX_GIVEN));
+  if (need_ws) {
+    const size_t need = vdtq::hq_workspace_bytes(M, K);
+    if (!ws_dev || !aligned(ws_dev, 16) || ws_bytes < need)
+      return fail(VDTQ_EINVAL, "hadamard_quantize: workspace of %zu bytes (16-byte aligned) required, got %zu", need, ws_bytes);
+  }
+  hipError_t e = vdtq::launch_hadamard_quantize(x_dev, M, K, ldx, had_block, fmt, flags, q_dev, scales_dev,
+                                                tensor_scale_dev, stats_dev, ws_dev,
+                                                static_cast<hipStream_t>(stream));
+  return hip_status(e, "hadamard_quantize launch");
+}
+
+static int qgemm_check(const char* name, const void* a_q, const void* a_s, const void* w_q, const void* w_s,
+                       const float* w_ts, const float* bias, void* y, int64_t ldy, int out_dtype, int64_t M,
+                       int64_t N, int64_t K) {
+  if (M < 0 || M > kI32 || N < 0 || N > kI32) return fail(VDTQ_EINVAL, "%s: M=%lld N=%lld out of range", name, (long long)M, (long long)N);
+  if (K <= 0 || K > kI32 || K % 16) return fail(VDTQ_EINVAL, "%s: K=%lld must be a positive multiple of 16", name, (long long)K);
+  if (out_dtype != VDTQ_OUT_BF16 && out_dtype != VDTQ_OUT_F32) return fail(VDTQ_EINVAL, "%s: out_dtype=%d", name, out_dtype);
+  if (ldy < N) return fail(VDTQ_EINVAL, "%s: ldy=%lld < N=%lld", name, (long long)ldy, (long long)N);
+  if (M == 0 || N == 0) return VDTQ_OK;
+  if (!a_q || !a_s || !w_q || !w_s || !w_ts || !y) return fail(VDTQ_EINVAL, "%s: null pointer argument", name);
+  if (!aligned(a_q, 16) || !aligned(w_q, 16) || !aligned(w_ts, 4) || !aligned(y, out_dtype ? 4 : 2) ||
+      (bias && !aligned(bias, 4)))
+    return fail(VDTQ_EINVAL, "%s: misaligned pointer (codes need 16 bytes)", name);
+  if ((M + 127) / 128 > 65535) return fail(VDTQ_EUNSUPPORTED, "%s: M=%lld too large", name, (long long)M);
+  return VDTQ_OK;
+}
+
+int qgemm_w4a4(const uint8_t* a_q_dev, const uint8_t* a_s_dev, const float* a_ts_dev, const uint8_t* w_q_dev,
+               const uint8_t* w_s_dev, const float* w_ts_dev, const float* bias_dev, void* y_dev, int64_t ldy,
+               int out_dtype, int64_t M, int64_t N, int64_t K, void* stream) {
+  int rc = qgemm_check("qgemm_w4a4", a_q_dev, a_s_dev, w_q_dev, w_s_dev, w_ts_dev, bias_dev, y_dev, ldy,
+                       out_dtype, M, N, K);
+  if (rc) return rc;
+  if (M > 0 && N > 0 && (!a_ts_dev || !aligned(a_ts_dev, 4)))
+    return fail(VDTQ_EINVAL, "qgemm_w4a4: null or misaligned a_ts");
+  hipError_t e = vdtq::launch_qgemm(0, a_q_dev, a_s_dev, a_ts_dev, w_q_dev, w_s_dev, w_ts_dev, bias_dev, y_dev,
+                                    ldy, out_dtype, M, N, K, static_cast<hipStream_t>(stream));
+  return hip_status(e, "qgemm_w4a4 launch");
+}
+
+int qgemm_w4a8(const int8_t* a_q_dev, const float* a_s_dev, const uint8_t* w_q_dev, const uint8_t* w_s_dev,
+               const float* w_ts_dev, const float* bias_dev, void* y_dev, int64_t ldy, int out_dtype, int64_t M,
+               int64_t N, int64_t K, void* stream) {
+  int rc = qgemm_check("qgemm_w4a8", a_q_dev, a_s_dev, w_q_dev, w_s_dev, w_ts_dev, bias_dev, y_dev, ldy,
+                       out_dtype, M, N, K);
+  if (rc) return rc;
+  if (M > 0 && N > 0 && !aligned(a_s_dev, 4)) return fail(VDTQ_EINVAL, "qgemm_w4a8: misaligned a_s");
+  hipError_t e = vdtq::launch_qgemm(1, a_q_dev, a_s_dev, nullptr, w_q_dev, w_s_dev, w_ts_dev, bias_dev, y_dev,
+                                    ldy, out_dtype, M, N, K, static_cast<hipStream_t>(stream));
+  return hip_status(e, "qgemm_w4a8 launch");
+}
+
+int block_stats(const void* in_dev, const void* out_dev, const void* dprev_dev, void* dnew_dev, int64_t n,
+                double* stats_dev, void* ws_dev, size_t ws_bytes, void* stream) {
+  if (n < 0) return fail(VDTQ_EINVAL, "block_stats: n=%lld < 0", (long long)n);
+  if (!stats_dev || !aligned(stats_dev, 8)) return fail(VDTQ_EINVAL, "block_stats: null or misaligned stats");
+  if (n > 0 && (!in_dev || !out_dev)) return fail(VDTQ_EINVAL, "block_stats: null in/out");
+  if (!aligned(in_dev, 16) || !aligned(out_dev, 16) || !aligned(dprev_dev, 16) || !aligned(dnew_dev, 16))
+    return fail(VDTQ_EINVAL, "block_stats: bf16 buffers must be 16-byte aligned");
+  if (dnew_dev && dnew_dev == dprev_dev) return fail(VDTQ_EINVAL, "block_stats: dnew must not alias dprev");
+  const size_t need = vdtq::bs_workspace_bytes(n);
+  if (!ws_dev || !aligned(ws_dev, 16) || ws_bytes < need)
+    return fail(VDTQ_EINVAL, "block_stats: workspace of %zu bytes (16-byte aligned) required, got %zu", need, ws_bytes);
+  hipError_t e = vdtq::launch_block_stats(in_dev, out_dev, dprev_dev, dnew_dev, n, stats_dev, ws_dev,
+                                          static_cast<hipStream_t>(stream));
+  return hip_status(e, "block_stats launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,146 @@
+// block_stats: one pass over a transformer block's input, output and cached
+// residual delta (gfx950).
+//
+// The operation: gist.science "6Bit-Diffusion: Inference-Time Mixed-Precision
+// Quantization for Video Diffusion Models" §2.A (Gamma_{t-1}, the block's
+// relative input-output difference, picks the precision), §2.B (the
+// similarity of Delta_{t-1} and Delta_{t-2} predicts a skip; Delta is cached)
+// and youleyou.com article §三 (max/mean outlier ratio) and §七 (these online
+// metrics are an extra pass whose cost must stay small).
+//
+// HBM-bound: 8 bytes per element (in, out, Delta_prev read; Delta_new
+// written).  Each thread handles 8 elements per step with 16-byte accesses in
+// a grid-stride loop over a grid sized from n only, accumulates in fp64, and
+// the workgroup / grid reductions run in a fixed order: the eight results are
+// bit-identical from run to run.
+#include "device_common.h"
+#include "launch.h"
+
+namespace vdtq {
+
+constexpr int BS_THREADS = 256;
+constexpr int BS_MAX_GRID = 4096;
+
+static int bs_grid(int64_t n) {
+  int64_t vecs = (n + 7) / 8;
+  int64_t g = (vecs + BS_THREADS - 1) / BS_THREADS;
+  if (g > BS_MAX_GRID) g = BS_MAX_GRID;
+  return (int)(g < 1 ? 1 : g);
+}
+
+struct Acc8 {
+  double d2 = 0, i2 = 0, dd2 = 0, p2 = 0, si = 0, so = 0;
+  float mi = 0.0f, mo = 0.0f;
+};
+
+__device__ __forceinline__ void acc_one(Acc8& a, float xi, float xo, bool has_prev, float dp,
+                                        uint32_t& dnew_bits) {
+  const float d = xo - xi;                       // fp32 RN
+  dnew_bits = f32_to_bf16_bits(d);
+  const double dd = (double)d, ii = (double)xi;
+  a.d2 += dd * dd;
+  a.i2 += ii * ii;
+  if (has_prev) {
+    const double dn = (double)__uint_as_float(dnew_bits << 16);
+    const double pp = (double)dp;
+    const double df = dn - pp;                   // exact in fp64
+    a.dd2 += df * df;
+    a.p2 += pp * pp;
+  }
+  const float ai = fabsf(xi), ao = fabsf(xo);
+  a.mi = fmaxf(a.mi, ai);
+  a.mo = fmaxf(a.mo, ao);
+  a.si += (double)ai;
+  a.so += (double)ao;
+}
+
+__global__ __launch_bounds__(BS_THREADS) void block_stats_kernel(const uint16_t* in, const uint16_t* out,
+                                                                 const uint16_t* dprev, uint16_t* dnew,
+                                                                 int64_t n, double* part) {
+  Acc8 a;
+  const bool has_prev = dprev != nullptr;
+  const int64_t nvec = n / 8;
+  const int64_t stride = (int64_t)gridDim.x * BS_THREADS;
+  for (int64_t v = (int64_t)blockIdx.x * BS_THREADS + threadIdx.x; v < nvec; v += stride) {
+    const uint4 wi = reinterpret_cast<const uint4*>(in)[v];
+    const uint4 wo = reinterpret_cast<const uint4*>(out)[v];
+    uint4 wp = make_uint4(0u, 0u, 0u, 0u);
+    if (has_prev) wp = reinterpret_cast<const uint4*>(dprev)[v];
+    const uint32_t ii[4] = {wi.x, wi.y, wi.z, wi.w};
+    const uint32_t oo[4] = {wo.x, wo.y, wo.z, wo.w};
+    const uint32_t pp[4] = {wp.x, wp.y, wp.z, wp.w};
+    uint32_t res[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      uint32_t b0, b1;
+      acc_one(a, bf16_lo(ii[k]), bf16_lo(oo[k]), has_prev, bf16_lo(pp[k]), b0);
+      acc_one(a, bf16_hi(ii[k]), bf16_hi(oo[k]), has_prev, bf16_hi(pp[k]), b1);
+      res[k] = b0 | (b1 << 16);
+    }
+    if (dnew) reinterpret_cast<uint4*>(dnew)[v] = make_uint4(res[0], res[1], res[2], res[3]);
+  }
+  // scalar tail (n % 8 elements), taken by the first workgroup's first lanes
+  if (blockIdx.x == 0 && threadIdx.x < (n & 7)) {
+    const int64_t i = nvec * 8 + threadIdx.x;
+    uint32_t b;
+    const float pv = has_prev ? __uint_as_float((uint32_t)dprev[i] << 16) : 0.0f;
+    acc_one(a, __uint_as_float((uint32_t)in[i] << 16), __uint_as_float((uint32_t)out[i] << 16),
+            has_prev, pv, b);
+    if (dnew) dnew[i] = (uint16_t)b;
+  }
+
+  // workgroup reduction, fixed order
+  __shared__ double red[8][BS_THREADS / 64];
+  double vals[8] = {a.d2, a.i2, a.dd2, a.p2, (double)a.mi, a.si, (double)a.mo, a.so};
+#pragma unroll
+  for (int k = 0; k < 8; ++k) vals[k] = (k == 4 || k == 6) ? wave_max_d(vals[k]) : wave_sum(vals[k]);
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0)
+#pragma unroll
+    for (int k = 0; k < 8; ++k) red[k][w] = vals[k];
+  __syncthreads();
+  if (threadIdx.x < 8) {
+    const int k = threadIdx.x;
+    double r = red[k][0];
+    for (int i = 1; i < BS_THREADS / 64; ++i) r = (k == 4 || k == 6) ? fmax(r, red[k][i]) : r + red[k][i];
+    part[8 * (int64_t)blockIdx.x + k] = r;
+  }
+}
+
+__global__ __launch_bounds__(BS_THREADS) void block_stats_final_kernel(const double* part, int nparts,
+                                                                       double* stats) {
+  __shared__ double red[8][BS_THREADS / 64];
+  double vals[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int i = threadIdx.x; i < nparts; i += BS_THREADS)
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      vals[k] = (k == 4 || k == 6) ? fmax(vals[k], part[8 * i + k]) : vals[k] + part[8 * i + k];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) vals[k] = (k == 4 || k == 6) ? wave_max_d(vals[k]) : wave_sum(vals[k]);
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0)
+#pragma unroll
+    for (int k = 0; k < 8; ++k) red[k][w] = vals[k];
+  __syncthreads();
+  if (threadIdx.x < 8) {
+    const int k = threadIdx.x;
+    double r = red[k][0];
+    for (int i = 1; i < BS_THREADS / 64; ++i) r = (k == 4 || k == 6) ? fmax(r, red[k][i]) : r + red[k][i];
+    stats[k] = r;
+  }
+}
+
+size_t bs_workspace_bytes(int64_t n) { return (size_t)bs_grid(n) * 8 * sizeof(double); }
+
+hipError_t launch_block_stats(const void* in, const void* out, const void* dprev, void* dnew,
+                              int64_t n, double* stats, void* ws, hipStream_t st) {
+  const int grid = bs_grid(n);
+  double* part = static_cast<double*>(ws);
+  hipLaunchKernelGGL(block_stats_kernel, dim3(grid), dim3(BS_THREADS), 0, st,
+                     static_cast<const uint16_t*>(in), static_cast<const uint16_t*>(out),
+                     static_cast<const uint16_t*>(dprev), static_cast<uint16_t*>(dnew), n, part);
+  hipLaunchKernelGGL(block_stats_final_kernel, dim3(1), dim3(BS_THREADS), 0, st, part, grid, stats);
+  return hipGetLastError();
+}
+
+}  // namespace vdtq

@@ -1,0 +1,63 @@
+// Host-side per-block scheduler of 6Bit-Diffusion: dynamic precision (DMPQ),
+// temporal delta cache skips with an error accumulator (TDC), purified delta
+// refresh (PDR) and the INT8 restart rule.
+//
+// gist.science "6Bit-Diffusion: Inference-Time Mixed-Precision Quantization
+// for Video Diffusion Models": §2.A (low Gamma_{t-1} -> NVFP4, high -> INT8),
+// §2.B (skip when Delta_{t-1} and Delta_{t-2} are similar; error-guided
+// switching refreshes the cache), §2.C (outliers or temporal uncertainty force
+// FP16/BF16 before a cache write).  youleyou.com article §三: outlier ratio =
+// max / mean of the input; the first recompute after a skip runs INT8.
+//
+// Pure, deterministic host code: O(1) per block and step.
+#include <math.h>
+
+#include "../../include/vdtq.h"
+
+extern "C" {
+
+void dmpq_state_init(vdtq_dmpq_state* s) {
+  if (!s) return;
+  s->step = 0;
+  s->has_d1 = s->has_d2 = s->skipped_last = s->has_gamma = 0;
+  s->gamma_prev = 0.0;
+  s->r_last = INFINITY;
+  s->acc = 0.0;
+}
+
+double vdtq_outlier_ratio(double max_abs, double sum_abs, int64_t n) {
+  if (sum_abs == 0.0 || n <= 0) return 1.0;
+  return max_abs / (sum_abs / (double)n);
+}
+
+int dmpq_step(const vdtq_dmpq_params* p, vdtq_dmpq_state* s, const double* last_stats, double in_ratio,
+              int* action) {
+  if (!p || !s || !action) return VDTQ_EINVAL;
+  if (last_stats) {
+    // Gamma = ||out - in|| / ||in||; r = ||Dnew - Dprev|| / ||Dprev||
+    const double d2 = last_stats[0], i2 = last_stats[1], dd2 = last_stats[2], p2 = last_stats[3];
+    s->gamma_prev = (i2 == 0.0) ? (d2 == 0.0 ? 0.0 : INFINITY) : sqrt(d2 / i2);
+    s->has_gamma = 1;
+    if (s->has_d1) s->r_last = (p2 == 0.0) ? INFINITY : sqrt(dd2 / p2);
+    s->has_d2 = s->has_d1;
+    s->has_d1 = 1;
+    s->skipped_last = 0;
+    s->acc = 0.0;
+  }
+  const int64_t t = s->step++;
+  if (t >= p->warmup && s->has_d2 && s->r_last < p->tau && s->acc + s->r_last < p->tau_acc) {
+    s->acc += s->r_last;
+    s->skipped_last = 1;
+    *action = VDTQ_ACT_SKIP;
+    return VDTQ_OK;
+  }
+  if (in_ratio > p->rho || (s->has_d2 && s->r_last > p->tau_u))
+    *action = VDTQ_ACT_BF16;
+  else if (s->skipped_last || !s->has_gamma || s->gamma_prev >= p->gamma)
+    *action = VDTQ_ACT_INT8;
+  else
+    *action = VDTQ_ACT_NVFP4;
+  return VDTQ_OK;
+}
+
+}  // extern "C"

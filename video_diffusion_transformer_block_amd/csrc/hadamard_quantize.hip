@@ -1,0 +1,494 @@
+// Online block Hadamard transform + NVFP4 / per-token INT8 quantization of
+// bf16 activations, with the outlier statistics fused in (gfx950).
+//
+// The operation: gist.science "6Bit-Diffusion: Inference-Time Mixed-Precision
+// Quantization for Video Diffusion Models" §2.A (block Hadamard before
+// quantization; NVFP4 for stable blocks, INT8 for volatile ones) and
+// youleyou.com "清华大学6Bit-Diffusion技术..." §一 and §三 (max/mean outlier
+// ratio of the input); fused into one pass as §4 / §四 describe.
+//
+// Design (HBM-bound pass, 2 B/element in, 0.5625 (NVFP4) or 1 (INT8) out):
+//   * A 256-thread workgroup owns 256 "chunks" of 64 consecutive elements of
+//     a row.  The chunks are staged through LDS with fully coalesced 16-byte
+//     loads (a wavefront reads 1 KB contiguous per instruction) and an XOR
+//     swizzle, so that each thread then reads its own 128-byte chunk without
+//     bank conflicts.
+//   * Every thread keeps its 64 values in registers and runs the butterflies
+//     h = 1, 2, ..., min(b, 64)/2 in fp32 with no data exchange; for b = 128
+//     and 256 the remaining stages pair neighbouring lanes with one shuffle.
+//   * A 16-element NVFP4 group lies inside a thread, so group maxima are
+//     register-local.  Each group costs two correctly rounded divisions (the
+//     E4M3 scale and its reciprocal); each element costs one multiply and
+//     half of a hardware E2M1 conversion (v_cvt_scalef32_pk_fp4_f32, whose
+//     power-of-two scale operand also absorbs the 1/sqrt(b) normalisation
+//     when b is a power of four).
+//   * INT8: a workgroup owns whole rows; the row maximum is combined with
+//     LDS atomic max on the float bits (order independent), and rint is the
+//     2^23-magic-number add whose low byte is the two's complement code.
+//   * Statistics: fp32 over a thread's 64 elements, fp64 across threads and
+//     workgroups in a fixed order (bit-reproducible, no float atomics).
+#include <algorithm>
+
+#include "device_common.h"
+#include "launch.h"
+
+namespace vdtq {
+
+constexpr int HQ_THREADS = 256;
+
+struct HQParams {
+  const uint16_t* x;
+  int64_t ldx;
+  int32_t M, K, cpr;          // cpr = chunks of 64 per row = ceil(K / 64)
+  int32_t rows_per_wg;        // INT8: whole rows per workgroup
+  int64_t total_chunks;       // M * cpr
+  double inv_cpr;             // 1 / cpr, for the quotient estimate
+  uint8_t* q;
+  void* scales;
+  float* ts;                  // NVFP4 {amax_T, gs}
+  float* amax_part;           // [grid] partial maxima (amax pre-pass)
+  double* stats_part;         // [grid][4] partial statistics
+  unsigned flags;
+};
+
+__device__ __forceinline__ void divmod_cpr(int64_t g, const HQParams& p, int& row, int& col) {
+  int64_t r = (int64_t)((double)g * p.inv_cpr);
+  int64_t c = g - r * p.cpr;
+  if (c < 0) { --r; c += p.cpr; }
+  if (c >= p.cpr) { ++r; c -= p.cpr; }
+  row = (int)r;
+  col = (int)c;
+}
+
+// ---------------------------------------------------------------- staging
+// Loads the workgroup's 256 chunks into LDS (zeros where the chunk or the
+// 8-element slot lies outside X) and returns this thread's own chunk
+// coordinates.  ROWS: chunks are rows_per_wg whole rows; otherwise the
+// workgroup owns flat chunk ids [256 wg, 256 wg + 256).
+template <bool ROWS>
+__device__ __forceinline__ void stage(const HQParams& p, uint4* lds, int& my_row, int& my_col,
+                                      bool& my_valid) {
+  const int t = threadIdx.x;
+  const int wg = blockIdx.x;
+  const int j = t & 7;
+  int row, col;
+  int c0 = t >> 3;
+  if (ROWS) {
+    divmod_cpr(c0, p, row, col);
+    row += wg * p.rows_per_wg;
+  } else {
+    divmod_cpr((int64_t)wg * HQ_THREADS + c0, p, row, col);
+  }
+  const int chunk_limit = ROWS ? p.rows_per_wg * p.cpr : HQ_THREADS;
+  uint4 buf[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int c = c0 + 32 * i;
+    const int e = col * 64 + 8 * j;
+    const bool ok = (c < chunk_limit) && (row < p.M) && (e < p.K);
+    buf[i] = ok ? *reinterpret_cast<const uint4*>(p.x + (int64_t)row * p.ldx + e)
+                : make_uint4(0u, 0u, 0u, 0u);
+    col += 32;
+    while (col >= p.cpr) { col -= p.cpr; ++row; }
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int c = c0 + 32 * i;
+    lds[c * 8 + (j ^ (c & 7))] = buf[i];
+  }
+  if (ROWS) {
+    divmod_cpr(t, p, my_row, my_col);
+    my_row += wg * p.rows_per_wg;
+    my_valid = (t < chunk_limit) && (my_row < p.M);
+  } else {
+    divmod_cpr((int64_t)wg * HQ_THREADS + t, p, my_row, my_col);
+    my_valid = my_row < p.M;
+  }
+}
+
+// Reads this thread's chunk from LDS and widens bf16 -> fp32.
+__device__ __forceinline__ void load_chunk(const uint4* lds, float (&v)[64]) {
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int jj = 0; jj < 8; ++jj) {
+    uint4 w = lds[t * 8 + (jj ^ (t & 7))];
+    v[8 * jj + 0] = bf16_lo(w.x); v[8 * jj + 1] = bf16_hi(w.x);
+    v[8 * jj + 2] = bf16_lo(w.y); v[8 * jj + 3] = bf16_hi(w.y);
+    v[8 * jj + 4] = bf16_lo(w.z); v[8 * jj + 5] = bf16_hi(w.z);
+    v[8 * jj + 6] = bf16_lo(w.w); v[8 * jj + 7] = bf16_hi(w.w);
+  }
+}
+
+// Butterflies in the fixed order h = 1, 2, ..., b/2 (fp32, RNE).
+template <int B>
+__device__ __forceinline__ void fwht(float (&v)[64]) {
+  constexpr int HIN = B < 64 ? B : 64;
+#pragma unroll
+  for (int h = 1; h < HIN; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 64; ++i) {
+      if ((i & h) == 0) {
+        float a = v[i], b = v[i + h];
+        v[i] = a + b;
+        v[i + h] = a - b;
+      }
+    }
+  }
+  // stages across chunks: h = 64 pairs lanes t, t^1; h = 128 pairs t, t^2.
+  if (B >= 128) {
+    const bool upper = threadIdx.x & 1;
+#pragma unroll
+    for (int i = 0; i < 64; ++i) {
+      float o = __shfl_xor(v[i], 1, 64);
+      v[i] = upper ? (o - v[i]) : (v[i] + o);
+    }
+  }
+  if (B >= 256) {
+    const bool upper = threadIdx.x & 2;
+#pragma unroll
+    for (int i = 0; i < 64; ++i) {
+      float o = __shfl_xor(v[i], 2, 64);
+      v[i] = upper ? (o - v[i]) : (v[i] + o);
+    }
+  }
+}
+
+// Normalisation.  Powers of four keep v unscaled (y = v * 2^-k exactly, the
+// factor is folded downstream); b = 32 / 128 multiply by RN(1/sqrt(b)) here.
+template <int B> struct HadScale;
+template <> struct HadScale<16>  { static constexpr bool pow4 = true;  static constexpr float f = 0.25f;    static constexpr float inv = 4.0f; };
+template <> struct HadScale<64>  { static constexpr bool pow4 = true;  static constexpr float f = 0.125f;   static constexpr float inv = 8.0f; };
+template <> struct HadScale<256> { static constexpr bool pow4 = true;  static constexpr float f = 0.0625f;  static constexpr float inv = 16.0f; };
+// RN_fp32(sqrt 2) = 0x1.6a09e6p+0; 1/sqrt(32) = sqrt(2)/8, 1/sqrt(128) = sqrt(2)/16
+template <> struct HadScale<32>  { static constexpr bool pow4 = false; static constexpr float f = 0x1.6a09e6p-3f; static constexpr float inv = 1.0f; };
+template <> struct HadScale<128> { static constexpr bool pow4 = false; static constexpr float f = 0x1.6a09e6p-4f; static constexpr float inv = 1.0f; };
+
+template <int B>
+__device__ __forceinline__ void normalise(float (&v)[64]) {
+  if (!HadScale<B>::pow4) {
+#pragma unroll
+    for (int i = 0; i < 64; ++i) v[i] = v[i] * HadScale<B>::f;
+  }
+}
+// factor from the register values to y (1 when already applied)
+template <int B>
+__device__ __forceinline__ constexpr float yfac() { return HadScale<B>::pow4 ? HadScale<B>::f : 1.0f; }
+
+// Eight E2M1 codes of RN(v[i] * inv) / sc (sc a power of two, exact), packed
+// low nibble first: the hardware conversion rounds to nearest even,
+// saturates at 6 and keeps the sign of zero.
+__device__ __forceinline__ uint32_t pack8_e2m1(const float* v, float inv, float sc) {
+  uint32_t w = 0u;
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[0] * inv, v[1] * inv, sc, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[2] * inv, v[3] * inv, sc, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[4] * inv, v[5] * inv, sc, 2);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[6] * inv, v[7] * inv, sc, 3);
+  return w;
+}
+
+// ---------------------------------------------------------------- statistics
+__device__ __forceinline__ void input_stats(const float (&v)[64], int nvalid, float& mx, float& sx) {
+  mx = 0.0f;
+  sx = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 64; ++i) {
+    float a = (i < nvalid) ? fabsf(v[i]) : 0.0f;
+    mx = fmaxf(mx, a);
+    sx = sx + a;
+  }
+}
+
+// Sum / max of four per-thread values over the workgroup, fp64, fixed order;
+// thread 0 writes them to part[4].
+__device__ void wg_stats_write(double mx, double sx, double my, double sy, double* part) {
+  __shared__ double red[4][HQ_THREADS / 64];
+  mx = wave_max_d(mx);
+  sx = wave_sum(sx);
+  my = wave_max_d(my);
+  sy = wave_sum(sy);
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) { red[0][w] = mx; red[1][w] = sx; red[2][w] = my; red[3][w] = sy; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double a = red[0][0], b = red[1][0], c = red[2][0], d = red[3][0];
+    for (int i = 1; i < HQ_THREADS / 64; ++i) {
+      a = fmax(a, red[0][i]); b += red[1][i]; c = fmax(c, red[2][i]); d += red[3][i];
+    }
+    part[0] = a; part[1] = b; part[2] = c; part[3] = d;
+  }
+}
+
+// ---------------------------------------------------------------- amax pre-pass
+template <int B>
+__global__ __launch_bounds__(HQ_THREADS) void hq_amax_kernel(HQParams p) {
+  __shared__ uint4 lds[HQ_THREADS * 8];
+  __shared__ float wred[HQ_THREADS / 64];
+  int row, col;
+  bool valid;
+  stage<false>(p, lds, row, col, valid);
+  __syncthreads();
+  float v[64];
+  load_chunk(lds, v);
+  fwht<B>(v);
+  normalise<B>(v);
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 64; ++i) m = fmaxf(m, fabsf(v[i]));   // staged zeros pad the tail
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) wred[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float a = wred[0];
+    for (int i = 1; i < HQ_THREADS / 64; ++i) a = fmaxf(a, wred[i]);
+    p.amax_part[blockIdx.x] = a * yfac<B>();
+  }
+}
+
+// One workgroup: amax_T = max of the partial maxima; writes {amax_T, gs}.
+__global__ __launch_bounds__(256) void hq_amax_final_kernel(const float* part, int n, float* ts) {
+  __shared__ float wred[4];
+  float m = 0.0f;
+  for (int i = threadIdx.x; i < n; i += 256) m = fmaxf(m, part[i]);
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) wred[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float a = fmaxf(fmaxf(wred[0], wred[1]), fmaxf(wred[2], wred[3]));
+    ts[0] = a;
+    ts[1] = nvfp4_gs(a);
+  }
+}
+
+// Writes gs for a caller-supplied amax (used when there are no rows).
+__global__ void hq_gs_only_kernel(float* ts) {
+  if (threadIdx.x == 0) ts[1] = nvfp4_gs(ts[0]);
+}
+
+// Final fp64 reduction of the per-workgroup statistics.
+__global__ __launch_bounds__(256) void hq_stats_final_kernel(const double* part, int n, double* out) {
+  __shared__ double red[4][4];
+  double a = 0.0, b = 0.0, c = 0.0, d = 0.0;
+  for (int i = threadIdx.x; i < n; i += 256) {
+    a = fmax(a, part[4 * i + 0]);
+    b += part[4 * i + 1];
+    c = fmax(c, part[4 * i + 2]);
+    d += part[4 * i + 3];
+  }
+  a = wave_max_d(a); b = wave_sum(b); c = wave_max_d(c); d = wave_sum(d);
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) { red[0][w] = a; red[1][w] = b; red[2][w] = c; red[3][w] = d; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double x0 = red[0][0], x1 = red[1][0], x2 = red[2][0], x3 = red[3][0];
+    for (int i = 1; i < 4; ++i) { x0 = fmax(x0, red[0][i]); x1 += red[1][i]; x2 = fmax(x2, red[2][i]); x3 += red[3][i]; }
+    out[0] = x0; out[1] = x1; out[2] = x2; out[3] = x3;
+  }
+}
+
+// ---------------------------------------------------------------- NVFP4 pass
+template <int B>
+__global__ __launch_bounds__(HQ_THREADS) void hq_nvfp4_kernel(HQParams p) {
+  __shared__ uint4 lds[HQ_THREADS * 8];
+  int row, col;
+  bool valid;
+  stage<false>(p, lds, row, col, valid);
+  __syncthreads();
+  float v[64];
+  load_chunk(lds, v);
+  const int nvalid = valid ? min(64, p.K - col * 64) : 0;
+  const bool want_stats = (p.flags & 2u) != 0;
+  float mx = 0.0f, sx = 0.0f;
+  if (want_stats) input_stats(v, nvalid, mx, sx);
+  fwht<B>(v);
+  normalise<B>(v);
+
+  const float amax = p.ts[0];
+  const bool ok = nvfp4_amax_ok(amax);
+  const float gs = ok ? amax / 2688.0f : 1.0f;
+  const float d = 6.0f * gs;
+  if (blockIdx.x == 0 && threadIdx.x == 0) p.ts[1] = gs;
+
+  uint32_t words[8];
+  uint32_t sbytes = 0;
+  float my = 0.0f, sy = 0.0f;
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    float av = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) av = fmaxf(av, fabsf(v[16 * g + e]));
+    const float ag = av * yfac<B>();                 // exact (power of two)
+    uint32_t s8 = ok ? e4m3_encode_pos(ag / d) : 0u;
+    const float sdec = e4m3_decode_pos(s8) * gs;
+    const bool nz = sdec != 0.0f;
+    const float inv = nz ? 1.0f / sdec : 0.0f;
+    const uint32_t w0 = pack8_e2m1(&v[16 * g], inv, HadScale<B>::inv);
+    const uint32_t w1 = pack8_e2m1(&v[16 * g + 8], inv, HadScale<B>::inv);
+    words[2 * g] = nz ? w0 : 0u;
+    words[2 * g + 1] = nz ? w1 : 0u;
+    sbytes |= s8 << (8 * g);
+    if (want_stats && 16 * g < nvalid) {
+      my = fmaxf(my, ag);
+      float s = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s = s + fabsf(v[16 * g + e]);
+      sy = sy + s * yfac<B>();
+    }
+  }
+
+  if (valid) {
+    uint8_t* qrow = p.q + (int64_t)row * (p.K / 2) + col * 32;
+    uint8_t* srow = reinterpret_cast<uint8_t*>(p.scales) + (int64_t)row * (p.K / 16) + col * 4;
+    if (nvalid == 64 && (p.K % 32) == 0) {
+      reinterpret_cast<uint4*>(qrow)[0] = make_uint4(words[0], words[1], words[2], words[3]);
+      reinterpret_cast<uint4*>(qrow)[1] = make_uint4(words[4], words[5], words[6], words[7]);
+    } else {
+      for (int g = 0; 16 * g < nvalid; ++g)
+        reinterpret_cast<uint2*>(qrow)[g] = make_uint2(words[2 * g], words[2 * g + 1]);
+    }
+    if (nvalid == 64 && (p.K % 64) == 0) {
+      *reinterpret_cast<uint32_t*>(srow) = sbytes;
+    } else {
+      for (int g = 0; 16 * g < nvalid; ++g) srow[g] = (uint8_t)(sbytes >> (8 * g));
+    }
+  }
+  if (want_stats) wg_stats_write(mx, sx, my, sy, p.stats_part + 4 * (int64_t)blockIdx.x);
+}
+
+// ---------------------------------------------------------------- INT8 pass
+template <int B>
+__global__ __launch_bounds__(HQ_THREADS) void hq_int8_kernel(HQParams p) {
+  __shared__ uint4 lds[HQ_THREADS * 8];
+  __shared__ uint32_t rowmax[HQ_THREADS];
+  if (threadIdx.x < p.rows_per_wg) rowmax[threadIdx.x] = 0u;
+  int row, col;
+  bool valid;
+  stage<true>(p, lds, row, col, valid);
+  __syncthreads();
+  float v[64];
+  load_chunk(lds, v);
+  const int nvalid = valid ? min(64, p.K - col * 64) : 0;
+  const bool want_stats = (p.flags & 2u) != 0;
+  float mx = 0.0f, sx = 0.0f;
+  if (want_stats) input_stats(v, nvalid, mx, sx);
+  fwht<B>(v);
+  normalise<B>(v);
+
+  float av = 0.0f, sv = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 64; ++i) av = fmaxf(av, fabsf(v[i]));   // padded slots are 0
+  const float ay = av * yfac<B>();
+  const int rl = row - blockIdx.x * p.rows_per_wg;
+  if (valid) atomicMax(&rowmax[rl], __float_as_uint(ay));
+  __syncthreads();
+  const float a = valid ? __uint_as_float(rowmax[rl]) : 0.0f;
+  const bool ok = (a == a) && a >= kZeroLimit && a <= 3.0e38f;
+  const float s = ok ? a / 127.0f : 0.0f;
+  const float inv = ok ? 1.0f / s : 0.0f;
+  // rint_even(y * inv) with y = v * 2^-k: RN(v * inv) + 1.5 * 2^(23 + k) rounds
+  // at unit 2^k, and the low byte of the sum's bits is the int8 code.
+  constexpr float magic = 12582912.0f * HadScale<B>::inv;
+  uint32_t words[16];
+#pragma unroll
+  for (int w = 0; w < 16; ++w) {
+    uint32_t b0 = __float_as_uint(v[4 * w + 0] * inv + magic);
+    uint32_t b1 = __float_as_uint(v[4 * w + 1] * inv + magic);
+    uint32_t b2 = __float_as_uint(v[4 * w + 2] * inv + magic);
+    uint32_t b3 = __float_as_uint(v[4 * w + 3] * inv + magic);
+    uint32_t lo = __builtin_amdgcn_perm(b1, b0, 0x0c0c0400u);
+    uint32_t hi = __builtin_amdgcn_perm(b3, b2, 0x0c0c0400u);
+    words[w] = ok ? (lo | (hi << 16)) : 0u;
+  }
+  if (valid) {
+    int8_t* qrow = reinterpret_cast<int8_t*>(p.q) + (int64_t)row * p.K + col * 64;
+    for (int g = 0; g < 4; ++g)
+      if (16 * g < nvalid)
+        reinterpret_cast<uint4*>(qrow)[g] =
+            make_uint4(words[4 * g], words[4 * g + 1], words[4 * g + 2], words[4 * g + 3]);
+    if (col == 0) reinterpret_cast<float*>(p.scales)[row] = s;
+  }
+  if (want_stats) {
+    float my = valid ? ay : 0.0f;
+    for (int i = 0; i < 64; ++i) sv = sv + ((i < nvalid) ? fabsf(v[i]) : 0.0f);
+    wg_stats_write(mx, sx, my, (double)(sv * yfac<B>()), p.stats_part + 4 * (int64_t)blockIdx.x);
+  }
+}
+
+// ---------------------------------------------------------------- launcher
+template <int B>
+static hipError_t launch_b(const HQParams& p, int fmt, bool amax_given, int grid, hipStream_t st) {
+  if (fmt == 0) {
+    if (!amax_given) {
+      hipLaunchKernelGGL(hq_amax_kernel<B>, dim3(grid), dim3(HQ_THREADS), 0, st, p);
+      hipLaunchKernelGGL(hq_amax_final_kernel, dim3(1), dim3(256), 0, st, p.amax_part, grid, p.ts);
+    }
+    hipLaunchKernelGGL(hq_nvfp4_kernel<B>, dim3(grid), dim3(HQ_THREADS), 0, st, p);
+  } else {
+    hipLaunchKernelGGL(hq_int8_kernel<B>, dim3(grid), dim3(HQ_THREADS), 0, st, p);
+  }
+  return hipGetLastError();
+}
+
+size_t hq_workspace_bytes(int64_t M, int64_t K) {
+  if (M <= 0 || K <= 0) return 256;
+  const int64_t cpr = (K + 63) / 64;
+  // the largest grid of either format: flat chunks, or one row per group
+  const int64_t grid = std::max<int64_t>((M * cpr + HQ_THREADS - 1) / HQ_THREADS, M);
+  return (size_t)(((grid * 4 + 63) / 64) * 64 + grid * 4 * 8);
+}
+
+hipError_t launch_hadamard_quantize(const void* x, int64_t M, int64_t K, int64_t ldx, int b, int fmt,
+                                    unsigned flags, void* q, void* scales, float* ts,
+                                    double* stats, void* ws, hipStream_t st) {
+  HQParams p{};
+  p.x = static_cast<const uint16_t*>(x);
+  p.ldx = ldx;
+  p.M = (int32_t)M;
+  p.K = (int32_t)K;
+  p.cpr = (int32_t)((K + 63) / 64);
+  p.inv_cpr = 1.0 / (double)p.cpr;
+  p.total_chunks = M * p.cpr;
+  p.q = static_cast<uint8_t*>(q);
+  p.scales = scales;
+  p.ts = ts;
+  p.flags = flags;
+  const bool amax_given = (flags & 1u) != 0;
+  const bool want_stats = (flags & 2u) != 0;
+  int grid;
+  if (fmt == 0) {
+    grid = (int)((p.total_chunks + HQ_THREADS - 1) / HQ_THREADS);
+  } else {
+    p.rows_per_wg = std::max(1, HQ_THREADS / p.cpr);
+    grid = (int)((M + p.rows_per_wg - 1) / p.rows_per_wg);
+  }
+  char* wsb = static_cast<char*>(ws);
+  const int64_t grid_cap = std::max<int64_t>((M * p.cpr + HQ_THREADS - 1) / HQ_THREADS, M);
+  p.amax_part = reinterpret_cast<float*>(wsb);
+  p.stats_part = reinterpret_cast<double*>(wsb + ((grid_cap * 4 + 63) / 64) * 64);
+
+  if (M == 0) {
+    if (fmt == 0) {
+      if (amax_given)
+        hipLaunchKernelGGL(hq_gs_only_kernel, dim3(1), dim3(64), 0, st, ts);
+      else
+        hipLaunchKernelGGL(hq_amax_final_kernel, dim3(1), dim3(256), 0, st, p.amax_part, 0, ts);
+    }
+    if (want_stats) hipLaunchKernelGGL(hq_stats_final_kernel, dim3(1), dim3(256), 0, st, p.stats_part, 0, stats);
+    return hipGetLastError();
+  }
+  hipError_t e;
+  switch (b) {
+    case 16: e = launch_b<16>(p, fmt, amax_given, grid, st); break;
+    case 32: e = launch_b<32>(p, fmt, amax_given, grid, st); break;
+    case 64: e = launch_b<64>(p, fmt, amax_given, grid, st); break;
+    case 128: e = launch_b<128>(p, fmt, amax_given, grid, st); break;
+    default: e = launch_b<256>(p, fmt, amax_given, grid, st); break;
+  }
+  if (e != hipSuccess) return e;
+  if (want_stats) {
+    hipLaunchKernelGGL(hq_stats_final_kernel, dim3(1), dim3(256), 0, st, p.stats_part, grid, stats);
+    e = hipGetLastError();
+  }
+  return e;
+}
+
+}  // namespace vdtq

@@ -1,0 +1,25 @@
+// Host-side launchers of the gfx950 kernels (one per translation unit); the
+// C ABI in api.cpp validates every argument before calling them.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace vdtq {
+
+size_t hq_workspace_bytes(int64_t M, int64_t K);
+hipError_t launch_hadamard_quantize(const void* x, int64_t M, int64_t K, int64_t ldx, int b, int fmt,
+                                    unsigned flags, void* q, void* scales, float* ts,
+                                    double* stats, void* ws, hipStream_t st);
+
+hipError_t launch_qgemm(int afmt, const void* a_q, const void* a_s, const float* a_ts,
+                        const uint8_t* w_q, const uint8_t* w_s, const float* w_ts,
+                        const float* bias, void* y, int64_t ldy, int out_dtype, int64_t M,
+                        int64_t N, int64_t K, hipStream_t st);
+
+size_t bs_workspace_bytes(int64_t n);
+hipError_t launch_block_stats(const void* in, const void* out, const void* dprev, void* dnew,
+                              int64_t n, double* stats, void* ws, hipStream_t st);
+
+}  // namespace vdtq

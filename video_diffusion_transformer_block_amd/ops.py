@@ -1,0 +1,173 @@
+"""Torch-facing binding of the C ABI: the same five calls, argument
+marshalling only.  torch provides device memory and the current HIP stream;
+every step of the computation runs in libvdtq.so."""
+from __future__ import annotations
+
+import ctypes
+import math
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+from . import _lib as L
+
+
+def _p(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(dev: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _require(t: torch.Tensor, dtype, name: str):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+_ws = {}
+
+
+def workspace(device: torch.device, nbytes: int) -> torch.Tensor:
+    """A per-device scratch buffer reused by every call on that device (calls
+    on one stream run in order; do not share it across concurrent streams)."""
+    key = torch.device(device).index
+    buf = _ws.get(key)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.empty(max(nbytes, 4096), dtype=torch.uint8, device=device)
+        _ws[key] = buf
+    return buf
+
+
+@dataclass
+class NVFP4Tensor:
+    """Packed codes [R, K/2] u8, E4M3 scales [R, K/16] u8, {amax, gs} f32[2]."""
+    q: torch.Tensor
+    scales: torch.Tensor
+    ts: torch.Tensor
+    stats: Optional[torch.Tensor] = None
+
+
+@dataclass
+class INT8Tensor:
+    """Codes [M, K] int8 and per-row fp32 scales [M]."""
+    q: torch.Tensor
+    scales: torch.Tensor
+    stats: Optional[torch.Tensor] = None
+
+
+def hadamard_quantize(x: torch.Tensor, had_block: int = 64, fmt: str = "nvfp4", amax=None,
+                      stats: bool = False):
+    """Block Hadamard transform of bf16 rows + NVFP4 or INT8 quantization.
+    amax (NVFP4 only): a float or a 1-element device tensor to use as the
+    tensor amax instead of computing it."""
+    _require(x, torch.bfloat16, "x")
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be a 2-D tensor with unit column stride")
+    M, K = x.shape
+    dev = x.device
+    flags = L.STATS if stats else 0
+    st = torch.zeros(4, dtype=torch.float64, device=dev) if stats else None
+    nbytes = L.lib().vdtq_workspace_bytes(L.OP_HADAMARD_QUANTIZE, M, K)
+    ws = workspace(dev, nbytes)
+    if fmt == "nvfp4":
+        q = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+        s = torch.empty((M, K // 16), dtype=torch.uint8, device=dev)
+        ts = torch.zeros(2, dtype=torch.float32, device=dev)
+        if amax is not None:
+            flags |= L.AMAX_GIVEN
+            ts[0] = amax if not torch.is_tensor(amax) else amax.reshape(-1)[0]
+        fcode = L.FMT_NVFP4
+    elif fmt == "int8":
+        if amax is not None:
+            raise ValueError("amax applies to nvfp4 only")
+        q = torch.empty((M, K), dtype=torch.int8, device=dev)
+        s = torch.empty((M,), dtype=torch.float32, device=dev)
+        ts = None
+        fcode = L.FMT_INT8
+    else:
+        raise ValueError(fmt)
+    L.check(L.lib().hadamard_quantize(_p(x), M, K, x.stride(0), had_block, fcode, flags, _p(q), _p(s),
+                                      _p(ts), _p(st), _p(ws), ws.numel(), _stream(dev)))
+    if fcode == L.FMT_NVFP4:
+        return NVFP4Tensor(q, s, ts, st)
+    return INT8Tensor(q, s, st)
+
+
+def _out(M, N, out_dtype, dev, y):
+    if y is not None:
+        return y
+    return torch.empty((M, N), dtype=torch.bfloat16 if out_dtype == "bf16" else torch.float32, device=dev)
+
+
+def qgemm_w4a4(a: NVFP4Tensor, w: NVFP4Tensor, bias: Optional[torch.Tensor] = None,
+               out_dtype: str = "bf16", y: Optional[torch.Tensor] = None) -> torch.Tensor:
+    M, K = a.q.shape[0], a.q.shape[1] * 2
+    N = w.q.shape[0]
+    if w.q.shape[1] * 2 != K:
+        raise ValueError("K mismatch between activations and weights")
+    y = _out(M, N, out_dtype, a.q.device, y)
+    L.check(L.lib().qgemm_w4a4(_p(a.q), _p(a.scales), _p(a.ts), _p(w.q), _p(w.scales), _p(w.ts), _p(bias),
+                               _p(y), y.stride(0), L.OUT_BF16 if out_dtype == "bf16" else L.OUT_F32,
+                               M, N, K, _stream(a.q.device)))
+    return y
+
+
+def qgemm_w4a8(a: INT8Tensor, w: NVFP4Tensor, bias: Optional[torch.Tensor] = None,
+               out_dtype: str = "bf16", y: Optional[torch.Tensor] = None) -> torch.Tensor:
+    M, K = a.q.shape
+    N = w.q.shape[0]
+    if w.q.shape[1] * 2 != K:
+        raise ValueError("K mismatch between activations and weights")
+    y = _out(M, N, out_dtype, a.q.device, y)
+    L.check(L.lib().qgemm_w4a8(_p(a.q), _p(a.scales), _p(w.q), _p(w.scales), _p(w.ts), _p(bias),
+                               _p(y), y.stride(0), L.OUT_BF16 if out_dtype == "bf16" else L.OUT_F32,
+                               M, N, K, _stream(a.q.device)))
+    return y
+
+
+def block_stats(inp: torch.Tensor, out: torch.Tensor, dprev: Optional[torch.Tensor] = None,
+                dnew: Optional[torch.Tensor] = None, write_delta: bool = True):
+    """Returns (dnew or None, stats f64[8] device tensor)."""
+    _require(inp, torch.bfloat16, "inp")
+    _require(out, torch.bfloat16, "out")
+    if inp.shape != out.shape or not inp.is_contiguous() or not out.is_contiguous():
+        raise ValueError("inp/out must be contiguous tensors of one shape")
+    n = inp.numel()
+    dev = inp.device
+    if dnew is None and write_delta:
+        dnew = torch.empty_like(inp)
+    st = torch.empty(8, dtype=torch.float64, device=dev)
+    ws = workspace(dev, L.lib().vdtq_workspace_bytes(L.OP_BLOCK_STATS, n, 1))
+    L.check(L.lib().block_stats(_p(inp), _p(out), _p(dprev), _p(dnew), n, _p(st), _p(ws), ws.numel(),
+                                _stream(dev)))
+    return dnew, st
+
+
+def dmpq_params(gamma=0.1, tau=0.05, tau_acc=0.15, rho=50.0, tau_u=math.inf, warmup=2) -> L.DmpqParams:
+    return L.DmpqParams(gamma, tau, tau_acc, rho, tau_u, warmup, 0)
+
+
+def dmpq_state() -> L.DmpqState:
+    s = L.DmpqState()
+    L.lib().dmpq_state_init(ctypes.byref(s))
+    return s
+
+
+def dmpq_step(params: L.DmpqParams, state: L.DmpqState, last_stats, in_ratio: float) -> int:
+    """Host call.  last_stats: 8 floats (host) or None.  Returns VDTQ_ACT_*."""
+    act = ctypes.c_int(-1)
+    ptr = None
+    if last_stats is not None:
+        arr = (ctypes.c_double * 8)(*[float(v) for v in last_stats])
+        ptr = ctypes.cast(arr, ctypes.POINTER(ctypes.c_double))
+    L.check(L.lib().dmpq_step(ctypes.byref(params), ctypes.byref(state), ptr, float(in_ratio),
+                              ctypes.byref(act)))
+    return act.value
+
+
+def outlier_ratio(max_abs: float, sum_abs: float, n: int) -> float:
+    return L.lib().vdtq_outlier_ratio(float(max_abs), float(sum_abs), int(n))
