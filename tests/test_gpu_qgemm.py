@@ -115,6 +115,30 @@ def test_w4a4_unit_scale_exact_products():
     assert np.array_equal(y.cpu().numpy().astype(np.float64), want)
 
 
+@pytest.mark.parametrize("lo,hi", [(0x01, 0x08), (0x00, 0x7F)])
+def test_w4a4_full_scale_range_exact(lo, hi):
+    """Scale bytes over the subnormal E4M3 range (and the whole range): the
+    decoded operands are exact, so with sums that fit fp32 the result is
+    bit-exact; over the whole range it agrees to fp32 accumulation."""
+    need_gpu()
+    M, N, K = 64, 96, 256
+    ac = RNG.integers(0, 16, size=(M, K)).astype(np.uint8)
+    wc = RNG.integers(0, 16, size=(N, K)).astype(np.uint8)
+    as_ = RNG.integers(lo, hi, size=(M, K // 16)).astype(np.uint8)
+    ws = RNG.integers(lo, hi, size=(N, K // 16)).astype(np.uint8)
+    a = nvfp4_dev(F.pack_nibbles(ac), as_, [2688.0, 1.0])
+    w = nvfp4_dev(F.pack_nibbles(wc), ws, [2688.0, 1.0])
+    y = V.qgemm_w4a4(a, w, None, "f32")
+    torch.cuda.synchronize()
+    want, _ = G.qgemm_w4a4(F.pack_nibbles(ac), as_, 1.0, F.pack_nibbles(wc), ws, 1.0, None, "f32")
+    got = y.cpu().numpy().astype(np.float64)
+    if hi <= 0x08:
+        # products are multiples of 2^-20 below 2^-7: sums of 256 are exact
+        assert np.array_equal(got, want)
+    else:
+        assert rel_fro(got, want) < 1e-6
+
+
 @pytest.mark.parametrize("name", ["qkv", "out", "ffn_up", "ffn_down"])
 def test_cogvideox_5b_linears_sampled(name):
     need_gpu()

@@ -98,10 +98,11 @@ static int qgemm_check(const char* name, const void* a_q, const void* a_s, const
   if (ldy < N) return fail(VDTQ_EINVAL, "%s: ldy=%lld < N=%lld", name, (long long)ldy, (long long)N);
   if (M == 0 || N == 0) return VDTQ_OK;
   if (!a_q || !a_s || !w_q || !w_s || !w_ts || !y) return fail(VDTQ_EINVAL, "%s: null pointer argument", name);
-  if (!aligned(a_q, 16) || !aligned(w_q, 16) || !aligned(w_ts, 4) || !aligned(y, out_dtype ? 4 : 2) ||
-      (bias && !aligned(bias, 4)))
-    return fail(VDTQ_EINVAL, "%s: misaligned pointer (codes need 16 bytes)", name);
-  if ((M + 127) / 128 > 65535) return fail(VDTQ_EUNSUPPORTED, "%s: M=%lld too large", name, (long long)M);
+  if (!aligned(a_q, 16) || !aligned(w_q, 16) || !aligned(w_s, 8) || !aligned(w_ts, 4) ||
+      !aligned(y, out_dtype ? 4 : 2) || (bias && !aligned(bias, 4)))
+    return fail(VDTQ_EINVAL, "%s: misaligned pointer (codes need 16 bytes, scales 8)", name);
+  if (((M + 255) / 256) * ((N + 255) / 256) > kI32)
+    return fail(VDTQ_EUNSUPPORTED, "%s: too many output tiles", name);
   return VDTQ_OK;
 }
 
@@ -111,8 +112,8 @@ int qgemm_w4a4(const uint8_t* a_q_dev, const uint8_t* a_s_dev, const float* a_ts
   int rc = qgemm_check("qgemm_w4a4", a_q_dev, a_s_dev, w_q_dev, w_s_dev, w_ts_dev, bias_dev, y_dev, ldy,
                        out_dtype, M, N, K);
   if (rc) return rc;
-  if (M > 0 && N > 0 && (!a_ts_dev || !aligned(a_ts_dev, 4)))
-    return fail(VDTQ_EINVAL, "qgemm_w4a4: null or misaligned a_ts");
+  if (M > 0 && N > 0 && (!a_ts_dev || !aligned(a_ts_dev, 4) || !aligned(a_s_dev, 8)))
+    return fail(VDTQ_EINVAL, "qgemm_w4a4: null or misaligned a_ts / a_s");
   hipError_t e = vdtq::launch_qgemm(0, a_q_dev, a_s_dev, a_ts_dev, w_q_dev, w_s_dev, w_ts_dev, bias_dev, y_dev,
                                     ldy, out_dtype, M, N, K, static_cast<hipStream_t>(stream));
   return hip_status(e, "qgemm_w4a4 launch");

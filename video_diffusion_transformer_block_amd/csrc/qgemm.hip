@@ -15,21 +15,39 @@
 // tensor / token scales applied in the epilogue.  For W4A8 with unit weight
 // scales the fp32 accumulator holds the integer sum exactly (< 2^24).
 //
-// Tiling: 256 threads = 4 wavefronts in a 2 x 2 arrangement, a 128 x 128
-// output tile per workgroup, 64 x 64 per wavefront (2 x 2 MFMA 32x32 tiles),
-// K consumed 64 at a time.  Each thread loads 32 packed elements of one row of
-// A and of W, decodes them (hardware fp4 -> f16 conversion, then one packed
-// f16 multiply by the group scale; int8 -> f16 by the 0x6400 bias trick) and
-// writes them to LDS, from where the wavefronts read MFMA fragments with
-// 16-byte LDS reads.
+// Data flow (one workgroup = 4 wavefronts, 2 x 2; tile BM x BN, K in stages
+// of 128):
+//   global -> registers -> LDS   the operands stay packed (4-bit codes,
+//                                E4M3 scale bytes, int8 codes): 16-byte loads,
+//                                64 / 128 contiguous bytes per row and stage,
+//                                written to LDS with an XOR swizzle so that
+//                                the fragment reads below are conflict free;
+//                                double buffered, one barrier per stage.
+//   LDS -> MFMA fragments        each lane reads 32 codes of one row (one
+//                                16-byte read) and the two scale bytes, and
+//                                decodes them itself: the hardware fp4->f16
+//                                conversion (power-of-two scale 2^8 folded in)
+//                                and one packed f16 multiply by the scale
+//                                whose bits are the E4M3 byte shifted into an
+//                                fp16 (= scale * 2^-8); int8 -> f16 by the
+//                                0x6400 bias trick.  Decoding costs about one
+//                                VALU op per element per wavefront and runs
+//                                beside the MFMAs.
+//   K order inside a stage       lane half h and chunk c cover k = 64c + 32h
+//                                .. +32; step s of a chunk takes 8 of them.
+//                                A and W use the same map, so each MFMA sums
+//                                matching k and the stage covers all 128.
+//   tile order                   workgroups are dealt round-robin to the 8
+//                                XCDs; each XCD gets a contiguous range of
+//                                tile ids, walked in groups of 8 M-tiles, so
+//                                the A and W stripes it needs stay in its L2.
 #include "device_common.h"
 #include "launch.h"
 
 namespace vdtq {
 
-constexpr int GT = 256;          // threads
-constexpr int BM = 128, BN = 128, BK = 64;
-constexpr int LDSK = BK + 8;     // padded row (halves): 144 B, conflict-free 16-B reads
+constexpr int GT = 256;     // threads per workgroup
+constexpr int BK = 128;     // K per stage
 
 struct GemmParams {
   const void* a_q;
@@ -43,150 +61,285 @@ struct GemmParams {
   int64_t ldy;
   int32_t M, N, K;
   int32_t out_f32;
+  int32_t tiles_m, tiles_n;
 };
 
-// e4m3 byte -> fp16 pair (exact: e4m3 values lie in fp16's range)
-__device__ __forceinline__ half2v scale_pair(uint32_t s8) {
-  _Float16 h = (_Float16)e4m3_decode_pos(s8);
-  return half2v{h, h};
+// --------------------------------------------------------------- decoding
+// E4M3 byte pair -> fp16 pair holding scale * 2^-8 each: the 7 magnitude bits
+// eeeemmm placed at fp16 bits 13..7 give exponent eeee (bias 15 instead of 7)
+// and mantissa mmm, for normal and subnormal E4M3 alike.
+__device__ __forceinline__ uint32_t scale_pair_bits(uint32_t s2) {
+  return ((s2 & 0x7Fu) << 7) | ((s2 & 0x7F00u) << 15);
 }
 
-// 8 e2m1 codes (one dword) * fp16 scale -> 8 halves (exact products)
-__device__ __forceinline__ void dec_fp4x8(uint32_t w, half2v s, half2v* out) {
-  out[0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s;
-  out[1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s;
-  out[2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s;
-  out[3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s;
+// 8 e2m1 codes -> 8 halves = e2m1 * 2^8 * (scale * 2^-8), exact.
+__device__ __forceinline__ half8 dec_fp4x8(uint32_t w, half2v sc) {
+  half2v p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 0) * sc;
+  half2v p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 1) * sc;
+  half2v p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 2) * sc;
+  half2v p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 3) * sc;
+  return half8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
-// 4 int8 (one dword) -> 4 halves: fp16 0x6400 | (b ^ 0x80) is 1024 + b + 128
-__device__ __forceinline__ void dec_i8x4(uint32_t w, half2v* out) {
-  const uint32_t x = w ^ 0x80808080u;
-  const uint32_t lo = __builtin_amdgcn_perm(0x64646464u, x, 0x04010400u);
-  const uint32_t hi = __builtin_amdgcn_perm(0x64646464u, x, 0x04030402u);
+// 8 int8 (two dwords) -> 8 halves: fp16 0x6400 | (b ^ 0x80) is 1152 + b.
+__device__ __forceinline__ half8 dec_i8x8(uint32_t w0, uint32_t w1) {
   const half2v bias = {(_Float16)1152.0f, (_Float16)1152.0f};
-  out[0] = __builtin_bit_cast(half2v, lo) - bias;
-  out[1] = __builtin_bit_cast(half2v, hi) - bias;
+  const uint32_t x0 = w0 ^ 0x80808080u, x1 = w1 ^ 0x80808080u;
+  half2v p0 = __builtin_bit_cast(half2v, __builtin_amdgcn_perm(0x64646464u, x0, 0x04010400u)) - bias;
+  half2v p1 = __builtin_bit_cast(half2v, __builtin_amdgcn_perm(0x64646464u, x0, 0x04030402u)) - bias;
+  half2v p2 = __builtin_bit_cast(half2v, __builtin_amdgcn_perm(0x64646464u, x1, 0x04010400u)) - bias;
+  half2v p3 = __builtin_bit_cast(half2v, __builtin_amdgcn_perm(0x64646464u, x1, 0x04030402u)) - bias;
+  return half8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
-// Loads and decodes 32 consecutive NVFP4 elements (k0 .. k0+31) of one row.
-__device__ __forceinline__ void load_dec_fp4_row(const uint8_t* q, const uint8_t* s, int64_t row,
-                                                 int K, int k0, half2v (&h)[16]) {
-  const uint8_t* qr = q + row * (K / 2) + k0 / 2;
-  const uint8_t* sr = s + row * (K / 16) + k0 / 16;
-  uint4 w = make_uint4(0u, 0u, 0u, 0u);
-  uint32_t s0 = 0u, s1 = 0u;
-  if (k0 + 32 <= K) {
-    if ((K & 31) == 0) {
-      w = *reinterpret_cast<const uint4*>(qr);
-    } else {   // rows of K/2 bytes are only 8-byte aligned
-      uint2 a = reinterpret_cast<const uint2*>(qr)[0], b = reinterpret_cast<const uint2*>(qr)[1];
-      w = make_uint4(a.x, a.y, b.x, b.y);
+// --------------------------------------------------------------- LDS layout
+// NVFP4 rows: 64 bytes per stage = quads q = 0..3 (q = 2c + h), stored at
+// quad position q ^ ((row >> 1) & 3).  INT8 rows: 128 bytes = quads 0..7,
+// stored at q ^ (row & 7).  Scales: 8 bytes per row and stage, unswizzled.
+__device__ __forceinline__ int fp4_quad_off(int row, int q) { return row * 64 + 16 * (q ^ ((row >> 1) & 3)); }
+__device__ __forceinline__ int i8_quad_off(int row, int q) { return row * 128 + 16 * (q ^ (row & 7)); }
+
+// One stage of packed operand rows: `rows` rows from `row0` (clamped to the
+// last valid row), K columns k0 .. k0+127 (zero past K).
+template <int ROWS, bool INT8>
+struct StageLoader {
+  static constexpr int QPR = INT8 ? 8 : 4;                 // 16-byte quads per row
+  static constexpr int NQ = ROWS * QPR / GT;               // quads per thread
+  static constexpr int SB = INT8 ? 0 : ROWS * 8 / GT;      // scale bytes per thread
+  static constexpr int SW = SB > 0 ? (SB + 3) / 4 : 1;     // scale dwords per thread
+  uint4 q[NQ];
+  uint32_t s[SW];
+
+  __device__ __forceinline__ void load(const uint8_t* codes, const uint8_t* scales, int row0, int nrows,
+                                       int K, int k0) {
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int u = 0; u < NQ; ++u) {
+      const int G = t + GT * u;
+      const int r = G / QPR, qq = G % QPR;
+      const int64_t row = min(row0 + r, nrows - 1);
+      // first element of this quad, and how many of its 16-element groups are in K
+      const int kq = k0 + (INT8 ? 16 : 32) * qq;
+      const int ngroups = INT8 ? (kq < K ? 1 : 0) : (kq + 32 <= K ? 2 : (kq < K ? 1 : 0));
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (INT8) {
+        if (ngroups) v = *reinterpret_cast<const uint4*>(codes + row * K + kq);
+      } else {
+        const uint8_t* p = codes + row * (K / 2) + kq / 2;
+        if (ngroups == 2) {
+          if ((K & 31) == 0) {
+            v = *reinterpret_cast<const uint4*>(p);
+          } else {
+            uint2 a = reinterpret_cast<const uint2*>(p)[0], b = reinterpret_cast<const uint2*>(p)[1];
+            v = make_uint4(a.x, a.y, b.x, b.y);
+          }
+        } else if (ngroups == 1) {
+          uint2 a = *reinterpret_cast<const uint2*>(p);
+          v = make_uint4(a.x, a.y, 0u, 0u);
+        }
+      }
+      q[u] = v;
     }
-    s0 = sr[0];
-    s1 = sr[1];
-  } else if (k0 + 16 <= K) {
-    uint2 w2 = *reinterpret_cast<const uint2*>(qr);
-    w.x = w2.x;
-    w.y = w2.y;
-    s0 = sr[0];
+    if constexpr (!INT8) {
+      // SB bytes per thread: thread t covers row (t*SB)/8, bytes (t*SB)%8 ..
+      const int b0 = t * SB;
+      const int r = b0 / 8, j0 = b0 % 8;
+      const int64_t row = min(row0 + r, nrows - 1);
+      const int kg = k0 / 16 + j0;                 // first group index
+      const uint8_t* p = scales + row * (K / 16) + kg;
+      uint32_t w[SW];
+#pragma unroll
+      for (int i = 0; i < SW; ++i) w[i] = 0u;
+      if ((K % 128) == 0 && kg + SB <= K / 16) {
+        if constexpr (SB == 8) {
+          uint2 a = *reinterpret_cast<const uint2*>(p);
+          w[0] = a.x;
+          w[1] = a.y;
+        } else {
+          w[0] = *reinterpret_cast<const uint32_t*>(p);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < SB; ++i)
+          if (kg + i < K / 16) w[i / 4] |= (uint32_t)p[i] << (8 * (i % 4));
+      }
+#pragma unroll
+      for (int i = 0; i < SW; ++i) s[i] = w[i];
+    }
   }
-  const half2v sc0 = scale_pair(s0), sc1 = scale_pair(s1);
-  dec_fp4x8(w.x, sc0, &h[0]);
-  dec_fp4x8(w.y, sc0, &h[4]);
-  dec_fp4x8(w.z, sc1, &h[8]);
-  dec_fp4x8(w.w, sc1, &h[12]);
+
+  __device__ __forceinline__ void store(uint8_t* lds_codes, uint8_t* lds_scales) const {
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int u = 0; u < NQ; ++u) {
+      const int G = t + GT * u;
+      const int r = G / QPR, qq = G % QPR;
+      const int off = INT8 ? i8_quad_off(r, qq) : fp4_quad_off(r, qq);
+      *reinterpret_cast<uint4*>(lds_codes + off) = q[u];
+    }
+    if constexpr (!INT8) {
+      if constexpr (SB == 8)
+        *reinterpret_cast<uint2*>(lds_scales + t * 8) = make_uint2(s[0], s[1]);
+      else
+        *reinterpret_cast<uint32_t*>(lds_scales + t * 4) = s[0];
+    }
+  }
+};
+
+template <int AFMT, int TI, int TJ>
+struct Cfg {
+  static constexpr int BM = 64 * TI, BN = 64 * TJ;
+  static constexpr bool A8 = AFMT == 1;
+  static constexpr int A_CODES = BM * (A8 ? 128 : 64);
+  static constexpr int A_SC = A8 ? 0 : BM * 8;
+  static constexpr int W_CODES = BN * 64;
+  static constexpr int W_SC = BN * 8;
+  static constexpr int STAGE = A_CODES + A_SC + W_CODES + W_SC;
+};
+
+// Tile coordinates: XCD-contiguous ranges, grouped by 8 M-tiles.
+__device__ __forceinline__ void tile_of(int bid, int nblocks, int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int xcd = bid % 8, idx = bid / 8;
+  const int base = nblocks / 8, rem = nblocks % 8;
+  const int id = xcd * base + min(xcd, rem) + idx;
+  constexpr int GM = 8;
+  const int per_group = GM * tiles_n;
+  const int g = id / per_group;
+  const int first_m = g * GM;
+  const int gsz = min(tiles_m - first_m, GM);
+  const int in = id - g * per_group;
+  tm = first_m + in % gsz;
+  tn = in / gsz;
 }
 
-__device__ __forceinline__ void load_dec_i8_row(const int8_t* q, int64_t row, int K, int k0,
-                                                half2v (&h)[16]) {
-  const int8_t* qr = q + row * K + k0;
-  uint4 a = make_uint4(0u, 0u, 0u, 0u), b = make_uint4(0u, 0u, 0u, 0u);
-  if (k0 + 16 <= K) a = *reinterpret_cast<const uint4*>(qr);
-  if (k0 + 32 <= K) b = *reinterpret_cast<const uint4*>(qr + 16);
-  dec_i8x4(a.x, &h[0]); dec_i8x4(a.y, &h[2]); dec_i8x4(a.z, &h[4]); dec_i8x4(a.w, &h[6]);
-  dec_i8x4(b.x, &h[8]); dec_i8x4(b.y, &h[10]); dec_i8x4(b.z, &h[12]); dec_i8x4(b.w, &h[14]);
-}
-
-template <int AFMT>
-__global__ __launch_bounds__(GT) void qgemm_kernel(GemmParams p) {
-  __shared__ __attribute__((aligned(16))) _Float16 As[BM * LDSK];
-  __shared__ __attribute__((aligned(16))) _Float16 Ws[BN * LDSK];
+template <int AFMT, int TI, int TJ>
+__global__ __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void qgemm_kernel(GemmParams p) {
+  using C = Cfg<AFMT, TI, TJ>;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wv = t >> 6;
   const int wm = wv >> 1, wn = wv & 1;
-  const int m0 = blockIdx.y * BM;
-  const int n0 = blockIdx.x * BN;
+  int tm, tn;
+  tile_of(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, tm, tn);
+  const int m0 = tm * C::BM, n0 = tn * C::BN;
 
-  // loader role: row r of the tile, k half kh
-  const int r = t >> 1, kh = t & 1;
-  const int64_t arow = min(m0 + r, p.M - 1);   // clamped; rows >= M never stored
-  const int64_t wrow = min(n0 + r, p.N - 1);
+  StageLoader<C::BM, C::A8> la;
+  StageLoader<C::BN, false> lw;
 
-  float16v acc[2][2];
+  float16v acc[TI][TJ];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < TI; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < TJ; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-  for (int k0 = 0; k0 < p.K; k0 += BK) {
-    half2v ha[16], hw[16];
-    const int kk = k0 + 32 * kh;
-    if (AFMT == 0)
-      load_dec_fp4_row(static_cast<const uint8_t*>(p.a_q), static_cast<const uint8_t*>(p.a_s), arow,
-                       p.K, kk, ha);
-    else
-      load_dec_i8_row(static_cast<const int8_t*>(p.a_q), arow, p.K, kk, ha);
-    load_dec_fp4_row(p.w_q, p.w_s, wrow, p.K, kk, hw);
+  const uint8_t* aq = static_cast<const uint8_t*>(p.a_q);
+  const uint8_t* as = static_cast<const uint8_t*>(p.a_s);
+  const int nk = (p.K + BK - 1) / BK;
 
-    __syncthreads();   // previous iteration's fragment reads are done
-    uint4* adst = reinterpret_cast<uint4*>(&As[r * LDSK + 32 * kh]);
-    uint4* wdst = reinterpret_cast<uint4*>(&Ws[r * LDSK + 32 * kh]);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      adst[i] = __builtin_bit_cast(uint4, half8{ha[4 * i][0], ha[4 * i][1], ha[4 * i + 1][0], ha[4 * i + 1][1],
-                                                ha[4 * i + 2][0], ha[4 * i + 2][1], ha[4 * i + 3][0], ha[4 * i + 3][1]});
-      wdst[i] = __builtin_bit_cast(uint4, half8{hw[4 * i][0], hw[4 * i][1], hw[4 * i + 1][0], hw[4 * i + 1][1],
-                                                hw[4 * i + 2][0], hw[4 * i + 2][1], hw[4 * i + 3][0], hw[4 * i + 3][1]});
+  auto stage_ptr = [&](int buf) { return smem + buf * C::STAGE; };
+
+  la.load(aq, as, m0, p.M, p.K, 0);
+  lw.load(p.w_q, p.w_s, n0, p.N, p.K, 0);
+  {
+    uint8_t* s0 = stage_ptr(0);
+    la.store(s0, s0 + C::A_CODES);
+    lw.store(s0 + C::A_CODES + C::A_SC, s0 + C::A_CODES + C::A_SC + C::W_CODES);
+  }
+  __syncthreads();
+
+  const int r32 = lane & 31, h = lane >> 5;
+  for (int kt = 0; kt < nk; ++kt) {
+    if (kt + 1 < nk) {
+      la.load(aq, as, m0, p.M, p.K, (kt + 1) * BK);
+      lw.load(p.w_q, p.w_s, n0, p.N, p.K, (kt + 1) * BK);
     }
-    __syncthreads();
-
+    const uint8_t* st = stage_ptr(kt & 1);
+    const uint8_t* a_codes = st;
+    const uint8_t* a_sc = st + C::A_CODES;
+    const uint8_t* w_codes = st + C::A_CODES + C::A_SC;
+    const uint8_t* w_sc = w_codes + C::W_CODES;
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      half8 af[2], bf[2];
+    for (int c = 0; c < 2; ++c) {
+      const int qd = 2 * c + h;
+      uint4 araw[TI][C::A8 ? 2 : 1];
+      uint32_t asc[TI];
+      uint4 wraw[TJ];
+      uint32_t wsc[TJ];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        af[i] = *reinterpret_cast<const half8*>(
-            &As[(wm * 64 + 32 * i + (lane & 31)) * LDSK + 16 * ks + 8 * (lane >> 5)]);
-        bf[i] = *reinterpret_cast<const half8*>(
-            &Ws[(wn * 64 + 32 * i + (lane & 31)) * LDSK + 16 * ks + 8 * (lane >> 5)]);
+      for (int i = 0; i < TI; ++i) {
+        const int row = wm * 32 * TI + 32 * i + r32;
+        if (C::A8) {
+          araw[i][0] = *reinterpret_cast<const uint4*>(a_codes + i8_quad_off(row, 2 * qd));
+          araw[i][C::A8 ? 1 : 0] = *reinterpret_cast<const uint4*>(a_codes + i8_quad_off(row, 2 * qd + 1));
+          asc[i] = 0u;
+        } else {
+          araw[i][0] = *reinterpret_cast<const uint4*>(a_codes + fp4_quad_off(row, qd));
+          asc[i] = scale_pair_bits(*reinterpret_cast<const uint16_t*>(a_sc + row * 8 + 4 * c + 2 * h));
+        }
       }
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int j = 0; j < TJ; ++j) {
+        const int row = wn * 32 * TJ + 32 * j + r32;
+        wraw[j] = *reinterpret_cast<const uint4*>(w_codes + fp4_quad_off(row, qd));
+        wsc[j] = scale_pair_bits(*reinterpret_cast<const uint16_t*>(w_sc + row * 8 + 4 * c + 2 * h));
+      }
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+      for (int s = 0; s < 4; ++s) {
+        half8 af[TI], bf[TJ];
+#pragma unroll
+        for (int i = 0; i < TI; ++i) {
+          if (C::A8) {
+            const uint4& v = araw[i][s >> 1];
+            af[i] = (s & 1) ? dec_i8x8(v.z, v.w) : dec_i8x8(v.x, v.y);
+          } else {
+            const half2v sp = __builtin_bit_cast(half2v, asc[i]);
+            const half2v sc = (s < 2) ? half2v{sp[0], sp[0]} : half2v{sp[1], sp[1]};
+            const uint32_t w = s == 0 ? araw[i][0].x : s == 1 ? araw[i][0].y : s == 2 ? araw[i][0].z : araw[i][0].w;
+            af[i] = dec_fp4x8(w, sc);
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) {
+          const half2v sp = __builtin_bit_cast(half2v, wsc[j]);
+          const half2v sc = (s < 2) ? half2v{sp[0], sp[0]} : half2v{sp[1], sp[1]};
+          const uint32_t w = s == 0 ? wraw[j].x : s == 1 ? wraw[j].y : s == 2 ? wraw[j].z : wraw[j].w;
+          bf[j] = dec_fp4x8(w, sc);
+        }
+#pragma unroll
+        for (int i = 0; i < TI; ++i)
+#pragma unroll
+          for (int j = 0; j < TJ; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+      }
     }
+    if (kt + 1 < nk) {
+      uint8_t* sn = stage_ptr((kt + 1) & 1);
+      la.store(sn, sn + C::A_CODES);
+      lw.store(sn + C::A_CODES + C::A_SC, sn + C::A_CODES + C::A_SC + C::W_CODES);
+    }
+    __syncthreads();
   }
 
-  // epilogue: C[row][col] of MFMA tile (i, j): lane, register e ->
-  // row 8*(e/4) + 4*(lane/32) + e%4, col lane%32
+  // epilogue: MFMA tile (i, j), lane, register e -> row 8*(e/4) + 4*(lane/32)
+  // + e%4, col lane%32.  Decoded operands carry no extra factor (the 2^8 of
+  // the fp4 conversion cancels the 2^-8 of the scale bits).
   const float gsw = p.w_ts[1];
   const float alpha_t = (AFMT == 0) ? p.a_ts[1] * gsw : 0.0f;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < TI; ++i) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      const int row = m0 + wm * 64 + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+      const int row = m0 + wm * 32 * TI + 32 * i + 8 * (e >> 2) + 4 * h + (e & 3);
       if (row >= p.M) continue;
       const float alpha = (AFMT == 0) ? alpha_t : static_cast<const float*>(p.a_s)[row] * gsw;
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int col = n0 + wn * 64 + 32 * j + (lane & 31);
+      for (int j = 0; j < TJ; ++j) {
+        const int col = n0 + wn * 32 * TJ + 32 * j + r32;
         if (col >= p.N) continue;
         float v = acc[i][j][e] * alpha;
         if (p.bias) v = v + p.bias[col];
@@ -199,19 +352,343 @@ __global__ __launch_bounds__(GT) void qgemm_kernel(GemmParams p) {
   }
 }
 
+// =============================================================== pipelined
+// Fast path for K % 128 == 0: the same 256 x 256 tile and fragment decode,
+// with
+//   * direct-to-LDS loads (global_load_lds: each lane names the global 16-byte
+//     quad that lands in its LDS slot, which applies the XOR swizzle) into a
+//     3-deep ring of stages, issued two stages ahead;
+//   * one barrier per stage, placed mid-stage: each wave first waits for its
+//     own loads of the next stage (vmcnt) and for its LDS reads of the current
+//     one (lgkmcnt), so after the barrier the next stage is complete and the
+//     current buffer is free for the stage three ahead;
+//   * a step-level software pipeline: the 16 MFMAs of step s are interleaved
+//     (sched_group_barrier) with the decode of step s+1 and the LDS reads of
+//     the next chunk, so the VALU work hides under the MFMAs.
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ void wait_lgkm_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// The DMA is issued through inline asm so that the compiler's wait insertion,
+// which cannot tell the ring slots apart, does not drain every in-flight load
+// before each LDS read; the waits are explicit (wait_vm before the barrier).
+// M0 holds the wave-uniform LDS destination; lane i writes M0 + i * size.
+__device__ __forceinline__ void dma16(const uint8_t* g, uint8_t* l) {
+  const uint32_t la = (uint32_t)(size_t)(lds_void_t*)l;
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+               ::"s"(__builtin_amdgcn_readfirstlane(la)), "v"(g) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const uint8_t* g, uint8_t* l) {
+  const uint32_t la = (uint32_t)(size_t)(lds_void_t*)l;
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off"
+               ::"s"(__builtin_amdgcn_readfirstlane(la)), "v"(g) : "memory", "m0");
+}
+
+template <int AFMT>
+struct Pipe {
+  static constexpr bool A8 = AFMT == 1;
+  static constexpr int A_CODES = 256 * (A8 ? 128 : 64);
+  static constexpr int A_SC = A8 ? 0 : 256 * 8;
+  static constexpr int W_CODES = 256 * 64;
+  static constexpr int W_SC = 256 * 8;
+  static constexpr int STAGE = A_CODES + A_SC + W_CODES + W_SC;
+  static constexpr int NS = 3;
+  static constexpr int NA = A8 ? 8 : 4;        // A code loads per wave and stage (1 KB each)
+  static constexpr int NAS = A8 ? 0 : 2;       // A scale loads per wave and stage (256 B each)
+  static constexpr int NW = 4, NWS = 2;
+  static constexpr int LPS = NA + NAS + NW + NWS;   // loads per wave and stage
+};
+
+// per-chunk raw operands of one lane: codes for its 4 A and 4 W sub-blocks
+template <bool A8>
+struct Raw {
+  uint4 a[4][A8 ? 2 : 1];
+  uint32_t as[4];
+  uint4 w[4];
+  uint32_t ws[4];
+};
+
+template <int AFMT>
+__global__ __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void qgemm_pipe_kernel(GemmParams p) {
+  using P = Pipe<AFMT>;
+  constexpr bool A8 = P::A8;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wv = t >> 6;
+  const int wm = wv >> 1, wn = wv & 1;
+  int tm, tn;
+  tile_of(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, tm, tn);
+  const int m0 = tm * 256, n0 = tn * 256;
+  const int K = p.K;
+  const int nk = K / BK;
+
+  const uint8_t* aq = static_cast<const uint8_t*>(p.a_q);
+  const uint8_t* as = static_cast<const uint8_t*>(p.a_s);
+
+  // ---- per-lane byte offsets of the DMA sources at k0 = 0 (32-bit: every
+  // operand matrix is below 4 GB, checked on the host)
+  uint32_t offA[P::NA], offAS[P::NAS > 0 ? P::NAS : 1], offW[P::NW], offWS[P::NWS];
+#pragma unroll
+  for (int u = 0; u < P::NA; ++u) {
+    if (A8) {
+      const int r = (wv * P::NA + u) * 8 + (lane >> 3);
+      const int q = (lane & 7) ^ (r & 7);
+      offA[u] = (uint32_t)min(m0 + r, p.M - 1) * (uint32_t)K + 16u * q;
+    } else {
+      const int r = (wv * P::NA + u) * 16 + (lane >> 2);
+      const int q = (lane & 3) ^ ((r >> 1) & 3);
+      offA[u] = (uint32_t)min(m0 + r, p.M - 1) * (uint32_t)(K / 2) + 16u * q;
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < P::NAS; ++u) {
+    const int r = (wv * P::NAS + u) * 32 + (lane >> 1);
+    offAS[u] = (uint32_t)min(m0 + r, p.M - 1) * (uint32_t)(K / 16) + 4u * (lane & 1);
+  }
+#pragma unroll
+  for (int u = 0; u < P::NW; ++u) {
+    const int r = (wv * P::NW + u) * 16 + (lane >> 2);
+    const int q = (lane & 3) ^ ((r >> 1) & 3);
+    offW[u] = (uint32_t)min(n0 + r, p.N - 1) * (uint32_t)(K / 2) + 16u * q;
+  }
+#pragma unroll
+  for (int u = 0; u < P::NWS; ++u) {
+    const int r = (wv * P::NWS + u) * 32 + (lane >> 1);
+    offWS[u] = (uint32_t)min(n0 + r, p.N - 1) * (uint32_t)(K / 16) + 4u * (lane & 1);
+  }
+
+  auto issue_stage = [&](int kt) {
+    uint8_t* st = smem + (kt % P::NS) * P::STAGE;
+    const int k0 = kt * BK;
+    const uint32_t ka = A8 ? (uint32_t)k0 : (uint32_t)(k0 / 2);
+#pragma unroll
+    for (int u = 0; u < P::NA; ++u) dma16(aq + offA[u] + ka, st + (wv * P::NA + u) * 1024);
+#pragma unroll
+    for (int u = 0; u < P::NAS; ++u) dma4(as + offAS[u] + k0 / 16, st + P::A_CODES + (wv * P::NAS + u) * 256);
+#pragma unroll
+    for (int u = 0; u < P::NW; ++u)
+      dma16(p.w_q + offW[u] + k0 / 2, st + P::A_CODES + P::A_SC + (wv * P::NW + u) * 1024);
+#pragma unroll
+    for (int u = 0; u < P::NWS; ++u)
+      dma4(p.w_s + offWS[u] + k0 / 16, st + P::A_CODES + P::A_SC + P::W_CODES + (wv * P::NWS + u) * 256);
+  };
+
+  // ---- LDS read offsets of this lane's fragments (within a stage)
+  const int r32 = lane & 31, h = lane >> 5;
+  auto read_chunk = [&](int kt, int c, Raw<A8>& R) {
+    const uint8_t* st = smem + (kt % P::NS) * P::STAGE;
+    const int qd = 2 * c + h;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = wm * 128 + 32 * i + r32;
+      if (A8) {
+        R.a[i][0] = *reinterpret_cast<const uint4*>(st + i8_quad_off(row, 2 * qd));
+        R.a[i][A8 ? 1 : 0] = *reinterpret_cast<const uint4*>(st + i8_quad_off(row, 2 * qd + 1));
+        R.as[i] = 0u;
+      } else {
+        R.a[i][0] = *reinterpret_cast<const uint4*>(st + fp4_quad_off(row, qd));
+        R.as[i] = *reinterpret_cast<const uint16_t*>(st + P::A_CODES + row * 8 + 4 * c + 2 * h);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = wn * 128 + 32 * j + r32;
+      R.w[j] = *reinterpret_cast<const uint4*>(st + P::A_CODES + P::A_SC + fp4_quad_off(row, qd));
+      R.ws[j] = *reinterpret_cast<const uint16_t*>(st + P::A_CODES + P::A_SC + P::W_CODES + row * 8 + 4 * c + 2 * h);
+    }
+  };
+
+  auto decode = [&](const Raw<A8>& R, int s, half8 (&af)[4], half8 (&bf)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (A8) {
+        const uint4& v = R.a[i][s >> 1];
+        af[i] = (s & 1) ? dec_i8x8(v.z, v.w) : dec_i8x8(v.x, v.y);
+      } else {
+        const half2v sp = __builtin_bit_cast(half2v, scale_pair_bits(R.as[i]));
+        const half2v sc = (s < 2) ? half2v{sp[0], sp[0]} : half2v{sp[1], sp[1]};
+        const uint4& v = R.a[i][0];
+        af[i] = dec_fp4x8(s == 0 ? v.x : s == 1 ? v.y : s == 2 ? v.z : v.w, sc);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const half2v sp = __builtin_bit_cast(half2v, scale_pair_bits(R.ws[j]));
+      const half2v sc = (s < 2) ? half2v{sp[0], sp[0]} : half2v{sp[1], sp[1]};
+      const uint4& v = R.w[j];
+      bf[j] = dec_fp4x8(s == 0 ? v.x : s == 1 ? v.y : s == 2 ? v.z : v.w, sc);
+    }
+  };
+
+  float16v acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+  auto mfma16 = [&](const half8 (&af)[4], const half8 (&bf)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+  };
+  // interleave: each MFMA followed by a few VALU (decode) and, when present,
+  // one LDS read
+  auto interleave = [&]() {
+#pragma unroll
+    for (int x = 0; x < 16; ++x) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+    }
+  };
+
+  // ---- prologue: stages 0..2 in flight, wait for stage 0
+  issue_stage(0);
+  if (nk > 1) issue_stage(1);
+  if (nk > 2) issue_stage(2);
+  if (nk > 2) wait_vm<2 * P::LPS>();
+  else if (nk > 1) wait_vm<P::LPS>();
+  else wait_vm<0>();
+  wait_lgkm_barrier();
+
+  Raw<A8> R0, R1;
+  half8 fa[4], fb[4];
+  read_chunk(0, 0, R0);
+  decode(R0, 0, fa, fb);
+
+  for (int kt = 0; kt < nk; ++kt) {
+    const bool more = kt + 1 < nk;
+    half8 ga[4], gb[4];
+    // step 0: MFMA(step 0) | read chunk 1, decode step 1
+    read_chunk(kt, 1, R1);
+    decode(R0, 1, ga, gb);
+    mfma16(fa, fb);
+    interleave();
+    // step 1 | decode step 2
+    decode(R0, 2, fa, fb);
+    mfma16(ga, gb);
+    interleave();
+    // step 2 | decode step 3
+    decode(R0, 3, ga, gb);
+    mfma16(fa, fb);
+    interleave();
+    // step 3 | decode step 4 (chunk 1)
+    decode(R1, 0, fa, fb);
+    mfma16(ga, gb);
+    interleave();
+    // mid-stage barrier: next stage complete, this buffer free
+    if (more) {
+      if (kt + 2 < nk) wait_vm<P::LPS>();
+      else wait_vm<0>();
+    }
+    wait_lgkm_barrier();
+    if (kt + 3 < nk) issue_stage(kt + 3);
+    // step 4 | read next stage chunk 0, decode step 5
+    if (more) read_chunk(kt + 1, 0, R0);
+    decode(R1, 1, ga, gb);
+    mfma16(fa, fb);
+    interleave();
+    // step 5 | decode step 6
+    decode(R1, 2, fa, fb);
+    mfma16(ga, gb);
+    interleave();
+    // step 6 | decode step 7
+    decode(R1, 3, ga, gb);
+    mfma16(fa, fb);
+    interleave();
+    // step 7 | decode step 0 of the next stage
+    if (more) decode(R0, 0, fa, fb);
+    mfma16(ga, gb);
+    interleave();
+  }
+
+  const float gsw = p.w_ts[1];
+  const float alpha_t = (AFMT == 0) ? p.a_ts[1] * gsw : 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int row = m0 + wm * 128 + 32 * i + 8 * (e >> 2) + 4 * h + (e & 3);
+      if (row >= p.M) continue;
+      const float alpha = (AFMT == 0) ? alpha_t : static_cast<const float*>(p.a_s)[row] * gsw;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int col = n0 + wn * 128 + 32 * j + r32;
+        if (col >= p.N) continue;
+        float v = acc[i][j][e] * alpha;
+        if (p.bias) v = v + p.bias[col];
+        if (p.out_f32)
+          static_cast<float*>(p.y)[(int64_t)row * p.ldy + col] = v;
+        else
+          static_cast<uint16_t*>(p.y)[(int64_t)row * p.ldy + col] = (uint16_t)f32_to_bf16_bits(v);
+      }
+    }
+  }
+}
+
+template <int AFMT>
+static hipError_t launch_pipe(GemmParams p, hipStream_t st) {
+  using P = Pipe<AFMT>;
+  p.tiles_m = (p.M + 255) / 256;
+  p.tiles_n = (p.N + 255) / 256;
+  const int nblocks = p.tiles_m * p.tiles_n;
+  const size_t lds = (size_t)P::NS * P::STAGE;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&qgemm_pipe_kernel<AFMT>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL((qgemm_pipe_kernel<AFMT>), dim3(nblocks), dim3(GT), lds, st, p);
+  return hipGetLastError();
+}
+
+template <int AFMT, int TI, int TJ>
+static hipError_t launch_cfg(GemmParams p, hipStream_t st) {
+  using C = Cfg<AFMT, TI, TJ>;
+  p.tiles_m = (p.M + C::BM - 1) / C::BM;
+  p.tiles_n = (p.N + C::BN - 1) / C::BN;
+  const int nblocks = p.tiles_m * p.tiles_n;
+  const size_t lds = 2 * (size_t)C::STAGE;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&qgemm_kernel<AFMT, TI, TJ>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL((qgemm_kernel<AFMT, TI, TJ>), dim3(nblocks), dim3(GT), lds, st, p);
+  return hipGetLastError();
+}
+
 hipError_t launch_qgemm(int afmt, const void* a_q, const void* a_s, const float* a_ts,
                         const uint8_t* w_q, const uint8_t* w_s, const float* w_ts,
                         const float* bias, void* y, int64_t ldy, int out_dtype, int64_t M,
                         int64_t N, int64_t K, hipStream_t st) {
   if (M == 0 || N == 0) return hipSuccess;
   GemmParams p{a_q, a_s, a_ts, w_q, w_s, w_ts, bias, y, ldy, (int32_t)M, (int32_t)N, (int32_t)K,
-               out_dtype == 1};
-  dim3 grid((unsigned)((N + BN - 1) / BN), (unsigned)((M + BM - 1) / BM));
-  if (afmt == 0)
-    hipLaunchKernelGGL(qgemm_kernel<0>, grid, dim3(GT), 0, st, p);
-  else
-    hipLaunchKernelGGL(qgemm_kernel<1>, grid, dim3(GT), 0, st, p);
-  return hipGetLastError();
+               out_dtype == 1, 0, 0};
+  // The pipelined kernel needs whole 128-wide K stages and 32-bit byte
+  // offsets into every operand matrix.
+  const bool fast = (K % BK) == 0 && (afmt == 1 ? M * K : M * K / 2) < (int64_t(1) << 32) &&
+                    N * K / 2 < (int64_t(1) << 32);
+  if (fast) return afmt == 0 ? launch_pipe<0>(p, st) : launch_pipe<1>(p, st);
+  if (afmt == 0) return launch_cfg<0, 4, 4>(p, st);
+  return launch_cfg<1, 4, 4>(p, st);
 }
 
 }  // namespace vdtq

@@ -60,10 +60,12 @@ class INT8Tensor:
 
 
 def hadamard_quantize(x: torch.Tensor, had_block: int = 64, fmt: str = "nvfp4", amax=None,
-                      stats: bool = False):
+                      stats: bool = False, out=None):
     """Block Hadamard transform of bf16 rows + NVFP4 or INT8 quantization.
     amax (NVFP4 only): a float or a 1-element device tensor to use as the
-    tensor amax instead of computing it."""
+    tensor amax instead of computing it, or the string "given" to use the
+    value already in out.ts[0].  out: a previously returned NVFP4Tensor /
+    INT8Tensor of the same shape whose buffers are reused."""
     _require(x, torch.bfloat16, "x")
     if x.dim() != 2 or x.stride(1) != 1:
         raise ValueError("x must be a 2-D tensor with unit column stride")
@@ -73,19 +75,28 @@ def hadamard_quantize(x: torch.Tensor, had_block: int = 64, fmt: str = "nvfp4", 
     st = torch.zeros(4, dtype=torch.float64, device=dev) if stats else None
     nbytes = L.lib().vdtq_workspace_bytes(L.OP_HADAMARD_QUANTIZE, M, K)
     ws = workspace(dev, nbytes)
+    if out is not None and stats and out.stats is not None:
+        st = out.stats
     if fmt == "nvfp4":
-        q = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
-        s = torch.empty((M, K // 16), dtype=torch.uint8, device=dev)
-        ts = torch.zeros(2, dtype=torch.float32, device=dev)
+        if out is not None:
+            q, s, ts = out.q, out.scales, out.ts
+        else:
+            q = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+            s = torch.empty((M, K // 16), dtype=torch.uint8, device=dev)
+            ts = torch.zeros(2, dtype=torch.float32, device=dev)
         if amax is not None:
             flags |= L.AMAX_GIVEN
-            ts[0] = amax if not torch.is_tensor(amax) else amax.reshape(-1)[0]
+            if not (isinstance(amax, str) and amax == "given"):
+                ts[0] = amax if not torch.is_tensor(amax) else amax.reshape(-1)[0]
         fcode = L.FMT_NVFP4
     elif fmt == "int8":
         if amax is not None:
             raise ValueError("amax applies to nvfp4 only")
-        q = torch.empty((M, K), dtype=torch.int8, device=dev)
-        s = torch.empty((M,), dtype=torch.float32, device=dev)
+        if out is not None:
+            q, s = out.q, out.scales
+        else:
+            q = torch.empty((M, K), dtype=torch.int8, device=dev)
+            s = torch.empty((M,), dtype=torch.float32, device=dev)
         ts = None
         fcode = L.FMT_INT8
     else:
