@@ -378,16 +378,15 @@ __device__ __forceinline__ void wait_lgkm_barrier() {
 // The DMA is issued through inline asm so that the compiler's wait insertion,
 // which cannot tell the ring slots apart, does not drain every in-flight load
 // before each LDS read; the waits are explicit (wait_vm before the barrier).
-// M0 holds the wave-uniform LDS destination; lane i writes M0 + i * size.
-__device__ __forceinline__ void dma16(const uint8_t* g, uint8_t* l) {
-  const uint32_t la = (uint32_t)(size_t)(lds_void_t*)l;
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
-               ::"s"(__builtin_amdgcn_readfirstlane(la)), "v"(g) : "memory", "m0");
+// M0 holds the wave-uniform LDS destination (lane i writes M0 + i * size);
+// the global address is a scalar base plus a 32-bit per-lane offset.
+__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+               ::"s"(m0), "v"(voff), "s"(base) : "memory", "m0");
 }
-__device__ __forceinline__ void dma4(const uint8_t* g, uint8_t* l) {
-  const uint32_t la = (uint32_t)(size_t)(lds_void_t*)l;
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off"
-               ::"s"(__builtin_amdgcn_readfirstlane(la)), "v"(g) : "memory", "m0");
+__device__ __forceinline__ void dma4(const void* base, uint32_t voff, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2"
+               ::"s"(m0), "v"(voff), "s"(base) : "memory", "m0");
 }
 
 template <int AFMT>
@@ -409,9 +408,7 @@ struct Pipe {
 template <bool A8>
 struct Raw {
   uint4 a[4][A8 ? 2 : 1];
-  uint32_t as[4];
   uint4 w[4];
-  uint32_t ws[4];
 };
 
 template <int AFMT>
@@ -466,25 +463,30 @@ void qgemm_pipe_kernel(GemmParams p) {
     offWS[u] = (uint32_t)min(n0 + r, p.N - 1) * (uint32_t)(K / 16) + 4u * (lane & 1);
   }
 
+  // LDS byte address of smem and of this wave's regions (wave-uniform)
+  const uint32_t lds0 = (uint32_t)(size_t)(lds_void_t*)smem;
+  const uint32_t wvu = __builtin_amdgcn_readfirstlane(wv);
   auto issue_stage = [&](int kt) {
-    uint8_t* st = smem + (kt % P::NS) * P::STAGE;
+    const uint32_t st = lds0 + (uint32_t)(kt % P::NS) * P::STAGE;
     const int k0 = kt * BK;
-    const uint32_t ka = A8 ? (uint32_t)k0 : (uint32_t)(k0 / 2);
+    const uint8_t* abase = aq + (A8 ? k0 : k0 / 2);
+    const uint8_t* asbase = as + k0 / 16;
+    const uint8_t* wbase = p.w_q + k0 / 2;
+    const uint8_t* wsbase = p.w_s + k0 / 16;
 #pragma unroll
-    for (int u = 0; u < P::NA; ++u) dma16(aq + offA[u] + ka, st + (wv * P::NA + u) * 1024);
+    for (int u = 0; u < P::NA; ++u) dma16(abase, offA[u], st + (wvu * P::NA + u) * 1024);
 #pragma unroll
-    for (int u = 0; u < P::NAS; ++u) dma4(as + offAS[u] + k0 / 16, st + P::A_CODES + (wv * P::NAS + u) * 256);
+    for (int u = 0; u < P::NAS; ++u) dma4(asbase, offAS[u], st + P::A_CODES + (wvu * P::NAS + u) * 256);
 #pragma unroll
-    for (int u = 0; u < P::NW; ++u)
-      dma16(p.w_q + offW[u] + k0 / 2, st + P::A_CODES + P::A_SC + (wv * P::NW + u) * 1024);
+    for (int u = 0; u < P::NW; ++u) dma16(wbase, offW[u], st + P::A_CODES + P::A_SC + (wvu * P::NW + u) * 1024);
 #pragma unroll
     for (int u = 0; u < P::NWS; ++u)
-      dma4(p.w_s + offWS[u] + k0 / 16, st + P::A_CODES + P::A_SC + P::W_CODES + (wv * P::NWS + u) * 256);
+      dma4(wsbase, offWS[u], st + P::A_CODES + P::A_SC + P::W_CODES + (wvu * P::NWS + u) * 256);
   };
 
   // ---- LDS read offsets of this lane's fragments (within a stage)
   const int r32 = lane & 31, h = lane >> 5;
-  auto read_chunk = [&](int kt, int c, Raw<A8>& R) {
+  auto read_codes = [&](int kt, int c, Raw<A8>& R) {
     const uint8_t* st = smem + (kt % P::NS) * P::STAGE;
     const int qd = 2 * c + h;
 #pragma unroll
@@ -493,28 +495,40 @@ void qgemm_pipe_kernel(GemmParams p) {
       if (A8) {
         R.a[i][0] = *reinterpret_cast<const uint4*>(st + i8_quad_off(row, 2 * qd));
         R.a[i][A8 ? 1 : 0] = *reinterpret_cast<const uint4*>(st + i8_quad_off(row, 2 * qd + 1));
-        R.as[i] = 0u;
       } else {
         R.a[i][0] = *reinterpret_cast<const uint4*>(st + fp4_quad_off(row, qd));
-        R.as[i] = *reinterpret_cast<const uint16_t*>(st + P::A_CODES + row * 8 + 4 * c + 2 * h);
       }
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int row = wn * 128 + 32 * j + r32;
       R.w[j] = *reinterpret_cast<const uint4*>(st + P::A_CODES + P::A_SC + fp4_quad_off(row, qd));
-      R.ws[j] = *reinterpret_cast<const uint16_t*>(st + P::A_CODES + P::A_SC + P::W_CODES + row * 8 + 4 * c + 2 * h);
     }
   };
+  // the 8 scale bytes (groups of both chunks) of each of this lane's rows
+  auto read_scales = [&](int kt, uint2 (&sa)[4], uint2 (&sw)[4]) {
+    const uint8_t* st = smem + (kt % P::NS) * P::STAGE;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (!A8) sa[i] = *reinterpret_cast<const uint2*>(st + P::A_CODES + (wm * 128 + 32 * i + r32) * 8);
+      else sa[i] = make_uint2(0u, 0u);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      sw[j] = *reinterpret_cast<const uint2*>(st + P::A_CODES + P::A_SC + P::W_CODES + (wn * 128 + 32 * j + r32) * 8);
+  };
+  // scale pair of chunk c for this lane half: groups 4c + 2h, 4c + 2h + 1
+  auto scale_of = [&](const uint2& s8, int c) { return scale_pair_bits((c ? s8.y : s8.x) >> (16 * h)); };
 
-  auto decode = [&](const Raw<A8>& R, int s, half8 (&af)[4], half8 (&bf)[4]) {
+  auto decode = [&](const Raw<A8>& R, const uint2 (&sa)[4], const uint2 (&sw)[4], int c, int s,
+                    half8 (&af)[4], half8 (&bf)[4]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if (A8) {
         const uint4& v = R.a[i][s >> 1];
         af[i] = (s & 1) ? dec_i8x8(v.z, v.w) : dec_i8x8(v.x, v.y);
       } else {
-        const half2v sp = __builtin_bit_cast(half2v, scale_pair_bits(R.as[i]));
+        const half2v sp = __builtin_bit_cast(half2v, scale_of(sa[i], c));
         const half2v sc = (s < 2) ? half2v{sp[0], sp[0]} : half2v{sp[1], sp[1]};
         const uint4& v = R.a[i][0];
         af[i] = dec_fp4x8(s == 0 ? v.x : s == 1 ? v.y : s == 2 ? v.z : v.w, sc);
@@ -522,7 +536,7 @@ void qgemm_pipe_kernel(GemmParams p) {
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const half2v sp = __builtin_bit_cast(half2v, scale_pair_bits(R.ws[j]));
+      const half2v sp = __builtin_bit_cast(half2v, scale_of(sw[j], c));
       const half2v sc = (s < 2) ? half2v{sp[0], sp[0]} : half2v{sp[1], sp[1]};
       const uint4& v = R.w[j];
       bf[j] = dec_fp4x8(s == 0 ? v.x : s == 1 ? v.y : s == 2 ? v.z : v.w, sc);
@@ -553,6 +567,8 @@ void qgemm_pipe_kernel(GemmParams p) {
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
     }
+    // each step is its own scheduling region: nothing migrates between steps
+    __builtin_amdgcn_sched_barrier(0);
   };
 
   // ---- prologue: stages 0..2 in flight, wait for stage 0
@@ -565,52 +581,55 @@ void qgemm_pipe_kernel(GemmParams p) {
   wait_lgkm_barrier();
 
   Raw<A8> R0, R1;
-  half8 fa[4], fb[4];
-  read_chunk(0, 0, R0);
-  decode(R0, 0, fa, fb);
+  uint2 sa[4], sw[4], na[4], nw[4];
+  half8 fa[4], fb[4], ga[4], gb[4];
+  read_codes(0, 0, R0);
+  read_scales(0, sa, sw);
+  decode(R0, sa, sw, 0, 0, fa, fb);
 
+  // Every step has the same shape; past the last stage the reads of the
+  // "next" stage hit a stale ring slot and the extra decode is discarded.
   for (int kt = 0; kt < nk; ++kt) {
-    const bool more = kt + 1 < nk;
-    half8 ga[4], gb[4];
-    // step 0: MFMA(step 0) | read chunk 1, decode step 1
-    read_chunk(kt, 1, R1);
-    decode(R0, 1, ga, gb);
+    // step 0 | decode step 1
+    decode(R0, sa, sw, 0, 1, ga, gb);
     mfma16(fa, fb);
     interleave();
-    // step 1 | decode step 2
-    decode(R0, 2, fa, fb);
+    // step 1 | read chunk 1 codes, decode step 2
+    read_codes(kt, 1, R1);
+    decode(R0, sa, sw, 0, 2, fa, fb);
     mfma16(ga, gb);
     interleave();
     // step 2 | decode step 3
-    decode(R0, 3, ga, gb);
+    decode(R0, sa, sw, 0, 3, ga, gb);
     mfma16(fa, fb);
     interleave();
     // step 3 | decode step 4 (chunk 1)
-    decode(R1, 0, fa, fb);
+    decode(R1, sa, sw, 1, 0, fa, fb);
     mfma16(ga, gb);
     interleave();
     // mid-stage barrier: next stage complete, this buffer free
-    if (more) {
-      if (kt + 2 < nk) wait_vm<P::LPS>();
-      else wait_vm<0>();
-    }
+    if (kt + 2 < nk) wait_vm<P::LPS>();
+    else wait_vm<0>();
     wait_lgkm_barrier();
     if (kt + 3 < nk) issue_stage(kt + 3);
-    // step 4 | read next stage chunk 0, decode step 5
-    if (more) read_chunk(kt + 1, 0, R0);
-    decode(R1, 1, ga, gb);
+    // step 4 | read stage kt+1 scales, decode step 5
+    read_scales(kt + 1, na, nw);
+    decode(R1, sa, sw, 1, 1, ga, gb);
     mfma16(fa, fb);
     interleave();
-    // step 5 | decode step 6
-    decode(R1, 2, fa, fb);
+    // step 5 | read stage kt+1 chunk 0 codes, decode step 6
+    read_codes(kt + 1, 0, R0);
+    decode(R1, sa, sw, 1, 2, fa, fb);
     mfma16(ga, gb);
     interleave();
     // step 6 | decode step 7
-    decode(R1, 3, ga, gb);
+    decode(R1, sa, sw, 1, 3, ga, gb);
     mfma16(fa, fb);
     interleave();
-    // step 7 | decode step 0 of the next stage
-    if (more) decode(R0, 0, fa, fb);
+    // step 7 | decode step 0 of stage kt+1
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { sa[i] = na[i]; sw[i] = nw[i]; }
+    decode(R0, sa, sw, 0, 0, fa, fb);
     mfma16(ga, gb);
     interleave();
   }
