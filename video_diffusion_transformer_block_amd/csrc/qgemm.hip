@@ -551,12 +551,15 @@ void qgemm_pipe_kernel(GemmParams p) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
+  // D = W_frag x A_frag^T: each accumulator tile is a 32 x 32 block of Y^T,
+  // so a lane holds one token row and, per register group of 4, four
+  // consecutive output features (vector stores in the epilogue)
   auto mfma16 = [&](const half8 (&af)[4], const half8 (&bf)[4]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[j], af[i], acc[i][j], 0, 0, 0);
   };
   // interleave: each MFMA followed by a few VALU (decode) and, when present,
   // one LDS read
@@ -634,25 +637,51 @@ void qgemm_pipe_kernel(GemmParams p) {
     interleave();
   }
 
+  // epilogue: tile (i, j), lane, register e -> token row m0 + wm*128 + 32 i
+  // + lane%32, feature column n0 + wn*128 + 32 j + 8 (e/4) + 4 (lane/32) + e%4
   const float gsw = p.w_ts[1];
   const float alpha_t = (AFMT == 0) ? p.a_ts[1] * gsw : 0.0f;
+  const bool vec = (p.N % 4) == 0 && (p.ldy % 4) == 0 &&
+                   ((reinterpret_cast<uintptr_t>(p.y) & (p.out_f32 ? 15u : 7u)) == 0) &&
+                   (!p.bias || (reinterpret_cast<uintptr_t>(p.bias) & 15u) == 0);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
+    const int row = m0 + wm * 128 + 32 * i + r32;
+    if (row >= p.M) continue;
+    const float alpha = (AFMT == 0) ? alpha_t : static_cast<const float*>(p.a_s)[row] * gsw;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int row = m0 + wm * 128 + 32 * i + 8 * (e >> 2) + 4 * h + (e & 3);
-      if (row >= p.M) continue;
-      const float alpha = (AFMT == 0) ? alpha_t : static_cast<const float*>(p.a_s)[row] * gsw;
+    for (int j = 0; j < 4; ++j) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int col = n0 + wn * 128 + 32 * j + r32;
-        if (col >= p.N) continue;
-        float v = acc[i][j][e] * alpha;
-        if (p.bias) v = v + p.bias[col];
-        if (p.out_f32)
-          static_cast<float*>(p.y)[(int64_t)row * p.ldy + col] = v;
-        else
-          static_cast<uint16_t*>(p.y)[(int64_t)row * p.ldy + col] = (uint16_t)f32_to_bf16_bits(v);
+      for (int g = 0; g < 4; ++g) {
+        const int col = n0 + wn * 128 + 32 * j + 8 * g + 4 * h;
+        float v[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = acc[i][j][4 * g + q] * alpha;
+        if (vec && col + 4 <= p.N) {
+          if (p.bias) {
+            const float4 b = *reinterpret_cast<const float4*>(p.bias + col);
+            v[0] = v[0] + b.x; v[1] = v[1] + b.y; v[2] = v[2] + b.z; v[3] = v[3] + b.w;
+          }
+          if (p.out_f32) {
+            *reinterpret_cast<float4*>(static_cast<float*>(p.y) + (int64_t)row * p.ldy + col) =
+                make_float4(v[0], v[1], v[2], v[3]);
+          } else {
+            const uint32_t lo = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
+            const uint32_t hi = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
+            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.y) + (int64_t)row * p.ldy + col) = make_uint2(lo, hi);
+          }
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            if (col + q >= p.N) continue;
+            float x = v[q];
+            if (p.bias) x = x + p.bias[col + q];
+            if (p.out_f32)
+              static_cast<float*>(p.y)[(int64_t)row * p.ldy + col + q] = x;
+            else
+              static_cast<uint16_t*>(p.y)[(int64_t)row * p.ldy + col + q] = (uint16_t)f32_to_bf16_bits(x);
+          }
+        }
       }
     }
   }
