@@ -197,32 +197,33 @@ def main():
 
 def measure_quantize(torch, V, X, M, steps):
     """hadamard_quantize with the tensor amax supplied (the single fused
-    kernel) on the three K=3072 inputs in rotation (327 MB of bf16 read per
-    rotation, larger than the 256 MB last-level cache), plus INT8."""
+    kernel), timed per launch with HIP events.  The 3072-wide inputs rotate
+    over the three K=3072 activations (327 MB of bf16 per rotation, above the
+    256 MB last-level cache); the 12288-wide FFN-down input is 437 MB."""
     out = {}
-    names = ["qkv", "out", "ffn_up"]
-    K = 3072
-    elems = M * K
-    for fmt, bpe in (("nvfp4", 2 + 0.5 + 1 / 16), ("int8", 3.0)):
-        extra = 0 if fmt == "nvfp4" else 4 * M / elems
-        # buffers allocated (and the tensor amax written) outside the timed launches
-        outs = [V.hadamard_quantize(X[names[i]], HAD_BLOCK, fmt) for i in range(3)]
-        amax = "given" if fmt == "nvfp4" else None
-        torch.cuda.synchronize()
-        evs = []
-        for s in range(3 * steps):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            V.hadamard_quantize(X[names[s % 3]], HAD_BLOCK, fmt, amax=amax, out=outs[s % 3])
-            e1.record()
-            evs.append((e0, e1))
-        torch.cuda.synchronize()
-        us = 1e3 * float(np.mean([a.elapsed_time(b) for a, b in evs]))
-        gbs = (bpe + extra) * elems / (us * 1e-6) / 1e9
-        out[fmt] = {"bound": "hbm", "kernel": f"hq_{fmt}_kernel<64>", "achieved": round(gbs, 1),
-                    "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
-                    "traffic": None, "avg_launch_us": round(us, 2),
-                    "bytes_per_launch": (bpe + extra) * elems, "shape": [M, K]}
+    for K, names in ((3072, ["qkv", "out", "ffn_up"]), (12288, ["ffn_down"])):
+        elems = M * K
+        for fmt, bpe in (("nvfp4", 2 + 0.5 + 1 / 16), ("int8", 3.0)):
+            extra = 0 if fmt == "nvfp4" else 4 * M / elems
+            # buffers allocated (and the tensor amax written) outside the timed launches
+            outs = [V.hadamard_quantize(X[n], HAD_BLOCK, fmt) for n in names]
+            amax = "given" if fmt == "nvfp4" else None
+            torch.cuda.synchronize()
+            evs = []
+            for s in range(3 * steps):
+                i = s % len(names)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                V.hadamard_quantize(X[names[i]], HAD_BLOCK, fmt, amax=amax, out=outs[i])
+                e1.record()
+                evs.append((e0, e1))
+            torch.cuda.synchronize()
+            us = 1e3 * float(np.median([a.elapsed_time(b) for a, b in evs]))
+            gbs = (bpe + extra) * elems / (us * 1e-6) / 1e9
+            out[f"{fmt}_K{K}"] = {"bound": "hbm", "kernel": f"hq_{fmt}_kernel<64>", "achieved": round(gbs, 1),
+                                  "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                                  "traffic": None, "avg_launch_us": round(us, 2),
+                                  "bytes_per_launch": (bpe + extra) * elems, "shape": [M, K]}
     return out
 
 
