@@ -51,7 +51,12 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=96)
+    ap.add_argument("--cpu-rows", type=int, default=8192)
+    ap.add_argument("--sweeps", default=",".join(SWEEPS),
+                    help="comma-separated subset of " + ",".join(SWEEPS) + " (the first listed is the headline)")
+    ap.add_argument("--calibration-copy", action="store_true",
+                    help="after timing, run one plain elementwise pass over 512 MiB (reads 512 MiB, "
+                         "writes 512 MiB): the reference for counter runs")
     return ap.parse_args()
 
 
@@ -116,7 +121,9 @@ def main():
         dprev, dnew = dnew, dprev
 
     results = {}
-    for sweep, assign in SWEEPS.items():
+    chosen = [w for w in args.sweeps.split(",") if w]
+    for sweep in chosen:
+        assign = SWEEPS[sweep]
         for _ in range(args.warmup):
             step(assign)
         torch.cuda.synchronize()
@@ -140,7 +147,7 @@ def main():
         print(f"[bench] {sweep}: {ms:.3f} ms/step, {results[sweep]['tops']:.1f} TOPS", file=sys.stderr,
               flush=True)
 
-    head = results["mixed_w4a6"]
+    head = results[chosen[0]]
     # dominant kernel of the headline step: the qgemm variant with the most time
     kern = {}
     for name, d in head["per_linear"].items():
@@ -152,9 +159,18 @@ def main():
     dom = max(kern, key=lambda k: kern[k]["ms"])
     dk = kern[dom]
     achieved = dk["flops"] / (dk["ms"] * 1e-3) / 1e12
+    # HBM bytes per launch of the dominant kernel from the committed counter
+    # runs (FETCH_SIZE + WRITE_SIZE, copy-calibrated), while its sources match
+    from video_diffusion_transformer_block_amd import profiling
+    rec = profiling.load_traffic(os.path.join(ROOT, "profiles", "traffic_5b_mixed.json"))
+    kname = {"qgemm_w4a4": "qgemm_pipe_kernel<0>", "qgemm_w4a8": "qgemm_pipe_kernel<1>"}[dom]
+    traffic = None
+    if rec is not None and kname in rec["kernels"]:
+        traffic = round(rec["kernels"][kname]["bytes"])
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1),
                 "peak": PEAK_FP16_MFMA_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_FP16_MFMA_TFLOPS, 4), "traffic": None,
+                "frac": round(achieved / PEAK_FP16_MFMA_TFLOPS, 4), "traffic": traffic,
+                "traffic_unit": "bytes per launch (HBM/fabric, FETCH_SIZE+WRITE_SIZE)",
                 "avg_launch_us": round(1e3 * dk["ms"] / dk["launches"], 1),
                 "flops_per_launch": dk["flops"] / dk["launches"],
                 "note": "exact NVFP4/INT8 operands run on the fp16 MFMA (the peak used); "
@@ -163,6 +179,19 @@ def main():
 
     # quantize pass alone (tensor amax supplied: the single fused kernel), HBM bound
     qroof = measure_quantize(torch, V, X, M, args.steps)
+    if rec is not None:
+        for q in qroof.values():
+            e = rec["kernels"].get(q["kernel"], {}).get("grids", {}).get(str(q["grid_work_items"]))
+            if e is not None:
+                q["traffic"] = round(e["bytes"])
+
+    if args.calibration_copy:
+        src = torch.ones(256 << 20, dtype=torch.float16, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     cpu = None if args.no_cpu_baseline else cpu_baseline(host, M, args.cpu_rows)
 
@@ -195,35 +224,57 @@ def main():
     print(json.dumps(line))
 
 
+def hq_grid_work_items(M, K, fmt):
+    """Work-items of one quantize launch, as the library's launcher sizes it:
+    one 64-element chunk per thread for NVFP4; for INT8, max(1, 256 / chunks
+    per row) whole rows per 256-thread group.  Keys the counter record."""
+    cpr = (K + 63) // 64
+    if fmt == "nvfp4":
+        return -(-M * cpr // 256) * 256
+    rpw = max(1, 256 // cpr)
+    return -(-M // rpw) * 256
+
+
 def measure_quantize(torch, V, X, M, steps):
     """hadamard_quantize with the tensor amax supplied (the single fused
-    kernel), timed per launch with HIP events.  The 3072-wide inputs rotate
-    over the three K=3072 activations (327 MB of bf16 per rotation, above the
-    256 MB last-level cache); the 12288-wide FFN-down input is 437 MB."""
+    kernel).  The launches are captured in a graph and replayed, so the
+    per-launch time (HIP events around the replays / launches) excludes host
+    launch gaps.  The 3072-wide inputs rotate over the three K=3072
+    activations (327 MB of bf16 per rotation, above the 256 MB last-level
+    cache); the 12288-wide FFN-down input is 437 MB."""
     out = {}
     for K, names in ((3072, ["qkv", "out", "ffn_up"]), (12288, ["ffn_down"])):
         elems = M * K
         for fmt, bpe in (("nvfp4", 2 + 0.5 + 1 / 16), ("int8", 3.0)):
             extra = 0 if fmt == "nvfp4" else 4 * M / elems
-            # buffers allocated (and the tensor amax written) outside the timed launches
+            # buffers allocated (and the tensor amax written) before capture
             outs = [V.hadamard_quantize(X[n], HAD_BLOCK, fmt) for n in names]
             amax = "given" if fmt == "nvfp4" else None
+            n_launch = 12
             torch.cuda.synchronize()
-            evs = []
-            for s in range(3 * steps):
-                i = s % len(names)
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(n_launch):
+                    j = i % len(names)
+                    V.hadamard_quantize(X[names[j]], HAD_BLOCK, fmt, amax=amax, out=outs[j])
+            g.replay()
+            torch.cuda.synchronize()
+            times = []
+            for _ in range(max(3, steps // 4)):
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 e0.record()
-                V.hadamard_quantize(X[names[i]], HAD_BLOCK, fmt, amax=amax, out=outs[i])
+                g.replay()
                 e1.record()
-                evs.append((e0, e1))
-            torch.cuda.synchronize()
-            us = 1e3 * float(np.median([a.elapsed_time(b) for a, b in evs]))
+                torch.cuda.synchronize()
+                times.append(e0.elapsed_time(e1) / n_launch)
+            us = 1e3 * float(np.median(times))
             gbs = (bpe + extra) * elems / (us * 1e-6) / 1e9
             out[f"{fmt}_K{K}"] = {"bound": "hbm", "kernel": f"hq_{fmt}_kernel<64>", "achieved": round(gbs, 1),
                                   "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                                   "traffic": None, "avg_launch_us": round(us, 2),
-                                  "bytes_per_launch": (bpe + extra) * elems, "shape": [M, K]}
+                                  "bytes_per_launch": (bpe + extra) * elems, "shape": [M, K],
+                                  "grid_work_items": hq_grid_work_items(M, K, fmt)}
+            del g
     return out
 
 

@@ -1,0 +1,172 @@
+"""Summaries of rocprofv3 output for this library's kernels.
+
+    # kernel durations (rocprofv3 --kernel-trace --stats --output-format csv)
+    python -m video_diffusion_transformer_block_amd.profiling stats <dir>/<name>_kernel_stats.csv
+
+    # per-dispatch durations by kernel and grid (same run, kernel_trace.csv)
+    python -m video_diffusion_transformer_block_amd.profiling trace <dir>/<name>_kernel_trace.csv
+
+    # HBM traffic per dispatch from two counter runs (FETCH_SIZE, WRITE_SIZE),
+    # calibrated on the plain copy of known size that the run also performs
+    python -m video_diffusion_transformer_block_amd.profiling traffic \
+        <fetch>_counter_collection.csv <write>_counter_collection.csv \
+        --copy-bytes 536870912 --copy-kernel neg_kernel --out profiles/traffic_5b.json
+
+FETCH_SIZE and WRITE_SIZE are reported in KiB per dispatch.  The scale factor
+of each is the copy's known byte count divided by what the counter reads for
+that copy.  The traffic file records a hash of the kernel sources it was
+measured on; consumers treat it as stale once the sources change.
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import csv
+import hashlib
+import json
+import os
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+KERNEL_SOURCES = ["csrc/qgemm.hip", "csrc/hadamard_quantize.hip", "csrc/block_stats.hip",
+                  "csrc/device_common.h"]
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(HERE, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def short_name(name: str) -> str:
+    n = name.replace("void ", "").replace("vdtq::", "")
+    return n.split("(")[0]
+
+
+def stats_table(path: str) -> str:
+    rows = list(csv.DictReader(open(path)))
+    out = ["| kernel | calls | total ms | avg us | min us | max us | % |", "|---|---|---|---|---|---|---|"]
+    for r in rows:
+        out.append("| {} | {} | {:.3f} | {:.1f} | {:.1f} | {:.1f} | {:.2f} |".format(
+            short_name(r["Name"]), r["Calls"], float(r["TotalDurationNs"]) / 1e6,
+            float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3,
+            float(r["Percentage"])))
+    return "\n".join(out)
+
+
+def trace_table(path: str) -> str:
+    """Median / min / mean duration per (kernel, grid) from a kernel trace."""
+    per = collections.defaultdict(list)
+    for r in csv.DictReader(open(path)):
+        n = short_name(r["Kernel_Name"])
+        if "FillFunctor" in n or "copyBuffer" in n:
+            continue
+        per[(n, int(r["Grid_Size_X"]))].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    out = ["| kernel | grid (work-items) | dispatches | median us | min us | mean us |", "|---|---|---|---|---|---|"]
+    for (n, g), v in sorted(per.items()):
+        v = sorted(v)
+        out.append(f"| {n} | {g} | {len(v)} | {v[len(v) // 2]:.1f} | {v[0]:.1f} | {sum(v) / len(v):.1f} |")
+    return "\n".join(out)
+
+
+def _counter_values(path: str, counter: str):
+    """Counter values (KiB) per dispatch, keyed by (kernel name, grid size in
+    work-items)."""
+    per = collections.defaultdict(list)
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] == counter:
+            per[(short_name(r["Kernel_Name"]), int(r["Grid_Size"]))].append(float(r["Counter_Value"]))
+    return per
+
+
+def _mean(v):
+    return sum(v) / len(v) if v else 0.0
+
+
+def _by_kernel(per):
+    out = collections.defaultdict(list)
+    for (k, _), v in per.items():
+        out[k].extend(v)
+    return {k: _mean(v) for k, v in out.items()}
+
+
+def traffic(fetch_csv: str, write_csv: str, copy_bytes: int, copy_kernel: str = "neg_kernel"):
+    """copy_kernel: substring naming the reference dispatch (an ordinary
+    elementwise kernel reading and writing copy_bytes each)."""
+    fg = _counter_values(fetch_csv, "FETCH_SIZE")
+    wg = _counter_values(write_csv, "WRITE_SIZE")
+    f, w = _by_kernel(fg), _by_kernel(wg)
+    ref = [k for k in f if copy_kernel in k and k in w]
+    if len(ref) != 1:
+        raise SystemExit(f"expected one {copy_kernel} dispatch kind in the counter files, found {ref}")
+    fs = copy_bytes / (f[ref[0]] * 1024.0)
+    ws = copy_bytes / (w[ref[0]] * 1024.0)
+    kernels = {}
+    for k in sorted(set(f) | set(w)):
+        fb = f.get(k, 0.0) * 1024.0 * fs
+        wb = w.get(k, 0.0) * 1024.0 * ws
+        grids = {}
+        for g in sorted({g for (n, g) in list(fg) + list(wg) if n == k}):
+            gf = _mean(fg.get((k, g), [])) * 1024.0 * fs
+            gw = _mean(wg.get((k, g), [])) * 1024.0 * ws
+            grids[str(g)] = {"fetch_bytes": gf, "write_bytes": gw, "bytes": gf + gw,
+                             "dispatches": len(fg.get((k, g), []))}
+        kernels[k] = {"fetch_bytes": fb, "write_bytes": wb, "bytes": fb + wb,
+                      "fetch_kib_raw": f.get(k, 0.0), "write_kib_raw": w.get(k, 0.0), "grids": grids}
+    return {"source_hash": source_hash(), "fetch_scale": fs, "write_scale": ws,
+            "copy_bytes": copy_bytes, "copy_kernel": ref[0], "kernels": kernels}
+
+
+def traffic_table(rec) -> str:
+    out = [f"fetch scale {rec['fetch_scale']:.4f}, write scale {rec['write_scale']:.4f} "
+           f"(reference: {rec['copy_kernel']}, {rec['copy_bytes']} bytes read and written)", "",
+           "| kernel | grid (work-items) | dispatches | fetch MiB | write MiB |", "|---|---|---|---|---|"]
+    for k, v in rec["kernels"].items():
+        if "FillFunctor" in k or "copyBuffer" in k:
+            continue
+        for g, e in v["grids"].items():
+            out.append(f"| {k} | {g} | {e['dispatches']} | {e['fetch_bytes'] / 2**20:.1f} | "
+                       f"{e['write_bytes'] / 2**20:.1f} |")
+    return "\n".join(out)
+
+
+def load_traffic(path: str):
+    """The traffic record if it was measured on the current kernel sources."""
+    try:
+        with open(path) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    return rec if rec.get("source_hash") == source_hash() else None
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    a = sub.add_parser("stats")
+    a.add_argument("csv")
+    t = sub.add_parser("trace")
+    t.add_argument("csv")
+    b = sub.add_parser("traffic")
+    b.add_argument("fetch_csv")
+    b.add_argument("write_csv")
+    b.add_argument("--copy-bytes", type=int, required=True)
+    b.add_argument("--copy-kernel", default="neg_kernel")
+    b.add_argument("--out", required=True)
+    args = ap.parse_args(argv)
+    if args.cmd == "stats":
+        print(stats_table(args.csv))
+    elif args.cmd == "trace":
+        print(trace_table(args.csv))
+    else:
+        rec = traffic(args.fetch_csv, args.write_csv, args.copy_bytes, args.copy_kernel)
+        with open(args.out, "w") as fh:
+            json.dump(rec, fh, indent=1)
+        print(traffic_table(rec))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
