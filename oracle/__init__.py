@@ -21,8 +21,7 @@ follow their public definitions: OCP 8-bit Floating Point Specification
 NVIDIA's NVFP4 layout (E2M1 elements, one E4M3 scale per 16 elements, one
 fp32 per-tensor scale).
 
-Every reading the pages leave open is listed in the design doc and restated at the
-function that adopts it.
+Every reading the pages leave open is stated at the function that adopts it.
 
 Parity pinning: every function here is pinned by tests/test_oracle_*.py to
 facts outside this package (closed forms, brute force, library casts,

@@ -14,9 +14,9 @@ What the pages fix:
 * [yly] §三: the first recompute after a skip has no previous difference to
   go on, so the whole block runs INT8.
 
-Readings (also in the design doc): one accumulator per block with its own
+Readings: one accumulator per block with its own
 threshold tau_acc, reset on every compute; only computed deltas enter the
-history; "temporal uncertainty" is r_last > tau_u (off by default);
+history; temporal uncertainty is read as r_last > tau_u (off by default);
 ties: Gamma == gamma -> INT8, r == tau -> compute, ratio == rho -> quantized.
 
 One call per block per denoising step:

@@ -2,8 +2,8 @@
 
 Test infrastructure only (see oracle/__init__.py).
 
-[gist] §2.A / §3.1 and [yly] §四: every linear keeps 4-bit weights ("W4A6",
-"W4A8") and runs with NVFP4 or INT8 activations.  Both operands are already
+[gist] §2.A / §3.1 and [yly] §四: every linear keeps 4-bit weights (the W4A6 and
+W4A8 operating points) and runs with NVFP4 or INT8 activations.  Both operands are already
 rotated by the same block Hadamard transform along K, so the product is the
 linear layer's output without further correction.
 

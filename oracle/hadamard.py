@@ -2,7 +2,7 @@
 
 Test infrastructure only (see oracle/__init__.py).
 
-[gist] §2.A (DMPQ, "Suavizado de Valores Atípicos") and [yly] §一: an online
+[gist] §2.A (DMPQ, the outlier-smoothing item) and [yly] §一: an online
 block Hadamard transform spreads activation outliers over the block before
 quantization.  The pages give no normalisation, order or block size; the
 readings adopted here (binding on the GPU path too):

@@ -3,9 +3,9 @@
 Test infrastructure only (see oracle/__init__.py).
 
 [gist] §2.A: a stable block runs its linears with NVFP4 activations, a
-volatile one with INT8; [yly] §一 says the same (NVFP4 = "small fire", INT8 =
-"big fire").  Neither page defines the encodings; the readings below are the
-ones this project adopts (listed in the design doc), and the GPU path is bound to
+volatile one with INT8; [yly] §一 says the same, likening NVFP4 to a low
+flame and INT8 to a high one.  Neither page defines the encodings; the readings below are the
+ones this project adopts, and the GPU path is bound to
 them bit for bit.
 
 NVFP4 (per tensor Y [M, K], K % 16 == 0):

@@ -10,7 +10,7 @@ two computed steps) predicts whether the block can be skipped.  [yly] §三:
 the outlier ratio, maximum over mean of the input, flags a step whose input
 is hard to quantize.
 
-Readings (also in DESIGN.md):
+Readings:
 * Delta = out - in, computed in fp32 from the bf16 tensors and cached as
   bf16 (round to nearest even).
 * Gamma = ||out - in||_F / ||in||_F over the block's whole [tokens, hidden]
