@@ -123,11 +123,66 @@ def dyn_schedule(blocks: int = 30, steps: int = 50, M: int = TOKENS_DYN,
         phi = rng.uniform(0.0, 2 * np.pi)
         par.append((a, beta, phi))
     rng = np.random.Generator(np.random.PCG64(7000))
-    spikes = set()
+    spikes = {}
     while len(spikes) < n_spikes:
-        spikes.add((int(rng.integers(0, blocks)), int(rng.integers(2, steps))))
+        key = (int(rng.integers(0, blocks)), int(rng.integers(2, steps)))
+        spikes[key] = int(rng.integers(0, hidden))
     return {"blocks": blocks, "steps": steps, "M": M, "hidden": hidden,
-            "params": par, "spikes": sorted(spikes)}
+            "params": par, "spikes": spikes}
+
+
+class DynWorkload:
+    """Seeded inputs of the closed-loop schedule study (host, float32 / bf16
+    bits).  Block 0's input at step t is Laplace(0, 1) with round(0.005 *
+    hidden) channels x30 (seed 500 + t, channels from seed 3000); block b's
+    input is block b-1's output.  U_b ~ Laplace (seed 4000 + b); the noise
+    Z_{b,t} is a fixed N(0, 1) field per block (seed 5000 + b) rotated by
+    7919 * t elements, so every step sees different noise without a fresh
+    draw.  A spike multiplies one channel of the block input by 300 (fp32
+    product, then bf16 round to nearest even)."""
+
+    SPIKE_MULT = 300.0
+    ROLL = 7919
+
+    def __init__(self, blocks=30, steps=50, M=TOKENS_DYN, hidden=1920, n_spikes=3):
+        self.sched = dyn_schedule(blocks, steps, M, hidden, n_spikes)
+        self.blocks, self.steps, self.M, self.hidden = blocks, steps, M, hidden
+        self._U, self._N = {}, {}
+
+    def block0_input(self, t: int) -> np.ndarray:
+        return to_bf16_bits(dyn_block_input(t, self.M, self.hidden))
+
+    def spike_channel(self, b: int, t: int):
+        return self.sched["spikes"].get((b, t))
+
+    def coefficients(self, b: int, t: int):
+        """(smooth, noise) fp32 multipliers of U_b and Z_{b,t}."""
+        a, beta, phi = self.sched["params"][b]
+        return (np.float32(a * (1.0 + 0.5 * np.sin(np.pi * t / self.steps + phi))),
+                np.float32(beta * np.exp(-t / 10.0)))
+
+    def U(self, b: int) -> np.ndarray:
+        if b not in self._U:
+            ru = np.random.Generator(np.random.PCG64(4000 + b))
+            shape = (self.M, self.hidden)
+            self._U[b] = (ru.standard_exponential(shape, dtype=np.float32)
+                          - ru.standard_exponential(shape, dtype=np.float32))
+        return self._U[b]
+
+    def N(self, b: int) -> np.ndarray:
+        if b not in self._N:
+            rz = np.random.Generator(np.random.PCG64(5000 + b))
+            self._N[b] = rz.standard_normal((self.M, self.hidden), dtype=np.float32)
+        return self._N[b]
+
+    def shift(self, t: int) -> int:
+        return (self.ROLL * t) % (self.M * self.hidden)
+
+    def delta(self, b: int, t: int) -> np.ndarray:
+        """Delta_{b,t} in fp32: RN(RN(smooth * U_b) + RN(noise * Z_{b,t}))."""
+        sm, nz = self.coefficients(b, t)
+        Z = np.roll(self.N(b).reshape(-1), self.shift(t)).reshape(self.M, self.hidden)
+        return (sm * self.U(b)).astype(np.float32) + (nz * Z).astype(np.float32)
 
 
 def dyn_block_input(t: int, M: int, hidden: int) -> np.ndarray:
@@ -138,15 +193,3 @@ def dyn_block_input(t: int, M: int, hidden: int) -> np.ndarray:
     ch = outlier_channels(hidden, n_outliers(hidden), 3000)
     x[:, ch] *= np.float32(30.0)
     return x
-
-
-def dyn_delta(b: int, t: int, M: int, hidden: int, params, steps: int) -> np.ndarray:
-    a, beta, phi = params[b]
-    ru = np.random.Generator(np.random.PCG64(4000 + b))
-    U = (ru.standard_exponential((M, hidden), dtype=np.float32)
-         - ru.standard_exponential((M, hidden), dtype=np.float32))
-    rz = np.random.Generator(np.random.PCG64(5000 + 100 * b + t))
-    Z = rz.standard_normal((M, hidden), dtype=np.float32)
-    smooth = np.float32(a * (1.0 + 0.5 * np.sin(np.pi * t / steps + phi)))
-    noise = np.float32(beta * np.exp(-t / 10.0))
-    return smooth * U + noise * Z

@@ -1,0 +1,114 @@
+"""Closed-loop driver of the schedule study, run once through the oracle and
+once through the library.
+
+Every block b at step t:
+  in_{0,t} = seeded input; in_{b,t} = out_{b-1,t}; a spike multiplies one
+  channel of in_{b,t} by 300;
+  ratio = max|in| / mean|in| (a statistics pass over the input alone);
+  action = dmpq_step(state_b, stats of the last step if computed, ratio);
+  SKIP:     out = bf16(in + Delta_cache)       (the cached delta is reused)
+  compute:  out = bf16(in + Delta_{b,t})       (synthetic block residual)
+            block_stats(in, out, Delta_cache) -> Delta_new, 8 statistics;
+            Delta_cache <- Delta_new.
+The precision of a computed step does not change the synthetic residual:
+the loop exercises the scheduler and the statistics, not the linears.
+
+The two sides share only the seeded inputs (synth.DynWorkload); each runs
+its own statistics, cache and scheduler."""
+import numpy as np
+
+from oracle import dmpq as OD, formats as F, stats as OS
+
+
+def _spiked(w, b, t, x_bits):
+    ch = w.spike_channel(b, t)
+    if ch is None:
+        return x_bits
+    x = F.bf16_to_f32(x_bits)
+    x[:, ch] = (x[:, ch] * np.float32(w.SPIKE_MULT)).astype(np.float32)
+    return F.f32_to_bf16(x)
+
+
+def oracle_loop(w, params: OD.Params, record=None):
+    """Returns (actions int[B, T], stats dict (b, t) -> float64[8])."""
+    B, T = w.blocks, w.steps
+    acts = np.zeros((B, T), np.int32)
+    stats = {}
+    st = [OD.State() for _ in range(B)]
+    last = [None] * B
+    cache = [None] * B
+    n = w.M * w.hidden
+    for t in range(T):
+        x = w.block0_input(t)
+        for b in range(B):
+            x = _spiked(w, b, t, x)
+            _, rs = OS.block_stats(x, x)
+            ratio = OS.outlier_ratio(rs[4], rs[5], n)
+            a = OD.dmpq_step(params, st[b], last[b], ratio)
+            acts[b, t] = a
+            if a == OD.SKIP:
+                out = F.f32_to_bf16((F.bf16_to_f32(x) + F.bf16_to_f32(cache[b])).astype(np.float32))
+                last[b] = None
+            else:
+                out = F.f32_to_bf16((F.bf16_to_f32(x) + w.delta(b, t)).astype(np.float32))
+                dnew, s = OS.block_stats(x, out, cache[b])
+                stats[(b, t)] = s
+                last[b] = s
+                cache[b] = dnew
+            if record is not None:
+                record(b, t, a, ratio)
+            x = out
+    return acts, stats
+
+
+def gpu_loop(w, params, sample=(), on_sample=None):
+    """The same loop through libvdtq: block_stats on the device, dmpq_step in
+    the library's C code.  Delta_{b,t} is formed on the device from the same
+    seeded fields.  For (b, t) in `sample`, on_sample(b, t, in, out, cache,
+    dnew, stats) receives the device operands (cache None on a block's first
+    computed step) and the statistics the library returned."""
+    import torch
+    import video_diffusion_transformer_block_amd as V
+
+    B, T, M, H = w.blocks, w.steps, w.M, w.hidden
+    n = M * H
+    dev = torch.device("cuda")
+    U = {b: torch.from_numpy(w.U(b)).to(dev) for b in range(B)}
+    Nf = {b: torch.from_numpy(w.N(b)).reshape(-1).to(dev) for b in range(B)}
+    acts = np.zeros((B, T), np.int32)
+    stats = {}
+    st = [V.dmpq_state() for _ in range(B)]
+    last = [None] * B
+    cache = [None] * B
+    spare = [torch.empty((M, H), dtype=torch.bfloat16, device=dev) for _ in range(B)]
+    for t in range(T):
+        x = torch.from_numpy(w.block0_input(t).view(np.int16)).view(torch.bfloat16).to(dev)
+        for b in range(B):
+            ch = w.spike_channel(b, t)
+            if ch is not None:
+                x = x.clone()
+                x[:, ch] = (x[:, ch].float() * w.SPIKE_MULT).to(torch.bfloat16)
+            _, rs = V.block_stats(x, x)
+            rs = rs.cpu().numpy()
+            ratio = V.outlier_ratio(rs[4], rs[5], n)
+            a = V.dmpq_step(params, st[b], last[b], ratio)
+            acts[b, t] = a
+            if a == V.ACT_SKIP:
+                out = (x.float() + cache[b].float()).to(torch.bfloat16)
+                last[b] = None
+            else:
+                sm, nz = w.coefficients(b, t)
+                Z = torch.roll(Nf[b], w.shift(t)).reshape(M, H)
+                delta = (U[b] * float(sm)) + (Z * float(nz))
+                out = (x.float() + delta).to(torch.bfloat16)
+                dnew = spare[b]
+                _, s = V.block_stats(x, out, cache[b], dnew)
+                s = s.cpu().numpy()
+                stats[(b, t)] = s
+                last[b] = s
+                if (b, t) in sample and on_sample is not None:
+                    on_sample(b, t, x, out, cache[b], dnew, s)
+                spare[b] = cache[b] if cache[b] is not None else torch.empty_like(dnew)
+                cache[b] = dnew
+            x = out
+    return acts, stats

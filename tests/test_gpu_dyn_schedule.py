@@ -1,0 +1,65 @@
+"""Closed-loop schedule study (30 blocks x 50 steps) through the library:
+block_stats on the GPU and dmpq_step in C, against the oracle's own loop.
+
+Small tokens (M = 35, hidden 1920): the whole loop runs on both sides and
+the 1500 actions must be identical, the statistics within 1e-5 relative
+(maxima exact).  The oracle-side margins of every compared statistic to its
+threshold are far above that tolerance for these seeds, so no decision can
+flip on rounding.  Full size (M = 4446): the library's loop runs alone,
+every action must occur, and the statistics and Delta_new of sampled
+computed steps are checked against the oracle on the same operands."""
+import numpy as np
+import pytest
+
+import synth
+import video_diffusion_transformer_block_amd as V
+from oracle import dmpq as OD, stats as OS
+from helpers import host_bits, need_gpu, log
+import dyn_loop
+
+pytestmark = pytest.mark.gpu
+
+
+def same_stats(got, want):
+    got, want = np.asarray(got), np.asarray(want)
+    assert got[4] == want[4] and got[6] == want[6], (got, want)
+    assert np.allclose(got, want, rtol=1e-5, atol=0), (got, want)
+
+
+def test_closed_loop_matches_oracle():
+    need_gpu()
+    w = synth.DynWorkload(M=35)
+    p = dict(gamma=0.1, tau=0.05, tau_acc=0.15, rho=400.0)
+    log("dyn loop M=35 oracle side")
+    want_acts, want_stats = dyn_loop.oracle_loop(w, OD.Params(**p))
+    assert set(np.unique(want_acts).tolist()) == {0, 1, 2, 3}
+    log("dyn loop M=35 library side")
+    got_acts, got_stats = dyn_loop.gpu_loop(w, V.dmpq_params(**p))
+    bad = np.argwhere(got_acts != want_acts)
+    assert len(bad) == 0, f"first differing (block, step): {bad[:5].tolist()}"
+    assert set(got_stats) == set(want_stats)
+    for k in want_stats:
+        same_stats(got_stats[k], want_stats[k])
+
+
+def test_closed_loop_full_size_sampled():
+    need_gpu()
+    w = synth.DynWorkload()
+    rng = np.random.Generator(np.random.PCG64(8000))
+    sample = {(int(rng.integers(0, w.blocks)), int(rng.integers(0, w.steps))) for _ in range(24)}
+    checked = []
+
+    def on_sample(b, t, x, out, cache, dnew, s):
+        dp = host_bits(cache) if cache is not None else None
+        dn_o, s_o = OS.block_stats(host_bits(x), host_bits(out), dp)
+        assert np.array_equal(host_bits(dnew), dn_o), (b, t)
+        same_stats(s, s_o)
+        checked.append((b, t))
+
+    log(f"dyn loop M={w.M} library side, {len(sample)} sampled pairs")
+    acts, stats = dyn_loop.gpu_loop(w, V.dmpq_params(gamma=0.1, tau=0.05, tau_acc=0.15, rho=1000.0),
+                                    sample, on_sample)
+    counts = np.bincount(acts.ravel(), minlength=4)
+    log(f"  actions skip/nvfp4/int8/bf16 = {counts.tolist()}, checked {len(checked)}")
+    assert (counts > 0).all()
+    assert len(checked) >= 8

@@ -146,3 +146,13 @@ def test_cogvideox_5b_linears_sampled(name):
     K, N = {n: (k, nn) for n, k, nn in synth.block_linears(3072)}[name]
     x, w = synth.layer_inputs(M, name, K, N)
     check_layer(x, w, rows=synth.row_sample(M, 48), out_dtypes=("bf16",))
+
+
+@pytest.mark.parametrize("name", ["qkv", "out", "ffn_up", "ffn_down"])
+def test_cogvideox_2b_linears_sampled(name):
+    """CogVideoX-2B-shaped block (hidden 1920): K = 1920 / 7680, N up to 7680."""
+    need_gpu()
+    M = synth.TOKENS_2B_5B
+    K, N = {n: (k, nn) for n, k, nn in synth.block_linears(1920)}[name]
+    x, w = synth.layer_inputs(M, name, K, N)
+    check_layer(x, w, rows=synth.row_sample(M, 48), out_dtypes=("bf16",))

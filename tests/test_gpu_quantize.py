@@ -136,3 +136,13 @@ def test_cogvideox_5b_shapes_sampled(fmt, K):
     name = "ffn_down" if K == 12288 else "qkv"
     x, _ = synth.layer_inputs(M, name, K, 16)
     run_and_compare(x, 64, fmt, rows=synth.row_sample(M, 256), stats=False)
+
+
+@pytest.mark.parametrize("fmt,K", [("nvfp4", 1920), ("int8", 1920), ("nvfp4", 7680), ("int8", 7680)])
+def test_cogvideox_2b_shapes_sampled(fmt, K):
+    """CogVideoX-2B-shaped activations (M = 17776, hidden 1920, FFN 7680)."""
+    need_gpu()
+    M = synth.TOKENS_2B_5B
+    name = "ffn_down" if K == 7680 else "qkv"
+    x, _ = synth.layer_inputs(M, name, K, 16)
+    run_and_compare(x, 64, fmt, rows=synth.row_sample(M, 256), stats=False)
