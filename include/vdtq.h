@@ -73,11 +73,14 @@ extern "C" {
 /* vdtq_workspace_bytes op ids */
 #define VDTQ_OP_HADAMARD_QUANTIZE 0
 #define VDTQ_OP_BLOCK_STATS 1
+#define VDTQ_OP_QGEMM 2          /* vdtq_workspace_bytes(VDTQ_OP_QGEMM, M, N) */
 
 const char* vdtq_last_error(void);
 const char* vdtq_version(void);
 
-/* Bytes of workspace a call needs for the given problem size (0 if none). */
+/* Bytes of workspace a call needs for the given problem size (0 if none).
+ * The (M, K) arguments are (rows, row length) for hadamard_quantize,
+ * (n, ignored) for block_stats and (M, N) for the two GEMMs. */
 size_t vdtq_workspace_bytes(int op, int64_t M, int64_t K);
 
 /*
@@ -144,12 +147,18 @@ int hadamard_quantize(const void* x_dev, int64_t M, int64_t K, int64_t ldx,
  * bias_dev float [N] or NULL
  * y_dev    out_dtype [M][ldy], ldy >= N (elements)
  * M, N >= 0 (0 is a no-op); K > 0, multiple of 16.
+ * ws_dev/ws_bytes  workspace of vdtq_workspace_bytes(VDTQ_OP_QGEMM, M, N)
+ *   bytes, 256-byte aligned: fp32 partial sums of output tiles split along
+ *   K (the tiles of a partial last wave), added in a fixed order.  No
+ *   initial contents are needed; calls on one stream may share it,
+ *   concurrent calls need distinct workspaces.
  */
 int qgemm_w4a4(const uint8_t* a_q_dev, const uint8_t* a_s_dev,
                const float* a_ts_dev, const uint8_t* w_q_dev,
                const uint8_t* w_s_dev, const float* w_ts_dev,
                const float* bias_dev, void* y_dev, int64_t ldy, int out_dtype,
-               int64_t M, int64_t N, int64_t K, void* stream);
+               int64_t M, int64_t N, int64_t K, void* ws_dev, size_t ws_bytes,
+               void* stream);
 
 /*
  * qgemm_w4a8 -- Y[m][n] = s_a[m] * gs_w * sum_k q_a[m][k] W_hat[n][k] + bias
@@ -162,13 +171,14 @@ int qgemm_w4a4(const uint8_t* a_q_dev, const uint8_t* a_s_dev,
  * scales 1 (E4M3 byte 0x38), gs_w = 1 and s_a = 1 the result equals the
  * integer sum_k q_a * e2m1(w) exactly while partial sums stay below 2^24.
  *
- * a_q_dev int8 [M][K]   a_s_dev float [M]   weights as in qgemm_w4a4.
+ * a_q_dev int8 [M][K]   a_s_dev float [M]   weights, workspace as in
+ * qgemm_w4a4.
  */
 int qgemm_w4a8(const int8_t* a_q_dev, const float* a_s_dev,
                const uint8_t* w_q_dev, const uint8_t* w_s_dev,
                const float* w_ts_dev, const float* bias_dev, void* y_dev,
                int64_t ldy, int out_dtype, int64_t M, int64_t N, int64_t K,
-               void* stream);
+               void* ws_dev, size_t ws_bytes, void* stream);
 
 /*
  * block_stats -- one pass over a block's input, output and cached delta.

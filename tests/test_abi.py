@@ -71,21 +71,31 @@ def test_hadamard_quantize_rejects(kw, code):
 
 def _gemm(fn, **kw):
     a = dict(aq=FAKE, as_=FAKE, ats=FAKE, wq=FAKE, ws=FAKE, wts=FAKE, bias=None, y=FAKE, ldy=64, od=0,
-             M=8, N=64, K=64)
+             M=8, N=64, K=64, gws=FAKE, gwsb=1 << 28)
     a.update(kw)
     if fn == "w4a4":
         return V.lib().qgemm_w4a4(a["aq"], a["as_"], a["ats"], a["wq"], a["ws"], a["wts"], a["bias"], a["y"],
-                                  a["ldy"], a["od"], a["M"], a["N"], a["K"], None)
+                                  a["ldy"], a["od"], a["M"], a["N"], a["K"], a["gws"], a["gwsb"], None)
     return V.lib().qgemm_w4a8(a["aq"], a["as_"], a["wq"], a["ws"], a["wts"], a["bias"], a["y"], a["ldy"],
-                              a["od"], a["M"], a["N"], a["K"], None)
+                              a["od"], a["M"], a["N"], a["K"], a["gws"], a["gwsb"], None)
 
 
 @pytest.mark.parametrize("fn", ["w4a4", "w4a8"])
 @pytest.mark.parametrize("kw", [dict(K=0), dict(K=40), dict(M=-2), dict(ldy=10), dict(od=3),
                                 dict(aq=None), dict(wq=None), dict(wts=None), dict(y=None),
-                                dict(aq=FAKE8), dict(M=1 << 31)])
+                                dict(aq=FAKE8), dict(M=1 << 31), dict(gws=None), dict(gwsb=4096),
+                                dict(gws=FAKE8)])
 def test_qgemm_rejects(fn, kw):
     assert _gemm(fn, **kw) == L.EINVAL
+
+
+def test_qgemm_workspace_size():
+    """One fp32 256 x 256 partial tile per K slice, at most one slice per CU
+    (256 on MI355X) in flight."""
+    slots = 256 * 256 * 256 * 4
+    assert V.lib().vdtq_workspace_bytes(L.OP_QGEMM, 17776, 3072) == slots
+    assert V.lib().vdtq_workspace_bytes(L.OP_QGEMM, 1, 1) == slots
+    assert V.lib().vdtq_workspace_bytes(L.OP_QGEMM, 0, 64) == 0
 
 
 def test_qgemm_empty_is_noop():

@@ -156,3 +156,22 @@ def test_cogvideox_2b_linears_sampled(name):
     K, N = {n: (k, nn) for n, k, nn in synth.block_linears(1920)}[name]
     x, w = synth.layer_inputs(M, name, K, N)
     check_layer(x, w, rows=synth.row_sample(M, 48), out_dtypes=("bf16",))
+
+
+@pytest.mark.parametrize("M,N,K", [(1000, 700, 1024), (300, 260, 3072), (17, 2000, 2048), (4400, 4400, 1536)])
+def test_split_k_repeatable(M, N, K):
+    """Few tiles (or a partial last wave: 4400 x 4400 is 324 tiles) and long
+    K: tiles are split into K slices whose fp32 partial sums a reduce pass
+    adds in slice order.  The result matches the oracle and three calls give
+    identical bits."""
+    need_gpu()
+    x = synth.to_bf16_bits(RNG.laplace(size=(M, K)).astype(np.float32))
+    w = synth.to_bf16_bits(RNG.standard_normal((N, K)).astype(np.float32) * 0.02)
+    check_layer(x, w, out_dtypes=("f32", "bf16"), rows=synth.row_sample(M, 64) if M > 2000 else None)
+    wd = V.hadamard_quantize(dev_bf16(w), 64, "nvfp4")
+    ad = V.hadamard_quantize(dev_bf16(x), 64, "nvfp4")
+    a8 = V.hadamard_quantize(dev_bf16(x), 64, "int8")
+    for fn, a in ((V.qgemm_w4a4, ad), (V.qgemm_w4a8, a8)):
+        ys = [fn(a, wd, None, "f32") for _ in range(3)]
+        torch.cuda.synchronize()
+        assert all(torch.equal(ys[0], y) for y in ys[1:])

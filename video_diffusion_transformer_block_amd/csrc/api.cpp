@@ -48,6 +48,7 @@ const char* vdtq_version(void) { return "vdtq 0.1.0 gfx950"; }
 size_t vdtq_workspace_bytes(int op, int64_t M, int64_t K) {
   if (op == VDTQ_OP_HADAMARD_QUANTIZE) return vdtq::hq_workspace_bytes(M, K);
   if (op == VDTQ_OP_BLOCK_STATS) return vdtq::bs_workspace_bytes(M);
+  if (op == VDTQ_OP_QGEMM) return vdtq::qgemm_workspace_bytes(M, K);
   return 0;
 }
 
@@ -106,28 +107,40 @@ static int qgemm_check(const char* name, const void* a_q, const void* a_s, const
   return VDTQ_OK;
 }
 
+static int qgemm_ws_check(const char* name, int64_t M, int64_t N, const void* ws, size_t ws_bytes) {
+  if (M == 0 || N == 0) return VDTQ_OK;
+  const size_t need = vdtq::qgemm_workspace_bytes(M, N);
+  if (!ws || !aligned(ws, 256) || ws_bytes < need)
+    return fail(VDTQ_EINVAL, "%s: workspace of %zu bytes (256-byte aligned) required, got %zu", name, need, ws_bytes);
+  return VDTQ_OK;
+}
+
 int qgemm_w4a4(const uint8_t* a_q_dev, const uint8_t* a_s_dev, const float* a_ts_dev, const uint8_t* w_q_dev,
                const uint8_t* w_s_dev, const float* w_ts_dev, const float* bias_dev, void* y_dev, int64_t ldy,
-               int out_dtype, int64_t M, int64_t N, int64_t K, void* stream) {
+               int out_dtype, int64_t M, int64_t N, int64_t K, void* ws_dev, size_t ws_bytes, void* stream) {
   int rc = qgemm_check("qgemm_w4a4", a_q_dev, a_s_dev, w_q_dev, w_s_dev, w_ts_dev, bias_dev, y_dev, ldy,
                        out_dtype, M, N, K);
   if (rc) return rc;
   if (M > 0 && N > 0 && (!a_ts_dev || !aligned(a_ts_dev, 4) || !aligned(a_s_dev, 8)))
     return fail(VDTQ_EINVAL, "qgemm_w4a4: null or misaligned a_ts / a_s");
+  rc = qgemm_ws_check("qgemm_w4a4", M, N, ws_dev, ws_bytes);
+  if (rc) return rc;
   hipError_t e = vdtq::launch_qgemm(0, a_q_dev, a_s_dev, a_ts_dev, w_q_dev, w_s_dev, w_ts_dev, bias_dev, y_dev,
-                                    ldy, out_dtype, M, N, K, static_cast<hipStream_t>(stream));
+                                    ldy, out_dtype, M, N, K, ws_dev, static_cast<hipStream_t>(stream));
   return hip_status(e, "qgemm_w4a4 launch");
 }
 
 int qgemm_w4a8(const int8_t* a_q_dev, const float* a_s_dev, const uint8_t* w_q_dev, const uint8_t* w_s_dev,
                const float* w_ts_dev, const float* bias_dev, void* y_dev, int64_t ldy, int out_dtype, int64_t M,
-               int64_t N, int64_t K, void* stream) {
+               int64_t N, int64_t K, void* ws_dev, size_t ws_bytes, void* stream) {
   int rc = qgemm_check("qgemm_w4a8", a_q_dev, a_s_dev, w_q_dev, w_s_dev, w_ts_dev, bias_dev, y_dev, ldy,
                        out_dtype, M, N, K);
   if (rc) return rc;
   if (M > 0 && N > 0 && !aligned(a_s_dev, 4)) return fail(VDTQ_EINVAL, "qgemm_w4a8: misaligned a_s");
+  rc = qgemm_ws_check("qgemm_w4a8", M, N, ws_dev, ws_bytes);
+  if (rc) return rc;
   hipError_t e = vdtq::launch_qgemm(1, a_q_dev, a_s_dev, nullptr, w_q_dev, w_s_dev, w_ts_dev, bias_dev, y_dev,
-                                    ldy, out_dtype, M, N, K, static_cast<hipStream_t>(stream));
+                                    ldy, out_dtype, M, N, K, ws_dev, static_cast<hipStream_t>(stream));
   return hip_status(e, "qgemm_w4a8 launch");
 }
 

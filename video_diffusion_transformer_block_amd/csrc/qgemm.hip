@@ -41,12 +41,22 @@
 //                                XCDs; each XCD gets a contiguous range of
 //                                tile ids, walked in groups of 8 M-tiles, so
 //                                the A and W stripes it needs stay in its L2.
+//   work split (K % 128 == 0)    whole waves of tiles run data-parallel, one
+//                                tile per workgroup; the tiles of a partial
+//                                last wave are then split into K slices (one
+//                                workgroup each, at most one per CU in all)
+//                                when that beats the partial wave, and a
+//                                reduce pass adds the fp32 slices in slice
+//                                order (deterministic) and writes the output.
+#include <algorithm>
+
 #include "device_common.h"
 #include "launch.h"
 
 namespace vdtq {
 
 constexpr int GT = 256;     // threads per workgroup
+constexpr int kGemmMaxGrid = 256;   // pipelined path: at most one workgroup per CU
 constexpr int BK = 128;     // K per stage
 
 struct GemmParams {
@@ -62,6 +72,12 @@ struct GemmParams {
   int32_t M, N, K;
   int32_t out_f32;
   int32_t tiles_m, tiles_n;
+  // pipelined path: K stages per tile and the work split of the grid
+  int32_t nk;
+  int32_t sk_tiles;        // tiles 0 .. sk_tiles-1 are split along K (stream-K)
+  int32_t slices;          // K slices per split tile (>= 2 when sk_tiles > 0)
+  int32_t slice_nk;        // stages per slice (the last may be shorter)
+  float* part;             // [slices][sk_tiles][256 * 256] partial tiles
 };
 
 // --------------------------------------------------------------- decoding
@@ -197,7 +213,28 @@ struct Cfg {
   static constexpr int STAGE = A_CODES + A_SC + W_CODES + W_SC;
 };
 
-// Tile coordinates: XCD-contiguous ranges, grouped by 8 M-tiles.
+// Tile id -> coordinates: groups of 8 M-tiles, walked along N, so that tiles
+// with neighbouring ids share A and W stripes.
+__device__ __forceinline__ void tile_coords(int id, int tiles_m, int tiles_n, int& tm, int& tn) {
+  constexpr int GM = 8;
+  const int per_group = GM * tiles_n;
+  const int g = id / per_group;
+  const int first_m = g * GM;
+  const int gsz = min(tiles_m - first_m, GM);
+  const int in = id - g * per_group;
+  tm = first_m + in % gsz;
+  tn = in / gsz;
+}
+
+// Workgroups are dealt round-robin to the 8 XCDs: give each XCD a
+// contiguous range of ids, in dispatch order within the XCD.
+__device__ __forceinline__ int xcd_range_id(int bid, int nblocks) {
+  const int xcd = bid % 8, idx = bid / 8;
+  const int base = nblocks / 8, rem = nblocks % 8;
+  return xcd * base + min(xcd, rem) + idx;
+}
+
+// Tile coordinates of a data-parallel launch: XCD-contiguous id ranges.
 __device__ __forceinline__ void tile_of(int bid, int nblocks, int tiles_m, int tiles_n, int& tm, int& tn) {
   const int xcd = bid % 8, idx = bid / 8;
   const int base = nblocks / 8, rem = nblocks % 8;
@@ -389,6 +426,13 @@ __device__ __forceinline__ void dma4(const void* base, uint32_t voff, uint32_t m
                ::"s"(m0), "v"(voff), "s"(base) : "memory", "m0");
 }
 
+// Partial tile of slice `sl` of split tile `tile`.  Layout inside a slot:
+// [wave][64 float4][64 lanes], float4 q of a lane holding accumulator tile
+// (q / 16, (q / 4) % 4), registers 4 (q % 4) .. 4 (q % 4) + 3.
+__device__ __forceinline__ float4* part_slot(const GemmParams& p, int sl, int tile) {
+  return reinterpret_cast<float4*>(p.part) + ((size_t)sl * p.sk_tiles + tile) * (256 * 256 / 4);
+}
+
 template <int AFMT>
 struct Pipe {
   static constexpr bool A8 = AFMT == 1;
@@ -411,7 +455,12 @@ struct Raw {
   uint4 w[4];
 };
 
-template <int AFMT>
+// SPLIT = false: one whole tile per workgroup, tiles sk_tiles .. tiles-1
+// dealt in XCD-contiguous ranges (hardware dispatch balances the CUs).
+// SPLIT = true: one K slice of one of the tiles 0 .. sk_tiles-1 per
+// workgroup; the fp32 partial sums go to the workspace and qgemm_reduce_kernel
+// adds the slices and writes the output.
+template <int AFMT, bool SPLIT>
 __global__ __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void qgemm_pipe_kernel(GemmParams p) {
   using P = Pipe<AFMT>;
@@ -422,18 +471,21 @@ void qgemm_pipe_kernel(GemmParams p) {
   const int lane = t & 63;
   const int wv = t >> 6;
   const int wm = wv >> 1, wn = wv & 1;
-  int tm, tn;
-  tile_of(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, tm, tn);
-  const int m0 = tm * 256, n0 = tn * 256;
   const int K = p.K;
-  const int nk = K / BK;
+  const int nk = p.nk;
 
   const uint8_t* aq = static_cast<const uint8_t*>(p.a_q);
   const uint8_t* as = static_cast<const uint8_t*>(p.a_s);
 
-  // ---- per-lane byte offsets of the DMA sources at k0 = 0 (32-bit: every
-  // operand matrix is below 4 GB, checked on the host)
+  // ---- per-lane byte offsets of the DMA sources at k0 = 0 for the current
+  // tile (32-bit: every operand matrix is below 4 GB, checked on the host)
   uint32_t offA[P::NA], offAS[P::NAS > 0 ? P::NAS : 1], offW[P::NW], offWS[P::NWS];
+  int m0 = 0, n0 = 0;
+  auto set_tile = [&](int tile) {
+  int tm, tn;
+  tile_coords(tile, p.tiles_m, p.tiles_n, tm, tn);
+  m0 = tm * 256;
+  n0 = tn * 256;
 #pragma unroll
   for (int u = 0; u < P::NA; ++u) {
     if (A8) {
@@ -462,12 +514,16 @@ void qgemm_pipe_kernel(GemmParams p) {
     const int r = (wv * P::NWS + u) * 32 + (lane >> 1);
     offWS[u] = (uint32_t)min(n0 + r, p.N - 1) * (uint32_t)(K / 16) + 4u * (lane & 1);
   }
+  };
 
   // LDS byte address of smem and of this wave's regions (wave-uniform)
   const uint32_t lds0 = (uint32_t)(size_t)(lds_void_t*)smem;
   const uint32_t wvu = __builtin_amdgcn_readfirstlane(wv);
+  // ring slot of stage kt: counted from the first stage of the segment
+  int kbase = 0;
+  auto ring = [&](int kt) { return (kt - kbase) % P::NS; };
   auto issue_stage = [&](int kt) {
-    const uint32_t st = lds0 + (uint32_t)(kt % P::NS) * P::STAGE;
+    const uint32_t st = lds0 + (uint32_t)ring(kt) * P::STAGE;
     const int k0 = kt * BK;
     const uint8_t* abase = aq + (A8 ? k0 : k0 / 2);
     const uint8_t* asbase = as + k0 / 16;
@@ -487,7 +543,7 @@ void qgemm_pipe_kernel(GemmParams p) {
   // ---- LDS read offsets of this lane's fragments (within a stage)
   const int r32 = lane & 31, h = lane >> 5;
   auto read_codes = [&](int kt, int c, Raw<A8>& R) {
-    const uint8_t* st = smem + (kt % P::NS) * P::STAGE;
+    const uint8_t* st = smem + ring(kt) * P::STAGE;
     const int qd = 2 * c + h;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -507,7 +563,7 @@ void qgemm_pipe_kernel(GemmParams p) {
   };
   // the 8 scale bytes (groups of both chunks) of each of this lane's rows
   auto read_scales = [&](int kt, uint2 (&sa)[4], uint2 (&sw)[4]) {
-    const uint8_t* st = smem + (kt % P::NS) * P::STAGE;
+    const uint8_t* st = smem + ring(kt) * P::STAGE;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if (!A8) sa[i] = *reinterpret_cast<const uint2*>(st + P::A_CODES + (wm * 128 + 32 * i + r32) * 8);
@@ -544,12 +600,6 @@ void qgemm_pipe_kernel(GemmParams p) {
   };
 
   float16v acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
   // D = W_frag x A_frag^T: each accumulator tile is a 32 x 32 block of Y^T,
   // so a lane holds one token row and, per register group of 4, four
@@ -574,25 +624,45 @@ void qgemm_pipe_kernel(GemmParams p) {
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  // ---- prologue: stages 0..2 in flight, wait for stage 0
-  issue_stage(0);
-  if (nk > 1) issue_stage(1);
-  if (nk > 2) issue_stage(2);
-  if (nk > 2) wait_vm<2 * P::LPS>();
-  else if (nk > 1) wait_vm<P::LPS>();
+  int tile, kb, ke;
+  if constexpr (SPLIT) {
+    tile = (int)(blockIdx.x % p.sk_tiles);
+    const int sl = (int)(blockIdx.x / p.sk_tiles);
+    kb = sl * p.slice_nk;
+    ke = min(nk, kb + p.slice_nk);
+  } else {
+    tile = p.sk_tiles + xcd_range_id(blockIdx.x, gridDim.x);
+    kb = 0;
+    ke = nk;
+  }
+  set_tile(tile);
+  kbase = kb;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+  // ---- prologue: stages kb..kb+2 in flight, wait for stage kb
+  issue_stage(kb);
+  if (ke - kb > 1) issue_stage(kb + 1);
+  if (ke - kb > 2) issue_stage(kb + 2);
+  if (ke - kb > 2) wait_vm<2 * P::LPS>();
+  else if (ke - kb > 1) wait_vm<P::LPS>();
   else wait_vm<0>();
   wait_lgkm_barrier();
 
   Raw<A8> R0, R1;
   uint2 sa[4], sw[4], na[4], nw[4];
   half8 fa[4], fb[4], ga[4], gb[4];
-  read_codes(0, 0, R0);
-  read_scales(0, sa, sw);
+  read_codes(kb, 0, R0);
+  read_scales(kb, sa, sw);
   decode(R0, sa, sw, 0, 0, fa, fb);
 
   // Every step has the same shape; past the last stage the reads of the
   // "next" stage hit a stale ring slot and the extra decode is discarded.
-  for (int kt = 0; kt < nk; ++kt) {
+  for (int kt = kb; kt < ke; ++kt) {
     // step 0 | decode step 1
     decode(R0, sa, sw, 0, 1, ga, gb);
     mfma16(fa, fb);
@@ -611,10 +681,10 @@ void qgemm_pipe_kernel(GemmParams p) {
     mfma16(ga, gb);
     interleave();
     // mid-stage barrier: next stage complete, this buffer free
-    if (kt + 2 < nk) wait_vm<P::LPS>();
+    if (kt + 2 < ke) wait_vm<P::LPS>();
     else wait_vm<0>();
     wait_lgkm_barrier();
-    if (kt + 3 < nk) issue_stage(kt + 3);
+    if (kt + 3 < ke) issue_stage(kt + 3);
     // step 4 | read stage kt+1 scales, decode step 5
     read_scales(kt + 1, na, nw);
     decode(R1, sa, sw, 1, 1, ga, gb);
@@ -644,65 +714,176 @@ void qgemm_pipe_kernel(GemmParams p) {
   const bool vec = (p.N % 4) == 0 && (p.ldy % 4) == 0 &&
                    ((reinterpret_cast<uintptr_t>(p.y) & (p.out_f32 ? 15u : 7u)) == 0) &&
                    (!p.bias || (reinterpret_cast<uintptr_t>(p.bias) & 15u) == 0);
+  // four consecutive outputs of one row: scale, bias, convert, store
+  auto emit4 = [&](int row, int col, float alpha, float x0, float x1, float x2, float x3) {
+    float v[4] = {x0 * alpha, x1 * alpha, x2 * alpha, x3 * alpha};
+    if (vec && col + 4 <= p.N) {
+      if (p.bias) {
+        const float4 b = *reinterpret_cast<const float4*>(p.bias + col);
+        v[0] = v[0] + b.x; v[1] = v[1] + b.y; v[2] = v[2] + b.z; v[3] = v[3] + b.w;
+      }
+      if (p.out_f32) {
+        *reinterpret_cast<float4*>(static_cast<float*>(p.y) + (int64_t)row * p.ldy + col) =
+            make_float4(v[0], v[1], v[2], v[3]);
+      } else {
+        const uint32_t lo = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
+        const uint32_t hi = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.y) + (int64_t)row * p.ldy + col) = make_uint2(lo, hi);
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (col + q >= p.N) continue;
+        float x = v[q];
+        if (p.bias) x = x + p.bias[col + q];
+        if (p.out_f32)
+          static_cast<float*>(p.y)[(int64_t)row * p.ldy + col + q] = x;
+        else
+          static_cast<uint16_t*>(p.y)[(int64_t)row * p.ldy + col + q] = (uint16_t)f32_to_bf16_bits(x);
+      }
+    }
+  };
+  auto row_alpha = [&](int row) {
+    return (AFMT == 0) ? alpha_t : static_cast<const float*>(p.a_s)[row] * gsw;
+  };
+
+  if constexpr (SPLIT) {
+    // partial sums of this K slice; the reduce kernel finishes the tile
+    float4* mine = part_slot(p, (int)(blockIdx.x / p.sk_tiles), tile) + wv * 64 * 64 + lane;
+#pragma unroll
+    for (int q = 0; q < 64; ++q) {
+      const int i = q >> 4, j = (q >> 2) & 3, g = q & 3;
+      mine[q * 64] = make_float4(acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
+    }
+    return;
+  }
+
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int row = m0 + wm * 128 + 32 * i + r32;
     if (row >= p.M) continue;
-    const float alpha = (AFMT == 0) ? alpha_t : static_cast<const float*>(p.a_s)[row] * gsw;
+    const float alpha = row_alpha(row);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int col = n0 + wn * 128 + 32 * j + 8 * g + 4 * h;
-        float v[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) v[q] = acc[i][j][4 * g + q] * alpha;
-        if (vec && col + 4 <= p.N) {
-          if (p.bias) {
-            const float4 b = *reinterpret_cast<const float4*>(p.bias + col);
-            v[0] = v[0] + b.x; v[1] = v[1] + b.y; v[2] = v[2] + b.z; v[3] = v[3] + b.w;
-          }
-          if (p.out_f32) {
-            *reinterpret_cast<float4*>(static_cast<float*>(p.y) + (int64_t)row * p.ldy + col) =
-                make_float4(v[0], v[1], v[2], v[3]);
-          } else {
-            const uint32_t lo = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
-            const uint32_t hi = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
-            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.y) + (int64_t)row * p.ldy + col) = make_uint2(lo, hi);
-          }
-        } else {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            if (col + q >= p.N) continue;
-            float x = v[q];
-            if (p.bias) x = x + p.bias[col + q];
-            if (p.out_f32)
-              static_cast<float*>(p.y)[(int64_t)row * p.ldy + col + q] = x;
-            else
-              static_cast<uint16_t*>(p.y)[(int64_t)row * p.ldy + col + q] = (uint16_t)f32_to_bf16_bits(x);
-          }
-        }
-      }
-    }
+      for (int g = 0; g < 4; ++g)
+        emit4(row, n0 + wn * 128 + 32 * j + 8 * g + 4 * h, alpha, acc[i][j][4 * g], acc[i][j][4 * g + 1],
+              acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
   }
 }
 
+// Split tiles: out = alpha * (sum of the slices in slice order) + bias.
+// One thread per float4 of a partial slot; 64 workgroups per tile.
 template <int AFMT>
-static hipError_t launch_pipe(GemmParams p, hipStream_t st) {
-  using P = Pipe<AFMT>;
+__global__ __launch_bounds__(256) void qgemm_reduce_kernel(GemmParams p) {
+  const int tile = (int)(blockIdx.x / 64);
+  const int f = (int)(blockIdx.x % 64) * 256 + (int)threadIdx.x;   // float4 index in the slot
+  const int wv = f >> 12, q = (f >> 6) & 63, lane = f & 63;
+  const int i = q >> 4, j = (q >> 2) & 3, g = q & 3;
+  int tm, tn;
+  tile_coords(tile, p.tiles_m, p.tiles_n, tm, tn);
+  const int row = tm * 256 + (wv >> 1) * 128 + 32 * i + (lane & 31);
+  const int col = tn * 256 + (wv & 1) * 128 + 32 * j + 8 * g + 4 * (lane >> 5);
+  if (row >= p.M) return;
+  float4 sum = part_slot(p, 0, tile)[f];
+  for (int sl = 1; sl < p.slices; ++sl) {
+    const float4 x = part_slot(p, sl, tile)[f];
+    sum.x += x.x; sum.y += x.y; sum.z += x.z; sum.w += x.w;
+  }
+  const float gsw = p.w_ts[1];
+  const float alpha = (AFMT == 0) ? p.a_ts[1] * gsw : static_cast<const float*>(p.a_s)[row] * gsw;
+  float v[4] = {sum.x * alpha, sum.y * alpha, sum.z * alpha, sum.w * alpha};
+  const bool vec = (p.N % 4) == 0 && (p.ldy % 4) == 0 && col + 4 <= p.N &&
+                   ((reinterpret_cast<uintptr_t>(p.y) & (p.out_f32 ? 15u : 7u)) == 0) &&
+                   (!p.bias || (reinterpret_cast<uintptr_t>(p.bias) & 15u) == 0);
+  if (vec) {
+    if (p.bias) {
+      const float4 b = *reinterpret_cast<const float4*>(p.bias + col);
+      v[0] = v[0] + b.x; v[1] = v[1] + b.y; v[2] = v[2] + b.z; v[3] = v[3] + b.w;
+    }
+    if (p.out_f32) {
+      *reinterpret_cast<float4*>(static_cast<float*>(p.y) + (int64_t)row * p.ldy + col) =
+          make_float4(v[0], v[1], v[2], v[3]);
+    } else {
+      const uint32_t lo = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
+      const uint32_t hi = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
+      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.y) + (int64_t)row * p.ldy + col) = make_uint2(lo, hi);
+    }
+    return;
+  }
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    if (col + c >= p.N) continue;
+    float x = v[c];
+    if (p.bias) x = x + p.bias[col + c];
+    if (p.out_f32)
+      static_cast<float*>(p.y)[(int64_t)row * p.ldy + col + c] = x;
+    else
+      static_cast<uint16_t*>(p.y)[(int64_t)row * p.ldy + col + c] = (uint16_t)f32_to_bf16_bits(x);
+  }
+}
+// Work split of a pipelined call on `cus` compute units.  Whole waves of
+// tiles go to the data-parallel kernel.  The tiles of a last, partial wave
+// (all tiles when there are fewer than CUs) are split into `slices` K slices,
+// at most one workgroup per CU in all, when that is estimated to finish
+// sooner than a partial wave of whole tiles: a slice's stages plus about
+// kSplitOverhead stages of pipeline fill, partial-sum traffic and the reduce
+// pass, against nk.
+constexpr int kSplitOverhead = 3;
+
+static void plan_pipe(GemmParams& p, int cus, int& dp_grid, int& sk_grid) {
   p.tiles_m = (p.M + 255) / 256;
   p.tiles_n = (p.N + 255) / 256;
-  const int nblocks = p.tiles_m * p.tiles_n;
-  const size_t lds = (size_t)P::NS * P::STAGE;
+  p.nk = p.K / BK;
+  const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n;
+  const int G = std::max(1, std::min(cus, kGemmMaxGrid));
+  const int64_t left = tiles % G;
+  int slices = left > 0 ? (int)std::min<int64_t>(G / left, p.nk) : 0;
+  int slice_nk = slices > 0 ? (p.nk + slices - 1) / slices : 0;
+  if (slices > 0) slices = (p.nk + slice_nk - 1) / slice_nk;   // no empty slice
+  const bool split = slices >= 2 && slice_nk + kSplitOverhead < p.nk;
+  p.sk_tiles = split ? (int32_t)left : 0;
+  p.slices = split ? slices : 0;
+  p.slice_nk = split ? slice_nk : 0;
+  dp_grid = (int)(tiles - p.sk_tiles);
+  sk_grid = split ? (int)(left * slices) : 0;
+}
+
+template <int AFMT, bool SPLIT>
+static hipError_t set_lds_attr() {
+  using P = Pipe<AFMT>;
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&qgemm_pipe_kernel<AFMT>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&qgemm_pipe_kernel<AFMT, SPLIT>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)(P::NS * P::STAGE));
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL((qgemm_pipe_kernel<AFMT>), dim3(nblocks), dim3(GT), lds, st, p);
-  return hipGetLastError();
+  return hipSuccess;
+}
+
+template <int AFMT>
+static hipError_t launch_pipe(GemmParams p, int cus, hipStream_t st) {
+  using P = Pipe<AFMT>;
+  int dp_grid = 0, sk_grid = 0;
+  plan_pipe(p, cus, dp_grid, sk_grid);
+  const size_t lds = (size_t)P::NS * P::STAGE;
+  hipError_t e = set_lds_attr<AFMT, false>();
+  if (e == hipSuccess) e = set_lds_attr<AFMT, true>();
+  if (e != hipSuccess) return e;
+  if (dp_grid > 0) {
+    hipLaunchKernelGGL((qgemm_pipe_kernel<AFMT, false>), dim3(dp_grid), dim3(GT), lds, st, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (sk_grid > 0) {
+    hipLaunchKernelGGL((qgemm_pipe_kernel<AFMT, true>), dim3(sk_grid), dim3(GT), lds, st, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((qgemm_reduce_kernel<AFMT>), dim3(p.sk_tiles * 64), dim3(256), 0, st, p);
+    e = hipGetLastError();
+  }
+  return e;
 }
 
 template <int AFMT, int TI, int TJ>
@@ -723,18 +904,42 @@ static hipError_t launch_cfg(GemmParams p, hipStream_t st) {
   return hipGetLastError();
 }
 
+size_t qgemm_workspace_bytes(int64_t M, int64_t N) {
+  if (M <= 0 || N <= 0) return 0;
+  // at most one K slice per CU (kGemmMaxGrid) is in flight
+  return (size_t)kGemmMaxGrid * 256 * 256 * sizeof(float);
+}
+
+static int cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return kGemmMaxGrid;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = kGemmMaxGrid;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
 hipError_t launch_qgemm(int afmt, const void* a_q, const void* a_s, const float* a_ts,
                         const uint8_t* w_q, const uint8_t* w_s, const float* w_ts,
                         const float* bias, void* y, int64_t ldy, int out_dtype, int64_t M,
-                        int64_t N, int64_t K, hipStream_t st) {
+                        int64_t N, int64_t K, void* ws, hipStream_t st) {
   if (M == 0 || N == 0) return hipSuccess;
-  GemmParams p{a_q, a_s, a_ts, w_q, w_s, w_ts, bias, y, ldy, (int32_t)M, (int32_t)N, (int32_t)K,
-               out_dtype == 1, 0, 0};
+  GemmParams p{};
+  p.a_q = a_q; p.a_s = a_s; p.a_ts = a_ts;
+  p.w_q = w_q; p.w_s = w_s; p.w_ts = w_ts;
+  p.bias = bias; p.y = y; p.ldy = ldy;
+  p.M = (int32_t)M; p.N = (int32_t)N; p.K = (int32_t)K;
+  p.out_f32 = out_dtype == 1;
+  p.part = static_cast<float*>(ws);
   // The pipelined kernel needs whole 128-wide K stages and 32-bit byte
   // offsets into every operand matrix.
   const bool fast = (K % BK) == 0 && (afmt == 1 ? M * K : M * K / 2) < (int64_t(1) << 32) &&
                     N * K / 2 < (int64_t(1) << 32);
-  if (fast) return afmt == 0 ? launch_pipe<0>(p, st) : launch_pipe<1>(p, st);
+  if (fast) return afmt == 0 ? launch_pipe<0>(p, cu_count(), st) : launch_pipe<1>(p, cu_count(), st);
   if (afmt == 0) return launch_cfg<0, 4, 4>(p, st);
   return launch_cfg<1, 4, 4>(p, st);
 }

@@ -42,6 +42,21 @@ def workspace(device: torch.device, nbytes: int) -> torch.Tensor:
     return buf
 
 
+_gemm_ws = {}
+
+
+def gemm_workspace(device: torch.device, M: int, N: int) -> torch.Tensor:
+    """Per-device GEMM workspace (fp32 partial tiles of K slices), reused by
+    every GEMM call on that device (calls on one stream run in order)."""
+    key = torch.device(device).index
+    nbytes = L.lib().vdtq_workspace_bytes(L.OP_QGEMM, M, N)
+    buf = _gemm_ws.get(key)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.empty(max(nbytes, 4096), dtype=torch.uint8, device=device)
+        _gemm_ws[key] = buf
+    return buf
+
+
 @dataclass
 class NVFP4Tensor:
     """Packed codes [R, K/2] u8, E4M3 scales [R, K/16] u8, {amax, gs} f32[2]."""
@@ -121,9 +136,10 @@ def qgemm_w4a4(a: NVFP4Tensor, w: NVFP4Tensor, bias: Optional[torch.Tensor] = No
     if w.q.shape[1] * 2 != K:
         raise ValueError("K mismatch between activations and weights")
     y = _out(M, N, out_dtype, a.q.device, y)
+    ws = gemm_workspace(a.q.device, M, N)
     L.check(L.lib().qgemm_w4a4(_p(a.q), _p(a.scales), _p(a.ts), _p(w.q), _p(w.scales), _p(w.ts), _p(bias),
                                _p(y), y.stride(0), L.OUT_BF16 if out_dtype == "bf16" else L.OUT_F32,
-                               M, N, K, _stream(a.q.device)))
+                               M, N, K, _p(ws), ws.numel(), _stream(a.q.device)))
     return y
 
 
@@ -134,9 +150,10 @@ def qgemm_w4a8(a: INT8Tensor, w: NVFP4Tensor, bias: Optional[torch.Tensor] = Non
     if w.q.shape[1] * 2 != K:
         raise ValueError("K mismatch between activations and weights")
     y = _out(M, N, out_dtype, a.q.device, y)
+    ws = gemm_workspace(a.q.device, M, N)
     L.check(L.lib().qgemm_w4a8(_p(a.q), _p(a.scales), _p(w.q), _p(w.scales), _p(w.ts), _p(bias),
                                _p(y), y.stride(0), L.OUT_BF16 if out_dtype == "bf16" else L.OUT_F32,
-                               M, N, K, _stream(a.q.device)))
+                               M, N, K, _p(ws), ws.numel(), _stream(a.q.device)))
     return y
 
 
