@@ -87,7 +87,7 @@ def hadamard_quantize(x: torch.Tensor, had_block: int = 64, fmt: str = "nvfp4", 
     M, K = x.shape
     dev = x.device
     flags = L.STATS if stats else 0
-    st = torch.zeros(4, dtype=torch.float64, device=dev) if stats else None
+    st = torch.empty(4, dtype=torch.float64, device=dev) if stats else None
     nbytes = L.lib().vdtq_workspace_bytes(L.OP_HADAMARD_QUANTIZE, M, K)
     ws = workspace(dev, nbytes)
     if out is not None and stats and out.stats is not None:
@@ -98,7 +98,9 @@ def hadamard_quantize(x: torch.Tensor, had_block: int = 64, fmt: str = "nvfp4", 
         else:
             q = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
             s = torch.empty((M, K // 16), dtype=torch.uint8, device=dev)
-            ts = torch.zeros(2, dtype=torch.float32, device=dev)
+            ts = torch.empty(2, dtype=torch.float32, device=dev)
+            if isinstance(amax, str) and amax == "given":
+                raise ValueError('amax="given" reuses out.ts[0]: pass out=')
         if amax is not None:
             flags |= L.AMAX_GIVEN
             if not (isinstance(amax, str) and amax == "given"):
