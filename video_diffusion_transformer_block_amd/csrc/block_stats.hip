@@ -107,14 +107,18 @@ __global__ __launch_bounds__(BS_THREADS) void block_stats_kernel(const uint16_t*
   }
 }
 
-__global__ __launch_bounds__(BS_THREADS) void block_stats_final_kernel(const double* part, int nparts,
-                                                                       double* stats) {
-  __shared__ double red[8][BS_THREADS / 64];
+constexpr int kBsFinalThreads = 1024;
+
+__global__ __launch_bounds__(kBsFinalThreads) void block_stats_final_kernel(const double* part, int nparts,
+                                                                            double* stats) {
+  __shared__ double red[8][kBsFinalThreads / 64];
   double vals[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int i = threadIdx.x; i < nparts; i += BS_THREADS)
-#pragma unroll
-    for (int k = 0; k < 8; ++k)
-      vals[k] = (k == 4 || k == 6) ? fmax(vals[k], part[8 * i + k]) : vals[k] + part[8 * i + k];
+  for (int i = threadIdx.x; i < nparts; i += kBsFinalThreads) {
+    const double4 lo = reinterpret_cast<const double4*>(part)[2 * i];
+    const double4 hi = reinterpret_cast<const double4*>(part)[2 * i + 1];
+    vals[0] += lo.x; vals[1] += lo.y; vals[2] += lo.z; vals[3] += lo.w;
+    vals[4] = fmax(vals[4], hi.x); vals[5] += hi.y; vals[6] = fmax(vals[6], hi.z); vals[7] += hi.w;
+  }
 #pragma unroll
   for (int k = 0; k < 8; ++k) vals[k] = (k == 4 || k == 6) ? wave_max_d(vals[k]) : wave_sum(vals[k]);
   const int w = threadIdx.x >> 6;
@@ -125,7 +129,7 @@ __global__ __launch_bounds__(BS_THREADS) void block_stats_final_kernel(const dou
   if (threadIdx.x < 8) {
     const int k = threadIdx.x;
     double r = red[k][0];
-    for (int i = 1; i < BS_THREADS / 64; ++i) r = (k == 4 || k == 6) ? fmax(r, red[k][i]) : r + red[k][i];
+    for (int i = 1; i < kBsFinalThreads / 64; ++i) r = (k == 4 || k == 6) ? fmax(r, red[k][i]) : r + red[k][i];
     stats[k] = r;
   }
 }
@@ -139,7 +143,7 @@ hipError_t launch_block_stats(const void* in, const void* out, const void* dprev
   hipLaunchKernelGGL(block_stats_kernel, dim3(grid), dim3(BS_THREADS), 0, st,
                      static_cast<const uint16_t*>(in), static_cast<const uint16_t*>(out),
                      static_cast<const uint16_t*>(dprev), static_cast<uint16_t*>(dnew), n, part);
-  hipLaunchKernelGGL(block_stats_final_kernel, dim3(1), dim3(BS_THREADS), 0, st, part, grid, stats);
+  hipLaunchKernelGGL(block_stats_final_kernel, dim3(1), dim3(kBsFinalThreads), 0, st, part, grid, stats);
   return hipGetLastError();
 }
 

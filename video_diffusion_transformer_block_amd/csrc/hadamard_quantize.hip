@@ -244,16 +244,27 @@ __global__ __launch_bounds__(HQ_THREADS) void hq_amax_kernel(HQParams p) {
   }
 }
 
-// One workgroup: amax_T = max of the partial maxima; writes {amax_T, gs}.
-__global__ __launch_bounds__(256) void hq_amax_final_kernel(const float* part, int n, float* ts) {
-  __shared__ float wred[4];
-  float m = 0.0f;
-  for (int i = threadIdx.x; i < n; i += 256) m = fmaxf(m, part[i]);
-  m = wave_max(m);
+// One workgroup of kFinalThreads: amax_T = max of the partial maxima;
+// writes {amax_T, gs}.  Four independent loads in flight per thread.
+constexpr int kFinalThreads = 1024;
+
+__global__ __launch_bounds__(kFinalThreads) void hq_amax_final_kernel(const float* part, int n, float* ts) {
+  __shared__ float wred[kFinalThreads / 64];
+  float m0 = 0.0f, m1 = 0.0f, m2 = 0.0f, m3 = 0.0f;
+  int i = threadIdx.x;
+  for (; i + 3 * kFinalThreads < n; i += 4 * kFinalThreads) {
+    m0 = fmaxf(m0, part[i]);
+    m1 = fmaxf(m1, part[i + kFinalThreads]);
+    m2 = fmaxf(m2, part[i + 2 * kFinalThreads]);
+    m3 = fmaxf(m3, part[i + 3 * kFinalThreads]);
+  }
+  for (; i < n; i += kFinalThreads) m0 = fmaxf(m0, part[i]);
+  float m = wave_max(fmaxf(fmaxf(m0, m1), fmaxf(m2, m3)));
   if ((threadIdx.x & 63) == 0) wred[threadIdx.x >> 6] = m;
   __syncthreads();
   if (threadIdx.x == 0) {
-    float a = fmaxf(fmaxf(wred[0], wred[1]), fmaxf(wred[2], wred[3]));
+    float a = wred[0];
+    for (int w = 1; w < kFinalThreads / 64; ++w) a = fmaxf(a, wred[w]);
     ts[0] = a;
     ts[1] = nvfp4_gs(a);
   }
@@ -264,15 +275,16 @@ __global__ void hq_gs_only_kernel(float* ts) {
   if (threadIdx.x == 0) ts[1] = nvfp4_gs(ts[0]);
 }
 
-// Final fp64 reduction of the per-workgroup statistics.
-__global__ __launch_bounds__(256) void hq_stats_final_kernel(const double* part, int n, double* out) {
-  __shared__ double red[4][4];
+// Final fp64 reduction of the per-workgroup statistics (fixed order).
+__global__ __launch_bounds__(kFinalThreads) void hq_stats_final_kernel(const double* part, int n, double* out) {
+  __shared__ double red[4][kFinalThreads / 64];
   double a = 0.0, b = 0.0, c = 0.0, d = 0.0;
-  for (int i = threadIdx.x; i < n; i += 256) {
-    a = fmax(a, part[4 * i + 0]);
-    b += part[4 * i + 1];
-    c = fmax(c, part[4 * i + 2]);
-    d += part[4 * i + 3];
+  for (int i = threadIdx.x; i < n; i += kFinalThreads) {
+    const double4 v = reinterpret_cast<const double4*>(part)[i];
+    a = fmax(a, v.x);
+    b += v.y;
+    c = fmax(c, v.z);
+    d += v.w;
   }
   a = wave_max_d(a); b = wave_sum(b); c = wave_max_d(c); d = wave_sum(d);
   const int w = threadIdx.x >> 6;
@@ -280,7 +292,9 @@ __global__ __launch_bounds__(256) void hq_stats_final_kernel(const double* part,
   __syncthreads();
   if (threadIdx.x == 0) {
     double x0 = red[0][0], x1 = red[1][0], x2 = red[2][0], x3 = red[3][0];
-    for (int i = 1; i < 4; ++i) { x0 = fmax(x0, red[0][i]); x1 += red[1][i]; x2 = fmax(x2, red[2][i]); x3 += red[3][i]; }
+    for (int i = 1; i < kFinalThreads / 64; ++i) {
+      x0 = fmax(x0, red[0][i]); x1 += red[1][i]; x2 = fmax(x2, red[2][i]); x3 += red[3][i];
+    }
     out[0] = x0; out[1] = x1; out[2] = x2; out[3] = x3;
   }
 }
@@ -419,7 +433,7 @@ static hipError_t launch_b(const HQParams& p, int fmt, bool amax_given, int grid
   if (fmt == 0) {
     if (!amax_given) {
       hipLaunchKernelGGL(hq_amax_kernel<B>, dim3(grid), dim3(HQ_THREADS), 0, st, p);
-      hipLaunchKernelGGL(hq_amax_final_kernel, dim3(1), dim3(256), 0, st, p.amax_part, grid, p.ts);
+      hipLaunchKernelGGL(hq_amax_final_kernel, dim3(1), dim3(kFinalThreads), 0, st, p.amax_part, grid, p.ts);
     }
     hipLaunchKernelGGL(hq_nvfp4_kernel<B>, dim3(grid), dim3(HQ_THREADS), 0, st, p);
   } else {
@@ -470,9 +484,9 @@ hipError_t launch_hadamard_quantize(const void* x, int64_t M, int64_t K, int64_t
       if (amax_given)
         hipLaunchKernelGGL(hq_gs_only_kernel, dim3(1), dim3(64), 0, st, ts);
       else
-        hipLaunchKernelGGL(hq_amax_final_kernel, dim3(1), dim3(256), 0, st, p.amax_part, 0, ts);
+        hipLaunchKernelGGL(hq_amax_final_kernel, dim3(1), dim3(kFinalThreads), 0, st, p.amax_part, 0, ts);
     }
-    if (want_stats) hipLaunchKernelGGL(hq_stats_final_kernel, dim3(1), dim3(256), 0, st, p.stats_part, 0, stats);
+    if (want_stats) hipLaunchKernelGGL(hq_stats_final_kernel, dim3(1), dim3(kFinalThreads), 0, st, p.stats_part, 0, stats);
     return hipGetLastError();
   }
   hipError_t e;
@@ -485,7 +499,7 @@ hipError_t launch_hadamard_quantize(const void* x, int64_t M, int64_t K, int64_t
   }
   if (e != hipSuccess) return e;
   if (want_stats) {
-    hipLaunchKernelGGL(hq_stats_final_kernel, dim3(1), dim3(256), 0, st, p.stats_part, grid, stats);
+    hipLaunchKernelGGL(hq_stats_final_kernel, dim3(1), dim3(kFinalThreads), 0, st, p.stats_part, grid, stats);
     e = hipGetLastError();
   }
   return e;
