@@ -433,19 +433,30 @@ __device__ __forceinline__ float4* part_slot(const GemmParams& p, int sl, int ti
   return reinterpret_cast<float4*>(p.part) + ((size_t)sl * p.sk_tiles + tile) * (256 * 256 / 4);
 }
 
-template <int AFMT>
+// PAIRS (K % 256 == 0): the E4M3 scales of two consecutive stages (16
+// contiguous bytes per row) arrive in one 16-byte load per row, into a
+// double-buffered pair region after the ring, instead of two 4-byte loads
+// per row and stage.
+template <int AFMT, bool PAIRS>
 struct Pipe {
   static constexpr bool A8 = AFMT == 1;
   static constexpr int A_CODES = 256 * (A8 ? 128 : 64);
-  static constexpr int A_SC = A8 ? 0 : 256 * 8;
+  static constexpr int A_SC = (A8 || PAIRS) ? 0 : 256 * 8;
   static constexpr int W_CODES = 256 * 64;
-  static constexpr int W_SC = 256 * 8;
+  static constexpr int W_SC = PAIRS ? 0 : 256 * 8;
   static constexpr int STAGE = A_CODES + A_SC + W_CODES + W_SC;
   static constexpr int NS = 3;
-  static constexpr int NA = A8 ? 8 : 4;        // A code loads per wave and stage (1 KB each)
-  static constexpr int NAS = A8 ? 0 : 2;       // A scale loads per wave and stage (256 B each)
-  static constexpr int NW = 4, NWS = 2;
-  static constexpr int LPS = NA + NAS + NW + NWS;   // loads per wave and stage
+  static constexpr int NA = A8 ? 8 : 4;                 // A code loads per wave and stage (1 KB each)
+  static constexpr int NAS = (A8 || PAIRS) ? 0 : 2;     // A scale loads per wave and stage (256 B each)
+  static constexpr int NW = 4;
+  static constexpr int NWS = PAIRS ? 0 : 2;
+  static constexpr int LPS = NA + NAS + NW + NWS;       // loads per wave and stage (pairs apart)
+  static constexpr int PAIR_A = (PAIRS && !A8) ? 256 * 16 : 0;
+  static constexpr int PAIR_W = PAIRS ? 256 * 16 : 0;
+  static constexpr int PAIR_SLOT = PAIR_A + PAIR_W;
+  static constexpr int PAIR_BASE = NS * STAGE;
+  static constexpr int NPAIR = (PAIR_A ? 1 : 0) + (PAIR_W ? 1 : 0);   // pair loads per wave
+  static constexpr int LDS = NS * STAGE + 2 * PAIR_SLOT;
 };
 
 // per-chunk raw operands of one lane: codes for its 4 A and 4 W sub-blocks
@@ -460,10 +471,10 @@ struct Raw {
 // SPLIT = true: one K slice of one of the tiles 0 .. sk_tiles-1 per
 // workgroup; the fp32 partial sums go to the workspace and qgemm_reduce_kernel
 // adds the slices and writes the output.
-template <int AFMT, bool SPLIT>
+template <int AFMT, bool SPLIT, bool PAIRS>
 __global__ __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void qgemm_pipe_kernel(GemmParams p) {
-  using P = Pipe<AFMT>;
+  using P = Pipe<AFMT, PAIRS>;
   constexpr bool A8 = P::A8;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
@@ -479,7 +490,8 @@ void qgemm_pipe_kernel(GemmParams p) {
 
   // ---- per-lane byte offsets of the DMA sources at k0 = 0 for the current
   // tile (32-bit: every operand matrix is below 4 GB, checked on the host)
-  uint32_t offA[P::NA], offAS[P::NAS > 0 ? P::NAS : 1], offW[P::NW], offWS[P::NWS];
+  uint32_t offA[P::NA], offAS[P::NAS > 0 ? P::NAS : 1], offW[P::NW], offWS[P::NWS > 0 ? P::NWS : 1];
+  uint32_t offAP = 0, offWP = 0;   // scale pairs: row wv*64 + lane
   int m0 = 0, n0 = 0;
   auto set_tile = [&](int tile) {
   int tm, tn;
@@ -514,6 +526,10 @@ void qgemm_pipe_kernel(GemmParams p) {
     const int r = (wv * P::NWS + u) * 32 + (lane >> 1);
     offWS[u] = (uint32_t)min(n0 + r, p.N - 1) * (uint32_t)(K / 16) + 4u * (lane & 1);
   }
+  if (PAIRS) {
+    offAP = (uint32_t)min(m0 + wv * 64 + lane, p.M - 1) * (uint32_t)(K / 16);
+    offWP = (uint32_t)min(n0 + wv * 64 + lane, p.N - 1) * (uint32_t)(K / 16);
+  }
   };
 
   // LDS byte address of smem and of this wave's regions (wave-uniform)
@@ -538,6 +554,13 @@ void qgemm_pipe_kernel(GemmParams p) {
 #pragma unroll
     for (int u = 0; u < P::NWS; ++u)
       dma4(wsbase, offWS[u], st + P::A_CODES + P::A_SC + P::W_CODES + (wvu * P::NWS + u) * 256);
+    // the scale pair (kt & ~1, kt | 1), with the even stage or a segment's first
+    if (PAIRS && ((kt & 1) == 0 || kt == kbase)) {
+      const int pr = kt >> 1;
+      const uint32_t ps = lds0 + P::PAIR_BASE + (uint32_t)(pr & 1) * P::PAIR_SLOT + wvu * 64 * 16;
+      if (P::PAIR_A) dma16(as + 16 * pr, offAP, ps);
+      dma16(p.w_s + 16 * pr, offWP, ps + P::PAIR_A);
+    }
   };
 
   // ---- LDS read offsets of this lane's fragments (within a stage)
@@ -563,6 +586,18 @@ void qgemm_pipe_kernel(GemmParams p) {
   };
   // the 8 scale bytes (groups of both chunks) of each of this lane's rows
   auto read_scales = [&](int kt, uint2 (&sa)[4], uint2 (&sw)[4]) {
+    if (PAIRS) {
+      const uint8_t* ps = smem + P::PAIR_BASE + ((kt >> 1) & 1) * P::PAIR_SLOT + (kt & 1) * 8;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (!A8) sa[i] = *reinterpret_cast<const uint2*>(ps + (wm * 128 + 32 * i + r32) * 16);
+        else sa[i] = make_uint2(0u, 0u);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        sw[j] = *reinterpret_cast<const uint2*>(ps + P::PAIR_A + (wn * 128 + 32 * j + r32) * 16);
+      return;
+    }
     const uint8_t* st = smem + ring(kt) * P::STAGE;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -645,12 +680,19 @@ void qgemm_pipe_kernel(GemmParams p) {
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
   // ---- prologue: stages kb..kb+2 in flight, wait for stage kb
+  // (loads still allowed in flight: those of stages kb+1 and kb+2, a scale
+  // pair with whichever of them is even)
   issue_stage(kb);
   if (ke - kb > 1) issue_stage(kb + 1);
   if (ke - kb > 2) issue_stage(kb + 2);
-  if (ke - kb > 2) wait_vm<2 * P::LPS>();
-  else if (ke - kb > 1) wait_vm<P::LPS>();
-  else wait_vm<0>();
+  if (ke - kb > 2) {
+    wait_vm<2 * P::LPS + P::NPAIR>();
+  } else if (ke - kb > 1) {
+    if (PAIRS && ((kb + 1) & 1) == 0) wait_vm<P::LPS + P::NPAIR>();
+    else wait_vm<P::LPS>();
+  } else {
+    wait_vm<0>();
+  }
   wait_lgkm_barrier();
 
   Raw<A8> R0, R1;
@@ -680,9 +722,14 @@ void qgemm_pipe_kernel(GemmParams p) {
     decode(R1, sa, sw, 1, 0, fa, fb);
     mfma16(ga, gb);
     interleave();
-    // mid-stage barrier: next stage complete, this buffer free
-    if (kt + 2 < ke) wait_vm<P::LPS>();
-    else wait_vm<0>();
+    // mid-stage barrier: next stage complete (only stage kt+2's loads may
+    // still be in flight), this buffer free
+    if (kt + 2 < ke) {
+      if (PAIRS && ((kt + 2) & 1) == 0) wait_vm<P::LPS + P::NPAIR>();
+      else wait_vm<P::LPS>();
+    } else {
+      wait_vm<0>();
+    }
     wait_lgkm_barrier();
     if (kt + 3 < ke) issue_stage(kt + 3);
     // step 4 | read stage kt+1 scales, decode step 5
@@ -849,35 +896,33 @@ static void plan_pipe(GemmParams& p, int cus, int& dp_grid, int& sk_grid) {
   sk_grid = split ? (int)(left * slices) : 0;
 }
 
-template <int AFMT, bool SPLIT>
+template <int AFMT, bool SPLIT, bool PAIRS>
 static hipError_t set_lds_attr() {
-  using P = Pipe<AFMT>;
+  using P = Pipe<AFMT, PAIRS>;
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&qgemm_pipe_kernel<AFMT, SPLIT>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)(P::NS * P::STAGE));
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&qgemm_pipe_kernel<AFMT, SPLIT, PAIRS>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, P::LDS);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   return hipSuccess;
 }
 
-template <int AFMT>
-static hipError_t launch_pipe(GemmParams p, int cus, hipStream_t st) {
-  using P = Pipe<AFMT>;
-  int dp_grid = 0, sk_grid = 0;
-  plan_pipe(p, cus, dp_grid, sk_grid);
-  const size_t lds = (size_t)P::NS * P::STAGE;
-  hipError_t e = set_lds_attr<AFMT, false>();
-  if (e == hipSuccess) e = set_lds_attr<AFMT, true>();
+template <int AFMT, bool PAIRS>
+static hipError_t launch_pipe(GemmParams p, int dp_grid, int sk_grid, hipStream_t st) {
+  using P = Pipe<AFMT, PAIRS>;
+  const size_t lds = (size_t)P::LDS;
+  hipError_t e = set_lds_attr<AFMT, false, PAIRS>();
+  if (e == hipSuccess) e = set_lds_attr<AFMT, true, PAIRS>();
   if (e != hipSuccess) return e;
   if (dp_grid > 0) {
-    hipLaunchKernelGGL((qgemm_pipe_kernel<AFMT, false>), dim3(dp_grid), dim3(GT), lds, st, p);
+    hipLaunchKernelGGL((qgemm_pipe_kernel<AFMT, false, PAIRS>), dim3(dp_grid), dim3(GT), lds, st, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (sk_grid > 0) {
-    hipLaunchKernelGGL((qgemm_pipe_kernel<AFMT, true>), dim3(sk_grid), dim3(GT), lds, st, p);
+    hipLaunchKernelGGL((qgemm_pipe_kernel<AFMT, true, PAIRS>), dim3(sk_grid), dim3(GT), lds, st, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((qgemm_reduce_kernel<AFMT>), dim3(p.sk_tiles * 64), dim3(256), 0, st, p);
@@ -939,7 +984,15 @@ hipError_t launch_qgemm(int afmt, const void* a_q, const void* a_s, const float*
   // offsets into every operand matrix.
   const bool fast = (K % BK) == 0 && (afmt == 1 ? M * K : M * K / 2) < (int64_t(1) << 32) &&
                     N * K / 2 < (int64_t(1) << 32);
-  if (fast) return afmt == 0 ? launch_pipe<0>(p, cu_count(), st) : launch_pipe<1>(p, cu_count(), st);
+  if (fast) {
+    int dp_grid = 0, sk_grid = 0;
+    plan_pipe(p, cu_count(), dp_grid, sk_grid);
+    // whole scale pairs (K % 256 == 0) and 16-byte aligned scale rows
+    const bool pairs = (p.nk % 2) == 0 && (reinterpret_cast<uintptr_t>(w_s) & 15u) == 0 &&
+                       (afmt == 1 || (reinterpret_cast<uintptr_t>(a_s) & 15u) == 0);
+    if (afmt == 0) return pairs ? launch_pipe<0, true>(p, dp_grid, sk_grid, st) : launch_pipe<0, false>(p, dp_grid, sk_grid, st);
+    return pairs ? launch_pipe<1, true>(p, dp_grid, sk_grid, st) : launch_pipe<1, false>(p, dp_grid, sk_grid, st);
+  }
   if (afmt == 0) return launch_cfg<0, 4, 4>(p, st);
   return launch_cfg<1, 4, 4>(p, st);
 }
