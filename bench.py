@@ -184,19 +184,20 @@ def main():
     dom = max(kern, key=lambda k: kern[k]["ms"])
     dk = kern[dom]
     achieved = dk["flops"] / (dk["ms"] * 1e-3) / 1e12
-    # HBM bytes per launch of the dominant kernel from the committed counter
-    # runs (FETCH_SIZE + WRITE_SIZE, copy-calibrated), while its sources match
+    # HBM bytes per call of the dominant GEMM from the committed counter runs
+    # (FETCH_SIZE + WRITE_SIZE, copy-calibrated), while its sources match.  A
+    # call is one data-parallel kernel plus, when the last wave is split along
+    # K, the slice kernel and the reduce kernel: all of them are summed and
+    # divided by the number of calls (= data-parallel dispatches).
     from video_diffusion_transformer_block_amd import profiling
     rec = profiling.load_traffic(os.path.join(ROOT, "profiles", "traffic_5b_mixed.json"))
-    kname = {"qgemm_w4a4": "qgemm_pipe_kernel<0>", "qgemm_w4a8": "qgemm_pipe_kernel<1>"}[dom]
-    traffic = None
-    if rec is not None and kname in rec["kernels"]:
-        traffic = round(rec["kernels"][kname]["bytes"])
+    traffic = gemm_call_traffic(rec, 0 if dom == "qgemm_w4a4" else 1) if rec is not None else None
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1),
                 "peak": PEAK_FP16_MFMA_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_FP16_MFMA_TFLOPS, 4), "traffic": traffic,
-                "traffic_unit": "bytes per launch (HBM/fabric, FETCH_SIZE+WRITE_SIZE)",
+                "traffic_unit": "bytes per call (HBM/fabric, FETCH_SIZE+WRITE_SIZE)",
                 "avg_launch_us": round(1e3 * dk["ms"] / dk["launches"], 1),
+                "launch": "one GEMM call: data-parallel kernel (+ K-slice and reduce kernels for a split last wave)",
                 "flops_per_launch": dk["flops"] / dk["launches"],
                 "note": "exact NVFP4/INT8 operands run on the fp16 MFMA (the peak used); "
                         f"same rate vs fp8 {PEAK_FP8_TFLOPS:.0f}, fp4 {PEAK_FP4_TFLOPS:.0f} TFLOP/s: "
@@ -247,6 +248,20 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(line))
+
+
+def gemm_call_traffic(rec, afmt):
+    """Mean FETCH+WRITE bytes per GEMM call of activation format afmt (0
+    NVFP4, 1 INT8) in a counter record: every dispatch of that format's GEMM
+    kernels summed, over the number of data-parallel dispatches (one per call)."""
+    total, calls = 0.0, 0
+    for name, k in rec["kernels"].items():
+        if name.startswith(f"qgemm_pipe_kernel<{afmt}, ") or name == f"qgemm_reduce_kernel<{afmt}>":
+            for e in k["grids"].values():
+                total += e["bytes"] * e["dispatches"]
+                if name.startswith(f"qgemm_pipe_kernel<{afmt}, false"):
+                    calls += e["dispatches"]
+    return round(total / calls) if calls else None
 
 
 def hq_grid_work_items(M, K, fmt):

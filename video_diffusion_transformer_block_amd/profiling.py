@@ -6,6 +6,10 @@
     # per-dispatch durations by kernel and grid (same run, kernel_trace.csv)
     python -m video_diffusion_transformer_block_amd.profiling trace <dir>/<name>_kernel_trace.csv
 
+    # MFMA utilisation and clock of the GEMM kernels from one counter run
+    # (--pmc GRBM_GUI_ACTIVE SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_MFMA SQ_INSTS_VALU)
+    python -m video_diffusion_transformer_block_amd.profiling mfma <dir>/<name>_counter_collection.csv
+
     # HBM traffic per dispatch from two counter runs (FETCH_SIZE, WRITE_SIZE),
     # calibrated on the plain copy of known size that the run also performs
     python -m video_diffusion_transformer_block_amd.profiling traffic \
@@ -68,6 +72,37 @@ def trace_table(path: str) -> str:
     for (n, g), v in sorted(per.items()):
         v = sorted(v)
         out.append(f"| {n} | {g} | {len(v)} | {v[len(v) // 2]:.1f} | {v[0]:.1f} | {sum(v) / len(v):.1f} |")
+    return "\n".join(out)
+
+
+def mfma_table(path: str, simds: int = 1024, xcds: int = 8) -> str:
+    """Per (kernel, grid): MFMA busy share = SQ_VALU_MFMA_BUSY_CYCLES /
+    (GRBM_GUI_ACTIVE per XCD x SIMDs), the shader clock = GRBM_GUI_ACTIVE per
+    XCD / duration, and non-MFMA VALU instructions per MFMA."""
+    per = collections.defaultdict(lambda: collections.defaultdict(list))
+    dur = collections.defaultdict(dict)
+    for r in csv.DictReader(open(path)):
+        n = short_name(r["Kernel_Name"])
+        if not n.startswith("qgemm_pipe"):
+            continue
+        k = (n, int(r["Grid_Size"]))
+        per[k][r["Counter_Name"]].append(float(r["Counter_Value"]))
+        dur[k][r["Dispatch_Id"]] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    out = ["| kernel | grid (work-items) | dispatches | duration us | clock GHz | MFMA busy % | VALU / MFMA |",
+           "|---|---|---|---|---|---|---|"]
+    for k, c in sorted(per.items()):
+        if "SQ_VALU_MFMA_BUSY_CYCLES" not in c or "GRBM_GUI_ACTIVE" not in c:
+            continue
+        g = _mean(c["GRBM_GUI_ACTIVE"]) / xcds
+        busy = _mean(c["SQ_VALU_MFMA_BUSY_CYCLES"])
+        ds = sorted(dur[k].values())
+        d = ds[len(ds) // 2] / 1e9
+        vpm = ""
+        if c.get("SQ_INSTS_MFMA") and c.get("SQ_INSTS_VALU"):
+            mf = _mean(c["SQ_INSTS_MFMA"])
+            vpm = f"{(_mean(c['SQ_INSTS_VALU']) - mf) / mf:.2f}" if mf else ""
+        out.append(f"| {k[0]} | {k[1]} | {len(dur[k])} | {d * 1e6:.0f} | {g / d / 1e9:.2f} | "
+                   f"{100 * busy / (g * simds):.1f} | {vpm} |")
     return "\n".join(out)
 
 
@@ -149,6 +184,8 @@ def main(argv=None):
     a.add_argument("csv")
     t = sub.add_parser("trace")
     t.add_argument("csv")
+    mf = sub.add_parser("mfma")
+    mf.add_argument("csv")
     b = sub.add_parser("traffic")
     b.add_argument("fetch_csv")
     b.add_argument("write_csv")
@@ -160,6 +197,8 @@ def main(argv=None):
         print(stats_table(args.csv))
     elif args.cmd == "trace":
         print(trace_table(args.csv))
+    elif args.cmd == "mfma":
+        print(mfma_table(args.csv))
     else:
         rec = traffic(args.fetch_csv, args.write_csv, args.copy_bytes, args.copy_kernel)
         with open(args.out, "w") as fh:
