@@ -1,4 +1,5 @@
-"""Quantized GEMMs: W4A4 (NVFP4 x NVFP4) and W4A8 (INT8 x NVFP4).
+"""Quantized GEMMs: W4A4 (NVFP4 x NVFP4), W4A8 (INT8 x NVFP4) and the
+full-precision fallback W4A16 (bf16 x NVFP4).
 
 Test infrastructure only (see oracle/__init__.py).
 
@@ -13,6 +14,9 @@ token scales and the optional bias, then round once to the output type.
 
 W4A4:  Y = gs_a * gs_w * (A_hat @ W_hat^T) + bias
 W4A8:  Y = s_a[m] * gs_w * (Q_a @ W_hat^T) + bias
+W4A16: Y = gs_w * (A @ W_hat^T) + bias, A the rotated activations in bf16
+       ([gist] §2.C: a step flagged by the outlier check runs in FP16/BF16;
+       the weights stay 4-bit, [gist] §4 memory figure)
 with A_hat = e2m1 * e4m3, W_hat likewise (no tensor scale), Q_a the int8
 codes.  For W4A8 every product and partial sum is exact in float64 (at most
 29 bits of dynamic range plus log2(K) bits of growth), so Q_a @ W_hat^T is
@@ -50,6 +54,15 @@ def qgemm_w4a8(a_q, a_s, w_q, w_s, w_gs, bias=None, out_dtype="bf16"):
     W = nvfp4_dequantize(w_q, w_s)
     acc = np.asarray(a_q, dtype=np.float64) @ W.T
     y = (np.asarray(a_s, dtype=np.float64)[:, None] * float(np.float32(w_gs))) * acc
+    return _finish(y, bias, out_dtype)
+
+
+def qgemm_w4a16(a_bits, w_q, w_s, w_gs, bias=None, out_dtype="bf16"):
+    """a_bits: bf16 bit patterns [M, K] of the rotated activations."""
+    from .formats import bf16_to_f32
+    A = bf16_to_f32(a_bits).astype(np.float64)
+    W = nvfp4_dequantize(w_q, w_s)
+    y = float(np.float32(w_gs)) * (A @ W.T)
     return _finish(y, bias, out_dtype)
 
 

@@ -32,13 +32,18 @@ INT8 (per token row):
   scale 0 and all-zero codes.  Otherwise s_m = RN(a_m / 127),
   inv = RN(1 / s_m), q = clamp(rint_even(RN(y * inv)), -127, 127).
   Dequantized value: q * s_m.
+
+BF16 (the full-precision fallback of [gist] §2.C / [yly] §三):
+  the rotated activations themselves, y rounded to bf16 (nearest even).  The
+  weights exist only rotated, so the fallback multiplies rotated bf16
+  activations by the dequantized 4-bit weights (W4A16).
 """
 from __future__ import annotations
 
 import numpy as np
 
 from .formats import (e2m1_to_float, e4m3_to_float, float_to_e2m1,
-                      float_to_e4m3, pack_nibbles, unpack_nibbles, bf16_to_f32)
+                      float_to_e4m3, pack_nibbles, unpack_nibbles, bf16_to_f32, f32_to_bf16)
 from .hadamard import block_hadamard_f32
 
 F32 = np.float32
@@ -119,8 +124,9 @@ def activation_stats(x_bits: np.ndarray, y: np.ndarray) -> np.ndarray:
 
 def hadamard_quantize(x_bits: np.ndarray, had_block: int, fmt: str, amax=None):
     """The full per-linear activation pass: block Hadamard of bf16 rows, then
-    NVFP4 or INT8 quantization, plus the fused outlier statistics.
-    fmt is "nvfp4" or "int8".  Returns a dict."""
+    NVFP4 or INT8 quantization (or bf16 rounding for the full-precision
+    fallback), plus the fused outlier statistics.
+    fmt is "nvfp4", "int8" or "bf16".  Returns a dict."""
     x = bf16_to_f32(x_bits)
     y = block_hadamard_f32(x, had_block)
     out = {"y": y, "stats": activation_stats(x_bits, y)}
@@ -130,6 +136,8 @@ def hadamard_quantize(x_bits: np.ndarray, had_block: int, fmt: str, amax=None):
     elif fmt == "int8":
         q, s = int8_quantize(y)
         out.update(q=q, scales=s)
+    elif fmt == "bf16":
+        out.update(q=f32_to_bf16(y))
     else:
         raise ValueError(fmt)
     return out

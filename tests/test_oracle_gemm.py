@@ -2,7 +2,7 @@
 accumulators."""
 import numpy as np
 
-from oracle import formats as F, gemm as G, quant as Q
+from oracle import formats as F, gemm as G, hadamard as H, quant as Q
 
 RNG = np.random.Generator(np.random.PCG64(14))
 
@@ -80,3 +80,60 @@ def test_one_hot_rows_pick_weight_columns():
     as_ = np.full((K, K // 16), 0x38, np.uint8)
     y64, _ = G.qgemm_w4a4(aq, as_, np.float32(1), wq, ws, np.float32(1), out_dtype="f32")
     assert np.array_equal(y64, W.T)
+
+
+def test_w4a16_brute_force():
+    """bf16 activations straight from their bits, weights from the format
+    definitions, products summed in a Python loop."""
+    M, N, K = 3, 5, 48
+    # random signs, mantissas and exponents 2^-27 .. 2^24 (no overflow)
+    a_bits = ((RNG.integers(0, 2, size=(M, K)) << 15) | (RNG.integers(100, 151, size=(M, K)) << 7)
+              | RNG.integers(0, 128, size=(M, K))).astype(np.uint16)
+    wq, ws, wc = _rand_nvfp4(N, K)
+    w_gs = np.float32(0.75)
+    av = [[struct_bf16(a_bits[m, k]) for k in range(K)] for m in range(M)]
+    wv = [[F.E2M1_VALUES[wc[n, k] & 7] * (-1 if wc[n, k] & 8 else 1)
+           * F.e4m3_to_float(ws[n, k // 16]) for k in range(K)] for n in range(N)]
+    want = _loop_dot(np.array(av), np.array(wv)) * 0.75
+    y64, _ = G.qgemm_w4a16(a_bits, wq, ws, w_gs, out_dtype="f32")
+    assert np.allclose(y64, want, rtol=1e-12, atol=0)
+
+
+def struct_bf16(bits):
+    """bf16 bits -> float through the IEEE single layout (struct module)."""
+    import struct
+    return struct.unpack("<f", struct.pack("<I", int(bits) << 16))[0]
+
+
+def test_w4a16_integer_inputs_exact():
+    """Small-integer activations and unit weight scales: Y is the exact
+    integer sum of a * e2m1(w)."""
+    M, N, K = 4, 6, 64
+    a = RNG.integers(-20, 21, size=(M, K)).astype(np.float32)
+    a_bits = (a.view(np.uint32) >> 16).astype(np.uint16)      # exact in bf16
+    wq, _, wc = _rand_nvfp4(N, K)
+    ones = np.full((N, K // 16), 0x38, np.uint8)
+    y64, y32 = G.qgemm_w4a16(a_bits, wq, ones, np.float32(1.0), out_dtype="f32")
+    c = np.array([[F.E2M1_VALUES[wc[n, k] & 7] * (-1 if wc[n, k] & 8 else 1) for k in range(K)]
+                  for n in range(N)])
+    assert np.array_equal(y64, a.astype(np.float64) @ c.T)
+
+
+def test_w4a16_rotation_cancels():
+    """bf16 fallback of a whole linear: rotating activations and weights by
+    the same block Hadamard transform leaves X W^T, up to the weights'
+    4-bit error and the bf16 rounding of the rotated activations."""
+    M, N, K = 32, 24, 128
+    x = RNG.standard_normal((M, K)).astype(np.float32)
+    w = (RNG.standard_normal((N, K)) * 0.02).astype(np.float32)
+    xb, wb = F.f32_to_bf16(x), F.f32_to_bf16(w)
+    wq, ws, wgs = Q.prepare_weight(wb, 64)
+    a = Q.hadamard_quantize(xb, 64, "bf16")["q"]
+    y64, _ = G.qgemm_w4a16(a, wq, ws, wgs, out_dtype="f32")
+    ref = F.bf16_to_f32(xb).astype(np.float64) @ F.bf16_to_f32(wb).astype(np.float64).T
+    rel = np.linalg.norm(y64 - ref) / np.linalg.norm(ref)
+    assert rel < 0.15            # NVFP4 weights: ~10% relative error per element
+    # the bf16 activations alone (weights exact) reproduce X W^T to bf16 precision
+    Wrot = H.block_hadamard_f32(F.bf16_to_f32(wb), 64).astype(np.float64)
+    y_exact_w = F.bf16_to_f32(a).astype(np.float64) @ Wrot.T
+    assert np.linalg.norm(y_exact_w - ref) / np.linalg.norm(ref) < 1e-2

@@ -151,3 +151,16 @@ def test_weight_prep_rotation_cancels():
     a_bad = Q.int8_quantize(F.bf16_to_f32(d["x"]))
     yb, _ = G.qgemm_w4a8(a_bad[0], a_bad[1], wq, ws, wgs, out_dtype="f32")
     assert np.linalg.norm(yb - ref) / np.linalg.norm(ref) > 0.8
+
+
+def test_bf16_fallback_is_rounded_transform():
+    """The BF16 format is the transform output rounded to bf16: checked
+    against torch's own bf16 cast of the oracle's fp32 transform."""
+    import torch
+    x = synth.laplace_activations(40, 256, 11, 12)
+    for b in (16, 64, 128):
+        r = Q.hadamard_quantize(x, b, "bf16")
+        y = H.block_hadamard_bf16(x, b)
+        want = torch.from_numpy(y).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        assert np.array_equal(r["q"], want)
+        assert np.allclose(r["stats"], Q.activation_stats(x, y))
