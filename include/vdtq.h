@@ -56,6 +56,7 @@ extern "C" {
 /* ------------------------------------------------------------ enums */
 #define VDTQ_FMT_NVFP4 0
 #define VDTQ_FMT_INT8 1
+#define VDTQ_FMT_BF16 2      /* rotated activations in bf16 (W4A16 fallback) */
 
 #define VDTQ_OUT_BF16 0
 #define VDTQ_OUT_F32 1
@@ -85,8 +86,9 @@ size_t vdtq_workspace_bytes(int op, int64_t M, int64_t K);
 
 /*
  * hadamard_quantize -- online block Hadamard transform of bf16 activations
- * followed by NVFP4 or per-token INT8 quantization, with the outlier
- * statistics fused in.
+ * followed by NVFP4 or per-token INT8 quantization (or, for the
+ * full-precision fallback, bf16 rounding), with the outlier statistics fused
+ * in.
  *
  * Defined by: [gist] §2.A (block Hadamard before quantization; NVFP4 for
  * stable blocks, INT8 for volatile ones), [yly] §一 (same), [yly] §三 (the
@@ -104,6 +106,8 @@ size_t vdtq_workspace_bytes(int op, int64_t M, int64_t K);
  *     (nearest-even, saturating, sign copied), 0 if s_dec == 0.
  *   INT8: per row a = max|y|; a non-finite or < 2^-100 => scale 0, codes 0;
  *     else s = RN(a / 127), q = rint_even(RN(y * RN(1 / s))), |q| <= 127.
+ *   BF16: q = bf16_RNE(y) ([gist] §2.C: a flagged step runs in FP16/BF16;
+ *     the weights exist only rotated, so the activations are rotated too).
  *
  * x_dev          bf16 [M][ldx], ldx >= K (elements)
  * M              rows (tokens), >= 0; M == 0 is a no-op (NVFP4 still writes
@@ -111,12 +115,13 @@ size_t vdtq_workspace_bytes(int op, int64_t M, int64_t K);
  * K              columns, > 0, multiple of 16 and of had_block; for INT8,
  *                K <= 16384
  * had_block      16, 32, 64, 128 or 256
- * fmt            VDTQ_FMT_NVFP4 or VDTQ_FMT_INT8
+ * fmt            VDTQ_FMT_NVFP4, VDTQ_FMT_INT8 or VDTQ_FMT_BF16
  * flags          VDTQ_AMAX_GIVEN (NVFP4 only) | VDTQ_STATS
- * q_dev          NVFP4: uint8 [M][K/2]; INT8: int8 [M][K]
- * scales_dev     NVFP4: uint8 E4M3 [M][K/16]; INT8: float [M]
+ * q_dev          NVFP4: uint8 [M][K/2]; INT8: int8 [M][K]; BF16: bf16 [M][K]
+ * scales_dev     NVFP4: uint8 E4M3 [M][K/16]; INT8: float [M]; BF16:
+ *                ignored, may be NULL
  * tensor_scale_dev  NVFP4: float[2] {amax_T, gs} (amax_T is read when
- *                AMAX_GIVEN, else written); INT8: ignored, may be NULL
+ *                AMAX_GIVEN, else written); INT8, BF16: ignored, may be NULL
  * stats_dev      double[4] {max|x|, sum|x|, max|y|, sum|y|} when
  *                VDTQ_STATS (x before, y after the transform), else ignored
  * ws_dev/ws_bytes  workspace of vdtq_workspace_bytes(VDTQ_OP_HADAMARD_QUANTIZE,
@@ -179,6 +184,32 @@ int qgemm_w4a8(const int8_t* a_q_dev, const float* a_s_dev,
                const float* w_ts_dev, const float* bias_dev, void* y_dev,
                int64_t ldy, int out_dtype, int64_t M, int64_t N, int64_t K,
                void* ws_dev, size_t ws_bytes, void* stream);
+
+/*
+ * qgemm_w4a16 -- Y = gs_w * (A W_hat^T) + bias with bf16 activations: the
+ * full-precision fallback of a step whose input fails the outlier check.
+ *
+ * Defined by: [gist] §2.C and [yly] §三 (full precision, FP16/BF16, for a
+ * step flagged by the max/mean outlier ratio before its delta is cached),
+ * [gist] §4 (the weights stay 4-bit: the memory figure).
+ *
+ * A = the rotated activations in bf16 (hadamard_quantize with
+ * VDTQ_FMT_BF16); W_hat = e2m1(code) * e4m3(scale), exact in bf16; products
+ * exact, accumulated in fp32 (any order), result rounded to out_dtype.
+ *
+ * a_dev    bf16 [M][K], 16-byte aligned
+ * w_q_dev, w_s_dev, w_ts_dev   NVFP4 weights as in qgemm_w4a4 (w_s_dev
+ *          4-byte aligned)
+ * bias_dev float [N] or NULL; y_dev out_dtype [M][ldy], ldy >= N
+ * M, N >= 0 (0 is a no-op); K > 0, multiple of 16.
+ * Errors: VDTQ_EINVAL as for the other GEMMs; VDTQ_EUNSUPPORTED when K is
+ * not a multiple of 64 or an operand reaches 4 GB.  No workspace.
+ */
+int qgemm_w4a16(const void* a_dev, const uint8_t* w_q_dev,
+                const uint8_t* w_s_dev, const float* w_ts_dev,
+                const float* bias_dev, void* y_dev, int64_t ldy,
+                int out_dtype, int64_t M, int64_t N, int64_t K,
+                void* stream);
 
 /*
  * block_stats -- one pass over a block's input, output and cached delta.

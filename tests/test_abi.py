@@ -57,12 +57,14 @@ def _hq(**kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(K=15), L.EINVAL), (dict(K=0), L.EINVAL), (dict(M=-1), L.EINVAL),
     (dict(b=48), L.EINVAL), (dict(b=512), L.EINVAL), (dict(K=96, ldx=96, b=64), L.EINVAL),
-    (dict(ldx=60), L.EINVAL), (dict(ldx=68), L.EINVAL), (dict(fmt=2), L.EINVAL),
+    (dict(ldx=60), L.EINVAL), (dict(ldx=68), L.EINVAL), (dict(fmt=4), L.EINVAL),
     (dict(flags=4), L.EINVAL), (dict(fmt=1, flags=1), L.EINVAL),
     (dict(fmt=1, K=16384 + 64, ldx=16448), L.EUNSUPPORTED),
     (dict(x=None), L.EINVAL), (dict(q=None), L.EINVAL), (dict(x=FAKE8), L.EINVAL),
     (dict(ts=None), L.EINVAL), (dict(flags=2, st=None), L.EINVAL),
     (dict(ws=None), L.EINVAL), (dict(wsb=8), L.EINVAL),
+    (dict(fmt=3), L.EINVAL), (dict(fmt=2, flags=1), L.EINVAL), (dict(fmt=2, q=None), L.EINVAL),
+    (dict(fmt=2, q=FAKE8), L.EINVAL), (dict(fmt=2, flags=2, st=None), L.EINVAL),
 ])
 def test_hadamard_quantize_rejects(kw, code):
     assert _hq(**kw) == code
@@ -101,6 +103,29 @@ def test_qgemm_workspace_size():
 def test_qgemm_empty_is_noop():
     assert _gemm("w4a4", M=0) == L.OK
     assert _gemm("w4a8", N=0, aq=None, y=None) == L.OK
+
+
+def _a16(**kw):
+    a = dict(a=FAKE, wq=FAKE, ws=FAKE, wts=FAKE, bias=None, y=FAKE, ldy=64, od=0, M=8, N=64, K=128)
+    a.update(kw)
+    return V.lib().qgemm_w4a16(a["a"], a["wq"], a["ws"], a["wts"], a["bias"], a["y"], a["ldy"], a["od"],
+                               a["M"], a["N"], a["K"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(K=0), L.EINVAL), (dict(K=40), L.EINVAL), (dict(M=-1), L.EINVAL), (dict(ldy=10), L.EINVAL),
+    (dict(od=2), L.EINVAL), (dict(a=None), L.EINVAL), (dict(wq=None), L.EINVAL), (dict(wts=None), L.EINVAL),
+    (dict(y=None), L.EINVAL), (dict(a=FAKE8), L.EINVAL), (dict(K=96), L.EUNSUPPORTED),
+    (dict(M=1 << 20, K=1 << 11), L.EUNSUPPORTED),
+])
+def test_qgemm_w4a16_rejects(kw, code):
+    assert _a16(**kw) == code
+    assert V.lib().vdtq_last_error()
+
+
+def test_qgemm_w4a16_empty_is_noop():
+    assert _a16(M=0, a=None) == L.OK
+    assert _a16(N=0, y=None) == L.OK
 
 
 @pytest.mark.parametrize("kw", [dict(n=-1), dict(st=None), dict(inp=None), dict(dnew=FAKE, dprev=FAKE),

@@ -427,6 +427,47 @@ __global__ __launch_bounds__(HQ_THREADS) void hq_int8_kernel(HQParams p) {
   }
 }
 
+// ---------------------------------------------------------------- BF16 pass
+// The full-precision fallback: the rotated activations rounded to bf16
+// (nearest even), flat chunks as in the NVFP4 pass.
+template <int B>
+__global__ __launch_bounds__(HQ_THREADS) void hq_bf16_kernel(HQParams p) {
+  __shared__ uint4 lds[HQ_THREADS * 8];
+  int row, col;
+  bool valid;
+  stage<false>(p, lds, row, col, valid);
+  __syncthreads();
+  float v[64];
+  load_chunk(lds, v);
+  const int nvalid = valid ? min(64, p.K - col * 64) : 0;
+  const bool want_stats = (p.flags & 2u) != 0;
+  float mx = 0.0f, sx = 0.0f;
+  if (want_stats) input_stats(v, nvalid, mx, sx);
+  fwht<B>(v);
+  normalise<B>(v);
+  constexpr float f = yfac<B>();                     // exact power of two (1 when applied)
+  uint32_t words[32];
+#pragma unroll
+  for (int w = 0; w < 32; ++w)
+    words[w] = f32_to_bf16_bits(v[2 * w] * f) | (f32_to_bf16_bits(v[2 * w + 1] * f) << 16);
+  if (valid) {
+    uint4* qrow = reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(p.q) + (int64_t)row * p.K + col * 64);
+#pragma unroll
+    for (int g = 0; g < 8; ++g)
+      if (8 * g < nvalid)
+        qrow[g] = make_uint4(words[4 * g], words[4 * g + 1], words[4 * g + 2], words[4 * g + 3]);
+  }
+  if (want_stats) {
+    float my = 0.0f, sy = 0.0f;
+    for (int i = 0; i < 64; ++i) {
+      const float a = (i < nvalid) ? fabsf(v[i]) : 0.0f;
+      my = fmaxf(my, a);
+      sy = sy + a;
+    }
+    wg_stats_write(mx, sx, (double)(my * f), (double)(sy * f), p.stats_part + 4 * (int64_t)blockIdx.x);
+  }
+}
+
 // ---------------------------------------------------------------- launcher
 template <int B>
 static hipError_t launch_b(const HQParams& p, int fmt, bool amax_given, int grid, hipStream_t st) {
@@ -436,8 +477,10 @@ static hipError_t launch_b(const HQParams& p, int fmt, bool amax_given, int grid
       hipLaunchKernelGGL(hq_amax_final_kernel, dim3(1), dim3(kFinalThreads), 0, st, p.amax_part, grid, p.ts);
     }
     hipLaunchKernelGGL(hq_nvfp4_kernel<B>, dim3(grid), dim3(HQ_THREADS), 0, st, p);
-  } else {
+  } else if (fmt == 1) {
     hipLaunchKernelGGL(hq_int8_kernel<B>, dim3(grid), dim3(HQ_THREADS), 0, st, p);
+  } else {
+    hipLaunchKernelGGL(hq_bf16_kernel<B>, dim3(grid), dim3(HQ_THREADS), 0, st, p);
   }
   return hipGetLastError();
 }
@@ -468,7 +511,7 @@ hipError_t launch_hadamard_quantize(const void* x, int64_t M, int64_t K, int64_t
   const bool amax_given = (flags & 1u) != 0;
   const bool want_stats = (flags & 2u) != 0;
   int grid;
-  if (fmt == 0) {
+  if (fmt != 1) {
     grid = (int)((p.total_chunks + HQ_THREADS - 1) / HQ_THREADS);
   } else {
     p.rows_per_wg = std::max(1, HQ_THREADS / p.cpr);

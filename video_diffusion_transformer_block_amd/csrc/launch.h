@@ -19,6 +19,10 @@ hipError_t launch_qgemm(int afmt, const void* a_q, const void* a_s, const float*
                         const float* bias, void* y, int64_t ldy, int out_dtype, int64_t M,
                         int64_t N, int64_t K, void* ws, hipStream_t st);
 
+hipError_t launch_qgemm_w4a16(const void* a, const uint8_t* w_q, const uint8_t* w_s, const float* w_ts,
+                              const float* bias, void* y, int64_t ldy, int out_dtype, int64_t M, int64_t N,
+                              int64_t K, hipStream_t st);
+
 size_t bs_workspace_bytes(int64_t n);
 hipError_t launch_block_stats(const void* in, const void* out, const void* dprev, void* dnew,
                               int64_t n, double* stats, void* ws, hipStream_t st);

@@ -67,6 +67,13 @@ class NVFP4Tensor:
 
 
 @dataclass
+class BF16Tensor:
+    """The rotated activations in bf16 [M, K] (full-precision fallback)."""
+    q: torch.Tensor
+    stats: Optional[torch.Tensor] = None
+
+
+@dataclass
 class INT8Tensor:
     """Codes [M, K] int8 and per-row fp32 scales [M]."""
     q: torch.Tensor
@@ -116,12 +123,20 @@ def hadamard_quantize(x: torch.Tensor, had_block: int = 64, fmt: str = "nvfp4", 
             s = torch.empty((M,), dtype=torch.float32, device=dev)
         ts = None
         fcode = L.FMT_INT8
+    elif fmt == "bf16":
+        if amax is not None:
+            raise ValueError("amax applies to nvfp4 only")
+        q = out.q if out is not None else torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+        s = ts = None
+        fcode = L.FMT_BF16
     else:
         raise ValueError(fmt)
     L.check(L.lib().hadamard_quantize(_p(x), M, K, x.stride(0), had_block, fcode, flags, _p(q), _p(s),
                                       _p(ts), _p(st), _p(ws), ws.numel(), _stream(dev)))
     if fcode == L.FMT_NVFP4:
         return NVFP4Tensor(q, s, ts, st)
+    if fcode == L.FMT_BF16:
+        return BF16Tensor(q, st)
     return INT8Tensor(q, s, st)
 
 
@@ -156,6 +171,23 @@ def qgemm_w4a8(a: INT8Tensor, w: NVFP4Tensor, bias: Optional[torch.Tensor] = Non
     L.check(L.lib().qgemm_w4a8(_p(a.q), _p(a.scales), _p(w.q), _p(w.scales), _p(w.ts), _p(bias),
                                _p(y), y.stride(0), L.OUT_BF16 if out_dtype == "bf16" else L.OUT_F32,
                                M, N, K, _p(ws), ws.numel(), _stream(a.q.device)))
+    return y
+
+
+def qgemm_w4a16(a: BF16Tensor, w: NVFP4Tensor, bias: Optional[torch.Tensor] = None,
+                out_dtype: str = "bf16", y: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Full-precision fallback: rotated bf16 activations x NVFP4 weights."""
+    _require(a.q, torch.bfloat16, "a.q")
+    if a.q.dim() != 2 or not a.q.is_contiguous():
+        raise ValueError("a.q must be a contiguous [M, K] tensor")
+    M, K = a.q.shape
+    N = w.q.shape[0]
+    if w.q.shape[1] * 2 != K:
+        raise ValueError("K mismatch between activations and weights")
+    y = _out(M, N, out_dtype, a.q.device, y)
+    L.check(L.lib().qgemm_w4a16(_p(a.q), _p(w.q), _p(w.scales), _p(w.ts), _p(bias), _p(y), y.stride(0),
+                                L.OUT_BF16 if out_dtype == "bf16" else L.OUT_F32, M, N, K,
+                                _stream(a.q.device)))
     return y
 
 

@@ -32,8 +32,8 @@ import os
 import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-KERNEL_SOURCES = ["csrc/qgemm.hip", "csrc/hadamard_quantize.hip", "csrc/block_stats.hip",
-                  "csrc/device_common.h"]
+KERNEL_SOURCES = ["csrc/qgemm.hip", "csrc/qgemm_w4a16.hip", "csrc/hadamard_quantize.hip",
+                  "csrc/block_stats.hip", "csrc/device_common.h", "csrc/lds_dma.h"]
 
 
 def source_hash() -> str:
