@@ -44,7 +44,10 @@ HAD_BLOCK = 64
 MIXED = {"qkv": "nvfp4", "out": "int8", "ffn_up": "int8", "ffn_down": "nvfp4"}
 SWEEPS = {"mixed_w4a6": MIXED,
           "all_w4a4": {k: "nvfp4" for k in MIXED},
-          "all_w4a8": {k: "int8" for k in MIXED}}
+          "all_w4a8": {k: "int8" for k in MIXED},
+          # the full-precision fallback (bf16 activations, 4-bit weights) on every linear
+          "all_w4a16": {k: "bf16" for k in MIXED}}
+GEMM_OF = {"nvfp4": "qgemm_w4a4", "int8": "qgemm_w4a8", "bf16": "qgemm_w4a16"}
 
 
 def parse():
@@ -114,8 +117,10 @@ def main():
                 e1.record()
             if fmt == "nvfp4":
                 V.qgemm_w4a4(a, W[name], None, "bf16", y=Y[name])
-            else:
+            elif fmt == "int8":
                 V.qgemm_w4a8(a, W[name], None, "bf16", y=Y[name])
+            else:
+                V.qgemm_w4a16(a, W[name], None, "bf16", y=Y[name])
             if rec is not None:
                 e2.record()
                 rec.append((name, fmt, e0, e1, e2))
@@ -176,7 +181,7 @@ def main():
     # dominant kernel of the headline step: the qgemm variant with the most time
     kern = {}
     for name, d in head["per_linear"].items():
-        k = "qgemm_w4a4" if d["fmt"] == "nvfp4" else "qgemm_w4a8"
+        k = GEMM_OF[d["fmt"]]
         kk = kern.setdefault(k, {"ms": 0.0, "flops": 0.0, "launches": 0})
         kk["ms"] += d["gemm_ms"]
         kk["flops"] += flops[name]
@@ -191,7 +196,8 @@ def main():
     # divided by the number of calls (= data-parallel dispatches).
     from video_diffusion_transformer_block_amd import profiling
     rec = profiling.load_traffic(os.path.join(ROOT, "profiles", "traffic_5b_mixed.json"))
-    traffic = gemm_call_traffic(rec, 0 if dom == "qgemm_w4a4" else 1) if rec is not None else None
+    afmt = {"qgemm_w4a4": 0, "qgemm_w4a8": 1}.get(dom)
+    traffic = gemm_call_traffic(rec, afmt) if rec is not None and afmt is not None else None
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1),
                 "peak": PEAK_FP16_MFMA_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_FP16_MFMA_TFLOPS, 4), "traffic": traffic,
@@ -242,6 +248,8 @@ def main():
         "roofline": roofline,
         "quantize_roofline": qroof,
         "sweeps": {k: {"tops": round(v["tops"], 2), "ms_per_step": round(v["ms_per_step"], 4),
+                       "gemm_tflops": round(total_flops / (sum(d["gemm_ms"] for d in v["per_linear"].values())
+                                                           * 1e-3) / 1e12, 1),
                        "per_linear_ms": {n: [round(d["quant_ms"], 4), round(d["gemm_ms"], 4)]
                                          for n, d in v["per_linear"].items()}}
                    for k, v in results.items()},
