@@ -57,6 +57,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=8192)
+    ap.add_argument("--no-dyn", action="store_true", help="skip the closed-loop schedule measurement")
     ap.add_argument("--sweeps", default=",".join(SWEEPS),
                     help="comma-separated subset of " + ",".join(SWEEPS) + " (the first listed is the headline)")
     ap.add_argument("--calibration-copy", action="store_true",
@@ -225,6 +226,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    dyn = None if args.no_dyn else measure_dyn(torch, V, synth)
     cpu = None if args.no_cpu_baseline else cpu_baseline(host, M, args.cpu_rows)
 
     line = {
@@ -253,9 +255,119 @@ def main():
                        "per_linear_ms": {n: [round(d["quant_ms"], 4), round(d["gemm_ms"], 4)]
                                          for n, d in v["per_linear"].items()}}
                    for k, v in results.items()},
+        "dyn_schedule": dyn,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line))
+
+
+def measure_dyn(torch, V, synth, blocks=30, steps=50, M=4446, hidden=1920):
+    """The closed-loop schedule study (30 blocks x 50 denoising steps, 4446
+    tokens, hidden 1920) driven by dmpq_step, with the real linear on every
+    computed block-step: the block's QKV projection (1920 -> 5760) runs at the
+    precision the scheduler chose (NVFP4 -> W4A4, INT8 -> W4A8, BF16 -> the
+    W4A16 fallback); a skipped block reuses its cached delta.  Block 0's input
+    is Laplace(0, 1) with 0.5% of the channels x30; each computed block adds
+    a smooth seeded residual plus decaying noise; three (block, step) pairs
+    carry one channel x300.  Inputs and weights come from torch's seeded GPU
+    generator.  The same loop is run again with every block-step forced to
+    the BF16 fallback and no skip, for the reference.  Times are HIP events
+    around each computed block's quantize + GEMM."""
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+
+    def laplace(shape, seed):
+        gen.manual_seed(seed)
+        e1 = torch.empty(shape, device=dev).exponential_(generator=gen)
+        e2 = torch.empty(shape, device=dev).exponential_(generator=gen)
+        return e1 - e2
+
+    sched = synth.dyn_schedule(blocks, steps, M, hidden)
+    ch = torch.from_numpy(synth.outlier_channels(hidden, synth.n_outliers(hidden), 3000)).to(dev)
+    U = [laplace((M, hidden), 4000 + b) for b in range(blocks)]
+    noise = []
+    for b in range(blocks):
+        gen.manual_seed(5000 + b)
+        noise.append(torch.randn(M * hidden, generator=gen, device=dev))
+    Wq = []
+    for b in range(blocks):
+        gen.manual_seed(2000 + b)
+        w = (torch.randn((3 * hidden, hidden), generator=gen, device=dev) * 0.02).to(torch.bfloat16)
+        Wq.append(V.hadamard_quantize(w, HAD_BLOCK, "nvfp4"))
+    Ybuf = torch.empty((M, 3 * hidden), dtype=torch.bfloat16, device=dev)
+    flops = 2.0 * M * hidden * 3 * hidden
+    fmt_of = {V.ACT_NVFP4: "nvfp4", V.ACT_INT8: "int8", V.ACT_BF16: "bf16"}
+
+    def run(params):
+        states = [V.dmpq_state() for _ in range(blocks)]
+        last = [None] * blocks
+        cache = [None] * blocks
+        spare = [torch.empty((M, hidden), dtype=torch.bfloat16, device=dev) for _ in range(blocks)]
+        counts = {"skip": 0, "nvfp4": 0, "int8": 0, "bf16": 0}
+        events = []
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for t in range(steps):
+            x = laplace((M, hidden), 500 + t)
+            x[:, ch] *= 30.0
+            x = x.to(torch.bfloat16)
+            for b in range(blocks):
+                spike = sched["spikes"].get((b, t))
+                if spike is not None:
+                    x = x.clone()
+                    x[:, spike] = (x[:, spike].float() * 300.0).to(torch.bfloat16)
+                _, rs = V.block_stats(x, x, write_delta=False)
+                rs = rs.cpu().numpy()
+                act = V.dmpq_step(params, states[b], last[b], V.outlier_ratio(rs[4], rs[5], M * hidden))
+                if act == V.ACT_SKIP:
+                    counts["skip"] += 1
+                    out = (x.float() + cache[b].float()).to(torch.bfloat16)
+                    last[b] = None
+                else:
+                    fmt = fmt_of[act]
+                    counts[fmt] += 1
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record()
+                    a = V.hadamard_quantize(x, HAD_BLOCK, fmt)
+                    {"nvfp4": V.qgemm_w4a4, "int8": V.qgemm_w4a8, "bf16": V.qgemm_w4a16}[fmt](
+                        a, Wq[b], None, "bf16", y=Ybuf)
+                    e1.record()
+                    events.append((fmt, e0, e1))
+                    a_b, beta_b, phi_b = sched["params"][b]
+                    smooth = float(np.float32(a_b * (1.0 + 0.5 * np.sin(np.pi * t / steps + phi_b))))
+                    decay = float(np.float32(beta_b * np.exp(-t / 10.0)))
+                    z = torch.roll(noise[b], (7919 * t) % (M * hidden)).view(M, hidden)
+                    out = (x.float() + (U[b] * smooth + z * decay)).to(torch.bfloat16)
+                    dnew = spare[b]
+                    _, st = V.block_stats(x, out, cache[b], dnew)
+                    last[b] = st.cpu().numpy()
+                    spare[b] = cache[b] if cache[b] is not None else torch.empty_like(dnew)
+                    cache[b] = dnew
+                x = out
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        per = {}
+        for fmt, e0, e1 in events:
+            per.setdefault(fmt, []).append(e0.elapsed_time(e1))
+        total = sum(sum(v) for v in per.values())
+        return counts, per, total, wall
+
+    p_dyn = V.dmpq_params(gamma=0.1, tau=0.05, tau_acc=0.15, rho=1000.0)
+    p_ref = V.dmpq_params(gamma=0.1, tau=0.0, tau_acc=0.0, rho=-1.0)    # always computes, always BF16
+    counts, per, total, wall = run(p_dyn)
+    rcounts, rper, rtotal, rwall = run(p_ref)
+    print(f"[bench] dyn schedule: actions {counts}, linear path {total:.1f} ms vs {rtotal:.1f} ms all-BF16",
+          file=sys.stderr, flush=True)
+    return {"workload": f"closed loop, {blocks} blocks x {steps} steps, M={M}, hidden {hidden}, "
+                        f"QKV {hidden}->{3 * hidden} at the scheduled precision",
+            "params": {"gamma": 0.1, "tau": 0.05, "tau_acc": 0.15, "rho": 1000.0, "warmup": 2},
+            "actions": counts,
+            "linear_ms_per_call": {k: round(float(np.mean(v)), 4) for k, v in per.items()},
+            "linear_tflops": {k: round(flops / (float(np.mean(v)) * 1e-3) / 1e12, 1) for k, v in per.items()},
+            "linear_ms_total": round(total, 2),
+            "all_bf16_linear_ms_total": round(rtotal, 2),
+            "linear_speedup_vs_all_bf16": round(rtotal / total, 3) if total else None,
+            "wall_s": round(wall, 2), "all_bf16_wall_s": round(rwall, 2)}
 
 
 def gemm_call_traffic(rec, afmt):
