@@ -122,20 +122,11 @@ void qgemm_a16_kernel(A16Params p) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-  issue_stage(0);
-  if (nk > 1) issue_stage(1);
-
-  for (int kt = 0; kt < nk; ++kt) {
-    // stage kt complete (only stage kt+1 may be in flight); every wave is
-    // done with stage kt-1, whose slot takes stage kt+2
-    if (kt + 1 < nk) wait_vm<A16_LPS>();
-    else wait_vm<0>();
-    wait_lgkm_barrier();
-    if (kt + 2 < nk) issue_stage(kt + 2);
-
+  // this lane's W quads and group scales of a stage
+  uint4 wq[4];
+  float wsc[4][2];
+  auto read_w = [&](int kt) {
     const uint8_t* st = smem + (kt % A16_NS) * A16_STAGE;
-    uint4 wq[4];
-    float wsc[4][2];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int row = wn * 128 + 32 * j + r32;
@@ -145,25 +136,89 @@ void qgemm_a16_kernel(A16Params p) {
       wsc[j][0] = e4m3_decode_pos((s4 >> (16 * h)) & 0xFFu);
       wsc[j][1] = e4m3_decode_pos((s4 >> (16 * h + 8)) & 0xFFu);
     }
+  };
+  // A fragments of step s read from LDS; W fragments decoded
+  auto read_a = [&](int kt, int s, bf16x8 (&af)[4]) {
+    const uint8_t* st = smem + (kt % A16_NS) * A16_STAGE;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      bf16x8 af[4], bf[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = wm * 128 + 32 * i + r32;
-        af[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(st + a16_quad_off(row, 4 * h + s)));
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t w = s == 0 ? wq[j].x : s == 1 ? wq[j].y : s == 2 ? wq[j].z : wq[j].w;
-        bf[j] = dec_fp4x8_bf16(w, wsc[j][s >> 1]);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[j], af[i], acc[i][j], 0, 0, 0);
+    for (int i = 0; i < 4; ++i) {
+      const int row = wm * 128 + 32 * i + r32;
+      af[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(st + a16_quad_off(row, 4 * h + s)));
     }
+  };
+  auto decode_w = [&](int s, bf16x8 (&bf)[4]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t w = s == 0 ? wq[j].x : s == 1 ? wq[j].y : s == 2 ? wq[j].z : wq[j].w;
+      bf[j] = dec_fp4x8_bf16(w, wsc[j][s >> 1]);
+    }
+  };
+  auto mfma16 = [&](const bf16x8 (&af)[4], const bf16x8 (&bf)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[j], af[i], acc[i][j], 0, 0, 0);
+  };
+  // each MFMA followed by a few VALU (decode) and, when present, one LDS read
+  auto interleave = [&]() {
+#pragma unroll
+    for (int x = 0; x < 16; ++x) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // ---- prologue: stages 0..2 in flight, wait for stage 0
+  issue_stage(0);
+  if (nk > 1) issue_stage(1);
+  if (nk > 2) issue_stage(2);
+  if (nk > 2) wait_vm<2 * A16_LPS>();
+  else if (nk > 1) wait_vm<A16_LPS>();
+  else wait_vm<0>();
+  wait_lgkm_barrier();
+
+  bf16x8 fa[4], fb[4], ga[4], gb[4];
+  read_w(0);
+  read_a(0, 0, fa);
+  decode_w(0, fb);
+
+  // Every step has the same shape: the MFMAs of step s run beside the LDS
+  // reads and W decode of step s+1.  The barrier sits before the last step:
+  // by then every read of this stage's slot has been issued (lgkmcnt(0)), so
+  // the slot takes the stage three ahead, and the next stage is complete, so
+  // the last step can prepare its first.  Past the last stage those reads hit
+  // a stale slot and are discarded.
+  for (int kt = 0; kt < nk; ++kt) {
+    // step 0 | step 1
+    read_a(kt, 1, ga);
+    decode_w(1, gb);
+    mfma16(fa, fb);
+    interleave();
+    // step 1 | step 2
+    read_a(kt, 2, fa);
+    decode_w(2, fb);
+    mfma16(ga, gb);
+    interleave();
+    // step 2 | step 3
+    read_a(kt, 3, ga);
+    decode_w(3, gb);
+    mfma16(fa, fb);
+    interleave();
+    // stage kt+1 complete (only stage kt+2's loads may be in flight), every
+    // wave done reading stage kt
+    if (kt + 2 < nk) wait_vm<A16_LPS>();
+    else wait_vm<0>();
+    wait_lgkm_barrier();
+    if (kt + 3 < nk) issue_stage(kt + 3);
+    // step 3 | step 0 of stage kt+1
+    read_w(kt + 1);
+    read_a(kt + 1, 0, fa);
+    decode_w(0, fb);
+    mfma16(ga, gb);
+    interleave();
   }
 
   // epilogue: tile (i, j), lane, register e -> token row m0 + wm*128 + 32 i
