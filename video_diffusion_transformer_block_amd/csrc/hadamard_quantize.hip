@@ -49,6 +49,7 @@ struct HQParams {
   float* amax_part;           // [grid] partial maxima (amax pre-pass)
   double* stats_part;         // [grid][4] partial statistics
   unsigned flags;
+  int32_t flat;               // ldx == K and K % 64 == 0: chunk g starts at element 64 g
 };
 
 __device__ __forceinline__ void divmod_cpr(int64_t g, const HQParams& p, int& row, int& col) {
@@ -73,6 +74,34 @@ __device__ __forceinline__ void stage(const HQParams& p, uint4* lds, int& my_row
   const int j = t & 7;
   int row, col;
   int c0 = t >> 3;
+  if (p.flat) {
+    // contiguous whole-chunk rows: the workgroup's chunks are one contiguous
+    // run starting at chunk g0, so loads need no row / column arithmetic
+    const int chunk_limit = ROWS ? p.rows_per_wg * p.cpr : HQ_THREADS;
+    const int64_t g0 = ROWS ? (int64_t)wg * p.rows_per_wg * p.cpr : (int64_t)wg * HQ_THREADS;
+    const int64_t left = p.total_chunks - g0;
+    const int lim = (int)min<int64_t>(chunk_limit, left);
+    const uint16_t* base = p.x + (g0 + c0) * 64 + 8 * j;
+    uint4 buf[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      buf[i] = (c0 + 32 * i < lim) ? *reinterpret_cast<const uint4*>(base + i * (32 * 64))
+                                   : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int c = c0 + 32 * i;
+      lds[c * 8 + (j ^ (c & 7))] = buf[i];
+    }
+    if (ROWS) {
+      divmod_cpr(t, p, my_row, my_col);
+      my_row += wg * p.rows_per_wg;
+      my_valid = t < lim;
+    } else {
+      divmod_cpr(g0 + t, p, my_row, my_col);
+      my_valid = t < lim;
+    }
+    return;
+  }
   if (ROWS) {
     divmod_cpr(c0, p, row, col);
     row += wg * p.rows_per_wg;
@@ -303,6 +332,16 @@ __global__ __launch_bounds__(kFinalThreads) void hq_stats_final_kernel(const dou
 template <int B>
 __global__ __launch_bounds__(HQ_THREADS) void hq_nvfp4_kernel(HQParams p) {
   __shared__ uint4 lds[HQ_THREADS * 8];
+  __shared__ float inv_tab[128];
+  const float amax = p.ts[0];
+  const bool ok = nvfp4_amax_ok(amax);
+  const float gs = ok ? amax / 2688.0f : 1.0f;
+  // RN(1 / s_dec) for every E4M3 code (s_dec = RN(e4m3 * gs), 0 -> 0): the
+  // per-group reciprocal becomes a table read
+  if (threadIdx.x < 128) {
+    const float sd = e4m3_decode_pos(threadIdx.x) * gs;
+    inv_tab[threadIdx.x] = sd != 0.0f ? 1.0f / sd : 0.0f;
+  }
   int row, col;
   bool valid;
   stage<false>(p, lds, row, col, valid);
@@ -316,9 +355,6 @@ __global__ __launch_bounds__(HQ_THREADS) void hq_nvfp4_kernel(HQParams p) {
   fwht<B>(v);
   normalise<B>(v);
 
-  const float amax = p.ts[0];
-  const bool ok = nvfp4_amax_ok(amax);
-  const float gs = ok ? amax / 2688.0f : 1.0f;
   const float d = 6.0f * gs;
   if (blockIdx.x == 0 && threadIdx.x == 0) p.ts[1] = gs;
 
@@ -332,9 +368,8 @@ __global__ __launch_bounds__(HQ_THREADS) void hq_nvfp4_kernel(HQParams p) {
     for (int e = 0; e < 16; ++e) av = fmaxf(av, fabsf(v[16 * g + e]));
     const float ag = av * yfac<B>();                 // exact (power of two)
     uint32_t s8 = ok ? e4m3_encode_pos(ag / d) : 0u;
-    const float sdec = e4m3_decode_pos(s8) * gs;
-    const bool nz = sdec != 0.0f;
-    const float inv = nz ? 1.0f / sdec : 0.0f;
+    const float inv = inv_tab[s8];                  // 0 exactly when s_dec == 0
+    const bool nz = inv != 0.0f;
     const uint32_t w0 = pack8_e2m1(&v[16 * g], inv, HadScale<B>::inv);
     const uint32_t w1 = pack8_e2m1(&v[16 * g + 8], inv, HadScale<B>::inv);
     words[2 * g] = nz ? w0 : 0u;
@@ -508,6 +543,7 @@ hipError_t launch_hadamard_quantize(const void* x, int64_t M, int64_t K, int64_t
   p.scales = scales;
   p.ts = ts;
   p.flags = flags;
+  p.flat = (ldx == K) && (K % 64) == 0;
   const bool amax_given = (flags & 1u) != 0;
   const bool want_stats = (flags & 2u) != 0;
   int grid;
