@@ -1,5 +1,6 @@
-"""Quantized GEMMs: W4A4 (NVFP4 x NVFP4), W4A8 (INT8 x NVFP4) and the
-full-precision fallback W4A16 (bf16 x NVFP4).
+"""Quantized GEMMs: W4A4 (NVFP4 x NVFP4), W4A8 (INT8 x NVFP4), the
+full-precision fallback W4A16 (bf16 x NVFP4), and the MX-native variant
+(MXFP4 or MXFP8 activations x MXFP4 weights).
 
 Test infrastructure only (see oracle/__init__.py).
 
@@ -14,6 +15,8 @@ token scales and the optional bias, then round once to the output type.
 
 W4A4:  Y = gs_a * gs_w * (A_hat @ W_hat^T) + bias
 W4A8:  Y = s_a[m] * gs_w * (Q_a @ W_hat^T) + bias
+MX:    Y = A_hat @ W_hat^T + bias with A_hat, W_hat the MX dequantized
+       operands (element * 2^(E8M0 - 127) per 32-element block)
 W4A16: Y = gs_w * (A @ W_hat^T) + bias, A the rotated activations in bf16
        ([gist] §2.C: a step flagged by the outlier check runs in FP16/BF16;
        the weights stay 4-bit, [gist] §4 memory figure)
@@ -27,7 +30,7 @@ from __future__ import annotations
 import numpy as np
 
 from .formats import unpack_nibbles, f32_to_bf16
-from .quant import nvfp4_dequantize, GROUP
+from .quant import nvfp4_dequantize, mx_dequantize, MX_ELEM, GROUP
 
 
 def _finish(y64: np.ndarray, bias, out_dtype: str):
@@ -64,6 +67,15 @@ def qgemm_w4a16(a_bits, w_q, w_s, w_gs, bias=None, out_dtype="bf16"):
     W = nvfp4_dequantize(w_q, w_s)
     y = float(np.float32(w_gs)) * (A @ W.T)
     return _finish(y, bias, out_dtype)
+
+
+def qgemm_mx(a_q, a_s, a_fmt, w_q, w_s, bias=None, out_dtype="bf16"):
+    """a_fmt "mxfp4" (packed E2M1 codes [M, K/2]) or "mxfp8" (E4M3 bytes
+    [M, K]); a_s, w_s E8M0 bytes [rows, K/32]; w_q packed E2M1 [N, K/2].
+    Returns (float64 Y, Y rounded to out_dtype)."""
+    A = mx_dequantize(a_q, a_s, MX_ELEM[a_fmt])
+    W = mx_dequantize(w_q, w_s, "e2m1")
+    return _finish(A @ W.T, bias, out_dtype)
 
 
 def w4a8_integer_accumulator(a_q, w_q) -> np.ndarray:

@@ -33,6 +33,23 @@ INT8 (per token row):
   inv = RN(1 / s_m), q = clamp(rint_even(RN(y * inv)), -127, 127).
   Dequantized value: q * s_m.
 
+MXFP4 / MXFP8 (the MX-native variant of the two activation formats; the
+pages name NVFP4 as a Blackwell format, [gist] §2.A, and this variant keeps
+the method on the block-scaled matrix instructions other hardware offers).
+The encoding is the conversion of the OCP Microscaling Formats v1.0
+specification (section 6.3), per block of 32 consecutive elements of a row
+(K % 32 == 0):
+  a = max |y| over the block (exact);
+  e = floor(log2 a) - emax, emax = 2 for E2M1 elements, 8 for E4M3;
+      clamped to [-127, 127]; a block of zeros takes e = -127;
+  scale byte (E8M0) = e + 127;
+  element = nearest-even encoding of y / 2^e (exact division by a power of
+      two), saturating at the element format's largest finite value (6 or
+      448), sign bit kept.
+  Codes: E2M1 packed two per byte as for NVFP4; E4M3 one byte per element.
+  Scales: one byte per block, row-major [M, K/32].  Dequantized value:
+  element * 2^(byte - 127).  No tensor scale.
+
 BF16 (the full-precision fallback of [gist] §2.C / [yly] §三):
   the rotated activations themselves, y rounded to bf16 (nearest even).  The
   weights exist only rotated, so the fallback multiplies rotated bf16
@@ -48,6 +65,8 @@ from .hadamard import block_hadamard_f32
 
 F32 = np.float32
 GROUP = 16
+MX_BLOCK = 32
+MX_EMAX = {"e2m1": 2, "e4m3": 8}
 ZERO_LIMIT = F32(2.0 ** -100)
 
 
@@ -110,6 +129,45 @@ def int8_dequantize(q: np.ndarray, s: np.ndarray) -> np.ndarray:
     return q.astype(np.float64) * s.astype(np.float64)[:, None]
 
 
+def mx_quantize(y: np.ndarray, elem: str):
+    """y: fp32 [M, K], K % 32 == 0; elem "e2m1" or "e4m3".  Returns (codes,
+    E8M0 scale bytes u8 [M, K/32]): codes are packed E2M1 nibbles u8
+    [M, K/2] or E4M3 bytes u8 [M, K]."""
+    y = np.ascontiguousarray(y, dtype=np.float32)
+    M, K = y.shape
+    assert K % MX_BLOCK == 0
+    yb = y.astype(np.float64).reshape(M, K // MX_BLOCK, MX_BLOCK)
+    a = np.max(np.abs(yb), axis=-1) if K else np.zeros((M, 0))
+    # floor(log2 a) exactly: frexp gives a = f * 2^x with f in [0.5, 1)
+    _, x = np.frexp(a)
+    e = np.where(a > 0, x.astype(np.int64) - 1 - MX_EMAX[elem], -127)
+    e = np.clip(e, -127, 127)
+    t = yb / np.power(2.0, e)[..., None]                      # exact
+    if elem == "e2m1":
+        codes = pack_nibbles(float_to_e2m1(t).reshape(M, K))
+    elif elem == "e4m3":
+        codes = float_to_e4m3(t).reshape(M, K)
+    else:
+        raise ValueError(elem)
+    return codes.astype(np.uint8), (e + 127).astype(np.uint8)
+
+
+def mx_dequantize(codes: np.ndarray, scales: np.ndarray, elem: str) -> np.ndarray:
+    """float64 [R, K] = element value * 2^(scale byte - 127) (exact)."""
+    if elem == "e2m1":
+        vals = e2m1_to_float(unpack_nibbles(codes))
+    elif elem == "e4m3":
+        vals = e4m3_to_float(codes)
+    else:
+        raise ValueError(elem)
+    R, K = vals.shape
+    x = np.power(2.0, np.asarray(scales, dtype=np.int64) - 127)
+    return (vals.reshape(R, K // MX_BLOCK, MX_BLOCK) * x[..., None]).reshape(R, K)
+
+
+MX_ELEM = {"mxfp4": "e2m1", "mxfp8": "e4m3"}
+
+
 def activation_stats(x_bits: np.ndarray, y: np.ndarray) -> np.ndarray:
     """The outlier statistics fused into the quantize pass, in float64:
     [max|x|, sum|x|, max|y|, sum|y|] with x the bf16 input before the
@@ -126,7 +184,7 @@ def hadamard_quantize(x_bits: np.ndarray, had_block: int, fmt: str, amax=None):
     """The full per-linear activation pass: block Hadamard of bf16 rows, then
     NVFP4 or INT8 quantization (or bf16 rounding for the full-precision
     fallback), plus the fused outlier statistics.
-    fmt is "nvfp4", "int8" or "bf16".  Returns a dict."""
+    fmt is "nvfp4", "int8", "bf16", "mxfp4" or "mxfp8".  Returns a dict."""
     x = bf16_to_f32(x_bits)
     y = block_hadamard_f32(x, had_block)
     out = {"y": y, "stats": activation_stats(x_bits, y)}
@@ -138,6 +196,9 @@ def hadamard_quantize(x_bits: np.ndarray, had_block: int, fmt: str, amax=None):
         out.update(q=q, scales=s)
     elif fmt == "bf16":
         out.update(q=f32_to_bf16(y))
+    elif fmt in MX_ELEM:
+        q, s = mx_quantize(y, MX_ELEM[fmt])
+        out.update(q=q, scales=s)
     else:
         raise ValueError(fmt)
     return out
@@ -150,3 +211,10 @@ def prepare_weight(w_bits: np.ndarray, had_block: int):
     quantized to NVFP4 with its own tensor scale."""
     r = hadamard_quantize(w_bits, had_block, "nvfp4")
     return r["q"], r["scales"], r["gs"]
+
+
+def prepare_weight_mx(w_bits: np.ndarray, had_block: int):
+    """The MX variant of the weight preparation: the rotated weights in
+    MXFP4 (E2M1 elements, one E8M0 scale per 32).  Returns (codes, scales)."""
+    r = hadamard_quantize(w_bits, had_block, "mxfp4")
+    return r["q"], r["scales"]
