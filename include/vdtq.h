@@ -36,6 +36,11 @@
  *           {amax_T, gs}; value = e2m1(code) * e4m3(scale) * gs.
  *   INT8    codes int8 [M][K] in [-127, 127], per-row fp32 scale s_m;
  *           value = q * s_m.
+ *   MXFP4   OCP Microscaling v1.0: E2M1 codes packed as for NVFP4, one E8M0
+ *           byte per 32 consecutive elements of a row (rows of K/32 bytes);
+ *           value = e2m1(code) * 2^(byte - 127).  No tensor scale.
+ *   MXFP8   the same with one E4M3 byte per element (rows of K bytes);
+ *           value = e4m3(code) * 2^(byte - 127).
  */
 #ifndef VDTQ_H
 #define VDTQ_H
@@ -57,6 +62,8 @@ extern "C" {
 #define VDTQ_FMT_NVFP4 0
 #define VDTQ_FMT_INT8 1
 #define VDTQ_FMT_BF16 2      /* rotated activations in bf16 (W4A16 fallback) */
+#define VDTQ_FMT_MXFP4 3     /* MX-native variant of NVFP4                   */
+#define VDTQ_FMT_MXFP8 4     /* MX-native variant of INT8 (E4M3 elements)    */
 
 #define VDTQ_OUT_BF16 0
 #define VDTQ_OUT_F32 1
@@ -108,20 +115,29 @@ size_t vdtq_workspace_bytes(int op, int64_t M, int64_t K);
  *     else s = RN(a / 127), q = rint_even(RN(y * RN(1 / s))), |q| <= 127.
  *   BF16: q = bf16_RNE(y) ([gist] §2.C: a flagged step runs in FP16/BF16;
  *     the weights exist only rotated, so the activations are rotated too).
+ *   MXFP4 / MXFP8 (the MX-native variant of the two activation formats, for
+ *     block-scaled matrix instructions; OCP Microscaling v1.0 §6.3): per
+ *     32-element block, e = floor(log2 max|y|) - emax (emax 2 for E2M1, 8 for
+ *     E4M3) clamped to [-127, 127] (-127 for an all-zero block), scale byte
+ *     e + 127, element = nearest-even encoding of y / 2^e, saturating at 6
+ *     or 448, sign copied.
  *
  * x_dev          bf16 [M][ldx], ldx >= K (elements)
  * M              rows (tokens), >= 0; M == 0 is a no-op (NVFP4 still writes
  *                the tensor scale {0, 1} unless AMAX_GIVEN)
  * K              columns, > 0, multiple of 16 and of had_block; for INT8,
- *                K <= 16384
+ *                K <= 16384; for MXFP4 / MXFP8 a multiple of 32
  * had_block      16, 32, 64, 128 or 256
- * fmt            VDTQ_FMT_NVFP4, VDTQ_FMT_INT8 or VDTQ_FMT_BF16
+ * fmt            VDTQ_FMT_NVFP4, VDTQ_FMT_INT8, VDTQ_FMT_BF16, VDTQ_FMT_MXFP4
+ *                or VDTQ_FMT_MXFP8
  * flags          VDTQ_AMAX_GIVEN (NVFP4 only) | VDTQ_STATS
- * q_dev          NVFP4: uint8 [M][K/2]; INT8: int8 [M][K]; BF16: bf16 [M][K]
- * scales_dev     NVFP4: uint8 E4M3 [M][K/16]; INT8: float [M]; BF16:
- *                ignored, may be NULL
+ * q_dev          NVFP4, MXFP4: uint8 [M][K/2]; INT8: int8 [M][K]; BF16:
+ *                bf16 [M][K]; MXFP8: uint8 E4M3 [M][K]
+ * scales_dev     NVFP4: uint8 E4M3 [M][K/16]; INT8: float [M]; MXFP4,
+ *                MXFP8: uint8 E8M0 [M][K/32]; BF16: ignored, may be NULL
  * tensor_scale_dev  NVFP4: float[2] {amax_T, gs} (amax_T is read when
- *                AMAX_GIVEN, else written); INT8, BF16: ignored, may be NULL
+ *                AMAX_GIVEN, else written); other formats: ignored, may be
+ *                NULL
  * stats_dev      double[4] {max|x|, sum|x|, max|y|, sum|y|} when
  *                VDTQ_STATS (x before, y after the transform), else ignored
  * ws_dev/ws_bytes  workspace of vdtq_workspace_bytes(VDTQ_OP_HADAMARD_QUANTIZE,
@@ -210,6 +226,39 @@ int qgemm_w4a16(const void* a_dev, const uint8_t* w_q_dev,
                 const float* bias_dev, void* y_dev, int64_t ldy,
                 int out_dtype, int64_t M, int64_t N, int64_t K,
                 void* stream);
+
+/*
+ * qgemm_mx -- the MX-native variant of qgemm_w4a4 / qgemm_w4a8:
+ * Y = A_hat W_hat^T + bias with MXFP4 weights and MXFP4 (4-bit) or MXFP8
+ * (E4M3, 8-bit) activations, both produced by hadamard_quantize with the
+ * same had_block, run on CDNA4's block-scaled matrix instruction.
+ *
+ * Defined by: [gist] §2.A / §3.1 and §4 (4-bit weights; 4- or 8-bit
+ * activations per block and step) with the operands in the OCP
+ * Microscaling v1.0 formats ([gist] §2.A names NVFP4 as a Blackwell format;
+ * this variant is the one CDNA4's matrix cores read without decoding).
+ * A_hat = element * 2^(scale byte - 127) per 32-element block, W_hat
+ * likewise; products of the elements are exact, sums are in fp32 inside
+ * the matrix instruction (E4M3 x E2M1 sums are not rounded per add: the
+ * instruction's own accumulation order and alignment apply).
+ *
+ * a_fmt          VDTQ_FMT_MXFP4 or VDTQ_FMT_MXFP8
+ * a_q_dev        MXFP4: uint8 [M][K/2]; MXFP8: uint8 E4M3 [M][K]
+ * a_s_dev        uint8 E8M0 [M][K/32] (4-byte aligned)
+ * w_q_dev        uint8 [N][K/2] E2M1 codes; w_s_dev uint8 E8M0 [N][K/32]
+ * bias_dev       float [N] or NULL
+ * y_dev/ldy/out_dtype  as for qgemm_w4a4
+ * ws_dev/ws_bytes  workspace of vdtq_workspace_bytes(VDTQ_OP_QGEMM, M, N)
+ *                bytes, 256-byte aligned (partial sums of split tiles)
+ * Errors: VDTQ_EINVAL for a bad a_fmt, K not a multiple of 32, null or
+ * misaligned pointers, ldy < N or a short workspace; VDTQ_EUNSUPPORTED for
+ * K not a multiple of 128 or an operand matrix of 4 GB or more.
+ */
+int qgemm_mx(int a_fmt, const uint8_t* a_q_dev, const uint8_t* a_s_dev,
+             const uint8_t* w_q_dev, const uint8_t* w_s_dev,
+             const float* bias_dev, void* y_dev, int64_t ldy, int out_dtype,
+             int64_t M, int64_t N, int64_t K, void* ws_dev, size_t ws_bytes,
+             void* stream);
 
 /*
  * block_stats -- one pass over a block's input, output and cached delta.

@@ -57,13 +57,15 @@ def _hq(**kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(K=15), L.EINVAL), (dict(K=0), L.EINVAL), (dict(M=-1), L.EINVAL),
     (dict(b=48), L.EINVAL), (dict(b=512), L.EINVAL), (dict(K=96, ldx=96, b=64), L.EINVAL),
-    (dict(ldx=60), L.EINVAL), (dict(ldx=68), L.EINVAL), (dict(fmt=4), L.EINVAL),
+    (dict(ldx=60), L.EINVAL), (dict(ldx=68), L.EINVAL), (dict(fmt=5), L.EINVAL), (dict(fmt=-1), L.EINVAL),
     (dict(flags=4), L.EINVAL), (dict(fmt=1, flags=1), L.EINVAL),
     (dict(fmt=1, K=16384 + 64, ldx=16448), L.EUNSUPPORTED),
     (dict(x=None), L.EINVAL), (dict(q=None), L.EINVAL), (dict(x=FAKE8), L.EINVAL),
     (dict(ts=None), L.EINVAL), (dict(flags=2, st=None), L.EINVAL),
     (dict(ws=None), L.EINVAL), (dict(wsb=8), L.EINVAL),
-    (dict(fmt=3), L.EINVAL), (dict(fmt=2, flags=1), L.EINVAL), (dict(fmt=2, q=None), L.EINVAL),
+    (dict(fmt=2, flags=1), L.EINVAL), (dict(fmt=2, q=None), L.EINVAL),
+    (dict(fmt=3, K=48, ldx=48, b=16), L.EINVAL), (dict(fmt=4, K=80, ldx=80, b=16), L.EINVAL),
+    (dict(fmt=3, flags=1), L.EINVAL), (dict(fmt=4, s=None), L.EINVAL), (dict(fmt=3, q=FAKE8), L.EINVAL),
     (dict(fmt=2, q=FAKE8), L.EINVAL), (dict(fmt=2, flags=2, st=None), L.EINVAL),
 ])
 def test_hadamard_quantize_rejects(kw, code):
@@ -126,6 +128,33 @@ def test_qgemm_w4a16_rejects(kw, code):
 def test_qgemm_w4a16_empty_is_noop():
     assert _a16(M=0, a=None) == L.OK
     assert _a16(N=0, y=None) == L.OK
+
+
+def _mx(**kw):
+    a = dict(fmt=L.FMT_MXFP4, aq=FAKE, as_=FAKE, wq=FAKE, ws=FAKE, bias=None, y=FAKE, ldy=64, od=0, M=8, N=64,
+             K=128, gws=FAKE, gwsb=1 << 28)
+    a.update(kw)
+    return V.lib().qgemm_mx(a["fmt"], a["aq"], a["as_"], a["wq"], a["ws"], a["bias"], a["y"], a["ldy"], a["od"],
+                            a["M"], a["N"], a["K"], a["gws"], a["gwsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(fmt=L.FMT_NVFP4), L.EINVAL), (dict(fmt=L.FMT_INT8), L.EINVAL), (dict(fmt=7), L.EINVAL),
+    (dict(K=0), L.EINVAL), (dict(K=48), L.EINVAL), (dict(M=-1), L.EINVAL), (dict(ldy=10), L.EINVAL),
+    (dict(od=2), L.EINVAL), (dict(aq=None), L.EINVAL), (dict(as_=None), L.EINVAL), (dict(wq=None), L.EINVAL),
+    (dict(ws=None), L.EINVAL), (dict(y=None), L.EINVAL), (dict(aq=FAKE8), L.EINVAL),
+    (dict(gws=None), L.EINVAL), (dict(gwsb=4096), L.EINVAL), (dict(gws=FAKE8), L.EINVAL),
+    (dict(K=96), L.EUNSUPPORTED), (dict(fmt=L.FMT_MXFP8, K=160), L.EUNSUPPORTED),
+    (dict(fmt=L.FMT_MXFP8, M=1 << 21, K=1 << 11), L.EUNSUPPORTED),
+])
+def test_qgemm_mx_rejects(kw, code):
+    assert _mx(**kw) == code
+    assert V.lib().vdtq_last_error()
+
+
+def test_qgemm_mx_empty_is_noop():
+    assert _mx(M=0, aq=None) == L.OK
+    assert _mx(N=0, y=None, gws=None) == L.OK
 
 
 @pytest.mark.parametrize("kw", [dict(n=-1), dict(st=None), dict(inp=None), dict(dnew=FAKE, dprev=FAKE),

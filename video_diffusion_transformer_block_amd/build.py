@@ -20,7 +20,8 @@ CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libvdtq.so")
-SOURCES = ["hadamard_quantize.hip", "qgemm.hip", "qgemm_w4a16.hip", "block_stats.hip", "api.cpp", "dmpq.cpp"]
+SOURCES = ["hadamard_quantize.hip", "qgemm.hip", "qgemm_mx.hip", "qgemm_w4a16.hip", "block_stats.hip", "api.cpp",
+           "dmpq.cpp"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -61,8 +61,11 @@ int hadamard_quantize(const void* x_dev, int64_t M, int64_t K, int64_t ldx, int 
     return fail(VDTQ_EINVAL, "hadamard_quantize: had_block=%d must be 16, 32, 64, 128 or 256", had_block);
   if (K % had_block) return fail(VDTQ_EINVAL, "hadamard_quantize: K=%lld not a multiple of had_block=%d", (long long)K, had_block);
   if (ldx < K || ldx % 8) return fail(VDTQ_EINVAL, "hadamard_quantize: ldx=%lld must be >= K and a multiple of 8", (long long)ldx);
-  if (fmt != VDTQ_FMT_NVFP4 && fmt != VDTQ_FMT_INT8 && fmt != VDTQ_FMT_BF16)
+  if (fmt != VDTQ_FMT_NVFP4 && fmt != VDTQ_FMT_INT8 && fmt != VDTQ_FMT_BF16 && fmt != VDTQ_FMT_MXFP4 &&
+      fmt != VDTQ_FMT_MXFP8)
     return fail(VDTQ_EINVAL, "hadamard_quantize: fmt=%d", fmt);
+  if ((fmt == VDTQ_FMT_MXFP4 || fmt == VDTQ_FMT_MXFP8) && K % 32)
+    return fail(VDTQ_EINVAL, "hadamard_quantize: MX formats need K=%lld to be a multiple of 32", (long long)K);
   if (flags & ~(VDTQ_AMAX_GIVEN | VDTQ_STATS)) return fail(VDTQ_EINVAL, "hadamard_quantize: unknown flags 0x%x", flags);
   if (fmt != VDTQ_FMT_NVFP4 && (flags & VDTQ_AMAX_GIVEN))
     return fail(VDTQ_EINVAL, "hadamard_quantize: VDTQ_AMAX_GIVEN applies to NVFP4 only");
@@ -166,6 +169,32 @@ int qgemm_w4a16(const void* a_dev, const uint8_t* w_q_dev, const uint8_t* w_s_de
   hipError_t e = vdtq::launch_qgemm_w4a16(a_dev, w_q_dev, w_s_dev, w_ts_dev, bias_dev, y_dev, ldy, out_dtype, M, N,
                                           K, static_cast<hipStream_t>(stream));
   return hip_status(e, "qgemm_w4a16 launch");
+}
+
+int qgemm_mx(int a_fmt, const uint8_t* a_q_dev, const uint8_t* a_s_dev, const uint8_t* w_q_dev,
+             const uint8_t* w_s_dev, const float* bias_dev, void* y_dev, int64_t ldy, int out_dtype, int64_t M,
+             int64_t N, int64_t K, void* ws_dev, size_t ws_bytes, void* stream) {
+  const char* name = "qgemm_mx";
+  if (a_fmt != VDTQ_FMT_MXFP4 && a_fmt != VDTQ_FMT_MXFP8) return fail(VDTQ_EINVAL, "%s: a_fmt=%d", name, a_fmt);
+  if (M < 0 || M > kI32 || N < 0 || N > kI32) return fail(VDTQ_EINVAL, "%s: M=%lld N=%lld out of range", name, (long long)M, (long long)N);
+  if (K <= 0 || K > kI32 || K % 32) return fail(VDTQ_EINVAL, "%s: K=%lld must be a positive multiple of 32", name, (long long)K);
+  if (out_dtype != VDTQ_OUT_BF16 && out_dtype != VDTQ_OUT_F32) return fail(VDTQ_EINVAL, "%s: out_dtype=%d", name, out_dtype);
+  if (ldy < N) return fail(VDTQ_EINVAL, "%s: ldy=%lld < N=%lld", name, (long long)ldy, (long long)N);
+  if (M == 0 || N == 0) return ok();
+  if (!a_q_dev || !a_s_dev || !w_q_dev || !w_s_dev || !y_dev) return fail(VDTQ_EINVAL, "%s: null pointer argument", name);
+  if (!aligned(a_q_dev, 16) || !aligned(w_q_dev, 16) || !aligned(a_s_dev, 4) || !aligned(w_s_dev, 4) ||
+      !aligned(y_dev, out_dtype ? 4 : 2) || (bias_dev && !aligned(bias_dev, 4)))
+    return fail(VDTQ_EINVAL, "%s: misaligned pointer (codes need 16 bytes, scales 4)", name);
+  if (K % 128) return fail(VDTQ_EUNSUPPORTED, "%s: K=%lld is not a multiple of 128", name, (long long)K);
+  const bool a8 = a_fmt == VDTQ_FMT_MXFP8;
+  if ((a8 ? M * K : M * K / 2) >= (int64_t(1) << 32) || N * K / 2 >= (int64_t(1) << 32))
+    return fail(VDTQ_EUNSUPPORTED, "%s: operands of 4 GB or more", name);
+  if (((M + 255) / 256) * ((N + 255) / 256) > kI32) return fail(VDTQ_EUNSUPPORTED, "%s: too many output tiles", name);
+  int rc = qgemm_ws_check(name, M, N, ws_dev, ws_bytes);
+  if (rc) return rc;
+  hipError_t e = vdtq::launch_qgemm_mx(a8, a_q_dev, a_s_dev, w_q_dev, w_s_dev, bias_dev, y_dev, ldy, out_dtype, M,
+                                       N, K, ws_dev, static_cast<hipStream_t>(stream));
+  return hip_status(e, "qgemm_mx launch");
 }
 
 int block_stats(const void* in_dev, const void* out_dev, const void* dprev_dev, void* dnew_dev, int64_t n,

@@ -1,5 +1,6 @@
-// Online block Hadamard transform + NVFP4 / per-token INT8 quantization of
-// bf16 activations, with the outlier statistics fused in (gfx950).
+// Online block Hadamard transform + NVFP4 / per-token INT8 / MX (MXFP4,
+// MXFP8) quantization of bf16 activations, with the outlier statistics fused
+// in (gfx950).
 //
 // The operation: gist.science "6Bit-Diffusion: Inference-Time Mixed-Precision
 // Quantization for Video Diffusion Models" §2.A (block Hadamard before
@@ -25,6 +26,12 @@
 //   * INT8: a workgroup owns whole rows; the row maximum is combined with
 //     LDS atomic max on the float bits (order independent), and rint is the
 //     2^23-magic-number add whose low byte is the two's complement code.
+//   * MX (OCP Microscaling v1.0 conversion; the variant of NVFP4 / INT8 for
+//     block-scaled matrix instructions): a thread's chunk is two 32-element
+//     blocks; the E8M0 exponent comes from the block maximum's exponent
+//     field, elements are scaled by exact powers of two and converted by the
+//     hardware (E2M1 saturates by itself; E4M3 is clamped to +-448 first,
+//     the conversion itself does not saturate).  No tensor scale, one pass.
 //   * Statistics: fp32 over a thread's 64 elements, fp64 across threads and
 //     workgroups in a fixed order (bit-reproducible, no float atomics).
 #include <algorithm>
@@ -503,6 +510,110 @@ __global__ __launch_bounds__(HQ_THREADS) void hq_bf16_kernel(HQParams p) {
   }
 }
 
+// ---------------------------------------------------------------- MX pass
+// E8M0 exponent e of a 32-element block from the maximum |v| of its register
+// values (y = v * 2^-KSH): e = floor(log2 max|y|) - EMAX clamped to
+// [-127, 127]; zero (and fp32-subnormal maxima, whose e clamps anyway) give
+// -127.
+template <int EMAX, int KSH>
+__device__ __forceinline__ int mx_exponent(float amax_v) {
+  const int ex = (int)((__float_as_uint(amax_v) >> 23) & 0xFFu);
+  if (ex == 0) return -127;
+  return min(max(ex - 127 - KSH - EMAX, -127), 127);
+}
+
+// 2^n as fp32 for n in [-126, 127] (exact)
+__device__ __forceinline__ float exp2i(int n) { return __uint_as_float((uint32_t)(n + 127) << 23); }
+
+// log2 of the power-of-two factor from register values to y (0 when the
+// normalisation is already applied)
+template <int B> struct HadShift { static constexpr int k = 0; };
+template <> struct HadShift<16>  { static constexpr int k = 2; };
+template <> struct HadShift<64>  { static constexpr int k = 3; };
+template <> struct HadShift<256> { static constexpr int k = 4; };
+
+template <int B, bool FP8>
+__global__ __launch_bounds__(HQ_THREADS) void hq_mx_kernel(HQParams p) {
+  __shared__ uint4 lds[HQ_THREADS * 8];
+  int row, col;
+  bool valid;
+  stage<false>(p, lds, row, col, valid);
+  __syncthreads();
+  float v[64];
+  load_chunk(lds, v);
+  const int nvalid = valid ? min(64, p.K - col * 64) : 0;
+  const bool want_stats = (p.flags & 2u) != 0;
+  float mx = 0.0f, sx = 0.0f;
+  if (want_stats) input_stats(v, nvalid, mx, sx);
+  fwht<B>(v);
+  normalise<B>(v);
+  constexpr int KSH = HadShift<B>::k;
+  constexpr int EMAX = FP8 ? 8 : 2;
+
+  uint32_t words[FP8 ? 16 : 8];
+  uint32_t sbytes = 0;
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk) {
+    const float* vb = &v[32 * blk];
+    float av = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) av = fmaxf(av, fabsf(vb[e]));
+    const int e = mx_exponent<EMAX, KSH>(av);
+    sbytes |= (uint32_t)(e + 127) << (8 * blk);
+    // t = v * 2^-(e + KSH) as two exact power-of-two factors, each a normal
+    // fp32 (|n1|, |n2| <= 65); an intermediate that underflows belongs to an
+    // element far below the smallest nonzero code
+    const int n = e + KSH;
+    const int n1 = n / 2, n2 = n - n1;
+    const float m1 = exp2i(-n1), m2 = exp2i(-n2);
+    if constexpr (FP8) {
+#pragma unroll
+      for (int w = 0; w < 8; ++w) {
+        float t[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) t[i] = __builtin_amdgcn_fmed3f((vb[4 * w + i] * m1) * m2, -448.0f, 448.0f);
+        int x = __builtin_amdgcn_cvt_pk_fp8_f32(t[0], t[1], 0, false);
+        x = __builtin_amdgcn_cvt_pk_fp8_f32(t[2], t[3], x, true);
+        words[8 * blk + w] = (uint32_t)x;
+      }
+    } else {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        uint32_t x = 0u;
+        x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, (vb[8 * w + 0] * m1) * m2, (vb[8 * w + 1] * m1) * m2, 1.0f, 0);
+        x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, (vb[8 * w + 2] * m1) * m2, (vb[8 * w + 3] * m1) * m2, 1.0f, 1);
+        x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, (vb[8 * w + 4] * m1) * m2, (vb[8 * w + 5] * m1) * m2, 1.0f, 2);
+        x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, (vb[8 * w + 6] * m1) * m2, (vb[8 * w + 7] * m1) * m2, 1.0f, 3);
+        words[4 * blk + w] = x;
+      }
+    }
+  }
+
+  if (valid) {
+    constexpr int BYTES = FP8 ? 64 : 32;                      // code bytes per chunk
+    uint4* qrow = reinterpret_cast<uint4*>(p.q + (int64_t)row * (FP8 ? p.K : p.K / 2) + col * BYTES);
+    uint8_t* srow = reinterpret_cast<uint8_t*>(p.scales) + (int64_t)row * (p.K / 32) + col * 2;
+    const int nq = (nvalid == 64 ? BYTES : BYTES / 2) / 16;  // a 32-element tail chunk: first block only
+#pragma unroll
+    for (int i = 0; i < BYTES / 16; ++i)
+      if (i < nq) qrow[i] = make_uint4(words[4 * i], words[4 * i + 1], words[4 * i + 2], words[4 * i + 3]);
+    if (nvalid == 64 && (p.K % 64) == 0)
+      *reinterpret_cast<uint16_t*>(srow) = (uint16_t)sbytes;
+    else
+      for (int b = 0; 32 * b < nvalid; ++b) srow[b] = (uint8_t)(sbytes >> (8 * b));
+  }
+  if (want_stats) {
+    constexpr float f = yfac<B>();
+    float my = 0.0f, sy = 0.0f;
+    for (int i = 0; i < 64; ++i) {
+      const float a = (i < nvalid) ? fabsf(v[i]) : 0.0f;
+      my = fmaxf(my, a);
+      sy = sy + a;
+    }
+    wg_stats_write(mx, sx, (double)(my * f), (double)(sy * f), p.stats_part + 4 * (int64_t)blockIdx.x);
+  }
+}
+
 // ---------------------------------------------------------------- launcher
 template <int B>
 static hipError_t launch_b(const HQParams& p, int fmt, bool amax_given, int grid, hipStream_t st) {
@@ -514,8 +625,12 @@ static hipError_t launch_b(const HQParams& p, int fmt, bool amax_given, int grid
     hipLaunchKernelGGL(hq_nvfp4_kernel<B>, dim3(grid), dim3(HQ_THREADS), 0, st, p);
   } else if (fmt == 1) {
     hipLaunchKernelGGL(hq_int8_kernel<B>, dim3(grid), dim3(HQ_THREADS), 0, st, p);
-  } else {
+  } else if (fmt == 2) {
     hipLaunchKernelGGL(hq_bf16_kernel<B>, dim3(grid), dim3(HQ_THREADS), 0, st, p);
+  } else if (fmt == 3) {
+    hipLaunchKernelGGL((hq_mx_kernel<B, false>), dim3(grid), dim3(HQ_THREADS), 0, st, p);
+  } else {
+    hipLaunchKernelGGL((hq_mx_kernel<B, true>), dim3(grid), dim3(HQ_THREADS), 0, st, p);
   }
   return hipGetLastError();
 }

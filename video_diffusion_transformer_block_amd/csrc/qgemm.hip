@@ -53,33 +53,9 @@
 #include "device_common.h"
 #include "launch.h"
 #include "lds_dma.h"
+#include "qgemm_common.h"
 
 namespace vdtq {
-
-constexpr int GT = 256;     // threads per workgroup
-constexpr int kGemmMaxGrid = 256;   // pipelined path: at most one workgroup per CU
-constexpr int BK = 128;     // K per stage
-
-struct GemmParams {
-  const void* a_q;
-  const void* a_s;
-  const float* a_ts;
-  const uint8_t* w_q;
-  const uint8_t* w_s;
-  const float* w_ts;
-  const float* bias;
-  void* y;
-  int64_t ldy;
-  int32_t M, N, K;
-  int32_t out_f32;
-  int32_t tiles_m, tiles_n;
-  // pipelined path: K stages per tile and the work split of the grid
-  int32_t nk;
-  int32_t sk_tiles;        // tiles 0 .. sk_tiles-1 are split along K (stream-K)
-  int32_t slices;          // K slices per split tile (>= 2 when sk_tiles > 0)
-  int32_t slice_nk;        // stages per slice (the last may be shorter)
-  float* part;             // [slices][sk_tiles][256 * 256] partial tiles
-};
 
 // --------------------------------------------------------------- decoding
 // E4M3 byte pair -> fp16 pair holding scale * 2^-8 each: the 7 magnitude bits
@@ -110,11 +86,8 @@ __device__ __forceinline__ half8 dec_i8x8(uint32_t w0, uint32_t w1) {
 }
 
 // --------------------------------------------------------------- LDS layout
-// NVFP4 rows: 64 bytes per stage = quads q = 0..3 (q = 2c + h), stored at
-// quad position q ^ ((row >> 1) & 3).  INT8 rows: 128 bytes = quads 0..7,
-// stored at q ^ (row & 7).  Scales: 8 bytes per row and stage, unswizzled.
-__device__ __forceinline__ int fp4_quad_off(int row, int q) { return row * 64 + 16 * (q ^ ((row >> 1) & 3)); }
-__device__ __forceinline__ int i8_quad_off(int row, int q) { return row * 128 + 16 * (q ^ (row & 7)); }
+// Code rows are swizzled (fp4_quad_off / i8_quad_off); NVFP4 scales: 8 bytes
+// per row and stage, unswizzled.
 
 // One stage of packed operand rows: `rows` rows from `row0` (clamped to the
 // last valid row), K columns k0 .. k0+127 (zero past K).
@@ -382,13 +355,6 @@ void qgemm_kernel(GemmParams p) {
 //   * a step-level software pipeline: the 16 MFMAs of step s are interleaved
 //     (sched_group_barrier) with the decode of step s+1 and the LDS reads of
 //     the next chunk, so the VALU work hides under the MFMAs.
-// Partial tile of slice `sl` of split tile `tile`.  Layout inside a slot:
-// [wave][64 float4][64 lanes], float4 q of a lane holding accumulator tile
-// (q / 16, (q / 4) % 4), registers 4 (q % 4) .. 4 (q % 4) + 3.
-__device__ __forceinline__ float4* part_slot(const GemmParams& p, int sl, int tile) {
-  return reinterpret_cast<float4*>(p.part) + ((size_t)sl * p.sk_tiles + tile) * (256 * 256 / 4);
-}
-
 // PAIRS (K % 256 == 0): the E4M3 scales of two consecutive stages (16
 // contiguous bytes per row) arrive in one 16-byte load per row, into a
 // double-buffered pair region after the ring, instead of two 4-byte loads
@@ -712,44 +678,7 @@ void qgemm_pipe_kernel(GemmParams p) {
 
   // epilogue: tile (i, j), lane, register e -> token row m0 + wm*128 + 32 i
   // + lane%32, feature column n0 + wn*128 + 32 j + 8 (e/4) + 4 (lane/32) + e%4
-  const float gsw = p.w_ts[1];
-  const float alpha_t = (AFMT == 0) ? p.a_ts[1] * gsw : 0.0f;
-  const bool vec = (p.N % 4) == 0 && (p.ldy % 4) == 0 &&
-                   ((reinterpret_cast<uintptr_t>(p.y) & (p.out_f32 ? 15u : 7u)) == 0) &&
-                   (!p.bias || (reinterpret_cast<uintptr_t>(p.bias) & 15u) == 0);
-  // four consecutive outputs of one row: scale, bias, convert, store
-  auto emit4 = [&](int row, int col, float alpha, float x0, float x1, float x2, float x3) {
-    float v[4] = {x0 * alpha, x1 * alpha, x2 * alpha, x3 * alpha};
-    if (vec && col + 4 <= p.N) {
-      if (p.bias) {
-        const float4 b = *reinterpret_cast<const float4*>(p.bias + col);
-        v[0] = v[0] + b.x; v[1] = v[1] + b.y; v[2] = v[2] + b.z; v[3] = v[3] + b.w;
-      }
-      if (p.out_f32) {
-        *reinterpret_cast<float4*>(static_cast<float*>(p.y) + (int64_t)row * p.ldy + col) =
-            make_float4(v[0], v[1], v[2], v[3]);
-      } else {
-        const uint32_t lo = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
-        const uint32_t hi = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
-        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.y) + (int64_t)row * p.ldy + col) = make_uint2(lo, hi);
-      }
-    } else {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if (col + q >= p.N) continue;
-        float x = v[q];
-        if (p.bias) x = x + p.bias[col + q];
-        if (p.out_f32)
-          static_cast<float*>(p.y)[(int64_t)row * p.ldy + col + q] = x;
-        else
-          static_cast<uint16_t*>(p.y)[(int64_t)row * p.ldy + col + q] = (uint16_t)f32_to_bf16_bits(x);
-      }
-    }
-  };
-  auto row_alpha = [&](int row) {
-    return (AFMT == 0) ? alpha_t : static_cast<const float*>(p.a_s)[row] * gsw;
-  };
-
+  const bool vec = out_vec_ok(p);
   if constexpr (SPLIT) {
     // partial sums of this K slice; the reduce kernel finishes the tile
     float4* mine = part_slot(p, (int)(blockIdx.x / p.sk_tiles), tile) + wv * 64 * 64 + lane;
@@ -765,91 +694,14 @@ void qgemm_pipe_kernel(GemmParams p) {
   for (int i = 0; i < 4; ++i) {
     const int row = m0 + wm * 128 + 32 * i + r32;
     if (row >= p.M) continue;
-    const float alpha = row_alpha(row);
+    const float alpha = row_alpha<AFMT>(p, row);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int g = 0; g < 4; ++g)
-        emit4(row, n0 + wn * 128 + 32 * j + 8 * g + 4 * h, alpha, acc[i][j][4 * g], acc[i][j][4 * g + 1],
+        emit4(p, vec, row, n0 + wn * 128 + 32 * j + 8 * g + 4 * h, alpha, acc[i][j][4 * g], acc[i][j][4 * g + 1],
               acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
   }
-}
-
-// Split tiles: out = alpha * (sum of the slices in slice order) + bias.
-// One thread per float4 of a partial slot; 64 workgroups per tile.
-template <int AFMT>
-__global__ __launch_bounds__(256) void qgemm_reduce_kernel(GemmParams p) {
-  const int tile = (int)(blockIdx.x / 64);
-  const int f = (int)(blockIdx.x % 64) * 256 + (int)threadIdx.x;   // float4 index in the slot
-  const int wv = f >> 12, q = (f >> 6) & 63, lane = f & 63;
-  const int i = q >> 4, j = (q >> 2) & 3, g = q & 3;
-  int tm, tn;
-  tile_coords(tile, p.tiles_m, p.tiles_n, tm, tn);
-  const int row = tm * 256 + (wv >> 1) * 128 + 32 * i + (lane & 31);
-  const int col = tn * 256 + (wv & 1) * 128 + 32 * j + 8 * g + 4 * (lane >> 5);
-  if (row >= p.M) return;
-  float4 sum = part_slot(p, 0, tile)[f];
-  for (int sl = 1; sl < p.slices; ++sl) {
-    const float4 x = part_slot(p, sl, tile)[f];
-    sum.x += x.x; sum.y += x.y; sum.z += x.z; sum.w += x.w;
-  }
-  const float gsw = p.w_ts[1];
-  const float alpha = (AFMT == 0) ? p.a_ts[1] * gsw : static_cast<const float*>(p.a_s)[row] * gsw;
-  float v[4] = {sum.x * alpha, sum.y * alpha, sum.z * alpha, sum.w * alpha};
-  const bool vec = (p.N % 4) == 0 && (p.ldy % 4) == 0 && col + 4 <= p.N &&
-                   ((reinterpret_cast<uintptr_t>(p.y) & (p.out_f32 ? 15u : 7u)) == 0) &&
-                   (!p.bias || (reinterpret_cast<uintptr_t>(p.bias) & 15u) == 0);
-  if (vec) {
-    if (p.bias) {
-      const float4 b = *reinterpret_cast<const float4*>(p.bias + col);
-      v[0] = v[0] + b.x; v[1] = v[1] + b.y; v[2] = v[2] + b.z; v[3] = v[3] + b.w;
-    }
-    if (p.out_f32) {
-      *reinterpret_cast<float4*>(static_cast<float*>(p.y) + (int64_t)row * p.ldy + col) =
-          make_float4(v[0], v[1], v[2], v[3]);
-    } else {
-      const uint32_t lo = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
-      const uint32_t hi = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
-      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.y) + (int64_t)row * p.ldy + col) = make_uint2(lo, hi);
-    }
-    return;
-  }
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    if (col + c >= p.N) continue;
-    float x = v[c];
-    if (p.bias) x = x + p.bias[col + c];
-    if (p.out_f32)
-      static_cast<float*>(p.y)[(int64_t)row * p.ldy + col + c] = x;
-    else
-      static_cast<uint16_t*>(p.y)[(int64_t)row * p.ldy + col + c] = (uint16_t)f32_to_bf16_bits(x);
-  }
-}
-// Work split of a pipelined call on `cus` compute units.  Whole waves of
-// tiles go to the data-parallel kernel.  The tiles of a last, partial wave
-// (all tiles when there are fewer than CUs) are split into `slices` K slices,
-// at most one workgroup per CU in all, when that is estimated to finish
-// sooner than a partial wave of whole tiles: a slice's stages plus about
-// kSplitOverhead stages of pipeline fill, partial-sum traffic and the reduce
-// pass, against nk.
-constexpr int kSplitOverhead = 3;
-
-static void plan_pipe(GemmParams& p, int cus, int& dp_grid, int& sk_grid) {
-  p.tiles_m = (p.M + 255) / 256;
-  p.tiles_n = (p.N + 255) / 256;
-  p.nk = p.K / BK;
-  const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n;
-  const int G = std::max(1, std::min(cus, kGemmMaxGrid));
-  const int64_t left = tiles % G;
-  int slices = left > 0 ? (int)std::min<int64_t>(G / left, p.nk) : 0;
-  int slice_nk = slices > 0 ? (p.nk + slices - 1) / slices : 0;
-  if (slices > 0) slices = (p.nk + slice_nk - 1) / slice_nk;   // no empty slice
-  const bool split = slices >= 2 && slice_nk + kSplitOverhead < p.nk;
-  p.sk_tiles = split ? (int32_t)left : 0;
-  p.slices = split ? slices : 0;
-  p.slice_nk = split ? slice_nk : 0;
-  dp_grid = (int)(tiles - p.sk_tiles);
-  sk_grid = split ? (int)(left * slices) : 0;
 }
 
 template <int AFMT, bool SPLIT, bool PAIRS>
@@ -909,19 +761,6 @@ size_t qgemm_workspace_bytes(int64_t M, int64_t N) {
   if (M <= 0 || N <= 0) return 0;
   // at most one K slice per CU (kGemmMaxGrid) is in flight
   return (size_t)kGemmMaxGrid * 256 * 256 * sizeof(float);
-}
-
-static int cu_count() {
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return kGemmMaxGrid;
-  if (cached[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-      n = kGemmMaxGrid;
-    cached[dev] = n;
-  }
-  return cached[dev];
 }
 
 hipError_t launch_qgemm(int afmt, const void* a_q, const void* a_s, const float* a_ts,

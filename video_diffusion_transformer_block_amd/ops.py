@@ -81,9 +81,20 @@ class INT8Tensor:
     stats: Optional[torch.Tensor] = None
 
 
+@dataclass
+class MXTensor:
+    """MX operand: codes (MXFP4: packed E2M1 [R, K/2] u8; MXFP8: E4M3 [R, K]
+    u8) and E8M0 scales [R, K/32] u8; fmt is "mxfp4" or "mxfp8"."""
+    q: torch.Tensor
+    scales: torch.Tensor
+    fmt: str
+    stats: Optional[torch.Tensor] = None
+
+
 def hadamard_quantize(x: torch.Tensor, had_block: int = 64, fmt: str = "nvfp4", amax=None,
                       stats: bool = False, out=None):
-    """Block Hadamard transform of bf16 rows + NVFP4 or INT8 quantization.
+    """Block Hadamard transform of bf16 rows + NVFP4, INT8, MXFP4 or MXFP8
+    quantization (or bf16 rounding).
     amax (NVFP4 only): a float or a 1-element device tensor to use as the
     tensor amax instead of computing it, or the string "given" to use the
     value already in out.ts[0].  out: a previously returned NVFP4Tensor /
@@ -129,6 +140,16 @@ def hadamard_quantize(x: torch.Tensor, had_block: int = 64, fmt: str = "nvfp4", 
         q = out.q if out is not None else torch.empty((M, K), dtype=torch.bfloat16, device=dev)
         s = ts = None
         fcode = L.FMT_BF16
+    elif fmt in ("mxfp4", "mxfp8"):
+        if amax is not None:
+            raise ValueError("amax applies to nvfp4 only")
+        if out is not None:
+            q, s = out.q, out.scales
+        else:
+            q = torch.empty((M, K // 2 if fmt == "mxfp4" else K), dtype=torch.uint8, device=dev)
+            s = torch.empty((M, K // 32), dtype=torch.uint8, device=dev)
+        ts = None
+        fcode = L.FMT_MXFP4 if fmt == "mxfp4" else L.FMT_MXFP8
     else:
         raise ValueError(fmt)
     L.check(L.lib().hadamard_quantize(_p(x), M, K, x.stride(0), had_block, fcode, flags, _p(q), _p(s),
@@ -137,6 +158,8 @@ def hadamard_quantize(x: torch.Tensor, had_block: int = 64, fmt: str = "nvfp4", 
         return NVFP4Tensor(q, s, ts, st)
     if fcode == L.FMT_BF16:
         return BF16Tensor(q, st)
+    if fcode in (L.FMT_MXFP4, L.FMT_MXFP8):
+        return MXTensor(q, s, fmt, st)
     return INT8Tensor(q, s, st)
 
 
@@ -188,6 +211,25 @@ def qgemm_w4a16(a: BF16Tensor, w: NVFP4Tensor, bias: Optional[torch.Tensor] = No
     L.check(L.lib().qgemm_w4a16(_p(a.q), _p(w.q), _p(w.scales), _p(w.ts), _p(bias), _p(y), y.stride(0),
                                 L.OUT_BF16 if out_dtype == "bf16" else L.OUT_F32, M, N, K,
                                 _stream(a.q.device)))
+    return y
+
+
+def qgemm_mx(a: MXTensor, w: MXTensor, bias: Optional[torch.Tensor] = None,
+             out_dtype: str = "bf16", y: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """MX-native product: MXFP4 or MXFP8 activations x MXFP4 weights."""
+    if w.fmt != "mxfp4":
+        raise ValueError("MX weights must be mxfp4")
+    M = a.q.shape[0]
+    K = a.q.shape[1] * (2 if a.fmt == "mxfp4" else 1)
+    N = w.q.shape[0]
+    if w.q.shape[1] * 2 != K:
+        raise ValueError("K mismatch between activations and weights")
+    y = _out(M, N, out_dtype, a.q.device, y)
+    ws = gemm_workspace(a.q.device, M, N)
+    L.check(L.lib().qgemm_mx(L.FMT_MXFP4 if a.fmt == "mxfp4" else L.FMT_MXFP8, _p(a.q), _p(a.scales), _p(w.q),
+                             _p(w.scales), _p(bias), _p(y), y.stride(0),
+                             L.OUT_BF16 if out_dtype == "bf16" else L.OUT_F32, M, N, K, _p(ws), ws.numel(),
+                             _stream(a.q.device)))
     return y
 
 
