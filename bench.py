@@ -12,7 +12,9 @@ One step = one pass of the whole hot path over one block:
   with more than one block).
 The headline step uses the 50/50 NVFP4/INT8 assignment (QKV and FFN-down
 NVFP4, out-proj and FFN-up INT8), the W4A6 operating point of the pages; the
-all-NVFP4 and all-INT8 sweeps are timed the same way after it.
+all-NVFP4, all-INT8 and all-W4A16 sweeps are timed the same way after it,
+then the MX-native variant (MXFP4 weights; MXFP4 / MXFP8 activations on the
+block-scaled MFMA) with the same 50/50 assignment, all-MXFP4 and all-MXFP8.
 
 value = sum of 2*M*N*K over the four linears / step time (TOPS).  Inputs are
 seeded synthetic bf16 (Laplace(0,1) with 0.5% of the channels x30), resident
@@ -46,8 +48,15 @@ SWEEPS = {"mixed_w4a6": MIXED,
           "all_w4a4": {k: "nvfp4" for k in MIXED},
           "all_w4a8": {k: "int8" for k in MIXED},
           # the full-precision fallback (bf16 activations, 4-bit weights) on every linear
-          "all_w4a16": {k: "bf16" for k in MIXED}}
-GEMM_OF = {"nvfp4": "qgemm_w4a4", "int8": "qgemm_w4a8", "bf16": "qgemm_w4a16"}
+          "all_w4a16": {k: "bf16" for k in MIXED},
+          # the MX-native variant: MXFP4 weights, MXFP4 / MXFP8 activations on the
+          # block-scaled MFMA, same 50/50 assignment, then all-4-bit / all-8-bit
+          "mx_mixed": {k: ("mxfp4" if v == "nvfp4" else "mxfp8") for k, v in MIXED.items()},
+          "all_mxfp4": {k: "mxfp4" for k in MIXED},
+          "all_mxfp8": {k: "mxfp8" for k in MIXED}}
+GEMM_OF = {"nvfp4": "qgemm_w4a4", "int8": "qgemm_w4a8", "bf16": "qgemm_w4a16", "mxfp4": "qgemm_mx",
+           "mxfp8": "qgemm_mx"}
+MX_PEAK = {"mxfp4": PEAK_FP4_TFLOPS, "mxfp8": PEAK_FP8_TFLOPS}
 
 
 def parse():
@@ -88,11 +97,15 @@ def main():
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
 
     t0 = time.time()
-    X, W, host = {}, {}, {}
+    chosen = [w for w in args.sweeps.split(",") if w]
+    want_mx = any(f.startswith("mx") for sw in chosen for f in SWEEPS[sw].values())
+    X, W, WM, host = {}, {}, {}, {}
     for name, K, N in linears:
         x, w = synth.layer_inputs(M, name, K, N)
         host[name] = (x, w)
         X[name], W[name] = up(x), V.hadamard_quantize(up(w), HAD_BLOCK, "nvfp4")  # offline weight prep
+        if want_mx:
+            WM[name] = V.hadamard_quantize(up(w), HAD_BLOCK, "mxfp4")
     dprev = torch.zeros((M, hidden), dtype=torch.bfloat16, device=dev)
     dnew = torch.empty_like(dprev)
     Y = {name: torch.empty((M, N), dtype=torch.bfloat16, device=dev) for name, K, N in linears}
@@ -120,8 +133,10 @@ def main():
                 V.qgemm_w4a4(a, W[name], None, "bf16", y=Y[name])
             elif fmt == "int8":
                 V.qgemm_w4a8(a, W[name], None, "bf16", y=Y[name])
-            else:
+            elif fmt == "bf16":
                 V.qgemm_w4a16(a, W[name], None, "bf16", y=Y[name])
+            else:
+                V.qgemm_mx(a, WM[name], None, "bf16", y=Y[name])
             if rec is not None:
                 e2.record()
                 rec.append((name, fmt, e0, e1, e2))
@@ -150,7 +165,6 @@ def main():
             sched["pending"] = None
 
     results = {}
-    chosen = [w for w in args.sweeps.split(",") if w]
     for sweep in chosen:
         assign = SWEEPS[sweep]
         for _ in range(args.warmup):
@@ -210,8 +224,25 @@ def main():
                         f"same rate vs fp8 {PEAK_FP8_TFLOPS:.0f}, fp4 {PEAK_FP4_TFLOPS:.0f} TFLOP/s: "
                         f"{achieved / PEAK_FP8_TFLOPS:.3f}, {achieved / PEAK_FP4_TFLOPS:.3f}"}
 
+    # the MX GEMMs against their own peaks (FP4 10.1 PF for MXFP4 x MXFP4, FP8
+    # 5.0 PF for MXFP8 x MXFP4), per activation format over the MX sweeps run
+    mx_roof = {}
+    for sweep, v in results.items():
+        for name, d in v["per_linear"].items():
+            if d["fmt"] in MX_PEAK:
+                m = mx_roof.setdefault(d["fmt"], {"ms": 0.0, "flops": 0.0, "launches": 0})
+                m["ms"] += d["gemm_ms"]
+                m["flops"] += flops[name]
+                m["launches"] += 1
+    for fmt, m in mx_roof.items():
+        ach = m["flops"] / (m["ms"] * 1e-3) / 1e12
+        mx_roof[fmt] = {"bound": "mfma", "kernel": f"qgemm_mx_kernel<{'true' if fmt == 'mxfp8' else 'false'}, *>",
+                        "achieved": round(ach, 1), "peak": MX_PEAK[fmt], "unit": "TFLOP/s",
+                        "frac": round(ach / MX_PEAK[fmt], 4), "avg_launch_us": round(1e3 * m["ms"] / m["launches"], 1),
+                        "launches": m["launches"]}
+
     # quantize pass alone (tensor amax supplied: the single fused kernel), HBM bound
-    qroof = measure_quantize(torch, V, X, M, args.steps)
+    qroof = measure_quantize(torch, V, X, M, args.steps, want_mx)
     if rec is not None:
         for q in qroof.values():
             e = rec["kernels"].get(q["kernel"], {}).get("grids", {}).get(str(q["grid_work_items"]))
@@ -249,6 +280,7 @@ def main():
         "pct_fp16_mfma_peak": round(100 * head["tops"] / PEAK_FP16_MFMA_TFLOPS, 2),
         "roofline": roofline,
         "quantize_roofline": qroof,
+        "mx_gemm_roofline": mx_roof or None,
         "sweeps": {k: {"tops": round(v["tops"], 2), "ms_per_step": round(v["ms_per_step"], 4),
                        "gemm_tflops": round(total_flops / (sum(d["gemm_ms"] for d in v["per_linear"].values())
                                                            * 1e-3) / 1e12, 1),
@@ -386,16 +418,21 @@ def gemm_call_traffic(rec, afmt):
 
 def hq_grid_work_items(M, K, fmt):
     """Work-items of one quantize launch, as the library's launcher sizes it:
-    one 64-element chunk per thread for NVFP4; for INT8, max(1, 256 / chunks
-    per row) whole rows per 256-thread group.  Keys the counter record."""
+    one 64-element chunk per thread for NVFP4 and MX; for INT8, max(1, 256 /
+    chunks per row) whole rows per 256-thread group.  Keys the counter record."""
     cpr = (K + 63) // 64
-    if fmt == "nvfp4":
+    if fmt != "int8":
         return -(-M * cpr // 256) * 256
     rpw = max(1, 256 // cpr)
     return -(-M // rpw) * 256
 
 
-def measure_quantize(torch, V, X, M, steps):
+QUANT_BYTES = {"nvfp4": 2 + 0.5 + 1 / 16, "int8": 3.0, "mxfp4": 2 + 0.5 + 1 / 32, "mxfp8": 2 + 1 + 1 / 32}
+QUANT_KERNEL = {"nvfp4": "hq_nvfp4_kernel<64>", "int8": "hq_int8_kernel<64>",
+                "mxfp4": "hq_mx_kernel<64, false>", "mxfp8": "hq_mx_kernel<64, true>"}
+
+
+def measure_quantize(torch, V, X, M, steps, with_mx=False):
     """hadamard_quantize with the tensor amax supplied (the single fused
     kernel).  The launches are captured in a graph and replayed, so the
     per-launch time (HIP events around the replays / launches) excludes host
@@ -405,7 +442,8 @@ def measure_quantize(torch, V, X, M, steps):
     out = {}
     for K, names in ((3072, ["qkv", "out", "ffn_up"]), (12288, ["ffn_down"])):
         elems = M * K
-        for fmt, bpe in (("nvfp4", 2 + 0.5 + 1 / 16), ("int8", 3.0)):
+        for fmt in ("nvfp4", "int8") + (("mxfp4", "mxfp8") if with_mx else ()):
+            bpe = QUANT_BYTES[fmt]
             extra = 0 if fmt == "nvfp4" else 4 * M / elems
             # buffers allocated (and the tensor amax written) before capture
             outs = [V.hadamard_quantize(X[n], HAD_BLOCK, fmt) for n in names]
@@ -429,7 +467,7 @@ def measure_quantize(torch, V, X, M, steps):
                 times.append(e0.elapsed_time(e1) / n_launch)
             us = 1e3 * float(np.median(times))
             gbs = (bpe + extra) * elems / (us * 1e-6) / 1e9
-            out[f"{fmt}_K{K}"] = {"bound": "hbm", "kernel": f"hq_{fmt}_kernel<64>", "achieved": round(gbs, 1),
+            out[f"{fmt}_K{K}"] = {"bound": "hbm", "kernel": QUANT_KERNEL[fmt], "achieved": round(gbs, 1),
                                   "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                                   "traffic": None, "avg_launch_us": round(us, 2),
                                   "bytes_per_launch": (bpe + extra) * elems, "shape": [M, K],
