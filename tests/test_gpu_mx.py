@@ -191,6 +191,35 @@ def test_gemm_cogvideox_5b_sampled(name):
     check_gemm(x, w, rows=synth.row_sample(M, 48), out_dtypes=("bf16",))
 
 
+def test_gemm_two_waves_and_split_tail():
+    """Two waves of data-parallel tiles (512 of 600) plus a split tail of 88
+    tiles in 2 K slices, ragged M, bias."""
+    need_gpu()
+    M, N, K = 2000, 19200, 1024
+    x = synth.to_bf16_bits(RNG.laplace(size=(M, K)).astype(np.float32))
+    w = synth.to_bf16_bits(RNG.standard_normal((N, K)).astype(np.float32) * 0.02)
+    check_gemm(x, w, rows=synth.row_sample(M, 96), out_dtypes=("bf16",))
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "mxfp8"])
+def test_gemm_bf16_output_is_rounded_f32(fmt):
+    """The bf16 output is the fp32 output (same accumulation order) rounded
+    to nearest even, bit for bit: pins the epilogue's bf16 conversion."""
+    need_gpu()
+    M, N, K = 4096, 9216, 1024
+    x = torch.from_numpy(RNG.laplace(size=(M, K)).astype(np.float32)).to(torch.bfloat16).cuda()
+    w = (torch.from_numpy(RNG.standard_normal((N, K)).astype(np.float32)) * 0.02).to(torch.bfloat16).cuda()
+    bias = torch.from_numpy(RNG.standard_normal(N).astype(np.float32)).cuda()
+    a = V.hadamard_quantize(x, 64, fmt)
+    wd = V.hadamard_quantize(w, 64, "mxfp4")
+    yb = V.qgemm_mx(a, wd, bias, "bf16")
+    yf = V.qgemm_mx(a, wd, bias, "f32")
+    torch.cuda.synchronize()
+    want = F.f32_to_bf16(yf.cpu().numpy())
+    got = host_bits(yb)
+    assert np.array_equal(got, want), np.argwhere(got != want)[:5]
+
+
 def test_gemm_rejects_unsupported_k():
     need_gpu()
     a = V.MXTensor(torch.zeros((4, 48), dtype=torch.uint8, device="cuda"),

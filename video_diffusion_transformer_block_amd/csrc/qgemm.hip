@@ -676,9 +676,6 @@ void qgemm_pipe_kernel(GemmParams p) {
     interleave();
   }
 
-  // epilogue: tile (i, j), lane, register e -> token row m0 + wm*128 + 32 i
-  // + lane%32, feature column n0 + wn*128 + 32 j + 8 (e/4) + 4 (lane/32) + e%4
-  const bool vec = out_vec_ok(p);
   if constexpr (SPLIT) {
     // partial sums of this K slice; the reduce kernel finishes the tile
     float4* mine = part_slot(p, (int)(blockIdx.x / p.sk_tiles), tile) + wv * 64 * 64 + lane;
@@ -689,6 +686,14 @@ void qgemm_pipe_kernel(GemmParams p) {
     }
     return;
   }
+  // bf16 output in whole 16-byte chunks: through LDS (the ring is free)
+  if (staged_store_ok(p)) {
+    stage_store_tile<AFMT, (P::LDS >= 4 * 32768) ? 1 : 2>(p, acc, smem, m0, n0);
+    return;
+  }
+  // epilogue: tile (i, j), lane, register e -> token row m0 + wm*128 + 32 i
+  // + lane%32, feature column n0 + wn*128 + 32 j + 8 (e/4) + 4 (lane/32) + e%4
+  const bool vec = out_vec_ok(p);
 
 #pragma unroll
   for (int i = 0; i < 4; ++i) {

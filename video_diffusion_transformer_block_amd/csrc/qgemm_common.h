@@ -58,6 +58,14 @@ __device__ __forceinline__ bool out_vec_ok(const GemmParams& p) {
          (!p.bias || (reinterpret_cast<uintptr_t>(p.bias) & 15u) == 0);
 }
 
+// Two fp32 -> packed bf16 by the hardware conversion (v_cvt_pk_bf16_f32,
+// round to nearest even): one instruction per pair in the epilogue.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16_pair(float a, float b) {
+  const bf16x2_t v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
 // Four consecutive outputs of one row: scale, bias, convert, store (columns
 // past N are dropped).
 __device__ __forceinline__ void emit4(const GemmParams& p, bool vec, int row, int col, float alpha, float x0,
@@ -72,9 +80,8 @@ __device__ __forceinline__ void emit4(const GemmParams& p, bool vec, int row, in
       *reinterpret_cast<float4*>(static_cast<float*>(p.y) + (int64_t)row * p.ldy + col) =
           make_float4(v[0], v[1], v[2], v[3]);
     } else {
-      const uint32_t lo = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
-      const uint32_t hi = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
-      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.y) + (int64_t)row * p.ldy + col) = make_uint2(lo, hi);
+      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.y) + (int64_t)row * p.ldy + col) =
+          make_uint2(bf16_pair(v[0], v[1]), bf16_pair(v[2], v[3]));
     }
     return;
   }
@@ -97,6 +104,71 @@ __device__ __forceinline__ float row_alpha(const GemmParams& p, int row) {
   if constexpr (AFMT == 0) return p.a_ts[1] * p.w_ts[1];
   else if constexpr (AFMT == 1) return static_cast<const float*>(p.a_s)[row] * p.w_ts[1];
   else return 1.0f;
+}
+
+// Whether a tile's bf16 outputs can leave through LDS as whole 16-byte
+// chunks (stage_store_tile).
+__device__ __forceinline__ bool staged_store_ok(const GemmParams& p) {
+  return !p.out_f32 && (p.N % 8) == 0 && (p.ldy % 8) == 0 && (reinterpret_cast<uintptr_t>(p.y) & 15u) == 0 &&
+         (!p.bias || (reinterpret_cast<uintptr_t>(p.bias) & 15u) == 0);
+}
+
+// bf16 epilogue of a 256 x 256 tile through LDS.  The accumulators hold Y^T
+// blocks (lane = one token row, 4 consecutive features per register group),
+// so direct stores would write 16 bytes into each of 32 rows per
+// instruction.  Instead each wave writes its 128 x 128 sub-tile, scaled,
+// biased and rounded to bf16, to LDS (rows of 256 bytes, 16-byte chunk c of
+// row r at chunk position c ^ (r & 15): conflict-free writes), reads it back
+// as 16-byte row chunks and stores 4 whole 256-byte row segments per
+// instruction.  ROUNDS: the sub-tile goes through LDS in that many parts
+// (32 KB / ROUNDS per wave); the caller has finished every LDS read of the
+// ring, and smem holds at least 4 x 32 KB / ROUNDS bytes.
+template <int AFMT, int ROUNDS>
+__device__ __forceinline__ void stage_store_tile(const GemmParams& p, const float16v (&acc)[4][4], uint8_t* smem,
+                                                 int m0, int n0) {
+  constexpr int IPR = 4 / ROUNDS;                       // 32-row blocks per round
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  const int wm = wv >> 1, wn = wv & 1, r32 = lane & 31, h = lane >> 5;
+  uint8_t* reg = smem + wv * (32768 / ROUNDS);
+  // bias of this lane's 64 columns: 32 j + 8 g + 4 h .. +3 (of the wave's 128)
+  float4 bias[4][4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      bias[j][g] = p.bias ? *reinterpret_cast<const float4*>(p.bias + min(n0 + wn * 128 + 32 * j + 8 * g + 4 * h, p.N - 4))
+                          : make_float4(0.f, 0.f, 0.f, 0.f);
+  __syncthreads();   // every wave is past its last read of the ring
+#pragma unroll
+  for (int rd = 0; rd < ROUNDS; ++rd) {
+#pragma unroll
+    for (int ii = 0; ii < IPR; ++ii) {
+      const int i = rd * IPR + ii;
+      const int lrow = 32 * ii + r32;                   // row within this round's part
+      const float alpha = row_alpha<AFMT>(p, min(m0 + wm * 128 + 32 * i + r32, p.M - 1));
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const float4 b = bias[j][g];
+          const float v0 = acc[i][j][4 * g] * alpha + b.x, v1 = acc[i][j][4 * g + 1] * alpha + b.y;
+          const float v2 = acc[i][j][4 * g + 2] * alpha + b.z, v3 = acc[i][j][4 * g + 3] * alpha + b.w;
+          const int c = (4 * j + g) ^ (lrow & 15);
+          *reinterpret_cast<uint2*>(reg + lrow * 256 + 16 * c + 8 * h) = make_uint2(bf16_pair(v0, v1), bf16_pair(v2, v3));
+        }
+    }
+    // the same wave reads back what it wrote (LDS operations of a wave run in order)
+    const int c = lane & 15;
+#pragma unroll
+    for (int it = 0; it < 8 * IPR; ++it) {
+      const int lrow = 4 * it + (lane >> 4);
+      const uint4 v = *reinterpret_cast<const uint4*>(reg + lrow * 256 + 16 * (c ^ (lrow & 15)));
+      const int row = m0 + wm * 128 + 32 * rd * IPR + lrow;
+      const int col = n0 + wn * 128 + 8 * c;
+      if (row < p.M && col < p.N)
+        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.y) + (int64_t)row * p.ldy + col) = v;
+    }
+  }
 }
 
 // Split tiles: out = alpha * (sum of the slices in slice order) + bias.

@@ -32,8 +32,9 @@
 //   * scales: one dword per row and stage (4 blocks); a lane shifts its
 //     row's dword by 8 (l / 32) bits so that op_sel 0 / 2 picks its block of
 //     step 0 / 1;
-//   * the tile order, the split of a partial last wave into K slices and the
-//     reduce pass are those of the NVFP4 / INT8 kernel (qgemm_common.h).
+//   * the tile order, the split of a partial last wave into K slices, the
+//     reduce pass and the bf16 epilogue through LDS are those of the NVFP4 /
+//     INT8 kernel (qgemm_common.h).
 #include <type_traits>
 
 #include "device_common.h"
@@ -268,6 +269,11 @@ void qgemm_mx_kernel(GemmParams p) {
     return;
   }
 
+  // bf16 output in whole 16-byte chunks: through LDS (the ring is free)
+  if (staged_store_ok(p)) {
+    stage_store_tile<2, (P::LDS >= 4 * 32768) ? 1 : 2>(p, acc, smem, m0, n0);
+    return;
+  }
   // epilogue: tile (i, j), lane, register e -> token row m0 + wm*128 + 32 i
   // + lane%32, feature column n0 + wn*128 + 32 j + 8 (e/4) + 4 (lane/32) + e%4
   const bool vec = out_vec_ok(p);
