@@ -86,7 +86,10 @@ __device__ __forceinline__ int8v mx_operand(const int4v& v) {
   return __builtin_shufflevector(v, v, 0, 1, 2, 3, -1, -1, -1, -1);
 }
 
-template <bool A8, bool SPLIT>
+// STAGED: the bf16 epilogue through LDS (the host checks staged_store_ok);
+// otherwise per-element stores.  One epilogue per instantiation keeps the
+// accumulators in AGPRs until they are read.
+template <bool A8, bool SPLIT, bool STAGED>
 __global__ __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void qgemm_mx_kernel(GemmParams p) {
   using P = MxPipe<A8>;
@@ -270,7 +273,7 @@ void qgemm_mx_kernel(GemmParams p) {
   }
 
   // bf16 output in whole 16-byte chunks: through LDS (the ring is free)
-  if (staged_store_ok(p)) {
+  if constexpr (STAGED) {
     stage_store_tile<2, (P::LDS >= 4 * 32768) ? 1 : 2>(p, acc, smem, m0, n0);
     return;
   }
@@ -290,11 +293,11 @@ void qgemm_mx_kernel(GemmParams p) {
   }
 }
 
-template <bool A8, bool SPLIT>
+template <bool A8, bool SPLIT, bool STAGED>
 static hipError_t set_mx_lds_attr() {
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&qgemm_mx_kernel<A8, SPLIT>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&qgemm_mx_kernel<A8, SPLIT, STAGED>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, MxPipe<A8>::LDS);
     if (e != hipSuccess) return e;
     attr_set = true;
@@ -307,16 +310,22 @@ static hipError_t launch_mx(GemmParams p, hipStream_t st) {
   int dp_grid = 0, sk_grid = 0;
   plan_pipe(p, cu_count(), dp_grid, sk_grid);
   const size_t lds = (size_t)MxPipe<A8>::LDS;
-  hipError_t e = set_mx_lds_attr<A8, false>();
-  if (e == hipSuccess) e = set_mx_lds_attr<A8, true>();
+  // the same test as the device-side staged_store_ok
+  const bool staged = !p.out_f32 && (p.N % 8) == 0 && (p.ldy % 8) == 0 && (reinterpret_cast<uintptr_t>(p.y) & 15u) == 0 &&
+                      (!p.bias || (reinterpret_cast<uintptr_t>(p.bias) & 15u) == 0);
+  hipError_t e = staged ? set_mx_lds_attr<A8, false, true>() : set_mx_lds_attr<A8, false, false>();
+  if (e == hipSuccess) e = set_mx_lds_attr<A8, true, false>();
   if (e != hipSuccess) return e;
   if (dp_grid > 0) {
-    hipLaunchKernelGGL((qgemm_mx_kernel<A8, false>), dim3(dp_grid), dim3(GT), lds, st, p);
+    if (staged)
+      hipLaunchKernelGGL((qgemm_mx_kernel<A8, false, true>), dim3(dp_grid), dim3(GT), lds, st, p);
+    else
+      hipLaunchKernelGGL((qgemm_mx_kernel<A8, false, false>), dim3(dp_grid), dim3(GT), lds, st, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (sk_grid > 0) {
-    hipLaunchKernelGGL((qgemm_mx_kernel<A8, true>), dim3(sk_grid), dim3(GT), lds, st, p);
+    hipLaunchKernelGGL((qgemm_mx_kernel<A8, true, false>), dim3(sk_grid), dim3(GT), lds, st, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((qgemm_reduce_kernel<2>), dim3(p.sk_tiles * 64), dim3(256), 0, st, p);
