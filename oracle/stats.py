@@ -22,6 +22,13 @@ Readings:
 block_stats returns eight float64 sums / maxima, in this order:
   [sum d^2, sum in^2, sum (Dnew - Dprev)^2, sum Dprev^2,
    max|in|, sum|in|, max|out|, sum|out|]
+
+Low-precision delta cache ([yly] §七: the cache's extra memory can be
+reduced by storing it in low precision).  block_stats_mx8 caches Delta in
+MXFP8 (E4M3 elements, one E8M0 scale per 32 consecutive elements, the MX
+conversion of oracle/quant.py) instead of bf16: Delta_new = MXFP8(d) with d
+as above, and entries 2 and 3 use the dequantized stored deltas (what a
+later step reads back).  The other six entries are unchanged.
 """
 from __future__ import annotations
 
@@ -56,6 +63,37 @@ def block_stats(in_bits, out_bits, dprev_bits=None):
     st[6] = np.max(np.abs(o64))
     st[7] = np.sum(np.abs(o64))
     return dnew, st
+
+
+def block_stats_mx8(in_bits, out_bits, dprev=None):
+    """dprev: None or (codes u8 [n], E8M0 scales u8 [n/32]) of the cached
+    delta, n % 32 == 0.  Returns ((codes, scales) of Delta_new, stats
+    float64[8])."""
+    from .quant import mx_quantize, mx_dequantize
+    xi = bf16_to_f32(in_bits).reshape(1, -1)
+    xo = bf16_to_f32(out_bits).reshape(1, -1)
+    n = xi.size
+    assert n % 32 == 0
+    d = (xo - xi).astype(np.float32)                 # fp32 RN
+    q, sc = mx_quantize(d, "e4m3")
+    st = np.zeros(8)
+    if n == 0:
+        return (q.reshape(-1), sc.reshape(-1)), st
+    d64 = d.astype(np.float64)
+    i64 = xi.astype(np.float64)
+    o64 = xo.astype(np.float64)
+    st[0] = np.sum(d64 * d64)
+    st[1] = np.sum(i64 * i64)
+    if dprev is not None:
+        dn = mx_dequantize(q, sc, "e4m3")
+        dp = mx_dequantize(np.asarray(dprev[0]).reshape(1, -1), np.asarray(dprev[1]).reshape(1, -1), "e4m3")
+        st[2] = np.sum((dn - dp) ** 2)
+        st[3] = np.sum(dp * dp)
+    st[4] = np.max(np.abs(i64))
+    st[5] = np.sum(np.abs(i64))
+    st[6] = np.max(np.abs(o64))
+    st[7] = np.sum(np.abs(o64))
+    return (q.reshape(-1), sc.reshape(-1)), st
 
 
 def gamma(st) -> float:
