@@ -257,6 +257,8 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    bsroof = measure_block_stats(torch, V, X["qkv"], Y["ffn_down"], M * hidden, args.steps)
+
     dyn = None if args.no_dyn else measure_dyn(torch, V, synth)
     cpu = None if args.no_cpu_baseline else cpu_baseline(host, M, args.cpu_rows)
 
@@ -281,6 +283,7 @@ def main():
         "roofline": roofline,
         "quantize_roofline": qroof,
         "mx_gemm_roofline": mx_roof or None,
+        "block_stats_roofline": bsroof,
         "sweeps": {k: {"tops": round(v["tops"], 2), "ms_per_step": round(v["ms_per_step"], 4),
                        "gemm_tflops": round(total_flops / (sum(d["gemm_ms"] for d in v["per_linear"].values())
                                                            * 1e-3) / 1e12, 1),
@@ -303,8 +306,10 @@ def measure_dyn(torch, V, synth, blocks=30, steps=50, M=4446, hidden=1920):
     a smooth seeded residual plus decaying noise; three (block, step) pairs
     carry one channel x300.  Inputs and weights come from torch's seeded GPU
     generator.  The same loop is run again with every block-step forced to
-    the BF16 fallback and no skip, for the reference.  Times are HIP events
-    around each computed block's quantize + GEMM."""
+    the BF16 fallback and no skip, for the reference, and once more with the
+    delta cache in MXFP8 (block_stats_mx8; a skipped block adds the
+    dequantized cached delta).  Times are HIP events around each computed
+    block's quantize + GEMM."""
     dev = torch.device("cuda:0")
     gen = torch.Generator(device=dev)
 
@@ -330,11 +335,18 @@ def measure_dyn(torch, V, synth, blocks=30, steps=50, M=4446, hidden=1920):
     flops = 2.0 * M * hidden * 3 * hidden
     fmt_of = {V.ACT_NVFP4: "nvfp4", V.ACT_INT8: "int8", V.ACT_BF16: "bf16"}
 
-    def run(params):
+    def deq_mx8(c):
+        # the cached MXFP8 delta as fp32 [M, hidden] (the skipped block's residual)
+        v = c.q.view(torch.float8_e4m3fn).float().view(-1, 32) * torch.exp2(c.scales.float() - 127.0)[:, None]
+        return v.view(M, hidden)
+
+    def run(params, cache_fmt="bf16"):
         states = [V.dmpq_state() for _ in range(blocks)]
         last = [None] * blocks
         cache = [None] * blocks
-        spare = [torch.empty((M, hidden), dtype=torch.bfloat16, device=dev) for _ in range(blocks)]
+        acts = []
+        spare = [None if cache_fmt == "mxfp8" else torch.empty((M, hidden), dtype=torch.bfloat16, device=dev)
+                 for _ in range(blocks)]
         counts = {"skip": 0, "nvfp4": 0, "int8": 0, "bf16": 0}
         events = []
         torch.cuda.synchronize()
@@ -351,9 +363,11 @@ def measure_dyn(torch, V, synth, blocks=30, steps=50, M=4446, hidden=1920):
                 _, rs = V.block_stats(x, x, write_delta=False)
                 rs = rs.cpu().numpy()
                 act = V.dmpq_step(params, states[b], last[b], V.outlier_ratio(rs[4], rs[5], M * hidden))
+                acts.append(act)
                 if act == V.ACT_SKIP:
                     counts["skip"] += 1
-                    out = (x.float() + cache[b].float()).to(torch.bfloat16)
+                    res = deq_mx8(cache[b]) if cache_fmt == "mxfp8" else cache[b].float()
+                    out = (x.float() + res).to(torch.bfloat16)
                     last[b] = None
                 else:
                     fmt = fmt_of[act]
@@ -370,10 +384,13 @@ def measure_dyn(torch, V, synth, blocks=30, steps=50, M=4446, hidden=1920):
                     decay = float(np.float32(beta_b * np.exp(-t / 10.0)))
                     z = torch.roll(noise[b], (7919 * t) % (M * hidden)).view(M, hidden)
                     out = (x.float() + (U[b] * smooth + z * decay)).to(torch.bfloat16)
-                    dnew = spare[b]
-                    _, st = V.block_stats(x, out, cache[b], dnew)
+                    if cache_fmt == "mxfp8":
+                        dnew, st = V.block_stats_mx8(x, out, cache[b], spare[b])
+                    else:
+                        dnew = spare[b]
+                        _, st = V.block_stats(x, out, cache[b], dnew)
                     last[b] = st.cpu().numpy()
-                    spare[b] = cache[b] if cache[b] is not None else torch.empty_like(dnew)
+                    spare[b] = cache[b] if cache[b] is not None or cache_fmt == "mxfp8" else torch.empty_like(dnew)
                     cache[b] = dnew
                 x = out
         torch.cuda.synchronize()
@@ -382,14 +399,16 @@ def measure_dyn(torch, V, synth, blocks=30, steps=50, M=4446, hidden=1920):
         for fmt, e0, e1 in events:
             per.setdefault(fmt, []).append(e0.elapsed_time(e1))
         total = sum(sum(v) for v in per.values())
-        return counts, per, total, wall
+        return counts, per, total, wall, acts
 
     p_dyn = V.dmpq_params(gamma=0.1, tau=0.05, tau_acc=0.15, rho=1000.0)
     p_ref = V.dmpq_params(gamma=0.1, tau=0.0, tau_acc=0.0, rho=-1.0)    # always computes, always BF16
-    counts, per, total, wall = run(p_dyn)
-    rcounts, rper, rtotal, rwall = run(p_ref)
-    print(f"[bench] dyn schedule: actions {counts}, linear path {total:.1f} ms vs {rtotal:.1f} ms all-BF16",
-          file=sys.stderr, flush=True)
+    counts, per, total, wall, acts = run(p_dyn)
+    rcounts, rper, rtotal, rwall, _ = run(p_ref)
+    c8, per8, total8, wall8, acts8 = run(p_dyn, "mxfp8")
+    same = float(np.mean(np.array(acts) == np.array(acts8)))
+    print(f"[bench] dyn schedule: actions {counts}, linear path {total:.1f} ms vs {rtotal:.1f} ms all-BF16; "
+          f"MXFP8 cache: actions {c8}, {100 * same:.1f}% of decisions unchanged", file=sys.stderr, flush=True)
     return {"workload": f"closed loop, {blocks} blocks x {steps} steps, M={M}, hidden {hidden}, "
                         f"QKV {hidden}->{3 * hidden} at the scheduled precision",
             "params": {"gamma": 0.1, "tau": 0.05, "tau_acc": 0.15, "rho": 1000.0, "warmup": 2},
@@ -399,7 +418,11 @@ def measure_dyn(torch, V, synth, blocks=30, steps=50, M=4446, hidden=1920):
             "linear_ms_total": round(total, 2),
             "all_bf16_linear_ms_total": round(rtotal, 2),
             "linear_speedup_vs_all_bf16": round(rtotal / total, 3) if total else None,
-            "wall_s": round(wall, 2), "all_bf16_wall_s": round(rwall, 2)}
+            "wall_s": round(wall, 2), "all_bf16_wall_s": round(rwall, 2),
+            "mxfp8_cache": {"actions": c8, "linear_ms_total": round(total8, 2),
+                            "same_action_fraction": round(same, 4),
+                            "cache_bytes_per_block": M * hidden * (1 + 1 / 32),
+                            "bf16_cache_bytes_per_block": M * hidden * 2}}
 
 
 def gemm_call_traffic(rec, afmt):
@@ -414,6 +437,42 @@ def gemm_call_traffic(rec, afmt):
                 if name.startswith(f"qgemm_pipe_kernel<{afmt}, false"):
                     calls += e["dispatches"]
     return round(total / calls) if calls else None
+
+
+def measure_block_stats(torch, V, inp, out, n, steps):
+    """block_stats over the 5B block's input and output (17776 x 3072) with
+    the delta cache in bf16 (8 bytes per element: in, out, Delta_prev read,
+    Delta_new written) and in MXFP8 (6 + 1/16 bytes per element), each
+    reading the delta the previous launch wrote; HIP events around 20
+    launches."""
+    res = {}
+    for cache, bpe in (("bf16", 8.0), ("mxfp8", 6.0 + 2 / 32)):
+        if cache == "bf16":
+            d0, _ = V.block_stats(inp, out)
+            d1 = torch.empty_like(d0)
+            run = lambda a, b: V.block_stats(inp, out, a, b)
+        else:
+            d0, _ = V.block_stats_mx8(inp, out)
+            d1, _ = V.block_stats_mx8(inp, out)
+            run = lambda a, b: V.block_stats_mx8(inp, out, a, b)
+        run(d0, d1)
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(max(3, steps // 4)):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for i in range(20):
+                run(d0, d1) if i % 2 == 0 else run(d1, d0)
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1) / 20)
+        us = 1e3 * float(np.median(times))
+        gbs = bpe * n / (us * 1e-6) / 1e9
+        res[cache] = {"bound": "hbm", "kernel": "block_stats_kernel" if cache == "bf16" else "block_stats_mx8_kernel",
+                      "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                      "avg_launch_us": round(us, 2), "bytes_per_launch": bpe * n,
+                      "cache_bytes": n * (2 if cache == "bf16" else 1 + 1 / 32)}
+    return res
 
 
 def hq_grid_work_items(M, K, fmt):

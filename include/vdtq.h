@@ -282,6 +282,36 @@ int block_stats(const void* in_dev, const void* out_dev,
                 double* stats_dev, void* ws_dev, size_t ws_bytes,
                 void* stream);
 
+/*
+ * block_stats_mx8 -- block_stats with the delta cache in MXFP8.
+ *
+ * Defined by: the passages of block_stats, and [yly] §七 (the temporal
+ * delta cache needs extra memory, which storing it in low precision
+ * reduces).
+ *
+ * d = RN_fp32(out - in); Delta_new = MXFP8(d): per 32 consecutive elements
+ * e = floor(log2 max|d|) - 8 clamped to [-127, 127] (-127 for an all-zero
+ * block), code = E4M3 nearest-even of d / 2^e saturating at 448 (sign kept),
+ * scale byte e + 127 (the MX conversion of hadamard_quantize's MXFP8).
+ * stats_dev double[8] as for block_stats, except that entries 2 and 3 are
+ * taken on the dequantized stored deltas: sum (dnew - dprev)^2 and
+ * sum dprev^2 with dnew, dprev = e4m3(code) * 2^(byte - 127).
+ * in_dev, out_dev  bf16 [n], n a multiple of 32 (16-byte aligned)
+ * dprev_q_dev, dprev_s_dev  the previous delta: uint8 E4M3 [n] (8-byte
+ *                aligned) and uint8 E8M0 [n/32], both NULL when there is none
+ * dnew_q_dev, dnew_s_dev  the new delta, same layout; both NULL to skip the
+ *                write; must not alias dprev
+ * ws_dev: vdtq_workspace_bytes(VDTQ_OP_BLOCK_STATS, n, 1) bytes.
+ * Errors: VDTQ_EINVAL for n not a multiple of 32, a null or misaligned
+ * pointer, codes without scales (or the reverse), aliasing, or a short
+ * workspace.
+ */
+int block_stats_mx8(const void* in_dev, const void* out_dev,
+                    const uint8_t* dprev_q_dev, const uint8_t* dprev_s_dev,
+                    uint8_t* dnew_q_dev, uint8_t* dnew_s_dev, int64_t n,
+                    double* stats_dev, void* ws_dev, size_t ws_bytes,
+                    void* stream);
+
 /* ------------------------------------------------------------ scheduler */
 
 typedef struct {

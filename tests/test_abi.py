@@ -166,6 +166,21 @@ def test_block_stats_rejects(kw):
     assert rc == L.EINVAL
 
 
+FAKE4 = ctypes.c_void_p(0x10004)
+
+
+@pytest.mark.parametrize("kw", [dict(n=-32), dict(n=48), dict(st=None), dict(inp=None), dict(pq=FAKE, ps=None),
+                                dict(nq=None), dict(nq=FAKE, pq=FAKE, ps=FAKE), dict(ws=None), dict(wsb=0),
+                                dict(inp=FAKE8), dict(nq=FAKE4)])
+def test_block_stats_mx8_rejects(kw):
+    a = dict(inp=FAKE, out=FAKE, pq=None, ps=None, nq=FAKE, ns=FAKE8, n=64, st=FAKE, ws=FAKE, wsb=1 << 20)
+    a.update(kw)
+    rc = V.lib().block_stats_mx8(a["inp"], a["out"], a["pq"], a["ps"], a["nq"], a["ns"], a["n"], a["st"], a["ws"],
+                                 a["wsb"], None)
+    assert rc == L.EINVAL
+    assert V.lib().vdtq_last_error()
+
+
 def test_dmpq_step_hand_sequence():
     g = json.load(open(os.path.join(ROOT, "tests", "golden", "dmpq_sequence.json")))
     p = V.dmpq_params(**g["params"])

@@ -62,3 +62,63 @@ def test_repeatable():
     _, s2 = V.block_stats(a, b, a)
     torch.cuda.synchronize()
     assert torch.equal(s1, s2)
+
+
+# ---- the delta cache in MXFP8
+
+def check_mx8(inp, out, dprev):
+    """dprev: None or (codes, scales) host arrays."""
+    log(f"block_stats_mx8 n={inp.size} dprev={dprev is not None}")
+    dp = None
+    if dprev is not None:
+        dp = V.MXTensor(torch.from_numpy(dprev[0]).cuda(), torch.from_numpy(dprev[1]).cuda(), "mxfp8")
+    dn, st = V.block_stats_mx8(dev_bf16(inp), dev_bf16(out), dp)
+    torch.cuda.synchronize()
+    (qref, sref_s), sref = S.block_stats_mx8(inp, out, dprev)
+    assert np.array_equal(dn.q.cpu().numpy(), qref)
+    assert np.array_equal(dn.scales.cpu().numpy(), sref_s)
+    got = st.cpu().numpy()
+    assert got[4] == sref[4] and got[6] == sref[6]
+    assert np.allclose(got, sref, rtol=1e-5, atol=0), (got, sref)
+    return got, (qref, sref_s)
+
+
+@pytest.mark.parametrize("n", [0, 32, 96, 1024, 65536 + 32, 4446 * 1920])
+def test_mx8_random(n):
+    need_gpu()
+    inp = synth.to_bf16_bits(RNG.laplace(size=n).astype(np.float32))
+    out = synth.to_bf16_bits(RNG.laplace(size=n).astype(np.float32) * 0.1 + F32(inp))
+    _, first = check_mx8(inp, out, None)
+    # the next step reads the cached delta back
+    out2 = synth.to_bf16_bits(RNG.laplace(size=n).astype(np.float32) * 0.1 + F32(inp))
+    check_mx8(inp, out2, first)
+
+
+def test_mx8_extreme_blocks():
+    """Zero deltas (exponent -127), bf16 subnormal deltas, deltas near 1e30,
+    and blocks whose largest delta lands in the clipping band."""
+    need_gpu()
+    n = 32 * 6
+    inp = np.zeros(n, np.float32)
+    out = np.zeros(n, np.float32)
+    out[32:64] = 2.0 ** -130
+    out[64:96] = RNG.standard_normal(32).astype(np.float32) * 1e30
+    out[96:128] = np.linspace(-15, 15, 32).astype(np.float32)
+    out[128:160] = -0.0
+    out[160:192] = RNG.standard_normal(32).astype(np.float32) * 3
+    prev = (np.full(n, 0x38, np.uint8), np.full(n // 32, 120, np.uint8))
+    check_mx8(synth.to_bf16_bits(inp), synth.to_bf16_bits(out), prev)
+
+
+def test_mx8_repeatable():
+    need_gpu()
+    n = 4446 * 1920
+    a = dev_bf16(synth.to_bf16_bits(RNG.laplace(size=n).astype(np.float32)))
+    b = dev_bf16(synth.to_bf16_bits(RNG.laplace(size=n).astype(np.float32)))
+    d1, s1 = V.block_stats_mx8(a, b)
+    _, s2 = V.block_stats_mx8(a, b, d1)
+    _, s3 = V.block_stats_mx8(a, b, d1)
+    torch.cuda.synchronize()
+    assert torch.equal(s2, s3)
+    assert float(s2[2].cpu()) == 0.0      # the same delta read back
+

@@ -213,4 +213,25 @@ int block_stats(const void* in_dev, const void* out_dev, const void* dprev_dev, 
   return hip_status(e, "block_stats launch");
 }
 
+int block_stats_mx8(const void* in_dev, const void* out_dev, const uint8_t* dprev_q_dev, const uint8_t* dprev_s_dev,
+                    uint8_t* dnew_q_dev, uint8_t* dnew_s_dev, int64_t n, double* stats_dev, void* ws_dev,
+                    size_t ws_bytes, void* stream) {
+  const char* name = "block_stats_mx8";
+  if (n < 0 || n % 32) return fail(VDTQ_EINVAL, "%s: n=%lld must be a non-negative multiple of 32", name, (long long)n);
+  if (!stats_dev || !aligned(stats_dev, 8)) return fail(VDTQ_EINVAL, "%s: null or misaligned stats", name);
+  if ((dprev_q_dev == nullptr) != (dprev_s_dev == nullptr) || (dnew_q_dev == nullptr) != (dnew_s_dev == nullptr))
+    return fail(VDTQ_EINVAL, "%s: codes and scales of a delta are given together or not at all", name);
+  if (n > 0 && (!in_dev || !out_dev)) return fail(VDTQ_EINVAL, "%s: null in/out", name);
+  if (!aligned(in_dev, 16) || !aligned(out_dev, 16) || !aligned(dprev_q_dev, 8) || !aligned(dnew_q_dev, 8))
+    return fail(VDTQ_EINVAL, "%s: in/out must be 16-byte aligned, delta codes 8-byte aligned", name);
+  if (dnew_q_dev && (dnew_q_dev == dprev_q_dev || dnew_s_dev == dprev_s_dev))
+    return fail(VDTQ_EINVAL, "%s: dnew must not alias dprev", name);
+  const size_t need = vdtq::bs_workspace_bytes(n);
+  if (!ws_dev || !aligned(ws_dev, 16) || ws_bytes < need)
+    return fail(VDTQ_EINVAL, "%s: workspace of %zu bytes (16-byte aligned) required, got %zu", name, need, ws_bytes);
+  hipError_t e = vdtq::launch_block_stats_mx8(in_dev, out_dev, dprev_q_dev, dprev_s_dev, dnew_q_dev, dnew_s_dev, n,
+                                              stats_dev, ws_dev, static_cast<hipStream_t>(stream));
+  return hip_status(e, "block_stats_mx8 launch");
+}
+
 }  // extern "C"

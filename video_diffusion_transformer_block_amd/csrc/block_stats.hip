@@ -13,6 +13,15 @@
 // a grid-stride loop over a grid sized from n only, accumulates in fp64, and
 // the workgroup / grid reductions run in a fixed order: the eight results are
 // bit-identical from run to run.
+//
+// block_stats_mx8_kernel is the same pass with the delta cache in MXFP8
+// (youleyou.com article §七: the cache's memory can be cut by storing it in
+// low precision): Delta_new = MXFP8(out - in) (E4M3 elements, one E8M0
+// exponent per 32 consecutive elements, the OCP Microscaling conversion)
+// and Delta_prev read as MXFP8, so a step moves 6 + 1/16 bytes per element
+// instead of 8.  Four consecutive lanes hold one 32-element block (8
+// elements each), combine its maximum with two lane exchanges, and write 32
+// contiguous code bytes.
 #include "device_common.h"
 #include "launch.h"
 
@@ -107,6 +116,112 @@ __global__ __launch_bounds__(BS_THREADS) void block_stats_kernel(const uint16_t*
   }
 }
 
+// 2^e as fp64 (e in [-127, 127])
+__device__ __forceinline__ double exp2d(int e) { return __longlong_as_double((long long)(e + 1023) << 52); }
+
+// The E4M3 value of each byte of w (hardware conversion, exact), times 2^e.
+__device__ __forceinline__ void fp8x4_values(uint32_t w, int e, double (&v)[4]) {
+  const float2v lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+  const float2v hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+  const double s = exp2d(e);
+  v[0] = (double)lo[0] * s; v[1] = (double)lo[1] * s; v[2] = (double)hi[0] * s; v[3] = (double)hi[1] * s;
+}
+
+__global__ __launch_bounds__(BS_THREADS) void block_stats_mx8_kernel(const uint16_t* in, const uint16_t* out,
+                                                                     const uint8_t* dprev_q, const uint8_t* dprev_s,
+                                                                     uint8_t* dnew_q, uint8_t* dnew_s, int64_t n,
+                                                                     double* part) {
+  Acc8 a;
+  const bool has_prev = dprev_q != nullptr;
+  const int64_t nvec = n / 8;                    // a multiple of 4: n % 32 == 0
+  const int64_t stride = (int64_t)gridDim.x * BS_THREADS;
+  for (int64_t v = (int64_t)blockIdx.x * BS_THREADS + threadIdx.x; v < nvec; v += stride) {
+    const uint4 wi = reinterpret_cast<const uint4*>(in)[v];
+    const uint4 wo = reinterpret_cast<const uint4*>(out)[v];
+    const uint32_t ii[4] = {wi.x, wi.y, wi.z, wi.w};
+    const uint32_t oo[4] = {wo.x, wo.y, wo.z, wo.w};
+    float d[8];
+    float amax = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float i0 = bf16_lo(ii[k]), i1 = bf16_hi(ii[k]), o0 = bf16_lo(oo[k]), o1 = bf16_hi(oo[k]);
+      d[2 * k] = o0 - i0;                         // fp32 RN
+      d[2 * k + 1] = o1 - i1;
+      const float e0[2] = {i0, i1}, e1[2] = {o0, o1};
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const double dd = (double)d[2 * k + q], xi = (double)e0[q];
+        a.d2 += dd * dd;
+        a.i2 += xi * xi;
+        const float ai = fabsf(e0[q]), ao = fabsf(e1[q]);
+        a.mi = fmaxf(a.mi, ai);
+        a.mo = fmaxf(a.mo, ao);
+        a.si += (double)ai;
+        a.so += (double)ao;
+      }
+      amax = fmaxf(amax, fmaxf(fabsf(d[2 * k]), fabsf(d[2 * k + 1])));
+    }
+    // the block's maximum over its four lanes (all active together)
+    amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+    amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+    // E8M0 exponent: floor(log2 amax) - 8 clamped to [-127, 127]; zero and
+    // fp32-subnormal maxima give -127
+    const int ex = (int)((__float_as_uint(amax) >> 23) & 0xFFu);
+    const int e = ex == 0 ? -127 : min(max(ex - 127 - 8, -127), 127);
+    // d * 2^-e as two exact power-of-two factors (normal fp32 each); clamp
+    // to +-448 (the conversion itself does not saturate)
+    const int n1 = -e / 2, n2 = -e - n1;
+    const float m1 = __uint_as_float((uint32_t)(n1 + 127) << 23), m2 = __uint_as_float((uint32_t)(n2 + 127) << 23);
+    uint32_t codes[2];
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      float t[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) t[i] = __builtin_amdgcn_fmed3f((d[4 * w + i] * m1) * m2, -448.0f, 448.0f);
+      int x = __builtin_amdgcn_cvt_pk_fp8_f32(t[0], t[1], 0, false);
+      x = __builtin_amdgcn_cvt_pk_fp8_f32(t[2], t[3], x, true);
+      codes[w] = (uint32_t)x;
+    }
+    if (dnew_q) {
+      reinterpret_cast<uint2*>(dnew_q)[v] = make_uint2(codes[0], codes[1]);
+      if ((threadIdx.x & 3) == 0) dnew_s[v >> 2] = (uint8_t)(e + 127);
+    }
+    if (has_prev) {
+      const uint2 pq = reinterpret_cast<const uint2*>(dprev_q)[v];
+      const int ep = (int)dprev_s[v >> 2] - 127;
+      const uint32_t pw[2] = {pq.x, pq.y};
+#pragma unroll
+      for (int w = 0; w < 2; ++w) {
+        double dn[4], dp[4];
+        fp8x4_values(codes[w], e, dn);
+        fp8x4_values(pw[w], ep, dp);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const double df = dn[i] - dp[i];
+          a.dd2 += df * df;
+          a.p2 += dp[i] * dp[i];
+        }
+      }
+    }
+  }
+
+  __shared__ double red[8][BS_THREADS / 64];
+  double vals[8] = {a.d2, a.i2, a.dd2, a.p2, (double)a.mi, a.si, (double)a.mo, a.so};
+#pragma unroll
+  for (int k = 0; k < 8; ++k) vals[k] = (k == 4 || k == 6) ? wave_max_d(vals[k]) : wave_sum(vals[k]);
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0)
+#pragma unroll
+    for (int k = 0; k < 8; ++k) red[k][w] = vals[k];
+  __syncthreads();
+  if (threadIdx.x < 8) {
+    const int k = threadIdx.x;
+    double r = red[k][0];
+    for (int i = 1; i < BS_THREADS / 64; ++i) r = (k == 4 || k == 6) ? fmax(r, red[k][i]) : r + red[k][i];
+    part[8 * (int64_t)blockIdx.x + k] = r;
+  }
+}
+
 constexpr int kBsFinalThreads = 1024;
 
 __global__ __launch_bounds__(kBsFinalThreads) void block_stats_final_kernel(const double* part, int nparts,
@@ -143,6 +258,19 @@ hipError_t launch_block_stats(const void* in, const void* out, const void* dprev
   hipLaunchKernelGGL(block_stats_kernel, dim3(grid), dim3(BS_THREADS), 0, st,
                      static_cast<const uint16_t*>(in), static_cast<const uint16_t*>(out),
                      static_cast<const uint16_t*>(dprev), static_cast<uint16_t*>(dnew), n, part);
+  hipLaunchKernelGGL(block_stats_final_kernel, dim3(1), dim3(kBsFinalThreads), 0, st, part, grid, stats);
+  return hipGetLastError();
+}
+
+hipError_t launch_block_stats_mx8(const void* in, const void* out, const uint8_t* dprev_q, const uint8_t* dprev_s,
+                                  uint8_t* dnew_q, uint8_t* dnew_s, int64_t n, double* stats, void* ws,
+                                  hipStream_t st) {
+  // same grid (and workspace) as the bf16 pass: a multiple of 4 lanes per block
+  const int grid = bs_grid(n);
+  double* part = static_cast<double*>(ws);
+  hipLaunchKernelGGL(block_stats_mx8_kernel, dim3(grid), dim3(BS_THREADS), 0, st,
+                     static_cast<const uint16_t*>(in), static_cast<const uint16_t*>(out), dprev_q, dprev_s,
+                     dnew_q, dnew_s, n, part);
   hipLaunchKernelGGL(block_stats_final_kernel, dim3(1), dim3(kBsFinalThreads), 0, st, part, grid, stats);
   return hipGetLastError();
 }

@@ -16,6 +16,7 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float float16v __attribute__((ext_vector_type(16)));
 typedef float float4v __attribute__((ext_vector_type(4)));
+typedef float float2v __attribute__((ext_vector_type(2)));
 
 // Threshold below which a tensor (NVFP4) or a row (INT8) quantizes to zero:
 // scales derived from smaller maxima would leave the fp32 normal range.

@@ -30,5 +30,8 @@ hipError_t launch_qgemm_mx(bool a_fp8, const uint8_t* a_q, const uint8_t* a_s, c
 size_t bs_workspace_bytes(int64_t n);
 hipError_t launch_block_stats(const void* in, const void* out, const void* dprev, void* dnew,
                               int64_t n, double* stats, void* ws, hipStream_t st);
+hipError_t launch_block_stats_mx8(const void* in, const void* out, const uint8_t* dprev_q, const uint8_t* dprev_s,
+                                  uint8_t* dnew_q, uint8_t* dnew_s, int64_t n, double* stats, void* ws,
+                                  hipStream_t st);
 
 }  // namespace vdtq

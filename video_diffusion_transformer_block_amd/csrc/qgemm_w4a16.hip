@@ -27,7 +27,6 @@
 namespace vdtq {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float float2v __attribute__((ext_vector_type(2)));
 
 constexpr int A16_THREADS = 256;
 constexpr int A16_BK = 64;

@@ -251,6 +251,29 @@ def block_stats(inp: torch.Tensor, out: torch.Tensor, dprev: Optional[torch.Tens
     return dnew, st
 
 
+def block_stats_mx8(inp: torch.Tensor, out: torch.Tensor, dprev: Optional[MXTensor] = None,
+                    dnew: Optional[MXTensor] = None, write_delta: bool = True):
+    """block_stats with the delta cache in MXFP8 (codes u8 [n], E8M0 scales
+    u8 [n/32], as an MXTensor of fmt "mxfp8" over the flattened tensor).
+    Returns (dnew or None, stats f64[8] device tensor)."""
+    _require(inp, torch.bfloat16, "inp")
+    _require(out, torch.bfloat16, "out")
+    if inp.shape != out.shape or not inp.is_contiguous() or not out.is_contiguous():
+        raise ValueError("inp/out must be contiguous tensors of one shape")
+    n = inp.numel()
+    dev = inp.device
+    if dnew is None and write_delta:
+        dnew = MXTensor(torch.empty(n, dtype=torch.uint8, device=dev),
+                        torch.empty(n // 32, dtype=torch.uint8, device=dev), "mxfp8")
+    st = torch.empty(8, dtype=torch.float64, device=dev)
+    ws = workspace(dev, L.lib().vdtq_workspace_bytes(L.OP_BLOCK_STATS, n, 1))
+    L.check(L.lib().block_stats_mx8(_p(inp), _p(out), _p(dprev.q if dprev else None),
+                                    _p(dprev.scales if dprev else None), _p(dnew.q if dnew else None),
+                                    _p(dnew.scales if dnew else None), n, _p(st), _p(ws), ws.numel(),
+                                    _stream(dev)))
+    return dnew, st
+
+
 def dmpq_params(gamma=0.1, tau=0.05, tau_acc=0.15, rho=50.0, tau_u=math.inf, warmup=2) -> L.DmpqParams:
     return L.DmpqParams(gamma, tau, tau_acc, rho, tau_u, warmup, 0)
 
