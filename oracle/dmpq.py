@@ -83,3 +83,23 @@ def dmpq_step(p: Params, s: State, last_stats, in_ratio: float) -> int:
     if s.gamma_prev >= p.gamma:
         return INT8
     return NVFP4
+
+
+def budget_gamma(gammas, avg_bits: float) -> float:
+    """Bit-budget mode ([gist] §2.A / [yly] §一: Gamma_{t-1} ranks the blocks'
+    sensitivity; [yly] §四: the W4A6 operating point averages 6 activation
+    bits).  At the start of a step, rank the blocks by Gamma_{t-1} and give
+    INT8 (8 bits) to the k most sensitive, NVFP4 (4 bits) to the rest, with
+    k = floor(n * (avg_bits - 4) / 4) clamped to [0, n]: the threshold passed
+    to dmpq_step as gamma is the k-th largest Gamma (+inf when k = 0).
+    Ties at the boundary all take INT8 (Gamma == gamma -> INT8), so the INT8
+    count can exceed k only by such ties.  Forced decisions (the restart
+    INT8, BF16, skips) stay outside the budget."""
+    g = sorted((float(x) for x in gammas), reverse=True)
+    n = len(g)
+    if n == 0 or not math.isfinite(avg_bits):
+        return math.inf
+    k = int(math.floor(n * (avg_bits - 4.0) / 4.0))
+    k = max(0, min(n, k))
+    return math.inf if k == 0 else g[k - 1]
+

@@ -59,3 +59,32 @@ def test_warmup_blocks_skips_and_ties():
     assert all(a == D.INT8 for a in acts[1:])
     acts = [D.dmpq_step(p, s, st, 3.0000001) for _ in range(2)]
     assert acts == [D.BF16, D.BF16]
+
+
+# ---- bit-budget mode
+
+def test_budget_gamma_closed_forms():
+    g = [0.3, 0.05, 0.2, 0.01, 0.12, 0.07]          # sorted: .3 .2 .12 .07 .05 .01
+    assert D.budget_gamma(g, 6.0) == 0.12            # k = 3: the three largest go INT8
+    assert D.budget_gamma(g, 4.0) == math.inf        # k = 0: all NVFP4
+    assert D.budget_gamma(g, 8.0) == 0.01            # k = 6: all INT8
+    assert D.budget_gamma(g, 5.0) == 0.3             # k = floor(6 * 1 / 4) = 1: the largest
+    assert D.budget_gamma(g, 3.0) == math.inf and D.budget_gamma(g, 9.0) == 0.01
+    assert D.budget_gamma([], 6.0) == math.inf
+
+
+def test_budget_gamma_meets_the_average():
+    rng = np.random.Generator(np.random.PCG64(77))
+    for trial in range(200):
+        n = int(rng.integers(1, 60))
+        g = rng.uniform(0, 0.3, n)
+        bits = float(rng.uniform(4, 8))
+        thr = D.budget_gamma(g, bits)
+        int8 = int(np.sum(g >= thr))
+        # distinct Gammas: exactly k INT8 blocks, and the average fits the budget
+        assert int8 == max(0, min(n, int(np.floor(n * (bits - 4) / 4))))
+        assert (8 * int8 + 4 * (n - int8)) / n <= bits + 1e-12
+
+
+def test_budget_gamma_ties_take_int8():
+    assert D.budget_gamma([0.1, 0.1, 0.1, 0.1], 6.0) == 0.1   # k = 2, all four tie -> all INT8
