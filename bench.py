@@ -27,6 +27,7 @@ from __future__ import annotations
 
 import argparse
 import json
+import math
 import os
 import sys
 import time
@@ -306,9 +307,11 @@ def measure_dyn(torch, V, synth, blocks=30, steps=50, M=4446, hidden=1920):
     a smooth seeded residual plus decaying noise; three (block, step) pairs
     carry one channel x300.  Inputs and weights come from torch's seeded GPU
     generator.  The same loop is run again with every block-step forced to
-    the BF16 fallback and no skip, for the reference, and once more with the
+    the BF16 fallback and no skip, for the reference; once more with the
     delta cache in MXFP8 (block_stats_mx8; a skipped block adds the
-    dequantized cached delta).  Times are HIP events around each computed
+    dequantized cached delta); and once in bit-budget mode (each step's
+    Gamma threshold from dmpq_budget_gamma for an average of 6 activation
+    bits over the ranked blocks).  Times are HIP events around each computed
     block's quantize + GEMM."""
     dev = torch.device("cuda:0")
     gen = torch.Generator(device=dev)
@@ -340,7 +343,20 @@ def measure_dyn(torch, V, synth, blocks=30, steps=50, M=4446, hidden=1920):
         v = c.q.view(torch.float8_e4m3fn).float().view(-1, 32) * torch.exp2(c.scales.float() - 127.0)[:, None]
         return v.view(M, hidden)
 
-    def run(params, cache_fmt="bf16"):
+    def step_gamma(states, last, avg_bits):
+        # bit-budget mode: this step's threshold from the Gamma_{t-1} of the
+        # blocks that have one (a block computed last step: its new Gamma;
+        # otherwise the Gamma it holds)
+        gs = []
+        for b in range(blocks):
+            if last[b] is not None:
+                d2, i2 = float(last[b][0]), float(last[b][1])
+                gs.append((0.0 if d2 == 0.0 else math.inf) if i2 == 0.0 else math.sqrt(d2 / i2))
+            elif states[b].has_gamma:
+                gs.append(states[b].gamma_prev)
+        return V.dmpq_budget_gamma(gs, avg_bits)
+
+    def run(params, cache_fmt="bf16", budget=None):
         states = [V.dmpq_state() for _ in range(blocks)]
         last = [None] * blocks
         cache = [None] * blocks
@@ -352,6 +368,10 @@ def measure_dyn(torch, V, synth, blocks=30, steps=50, M=4446, hidden=1920):
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for t in range(steps):
+            p_t = params
+            if budget is not None:
+                p_t = V.dmpq_params(gamma=step_gamma(states, last, budget), tau=params.tau, tau_acc=params.tau_acc,
+                                    rho=params.rho, tau_u=params.tau_u, warmup=params.warmup)
             x = laplace((M, hidden), 500 + t)
             x[:, ch] *= 30.0
             x = x.to(torch.bfloat16)
@@ -362,7 +382,7 @@ def measure_dyn(torch, V, synth, blocks=30, steps=50, M=4446, hidden=1920):
                     x[:, spike] = (x[:, spike].float() * 300.0).to(torch.bfloat16)
                 _, rs = V.block_stats(x, x, write_delta=False)
                 rs = rs.cpu().numpy()
-                act = V.dmpq_step(params, states[b], last[b], V.outlier_ratio(rs[4], rs[5], M * hidden))
+                act = V.dmpq_step(p_t, states[b], last[b], V.outlier_ratio(rs[4], rs[5], M * hidden))
                 acts.append(act)
                 if act == V.ACT_SKIP:
                     counts["skip"] += 1
@@ -407,8 +427,14 @@ def measure_dyn(torch, V, synth, blocks=30, steps=50, M=4446, hidden=1920):
     rcounts, rper, rtotal, rwall, _ = run(p_ref)
     c8, per8, total8, wall8, acts8 = run(p_dyn, "mxfp8")
     same = float(np.mean(np.array(acts) == np.array(acts8)))
+    cb, perb, totalb, wallb, _ = run(p_dyn, budget=6.0)
+
+    def avg_bits(c):
+        n = c["nvfp4"] + c["int8"] + c["bf16"]
+        return round((4 * c["nvfp4"] + 8 * c["int8"] + 16 * c["bf16"]) / n, 3) if n else None
     print(f"[bench] dyn schedule: actions {counts}, linear path {total:.1f} ms vs {rtotal:.1f} ms all-BF16; "
-          f"MXFP8 cache: actions {c8}, {100 * same:.1f}% of decisions unchanged", file=sys.stderr, flush=True)
+          f"MXFP8 cache: actions {c8}, {100 * same:.1f}% of decisions unchanged; budget 6 bits: actions {cb}",
+          file=sys.stderr, flush=True)
     return {"workload": f"closed loop, {blocks} blocks x {steps} steps, M={M}, hidden {hidden}, "
                         f"QKV {hidden}->{3 * hidden} at the scheduled precision",
             "params": {"gamma": 0.1, "tau": 0.05, "tau_acc": 0.15, "rho": 1000.0, "warmup": 2},
@@ -419,6 +445,11 @@ def measure_dyn(torch, V, synth, blocks=30, steps=50, M=4446, hidden=1920):
             "all_bf16_linear_ms_total": round(rtotal, 2),
             "linear_speedup_vs_all_bf16": round(rtotal / total, 3) if total else None,
             "wall_s": round(wall, 2), "all_bf16_wall_s": round(rwall, 2),
+            "avg_activation_bits": avg_bits(counts),
+            "budget_w4a6": {"actions": cb, "avg_activation_bits": avg_bits(cb),
+                            "avg_quantized_bits": round((4 * cb["nvfp4"] + 8 * cb["int8"]) / max(1, cb["nvfp4"] + cb["int8"]), 3),
+                            "linear_ms_total": round(totalb, 2),
+                            "linear_speedup_vs_all_bf16": round(rtotal / totalb, 3) if totalb else None},
             "mxfp8_cache": {"actions": c8, "linear_ms_total": round(total8, 2),
                             "same_action_fraction": round(same, 4),
                             "cache_bytes_per_block": M * hidden * (1 + 1 / 32),

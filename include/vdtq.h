@@ -360,6 +360,25 @@ int dmpq_step(const vdtq_dmpq_params* p, vdtq_dmpq_state* s,
 /* max / (sum / n); 1 when sum == 0 or n == 0. */
 double vdtq_outlier_ratio(double max_abs, double sum_abs, int64_t n);
 
+/*
+ * dmpq_budget_gamma -- the Gamma threshold of one denoising step in
+ * bit-budget mode.
+ *
+ * Defined by: [gist] §2.A and [yly] §一 (Gamma_{t-1} of a block predicts the
+ * precision its linears need: high -> INT8, low -> NVFP4) and [yly] §四 (the
+ * W4A6 operating point averages 6 activation bits).
+ *
+ * Ranks the blocks by Gamma_{t-1}: with k = floor(n * (avg_bits - 4) / 4)
+ * clamped to [0, n], returns the k-th largest of gammas[0..n-1] (+inf when
+ * k = 0), to be passed as params.gamma to every dmpq_step of the step, so
+ * that the k most sensitive blocks run INT8 and the others NVFP4.  Blocks
+ * tied at the boundary all take INT8 (Gamma >= gamma).  The restart INT8,
+ * BF16 and skips are decided by dmpq_step as usual, outside the budget.
+ * gammas: host double[n], no NaN (+inf allowed).  Returns +inf when
+ * gammas == NULL, n <= 0 or avg_bits is not finite.  Allocates nothing.
+ */
+double dmpq_budget_gamma(const double* gammas, int32_t n, double avg_bits);
+
 #ifdef __cplusplus
 }
 #endif

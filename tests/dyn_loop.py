@@ -17,6 +17,9 @@ The two sides share only the seeded inputs (synth.DynWorkload); each runs
 its own statistics, cache and scheduler."""
 import numpy as np
 
+import dataclasses
+import math
+
 from oracle import dmpq as OD, formats as F, stats as OS
 
 
@@ -29,8 +32,25 @@ def _spiked(w, b, t, x_bits):
     return F.f32_to_bf16(x)
 
 
-def oracle_loop(w, params: OD.Params, record=None):
-    """Returns (actions int[B, T], stats dict (b, t) -> float64[8])."""
+def _step_gammas(last, gamma_of_state):
+    """Gamma_{t-1} of each block that has one: from the stats of its last
+    step if that step was computed, else the value its state holds."""
+    out = []
+    for b, st in enumerate(last):
+        if st is not None:
+            d2, i2 = float(st[0]), float(st[1])
+            out.append((0.0 if d2 == 0.0 else math.inf) if i2 == 0.0 else math.sqrt(d2 / i2))
+        else:
+            g = gamma_of_state(b)
+            if g is not None:
+                out.append(g)
+    return out
+
+
+def oracle_loop(w, params: OD.Params, record=None, budget=None):
+    """Returns (actions int[B, T], stats dict (b, t) -> float64[8]).
+    budget: average activation bits of the bit-budget mode (each step's
+    Gamma threshold from the oracle's budget_gamma), or None."""
     B, T = w.blocks, w.steps
     acts = np.zeros((B, T), np.int32)
     stats = {}
@@ -39,12 +59,16 @@ def oracle_loop(w, params: OD.Params, record=None):
     cache = [None] * B
     n = w.M * w.hidden
     for t in range(T):
+        p_t = params
+        if budget is not None:
+            g = _step_gammas(last, lambda b: st[b].gamma_prev if st[b].has_gamma else None)
+            p_t = dataclasses.replace(params, gamma=OD.budget_gamma(g, budget))
         x = w.block0_input(t)
         for b in range(B):
             x = _spiked(w, b, t, x)
             _, rs = OS.block_stats(x, x)
             ratio = OS.outlier_ratio(rs[4], rs[5], n)
-            a = OD.dmpq_step(params, st[b], last[b], ratio)
+            a = OD.dmpq_step(p_t, st[b], last[b], ratio)
             acts[b, t] = a
             if a == OD.SKIP:
                 out = F.f32_to_bf16((F.bf16_to_f32(x) + F.bf16_to_f32(cache[b])).astype(np.float32))
@@ -61,7 +85,7 @@ def oracle_loop(w, params: OD.Params, record=None):
     return acts, stats
 
 
-def gpu_loop(w, params, sample=(), on_sample=None):
+def gpu_loop(w, params, sample=(), on_sample=None, budget=None):
     """The same loop through libvdtq: block_stats on the device, dmpq_step in
     the library's C code.  Delta_{b,t} is formed on the device from the same
     seeded fields.  For (b, t) in `sample`, on_sample(b, t, in, out, cache,
@@ -82,6 +106,11 @@ def gpu_loop(w, params, sample=(), on_sample=None):
     cache = [None] * B
     spare = [torch.empty((M, H), dtype=torch.bfloat16, device=dev) for _ in range(B)]
     for t in range(T):
+        p_t = params
+        if budget is not None:
+            g = _step_gammas(last, lambda b: st[b].gamma_prev if st[b].has_gamma else None)
+            p_t = V.dmpq_params(gamma=V.dmpq_budget_gamma(g, budget), tau=params.tau, tau_acc=params.tau_acc,
+                                rho=params.rho, tau_u=params.tau_u, warmup=params.warmup)
         x = torch.from_numpy(w.block0_input(t).view(np.int16)).view(torch.bfloat16).to(dev)
         for b in range(B):
             ch = w.spike_channel(b, t)
@@ -91,7 +120,7 @@ def gpu_loop(w, params, sample=(), on_sample=None):
             _, rs = V.block_stats(x, x)
             rs = rs.cpu().numpy()
             ratio = V.outlier_ratio(rs[4], rs[5], n)
-            a = V.dmpq_step(params, st[b], last[b], ratio)
+            a = V.dmpq_step(p_t, st[b], last[b], ratio)
             acts[b, t] = a
             if a == V.ACT_SKIP:
                 out = (x.float() + cache[b].float()).to(torch.bfloat16)

@@ -219,3 +219,18 @@ def test_dmpq_step_null_args():
 def test_outlier_ratio_c():
     assert V.outlier_ratio(4.0, 100.0, 100) == 4.0
     assert V.outlier_ratio(0.0, 0.0, 100) == 1.0
+
+
+def test_dmpq_budget_gamma_matches_oracle():
+    rng = np.random.Generator(np.random.PCG64(78))
+    for trial in range(300):
+        n = int(rng.integers(0, 80))
+        g = rng.uniform(0, 0.3, n)
+        if trial % 5 == 0 and n:
+            g[rng.integers(0, n, size=max(1, n // 3))] = 0.1          # ties
+        if trial % 7 == 0 and n:
+            g[0] = math.inf
+        bits = float(rng.uniform(3, 9))
+        assert V.dmpq_budget_gamma(g, bits) == D.budget_gamma(g, bits), (trial, n, bits)
+    assert V.dmpq_budget_gamma([0.2, 0.1], math.nan) == math.inf
+    assert V.lib().dmpq_budget_gamma(None, 4, 6.0) == math.inf

@@ -42,6 +42,23 @@ def test_closed_loop_matches_oracle():
         same_stats(got_stats[k], want_stats[k])
 
 
+def test_closed_loop_budget_mode_matches_oracle():
+    """Bit-budget mode (an average of 6 activation bits over the ranked
+    blocks): each step's Gamma threshold is the k-th largest Gamma_{t-1},
+    computed by the library in C and by the oracle; the 1500 actions match
+    and NVFP4 and INT8 both occur."""
+    need_gpu()
+    w = synth.DynWorkload(M=35)
+    p = dict(gamma=0.1, tau=0.05, tau_acc=0.15, rho=400.0)
+    want_acts, _ = dyn_loop.oracle_loop(w, OD.Params(**p), budget=6.0)
+    got_acts, _ = dyn_loop.gpu_loop(w, V.dmpq_params(**p), budget=6.0)
+    bad = np.argwhere(got_acts != want_acts)
+    assert len(bad) == 0, f"first differing (block, step): {bad[:5].tolist()}"
+    counts = np.bincount(want_acts.ravel(), minlength=4)
+    log(f"  budget mode actions skip/nvfp4/int8/bf16 = {counts.tolist()}")
+    assert counts[1] > 0 and counts[2] > 0
+
+
 def test_closed_loop_full_size_sampled():
     need_gpu()
     w = synth.DynWorkload()

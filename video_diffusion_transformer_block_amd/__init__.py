@@ -14,16 +14,16 @@ exposed through the C ABI in include/vdtq.h:
   block_stats        Gamma / delta-similarity / outlier reductions of a block
   block_stats_mx8    the same with the delta cache stored in MXFP8
   dmpq_step          host scheduler: SKIP / NVFP4 / INT8 / BF16 per block
+  dmpq_budget_gamma  host: the step's Gamma threshold in bit-budget mode
 
 This module only marshals torch tensors into those calls.
 """
 from ._lib import (ACT_BF16, ACT_INT8, ACT_NVFP4, ACT_SKIP, DmpqParams, DmpqState,  # noqa: F401
                    VdtqError, lib)
-from .ops import (BF16Tensor, INT8Tensor, MXTensor, NVFP4Tensor, block_stats, block_stats_mx8, dmpq_params,  # noqa: F401
-                  dmpq_state, dmpq_step, hadamard_quantize, outlier_ratio, qgemm_mx, qgemm_w4a4, qgemm_w4a8,
-                  qgemm_w4a16, workspace)
+from .ops import (BF16Tensor, INT8Tensor, MXTensor, NVFP4Tensor, block_stats, block_stats_mx8,  # noqa: F401
+                  dmpq_budget_gamma, dmpq_params, dmpq_state, dmpq_step, hadamard_quantize, outlier_ratio,
+                  qgemm_mx, qgemm_w4a4, qgemm_w4a8, qgemm_w4a16, workspace)
 
-__all__ = ["hadamard_quantize", "qgemm_w4a4", "qgemm_w4a8", "qgemm_w4a16", "qgemm_mx", "block_stats", "block_stats_mx8",
-           "dmpq_step", "dmpq_params", "dmpq_state", "outlier_ratio", "NVFP4Tensor", "INT8Tensor", "BF16Tensor",
-           "MXTensor",
-           "VdtqError", "lib"]
+__all__ = ["hadamard_quantize", "qgemm_w4a4", "qgemm_w4a8", "qgemm_w4a16", "qgemm_mx", "block_stats",
+           "block_stats_mx8", "dmpq_step", "dmpq_budget_gamma", "dmpq_params", "dmpq_state", "outlier_ratio",
+           "NVFP4Tensor", "INT8Tensor", "BF16Tensor", "MXTensor", "VdtqError", "lib"]

@@ -19,7 +19,7 @@ OP_HADAMARD_QUANTIZE, OP_BLOCK_STATS, OP_QGEMM = 0, 1, 2
 
 # every extern "C" symbol include/vdtq.h declares
 EXPORTED = ["vdtq_last_error", "vdtq_version", "vdtq_workspace_bytes", "hadamard_quantize",
-            "qgemm_w4a4", "qgemm_w4a8", "qgemm_w4a16", "qgemm_mx", "block_stats", "block_stats_mx8", "dmpq_state_init", "dmpq_step",
+            "qgemm_w4a4", "qgemm_w4a8", "qgemm_w4a16", "qgemm_mx", "block_stats", "block_stats_mx8", "dmpq_state_init", "dmpq_step", "dmpq_budget_gamma",
             "vdtq_outlier_ratio"]
 
 
@@ -78,6 +78,8 @@ def lib() -> ctypes.CDLL:
             L.block_stats_mx8.argtypes = [vp, vp, vp, vp, vp, vp, i64, vp, vp, sz, vp]
             L.block_stats.restype = i32
             L.block_stats.argtypes = [vp, vp, vp, vp, i64, vp, vp, sz, vp]
+            L.dmpq_budget_gamma.restype = dbl
+            L.dmpq_budget_gamma.argtypes = [ctypes.POINTER(ctypes.c_double), i32, dbl]
             L.dmpq_state_init.restype = None
             L.dmpq_state_init.argtypes = [ctypes.POINTER(DmpqState)]
             L.dmpq_step.restype = i32

@@ -60,4 +60,22 @@ int dmpq_step(const vdtq_dmpq_params* p, vdtq_dmpq_state* s, const double* last_
   return VDTQ_OK;
 }
 
+double dmpq_budget_gamma(const double* gammas, int32_t n, double avg_bits) {
+  if (!gammas || n <= 0 || !isfinite(avg_bits)) return INFINITY;
+  double kf = floor((double)n * (avg_bits - 4.0) / 4.0);
+  if (kf <= 0.0) return INFINITY;
+  const int32_t k = kf >= (double)n ? n : (int32_t)kf;
+  // the k-th largest value: more than k-1 values are >= it and at most k-1
+  // are strictly greater (O(n^2), n = blocks of a model; no allocation)
+  for (int32_t i = 0; i < n; ++i) {
+    int32_t greater = 0, at_least = 0;
+    for (int32_t j = 0; j < n; ++j) {
+      greater += gammas[j] > gammas[i];
+      at_least += gammas[j] >= gammas[i];
+    }
+    if (greater < k && k <= at_least) return gammas[i];
+  }
+  return INFINITY;   // unreachable for comparable values
+}
+
 }  // extern "C"

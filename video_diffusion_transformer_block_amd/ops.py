@@ -274,6 +274,14 @@ def block_stats_mx8(inp: torch.Tensor, out: torch.Tensor, dprev: Optional[MXTens
     return dnew, st
 
 
+def dmpq_budget_gamma(gammas, avg_bits: float = 6.0) -> float:
+    """Host call: the Gamma threshold of a step in bit-budget mode (the k-th
+    largest of the blocks' Gamma_{t-1}, k = floor(n (avg_bits - 4) / 4))."""
+    g = [float(x) for x in gammas]
+    arr = (ctypes.c_double * max(1, len(g)))(*g)
+    return float(L.lib().dmpq_budget_gamma(arr, len(g), float(avg_bits)))
+
+
 def dmpq_params(gamma=0.1, tau=0.05, tau_acc=0.15, rho=50.0, tau_u=math.inf, warmup=2) -> L.DmpqParams:
     return L.DmpqParams(gamma, tau, tau_acc, rho, tau_u, warmup, 0)
 
