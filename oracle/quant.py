@@ -57,6 +57,8 @@ BF16 (the full-precision fallback of [gist] §2.C / [yly] §三):
 """
 from __future__ import annotations
 
+import math
+
 import numpy as np
 
 from .formats import (e2m1_to_float, e4m3_to_float, float_to_e2m1,
@@ -168,6 +170,55 @@ def mx_dequantize(codes: np.ndarray, scales: np.ndarray, elem: str) -> np.ndarra
 MX_ELEM = {"mxfp4": "e2m1", "mxfp8": "e4m3"}
 
 
+# ---------------------------------------------------------------- GELU
+# The DiT feed-forward applies GELU (tanh form) between FFN-up and FFN-down;
+# fusing the FFN-down input quantization into FFN-up's epilogue puts it on
+# this path.  The pages do not define it numerically; the reading here is an
+# fp32 algorithm written out step by step, so that the GPU path can follow
+# the same roundings (every step one fp32 operation, round to nearest even):
+#   u = C0 * (y + C1 * ((y * y) * y))
+#   z = clamp(-2 u, -80, 90)
+#   GELU(y) = y / (1 + exp32(z))                    (= y * sigmoid(2u))
+# with C0 = RN32(sqrt(2/pi)), C1 = RN32(0.044715).  exp32 is Cody-Waite range
+# reduction, k = rint(z * RN32(1/ln 2)), r = (z - k ln2_hi) - k ln2_lo with
+# ln2_hi = ln 2 truncated to 12 significant bits (k * ln2_hi is exact), the
+# degree-7 Taylor polynomial of e^r in Horner form with coefficients
+# RN32(1/n!), then two exact scalings by 2^floor(k/2) and 2^(k - floor(k/2)),
+# so that z = 90 overflows to +inf (GELU -> -0 for large negative y) and
+# z = -80 stays normal (GELU -> y for large positive y).
+F32_C0 = np.float32(0.7978845608028654)
+F32_C1 = np.float32(0.044715)
+F32_LOG2E = np.float32(1.4426950408889634)
+F32_LN2_HI = np.float32(0.693115234375)
+F32_LN2_LO = np.float32(3.194618329871446e-05)
+F32_TAYLOR = [np.float32(1.0 / math.factorial(n)) for n in range(8)]
+
+
+def exp32(z: np.ndarray) -> np.ndarray:
+    """e^z in fp32 by the steps above (z in [-80, 90])."""
+    z = np.asarray(z, np.float32)
+    k = np.rint((z * F32_LOG2E).astype(np.float32)).astype(np.float32)
+    r = ((z - (k * F32_LN2_HI).astype(np.float32)).astype(np.float32) - (k * F32_LN2_LO).astype(np.float32)).astype(np.float32)
+    p = F32_TAYLOR[7]
+    for c in F32_TAYLOR[6::-1]:
+        p = ((p * r).astype(np.float32) + c).astype(np.float32)
+    ki = k.astype(np.int32)
+    k1 = ki // 2                                     # floor
+    with np.errstate(over="ignore"):
+        return np.ldexp(np.ldexp(p, k1).astype(np.float32), ki - k1).astype(np.float32)
+
+
+def gelu32(y: np.ndarray) -> np.ndarray:
+    """GELU (tanh form) of fp32 values by the fp32 steps above."""
+    y = np.asarray(y, np.float32)
+    with np.errstate(over="ignore", invalid="ignore"):
+        y3 = ((y * y).astype(np.float32) * y).astype(np.float32)
+        w = (y + (F32_C1 * y3).astype(np.float32)).astype(np.float32)
+        u = (F32_C0 * w).astype(np.float32)
+        z = np.clip((np.float32(-2) * u).astype(np.float32), np.float32(-80), np.float32(90)).astype(np.float32)
+        return (y / (np.float32(1) + exp32(z)).astype(np.float32)).astype(np.float32)
+
+
 def activation_stats(x_bits: np.ndarray, y: np.ndarray) -> np.ndarray:
     """The outlier statistics fused into the quantize pass, in float64:
     [max|x|, sum|x|, max|y|, sum|y|] with x the bf16 input before the
@@ -180,11 +231,16 @@ def activation_stats(x_bits: np.ndarray, y: np.ndarray) -> np.ndarray:
     return np.array([x.max(), x.sum(), ya.max(), ya.sum()])
 
 
-def hadamard_quantize(x_bits: np.ndarray, had_block: int, fmt: str, amax=None):
+def hadamard_quantize(x_bits: np.ndarray, had_block: int, fmt: str, amax=None, gelu: bool = False):
     """The full per-linear activation pass: block Hadamard of bf16 rows, then
     NVFP4 or INT8 quantization (or bf16 rounding for the full-precision
     fallback), plus the fused outlier statistics.
-    fmt is "nvfp4", "int8", "bf16", "mxfp4" or "mxfp8".  Returns a dict."""
+    fmt is "nvfp4", "int8", "bf16", "mxfp4" or "mxfp8".  gelu: the input is
+    first mapped through gelu32 and rounded to bf16 (the FFN-down input as
+    the model stores it); the statistics then describe that activation.
+    Returns a dict."""
+    if gelu:
+        x_bits = f32_to_bf16(gelu32(bf16_to_f32(x_bits)))
     x = bf16_to_f32(x_bits)
     y = block_hadamard_f32(x, had_block)
     out = {"y": y, "stats": activation_stats(x_bits, y)}
