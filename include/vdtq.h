@@ -71,6 +71,7 @@ extern "C" {
 /* hadamard_quantize flags */
 #define VDTQ_AMAX_GIVEN 1u   /* tensor_scale_dev[0] holds amax_T on entry    */
 #define VDTQ_STATS 2u        /* write the four outlier statistics            */
+#define VDTQ_GELU 4u         /* map X through GELU (bf16 result) first       */
 
 /* scheduler actions */
 #define VDTQ_ACT_SKIP 0
@@ -130,7 +131,20 @@ size_t vdtq_workspace_bytes(int op, int64_t M, int64_t K);
  * had_block      16, 32, 64, 128 or 256
  * fmt            VDTQ_FMT_NVFP4, VDTQ_FMT_INT8, VDTQ_FMT_BF16, VDTQ_FMT_MXFP4
  *                or VDTQ_FMT_MXFP8
- * flags          VDTQ_AMAX_GIVEN (NVFP4 only) | VDTQ_STATS
+ * flags          VDTQ_AMAX_GIVEN (NVFP4 only) | VDTQ_STATS | VDTQ_GELU.
+ *                VDTQ_GELU: every element is first replaced by
+ *                bf16_RNE(GELU(x)), GELU in its tanh form evaluated in fp32
+ *                by fixed steps: u = C0 (x + C1 x^3) (as (x*x)*x),
+ *                z = clamp(-2u, -80, 90), GELU = x / (1 + exp(z)) with a
+ *                correctly rounded division, C0 = RN(sqrt(2/pi)),
+ *                C1 = RN(0.044715); exp(z) = 2^k p(r), k = rint(z RN(1/ln 2)),
+ *                r = (z - k ln2_hi) - k ln2_lo (ln2_hi = 0x1.62ep-1,
+ *                ln2_lo = 0x1.0bfbe8p-15), p the degree-7 Taylor polynomial
+ *                with coefficients RN(1/n!) in Horner form, 2^k applied as
+ *                2^floor(k/2) then 2^(k - floor(k/2)).  This is the DiT
+ *                feed-forward's activation: quantizing FFN-up's bf16 output
+ *                for FFN-down ([gist] §4: quantization fused with the
+ *                kernels around it).  The statistics then describe GELU(x).
  * q_dev          NVFP4, MXFP4: uint8 [M][K/2]; INT8: int8 [M][K]; BF16:
  *                bf16 [M][K]; MXFP8: uint8 E4M3 [M][K]
  * scales_dev     NVFP4: uint8 E4M3 [M][K/16]; INT8: float [M]; MXFP4,
@@ -259,6 +273,46 @@ int qgemm_mx(int a_fmt, const uint8_t* a_q_dev, const uint8_t* a_s_dev,
              const float* bias_dev, void* y_dev, int64_t ldy, int out_dtype,
              int64_t M, int64_t N, int64_t K, void* ws_dev, size_t ws_bytes,
              void* stream);
+
+/*
+ * qgemm_mx_quant -- qgemm_mx whose output never reaches HBM in bf16: the
+ * epilogue turns each finished tile into the next linear's MX activation.
+ * For FFN-up it computes, per output row, exactly what
+ *   Y = qgemm_mx(A, W, bias) in bf16, then
+ *   hadamard_quantize(Y, 64, out_fmt, flags) (VDTQ_GELU: GELU first)
+ * would produce for FFN-down, in one kernel.
+ *
+ * Defined by: [gist] §4 and [yly] §四 (quantization fused with the kernels
+ * around it, so that low-precision activations do not make an extra round
+ * trip through memory), over the operations of qgemm_mx and
+ * hadamard_quantize; GELU is the DiT feed-forward's activation between
+ * FFN-up and FFN-down.
+ *
+ * Per row m and per 64-column chunk of Y: y = bf16_RNE(acc + bias) with acc
+ * the fp32 sum of qgemm_mx (bit-identical to qgemm_mx's bf16 output when
+ * that call does not split tiles along K), optional GELU as in
+ * hadamard_quantize, the 64-point Hadamard transform, MX encoding.
+ *
+ * a_fmt          VDTQ_FMT_MXFP4 or VDTQ_FMT_MXFP8 (the GEMM's activations)
+ * a_q_dev .. bias_dev  as for qgemm_mx; bias 16-byte aligned
+ * had_block      64 (the transform of the output rows)
+ * out_fmt        VDTQ_FMT_MXFP4 or VDTQ_FMT_MXFP8 (the next activation)
+ * flags          0 or VDTQ_GELU
+ * q_out_dev      MXFP4: uint8 [M][N/2]; MXFP8: uint8 E4M3 [M][N]
+ *                (16-byte aligned)
+ * s_out_dev      uint8 E8M0 [M][N/32] (4-byte aligned)
+ * M, N, K        as for qgemm_mx; N a multiple of 64
+ * No workspace: tiles are never split along K on this path.
+ * Errors: VDTQ_EINVAL for bad formats or flags, N not a multiple of 64, K
+ * not a multiple of 32, null or misaligned pointers; VDTQ_EUNSUPPORTED for
+ * had_block other than 64, K not a multiple of 128 or an operand matrix of
+ * 4 GB or more.
+ */
+int qgemm_mx_quant(int a_fmt, const uint8_t* a_q_dev, const uint8_t* a_s_dev,
+                   const uint8_t* w_q_dev, const uint8_t* w_s_dev,
+                   const float* bias_dev, int had_block, int out_fmt,
+                   unsigned flags, uint8_t* q_out_dev, uint8_t* s_out_dev,
+                   int64_t M, int64_t N, int64_t K, void* stream);
 
 /*
  * block_stats -- one pass over a block's input, output and cached delta.

@@ -58,7 +58,7 @@ def _hq(**kw):
     (dict(K=15), L.EINVAL), (dict(K=0), L.EINVAL), (dict(M=-1), L.EINVAL),
     (dict(b=48), L.EINVAL), (dict(b=512), L.EINVAL), (dict(K=96, ldx=96, b=64), L.EINVAL),
     (dict(ldx=60), L.EINVAL), (dict(ldx=68), L.EINVAL), (dict(fmt=5), L.EINVAL), (dict(fmt=-1), L.EINVAL),
-    (dict(flags=4), L.EINVAL), (dict(fmt=1, flags=1), L.EINVAL),
+    (dict(flags=8), L.EINVAL), (dict(fmt=1, flags=1), L.EINVAL),
     (dict(fmt=1, K=16384 + 64, ldx=16448), L.EUNSUPPORTED),
     (dict(x=None), L.EINVAL), (dict(q=None), L.EINVAL), (dict(x=FAKE8), L.EINVAL),
     (dict(ts=None), L.EINVAL), (dict(flags=2, st=None), L.EINVAL),
@@ -155,6 +155,32 @@ def test_qgemm_mx_rejects(kw, code):
 def test_qgemm_mx_empty_is_noop():
     assert _mx(M=0, aq=None) == L.OK
     assert _mx(N=0, y=None, gws=None) == L.OK
+
+
+def _mxq(**kw):
+    a = dict(fmt=L.FMT_MXFP4, aq=FAKE, as_=FAKE, wq=FAKE, ws=FAKE, bias=None, b=64, of=L.FMT_MXFP8, fl=L.GELU,
+             q=FAKE, s=FAKE, M=8, N=64, K=128)
+    a.update(kw)
+    return V.lib().qgemm_mx_quant(a["fmt"], a["aq"], a["as_"], a["wq"], a["ws"], a["bias"], a["b"], a["of"],
+                                  a["fl"], a["q"], a["s"], a["M"], a["N"], a["K"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(fmt=L.FMT_INT8), L.EINVAL), (dict(of=L.FMT_NVFP4), L.EINVAL), (dict(of=5), L.EINVAL),
+    (dict(fl=1), L.EINVAL), (dict(fl=8), L.EINVAL), (dict(b=32), L.EUNSUPPORTED), (dict(b=128), L.EUNSUPPORTED),
+    (dict(N=96), L.EINVAL), (dict(N=32), L.EINVAL), (dict(K=48), L.EINVAL), (dict(K=96), L.EUNSUPPORTED),
+    (dict(M=-1), L.EINVAL), (dict(q=None), L.EINVAL), (dict(s=None), L.EINVAL), (dict(ws=None), L.EINVAL),
+    (dict(q=FAKE8), L.EINVAL), (dict(s=ctypes.c_void_p(0x10002)), L.EINVAL),
+    (dict(bias=ctypes.c_void_p(0x10004)), L.EINVAL), (dict(aq=FAKE8), L.EINVAL), (dict(M=1 << 26, K=1 << 7, fmt=L.FMT_MXFP8), L.EUNSUPPORTED),
+])
+def test_qgemm_mx_quant_rejects(kw, code):
+    assert _mxq(**kw) == code
+    assert V.lib().vdtq_last_error()
+
+
+def test_qgemm_mx_quant_empty_is_noop():
+    assert _mxq(M=0, aq=None, q=None) == L.OK
+    assert _mxq(N=0, wq=None, s=None) == L.OK
 
 
 @pytest.mark.parametrize("kw", [dict(n=-1), dict(st=None), dict(inp=None), dict(dnew=FAKE, dprev=FAKE),

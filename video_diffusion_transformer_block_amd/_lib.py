@@ -13,13 +13,13 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libvdtq.so"
 OK, EINVAL, EUNSUPPORTED, EHIP = 0, 1, 2, 3
 FMT_NVFP4, FMT_INT8, FMT_BF16, FMT_MXFP4, FMT_MXFP8 = 0, 1, 2, 3, 4
 OUT_BF16, OUT_F32 = 0, 1
-AMAX_GIVEN, STATS = 1, 2
+AMAX_GIVEN, STATS, GELU = 1, 2, 4
 ACT_SKIP, ACT_NVFP4, ACT_INT8, ACT_BF16 = 0, 1, 2, 3
 OP_HADAMARD_QUANTIZE, OP_BLOCK_STATS, OP_QGEMM = 0, 1, 2
 
 # every extern "C" symbol include/vdtq.h declares
 EXPORTED = ["vdtq_last_error", "vdtq_version", "vdtq_workspace_bytes", "hadamard_quantize",
-            "qgemm_w4a4", "qgemm_w4a8", "qgemm_w4a16", "qgemm_mx", "block_stats", "block_stats_mx8", "dmpq_state_init", "dmpq_step", "dmpq_budget_gamma",
+            "qgemm_w4a4", "qgemm_w4a8", "qgemm_w4a16", "qgemm_mx", "qgemm_mx_quant", "block_stats", "block_stats_mx8", "dmpq_state_init", "dmpq_step", "dmpq_budget_gamma",
             "vdtq_outlier_ratio"]
 
 
@@ -72,6 +72,8 @@ def lib() -> ctypes.CDLL:
             L.qgemm_w4a16.argtypes = [vp, vp, vp, vp, vp, vp, i64, i32, i64, i64, i64, vp]
             L.qgemm_mx.restype = i32
             L.qgemm_mx.argtypes = [i32, vp, vp, vp, vp, vp, vp, i64, i32, i64, i64, i64, vp, sz, vp]
+            L.qgemm_mx_quant.restype = i32
+            L.qgemm_mx_quant.argtypes = [i32, vp, vp, vp, vp, vp, i32, i32, u32, vp, vp, i64, i64, i64, vp]
             L.qgemm_w4a8.restype = i32
             L.qgemm_w4a8.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i32, i64, i64, i64, vp, sz, vp]
             L.block_stats_mx8.restype = i32

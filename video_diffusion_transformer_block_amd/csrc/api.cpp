@@ -66,7 +66,7 @@ int hadamard_quantize(const void* x_dev, int64_t M, int64_t K, int64_t ldx, int 
     return fail(VDTQ_EINVAL, "hadamard_quantize: fmt=%d", fmt);
   if ((fmt == VDTQ_FMT_MXFP4 || fmt == VDTQ_FMT_MXFP8) && K % 32)
     return fail(VDTQ_EINVAL, "hadamard_quantize: MX formats need K=%lld to be a multiple of 32", (long long)K);
-  if (flags & ~(VDTQ_AMAX_GIVEN | VDTQ_STATS)) return fail(VDTQ_EINVAL, "hadamard_quantize: unknown flags 0x%x", flags);
+  if (flags & ~(VDTQ_AMAX_GIVEN | VDTQ_STATS | VDTQ_GELU)) return fail(VDTQ_EINVAL, "hadamard_quantize: unknown flags 0x%x", flags);
   if (fmt != VDTQ_FMT_NVFP4 && (flags & VDTQ_AMAX_GIVEN))
     return fail(VDTQ_EINVAL, "hadamard_quantize: VDTQ_AMAX_GIVEN applies to NVFP4 only");
   if (fmt == VDTQ_FMT_INT8 && K > 16384)
@@ -195,6 +195,34 @@ int qgemm_mx(int a_fmt, const uint8_t* a_q_dev, const uint8_t* a_s_dev, const ui
   hipError_t e = vdtq::launch_qgemm_mx(a8, a_q_dev, a_s_dev, w_q_dev, w_s_dev, bias_dev, y_dev, ldy, out_dtype, M,
                                        N, K, ws_dev, static_cast<hipStream_t>(stream));
   return hip_status(e, "qgemm_mx launch");
+}
+
+int qgemm_mx_quant(int a_fmt, const uint8_t* a_q_dev, const uint8_t* a_s_dev, const uint8_t* w_q_dev,
+                   const uint8_t* w_s_dev, const float* bias_dev, int had_block, int out_fmt, unsigned flags,
+                   uint8_t* q_out_dev, uint8_t* s_out_dev, int64_t M, int64_t N, int64_t K, void* stream) {
+  const char* name = "qgemm_mx_quant";
+  if (a_fmt != VDTQ_FMT_MXFP4 && a_fmt != VDTQ_FMT_MXFP8) return fail(VDTQ_EINVAL, "%s: a_fmt=%d", name, a_fmt);
+  if (out_fmt != VDTQ_FMT_MXFP4 && out_fmt != VDTQ_FMT_MXFP8) return fail(VDTQ_EINVAL, "%s: out_fmt=%d", name, out_fmt);
+  if (flags & ~VDTQ_GELU) return fail(VDTQ_EINVAL, "%s: unknown flags 0x%x", name, flags);
+  if (had_block != 64) return fail(VDTQ_EUNSUPPORTED, "%s: had_block=%d (only 64)", name, had_block);
+  if (M < 0 || M > kI32 || N < 0 || N > kI32) return fail(VDTQ_EINVAL, "%s: M=%lld N=%lld out of range", name, (long long)M, (long long)N);
+  if (N % 64) return fail(VDTQ_EINVAL, "%s: N=%lld not a multiple of had_block=64", name, (long long)N);
+  if (K <= 0 || K > kI32 || K % 32) return fail(VDTQ_EINVAL, "%s: K=%lld must be a positive multiple of 32", name, (long long)K);
+  if (M == 0 || N == 0) return ok();
+  if (!a_q_dev || !a_s_dev || !w_q_dev || !w_s_dev || !q_out_dev || !s_out_dev)
+    return fail(VDTQ_EINVAL, "%s: null pointer argument", name);
+  if (!aligned(a_q_dev, 16) || !aligned(w_q_dev, 16) || !aligned(q_out_dev, 16) || !aligned(a_s_dev, 4) ||
+      !aligned(w_s_dev, 4) || !aligned(s_out_dev, 4) || (bias_dev && !aligned(bias_dev, 16)))
+    return fail(VDTQ_EINVAL, "%s: misaligned pointer (codes and bias need 16 bytes, scales 4)", name);
+  if (K % 128) return fail(VDTQ_EUNSUPPORTED, "%s: K=%lld is not a multiple of 128", name, (long long)K);
+  const bool a8 = a_fmt == VDTQ_FMT_MXFP8;
+  if ((a8 ? M * K : M * K / 2) >= (int64_t(1) << 32) || N * K / 2 >= (int64_t(1) << 32))
+    return fail(VDTQ_EUNSUPPORTED, "%s: operands of 4 GB or more", name);
+  if (((M + 255) / 256) * ((N + 255) / 256) > kI32) return fail(VDTQ_EUNSUPPORTED, "%s: too many output tiles", name);
+  hipError_t e = vdtq::launch_qgemm_mx_quant(a8, a_q_dev, a_s_dev, w_q_dev, w_s_dev, bias_dev,
+                                             out_fmt == VDTQ_FMT_MXFP8, (flags & VDTQ_GELU) != 0, q_out_dev,
+                                             s_out_dev, M, N, K, static_cast<hipStream_t>(stream));
+  return hip_status(e, "qgemm_mx_quant launch");
 }
 
 int block_stats(const void* in_dev, const void* out_dev, const void* dprev_dev, void* dnew_dev, int64_t n,

@@ -32,11 +32,15 @@
 //     field, elements are scaled by exact powers of two and converted by the
 //     hardware (E2M1 saturates by itself; E4M3 is clamped to +-448 first,
 //     the conversion itself does not saturate).  No tensor scale, one pass.
+//   * GELU prologue (flag 4; the FFN-down input taken straight from FFN-up's
+//     bf16 output): each staged element goes through the fp32 GELU of
+//     hadamard_common.h and back to bf16 in LDS, before anything else.
 //   * Statistics: fp32 over a thread's 64 elements, fp64 across threads and
 //     workgroups in a fixed order (bit-reproducible, no float atomics).
 #include <algorithm>
 
 #include "device_common.h"
+#include "hadamard_common.h"
 #include "launch.h"
 
 namespace vdtq {
@@ -142,6 +146,32 @@ __device__ __forceinline__ void stage(const HQParams& p, uint4* lds, int& my_row
   }
 }
 
+// With the GELU flag (4) the kernels are launched with the GELU table in
+// dynamic LDS (gelu_lds); gelu_begin fills it before staging, gelu_chunk
+// maps this thread's staged chunk through it in place (the thread touches
+// only its own LDS slots) before load_chunk widens it.
+extern __shared__ __attribute__((aligned(16))) uint16_t gelu_lds[];
+
+__device__ __forceinline__ void gelu_begin(unsigned flags) {
+  if (flags & 4u) gelu_table_build(gelu_lds);
+}
+
+__device__ __forceinline__ void gelu_chunk(uint4* lds, unsigned flags) {
+  if (!(flags & 4u)) return;
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int jj = 0; jj < 8; ++jj) {
+    uint4& slot = lds[t * 8 + (jj ^ (t & 7))];
+    const uint4 w = slot;
+    const uint32_t in[4] = {w.x, w.y, w.z, w.w};
+    uint32_t out[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      out[i] = gelu_bf16_bits(in[i] & 0xFFFFu, gelu_lds) | (gelu_bf16_bits(in[i] >> 16, gelu_lds) << 16);
+    slot = make_uint4(out[0], out[1], out[2], out[3]);
+  }
+}
+
 // Reads this thread's chunk from LDS and widens bf16 -> fp32.
 __device__ __forceinline__ void load_chunk(const uint4* lds, float (&v)[64]) {
   const int t = threadIdx.x;
@@ -154,61 +184,6 @@ __device__ __forceinline__ void load_chunk(const uint4* lds, float (&v)[64]) {
     v[8 * jj + 6] = bf16_lo(w.w); v[8 * jj + 7] = bf16_hi(w.w);
   }
 }
-
-// Butterflies in the fixed order h = 1, 2, ..., b/2 (fp32, RNE).
-template <int B>
-__device__ __forceinline__ void fwht(float (&v)[64]) {
-  constexpr int HIN = B < 64 ? B : 64;
-#pragma unroll
-  for (int h = 1; h < HIN; h <<= 1) {
-#pragma unroll
-    for (int i = 0; i < 64; ++i) {
-      if ((i & h) == 0) {
-        float a = v[i], b = v[i + h];
-        v[i] = a + b;
-        v[i + h] = a - b;
-      }
-    }
-  }
-  // stages across chunks: h = 64 pairs lanes t, t^1; h = 128 pairs t, t^2.
-  if (B >= 128) {
-    const bool upper = threadIdx.x & 1;
-#pragma unroll
-    for (int i = 0; i < 64; ++i) {
-      float o = __shfl_xor(v[i], 1, 64);
-      v[i] = upper ? (o - v[i]) : (v[i] + o);
-    }
-  }
-  if (B >= 256) {
-    const bool upper = threadIdx.x & 2;
-#pragma unroll
-    for (int i = 0; i < 64; ++i) {
-      float o = __shfl_xor(v[i], 2, 64);
-      v[i] = upper ? (o - v[i]) : (v[i] + o);
-    }
-  }
-}
-
-// Normalisation.  Powers of four keep v unscaled (y = v * 2^-k exactly, the
-// factor is folded downstream); b = 32 / 128 multiply by RN(1/sqrt(b)) here.
-template <int B> struct HadScale;
-template <> struct HadScale<16>  { static constexpr bool pow4 = true;  static constexpr float f = 0.25f;    static constexpr float inv = 4.0f; };
-template <> struct HadScale<64>  { static constexpr bool pow4 = true;  static constexpr float f = 0.125f;   static constexpr float inv = 8.0f; };
-template <> struct HadScale<256> { static constexpr bool pow4 = true;  static constexpr float f = 0.0625f;  static constexpr float inv = 16.0f; };
-// RN_fp32(sqrt 2) = 0x1.6a09e6p+0; 1/sqrt(32) = sqrt(2)/8, 1/sqrt(128) = sqrt(2)/16
-template <> struct HadScale<32>  { static constexpr bool pow4 = false; static constexpr float f = 0x1.6a09e6p-3f; static constexpr float inv = 1.0f; };
-template <> struct HadScale<128> { static constexpr bool pow4 = false; static constexpr float f = 0x1.6a09e6p-4f; static constexpr float inv = 1.0f; };
-
-template <int B>
-__device__ __forceinline__ void normalise(float (&v)[64]) {
-  if (!HadScale<B>::pow4) {
-#pragma unroll
-    for (int i = 0; i < 64; ++i) v[i] = v[i] * HadScale<B>::f;
-  }
-}
-// factor from the register values to y (1 when already applied)
-template <int B>
-__device__ __forceinline__ constexpr float yfac() { return HadScale<B>::pow4 ? HadScale<B>::f : 1.0f; }
 
 // Eight E2M1 codes of RN(v[i] * inv) / sc (sc a power of two, exact), packed
 // low nibble first: the hardware conversion rounds to nearest even,
@@ -261,9 +236,11 @@ __global__ __launch_bounds__(HQ_THREADS) void hq_amax_kernel(HQParams p) {
   __shared__ float wred[HQ_THREADS / 64];
   int row, col;
   bool valid;
+  gelu_begin(p.flags);
   stage<false>(p, lds, row, col, valid);
   __syncthreads();
   float v[64];
+  gelu_chunk(lds, p.flags);
   load_chunk(lds, v);
   fwht<B>(v);
   normalise<B>(v);
@@ -351,9 +328,11 @@ __global__ __launch_bounds__(HQ_THREADS) void hq_nvfp4_kernel(HQParams p) {
   }
   int row, col;
   bool valid;
+  gelu_begin(p.flags);
   stage<false>(p, lds, row, col, valid);
   __syncthreads();
   float v[64];
+  gelu_chunk(lds, p.flags);
   load_chunk(lds, v);
   const int nvalid = valid ? min(64, p.K - col * 64) : 0;
   const bool want_stats = (p.flags & 2u) != 0;
@@ -418,9 +397,11 @@ __global__ __launch_bounds__(HQ_THREADS) void hq_int8_kernel(HQParams p) {
   if (threadIdx.x < p.rows_per_wg) rowmax[threadIdx.x] = 0u;
   int row, col;
   bool valid;
+  gelu_begin(p.flags);
   stage<true>(p, lds, row, col, valid);
   __syncthreads();
   float v[64];
+  gelu_chunk(lds, p.flags);
   load_chunk(lds, v);
   const int nvalid = valid ? min(64, p.K - col * 64) : 0;
   const bool want_stats = (p.flags & 2u) != 0;
@@ -477,9 +458,11 @@ __global__ __launch_bounds__(HQ_THREADS) void hq_bf16_kernel(HQParams p) {
   __shared__ uint4 lds[HQ_THREADS * 8];
   int row, col;
   bool valid;
+  gelu_begin(p.flags);
   stage<false>(p, lds, row, col, valid);
   __syncthreads();
   float v[64];
+  gelu_chunk(lds, p.flags);
   load_chunk(lds, v);
   const int nvalid = valid ? min(64, p.K - col * 64) : 0;
   const bool want_stats = (p.flags & 2u) != 0;
@@ -511,35 +494,16 @@ __global__ __launch_bounds__(HQ_THREADS) void hq_bf16_kernel(HQParams p) {
 }
 
 // ---------------------------------------------------------------- MX pass
-// E8M0 exponent e of a 32-element block from the maximum |v| of its register
-// values (y = v * 2^-KSH): e = floor(log2 max|y|) - EMAX clamped to
-// [-127, 127]; zero (and fp32-subnormal maxima, whose e clamps anyway) give
-// -127.
-template <int EMAX, int KSH>
-__device__ __forceinline__ int mx_exponent(float amax_v) {
-  const int ex = (int)((__float_as_uint(amax_v) >> 23) & 0xFFu);
-  if (ex == 0) return -127;
-  return min(max(ex - 127 - KSH - EMAX, -127), 127);
-}
-
-// 2^n as fp32 for n in [-126, 127] (exact)
-__device__ __forceinline__ float exp2i(int n) { return __uint_as_float((uint32_t)(n + 127) << 23); }
-
-// log2 of the power-of-two factor from register values to y (0 when the
-// normalisation is already applied)
-template <int B> struct HadShift { static constexpr int k = 0; };
-template <> struct HadShift<16>  { static constexpr int k = 2; };
-template <> struct HadShift<64>  { static constexpr int k = 3; };
-template <> struct HadShift<256> { static constexpr int k = 4; };
-
 template <int B, bool FP8>
 __global__ __launch_bounds__(HQ_THREADS) void hq_mx_kernel(HQParams p) {
   __shared__ uint4 lds[HQ_THREADS * 8];
   int row, col;
   bool valid;
+  gelu_begin(p.flags);
   stage<false>(p, lds, row, col, valid);
   __syncthreads();
   float v[64];
+  gelu_chunk(lds, p.flags);
   load_chunk(lds, v);
   const int nvalid = valid ? min(64, p.K - col * 64) : 0;
   const bool want_stats = (p.flags & 2u) != 0;
@@ -547,47 +511,9 @@ __global__ __launch_bounds__(HQ_THREADS) void hq_mx_kernel(HQParams p) {
   if (want_stats) input_stats(v, nvalid, mx, sx);
   fwht<B>(v);
   normalise<B>(v);
-  constexpr int KSH = HadShift<B>::k;
-  constexpr int EMAX = FP8 ? 8 : 2;
-
   uint32_t words[FP8 ? 16 : 8];
-  uint32_t sbytes = 0;
-#pragma unroll
-  for (int blk = 0; blk < 2; ++blk) {
-    const float* vb = &v[32 * blk];
-    float av = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 32; ++e) av = fmaxf(av, fabsf(vb[e]));
-    const int e = mx_exponent<EMAX, KSH>(av);
-    sbytes |= (uint32_t)(e + 127) << (8 * blk);
-    // t = v * 2^-(e + KSH) as two exact power-of-two factors, each a normal
-    // fp32 (|n1|, |n2| <= 65); an intermediate that underflows belongs to an
-    // element far below the smallest nonzero code
-    const int n = e + KSH;
-    const int n1 = n / 2, n2 = n - n1;
-    const float m1 = exp2i(-n1), m2 = exp2i(-n2);
-    if constexpr (FP8) {
-#pragma unroll
-      for (int w = 0; w < 8; ++w) {
-        float t[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) t[i] = __builtin_amdgcn_fmed3f((vb[4 * w + i] * m1) * m2, -448.0f, 448.0f);
-        int x = __builtin_amdgcn_cvt_pk_fp8_f32(t[0], t[1], 0, false);
-        x = __builtin_amdgcn_cvt_pk_fp8_f32(t[2], t[3], x, true);
-        words[8 * blk + w] = (uint32_t)x;
-      }
-    } else {
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        uint32_t x = 0u;
-        x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, (vb[8 * w + 0] * m1) * m2, (vb[8 * w + 1] * m1) * m2, 1.0f, 0);
-        x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, (vb[8 * w + 2] * m1) * m2, (vb[8 * w + 3] * m1) * m2, 1.0f, 1);
-        x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, (vb[8 * w + 4] * m1) * m2, (vb[8 * w + 5] * m1) * m2, 1.0f, 2);
-        x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, (vb[8 * w + 6] * m1) * m2, (vb[8 * w + 7] * m1) * m2, 1.0f, 3);
-        words[4 * blk + w] = x;
-      }
-    }
-  }
+  uint32_t sbytes;
+  mx_encode64<B, FP8>(v, words, sbytes);
 
   if (valid) {
     constexpr int BYTES = FP8 ? 64 : 32;                      // code bytes per chunk
@@ -617,20 +543,21 @@ __global__ __launch_bounds__(HQ_THREADS) void hq_mx_kernel(HQParams p) {
 // ---------------------------------------------------------------- launcher
 template <int B>
 static hipError_t launch_b(const HQParams& p, int fmt, bool amax_given, int grid, hipStream_t st) {
+  const size_t shm = (p.flags & 4u) ? (size_t)kGeluTabBytes : 0;   // the GELU table
   if (fmt == 0) {
     if (!amax_given) {
-      hipLaunchKernelGGL(hq_amax_kernel<B>, dim3(grid), dim3(HQ_THREADS), 0, st, p);
+      hipLaunchKernelGGL(hq_amax_kernel<B>, dim3(grid), dim3(HQ_THREADS), shm, st, p);
       hipLaunchKernelGGL(hq_amax_final_kernel, dim3(1), dim3(kFinalThreads), 0, st, p.amax_part, grid, p.ts);
     }
-    hipLaunchKernelGGL(hq_nvfp4_kernel<B>, dim3(grid), dim3(HQ_THREADS), 0, st, p);
+    hipLaunchKernelGGL(hq_nvfp4_kernel<B>, dim3(grid), dim3(HQ_THREADS), shm, st, p);
   } else if (fmt == 1) {
-    hipLaunchKernelGGL(hq_int8_kernel<B>, dim3(grid), dim3(HQ_THREADS), 0, st, p);
+    hipLaunchKernelGGL(hq_int8_kernel<B>, dim3(grid), dim3(HQ_THREADS), shm, st, p);
   } else if (fmt == 2) {
-    hipLaunchKernelGGL(hq_bf16_kernel<B>, dim3(grid), dim3(HQ_THREADS), 0, st, p);
+    hipLaunchKernelGGL(hq_bf16_kernel<B>, dim3(grid), dim3(HQ_THREADS), shm, st, p);
   } else if (fmt == 3) {
-    hipLaunchKernelGGL((hq_mx_kernel<B, false>), dim3(grid), dim3(HQ_THREADS), 0, st, p);
+    hipLaunchKernelGGL((hq_mx_kernel<B, false>), dim3(grid), dim3(HQ_THREADS), shm, st, p);
   } else {
-    hipLaunchKernelGGL((hq_mx_kernel<B, true>), dim3(grid), dim3(HQ_THREADS), 0, st, p);
+    hipLaunchKernelGGL((hq_mx_kernel<B, true>), dim3(grid), dim3(HQ_THREADS), shm, st, p);
   }
   return hipGetLastError();
 }

@@ -27,6 +27,10 @@ hipError_t launch_qgemm_mx(bool a_fp8, const uint8_t* a_q, const uint8_t* a_s, c
                            const uint8_t* w_s, const float* bias, void* y, int64_t ldy, int out_dtype, int64_t M,
                            int64_t N, int64_t K, void* ws, hipStream_t st);
 
+hipError_t launch_qgemm_mx_quant(bool a_fp8, const uint8_t* a_q, const uint8_t* a_s, const uint8_t* w_q,
+                                 const uint8_t* w_s, const float* bias, bool out_fp8, bool gelu, uint8_t* q_out,
+                                 uint8_t* s_out, int64_t M, int64_t N, int64_t K, hipStream_t st);
+
 size_t bs_workspace_bytes(int64_t n);
 hipError_t launch_block_stats(const void* in, const void* out, const void* dprev, void* dnew,
                               int64_t n, double* stats, void* ws, hipStream_t st);

@@ -34,6 +34,10 @@ struct GemmParams {
   int32_t slices;          // K slices per split tile (>= 2 when sk_tiles > 0)
   int32_t slice_nk;        // stages per slice (the last may be shorter)
   float* part;             // [slices][sk_tiles][256 * 256] partial tiles
+  // quantizing epilogue (MX GEMM only): the next linear's MX activation
+  uint8_t* q_out;          // [M][N / 2] E2M1 or [M][N] E4M3 codes
+  uint8_t* s_out;          // [M][N / 32] E8M0 scales
+  uint32_t qflags;         // 4: GELU before the transform
 };
 
 // Partial tile of slice `sl` of split tile `tile`.  Layout inside a slot:

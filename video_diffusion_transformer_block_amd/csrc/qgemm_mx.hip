@@ -35,9 +35,17 @@
 //   * the tile order, the split of a partial last wave into K slices, the
 //     reduce pass and the bf16 epilogue through LDS are those of the NVFP4 /
 //     INT8 kernel (qgemm_common.h).
+//   * quantizing epilogue (qgemm_mx_quant; FFN-up feeding FFN-down): the
+//     finished bf16 tile goes through LDS as in the bf16 epilogue, then each
+//     lane takes whole 64-element row chunks of it: GELU from a table that
+//     the workgroup fills while its first loads are in flight, the 64-point
+//     Hadamard butterflies, the MX encoding; only codes and scales reach
+//     HBM.  Tiles are never split along K on this path (the epilogue needs
+//     the whole sum).
 #include <type_traits>
 
 #include "device_common.h"
+#include "hadamard_common.h"
 #include "launch.h"
 #include "lds_dma.h"
 #include "qgemm_common.h"
@@ -86,10 +94,85 @@ __device__ __forceinline__ int8v mx_operand(const int4v& v) {
   return __builtin_shufflevector(v, v, 0, 1, 2, 3, -1, -1, -1, -1);
 }
 
+// Quantizing epilogue of a 256 x 256 tile: bf16(acc + bias) written to LDS
+// exactly as stage_store_tile does (the same values the bf16 output would
+// hold), then per lane 4 row chunks of 64 elements: optional GELU (table),
+// Hadamard butterflies h = 1 .. 32, MX encoding (E2M1 or E4M3 with E8M0
+// per 32).  Lanes 2r and 2r + 1 take the two chunks of one row, so their
+// code stores are contiguous.  The caller has finished every LDS read of
+// the ring; gtab is filled and a barrier has passed since.
+template <bool FP8OUT>
+__device__ __forceinline__ void quant_store_tile(const GemmParams& p, const float16v (&acc)[4][4], uint8_t* smem,
+                                                 const uint16_t* gtab, int m0, int n0) {
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  const int wm = wv >> 1, wn = wv & 1, r32 = lane & 31, h = lane >> 5;
+  uint8_t* reg = smem + wv * 32768;
+  float4 bias[4][4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      bias[j][g] = p.bias ? *reinterpret_cast<const float4*>(p.bias + min(n0 + wn * 128 + 32 * j + 8 * g + 4 * h, p.N - 4))
+                          : make_float4(0.f, 0.f, 0.f, 0.f);
+  __syncthreads();   // every wave is past its last read of the ring
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int lrow = 32 * i + r32;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const float4 b = bias[j][g];
+        const float v0 = acc[i][j][4 * g] * 1.0f + b.x, v1 = acc[i][j][4 * g + 1] * 1.0f + b.y;
+        const float v2 = acc[i][j][4 * g + 2] * 1.0f + b.z, v3 = acc[i][j][4 * g + 3] * 1.0f + b.w;
+        const int c = (4 * j + g) ^ (lrow & 15);
+        *reinterpret_cast<uint2*>(reg + lrow * 256 + 16 * c + 8 * h) = make_uint2(bf16_pair(v0, v1), bf16_pair(v2, v3));
+      }
+  }
+  // the same wave reads back what it wrote (LDS operations of a wave run in order)
+  const bool gelu = (p.qflags & 4u) != 0;
+  const int half = lane & 1;
+#pragma unroll 1
+  for (int it = 0; it < 4; ++it) {
+    const int lrow = 32 * it + (lane >> 1);
+    float v[64];
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      const int c = 8 * half + jj;
+      const uint4 w = *reinterpret_cast<const uint4*>(reg + lrow * 256 + 16 * (c ^ (lrow & 15)));
+      const uint32_t in[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        uint32_t lo = in[q] & 0xFFFFu, hi = in[q] >> 16;
+        if (gelu) {
+          lo = gelu_bf16_bits(lo, gtab);
+          hi = gelu_bf16_bits(hi, gtab);
+        }
+        v[8 * jj + 2 * q] = __uint_as_float(lo << 16);
+        v[8 * jj + 2 * q + 1] = __uint_as_float(hi << 16);
+      }
+    }
+    fwht<64>(v);
+    uint32_t words[FP8OUT ? 16 : 8];
+    uint32_t sbytes;
+    mx_encode64<64, FP8OUT>(v, words, sbytes);
+    const int row = m0 + wm * 128 + lrow;
+    const int col = n0 + wn * 128 + 64 * half;
+    if (row < p.M && col < p.N) {
+      constexpr int BYTES = FP8OUT ? 64 : 32;
+      uint4* q = reinterpret_cast<uint4*>(p.q_out + (int64_t)row * (FP8OUT ? p.N : p.N / 2) + (FP8OUT ? col : col / 2));
+#pragma unroll
+      for (int i = 0; i < BYTES / 16; ++i) q[i] = make_uint4(words[4 * i], words[4 * i + 1], words[4 * i + 2], words[4 * i + 3]);
+      *reinterpret_cast<uint16_t*>(p.s_out + (int64_t)row * (p.N / 32) + col / 32) = (uint16_t)sbytes;
+    }
+  }
+}
+
 // STAGED: the bf16 epilogue through LDS (the host checks staged_store_ok);
-// otherwise per-element stores.  One epilogue per instantiation keeps the
-// accumulators in AGPRs until they are read.
-template <bool A8, bool SPLIT, bool STAGED>
+// otherwise per-element stores.  QOUT 1 / 2: the quantizing epilogue with
+// MXFP4 / MXFP8 codes (the GELU table sits after the ring).  One epilogue
+// per instantiation keeps the accumulators in AGPRs until they are read.
+template <bool A8, bool SPLIT, bool STAGED, int QOUT = 0>
 __global__ __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void qgemm_mx_kernel(GemmParams p) {
   using P = MxPipe<A8>;
@@ -232,6 +315,10 @@ void qgemm_mx_kernel(GemmParams p) {
   // ---- prologue: every ring slot loading, wait for the first stage
   const int pre = min(P::NS, ke - kb);
   for (int s = 0; s < pre; ++s) issue_stage(kb + s);
+  if constexpr (QOUT != 0) {
+    // filled under the first loads; the loop's barriers order it before use
+    if (p.qflags & 4u) gelu_table_build(reinterpret_cast<uint16_t*>(smem + P::LDS));
+  }
   wait_stages<P::LPS>(pre - 1);
   wait_lgkm_barrier();
 
@@ -272,6 +359,10 @@ void qgemm_mx_kernel(GemmParams p) {
     return;
   }
 
+  if constexpr (QOUT != 0) {
+    quant_store_tile<QOUT == 2>(p, acc, smem, reinterpret_cast<const uint16_t*>(smem + P::LDS), m0, n0);
+    return;
+  }
   // bf16 output in whole 16-byte chunks: through LDS (the ring is free)
   if constexpr (STAGED) {
     stage_store_tile<2, (P::LDS >= 4 * 32768) ? 1 : 2>(p, acc, smem, m0, n0);
@@ -293,12 +384,13 @@ void qgemm_mx_kernel(GemmParams p) {
   }
 }
 
-template <bool A8, bool SPLIT, bool STAGED>
+template <bool A8, bool SPLIT, bool STAGED, int QOUT = 0>
 static hipError_t set_mx_lds_attr() {
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&qgemm_mx_kernel<A8, SPLIT, STAGED>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, MxPipe<A8>::LDS);
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&qgemm_mx_kernel<A8, SPLIT, STAGED, QOUT>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       MxPipe<A8>::LDS + (QOUT ? kGeluTabBytes : 0));
     if (e != hipSuccess) return e;
     attr_set = true;
   }
@@ -332,6 +424,36 @@ static hipError_t launch_mx(GemmParams p, hipStream_t st) {
     e = hipGetLastError();
   }
   return e;
+}
+
+// Quantizing variant: every tile in the data-parallel kernel (no K split).
+template <bool A8, int QOUT>
+static hipError_t launch_mx_quant(GemmParams p, hipStream_t st) {
+  int dp_grid = 0, sk_grid = 0;
+  plan_pipe(p, cu_count(), dp_grid, sk_grid);
+  p.sk_tiles = 0;
+  p.slices = 0;
+  p.slice_nk = 0;
+  dp_grid = p.tiles_m * p.tiles_n;
+  hipError_t e = set_mx_lds_attr<A8, false, false, QOUT>();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((qgemm_mx_kernel<A8, false, false, QOUT>), dim3(dp_grid), dim3(GT),
+                     (size_t)MxPipe<A8>::LDS + kGeluTabBytes, st, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_qgemm_mx_quant(bool a_fp8, const uint8_t* a_q, const uint8_t* a_s, const uint8_t* w_q,
+                                 const uint8_t* w_s, const float* bias, bool out_fp8, bool gelu, uint8_t* q_out,
+                                 uint8_t* s_out, int64_t M, int64_t N, int64_t K, hipStream_t st) {
+  if (M == 0 || N == 0) return hipSuccess;
+  GemmParams p{};
+  p.a_q = a_q; p.a_s = a_s; p.a_ts = nullptr;
+  p.w_q = w_q; p.w_s = w_s; p.w_ts = nullptr;
+  p.bias = bias; p.y = nullptr; p.ldy = 0;
+  p.M = (int32_t)M; p.N = (int32_t)N; p.K = (int32_t)K;
+  p.q_out = q_out; p.s_out = s_out; p.qflags = gelu ? 4u : 0u;
+  if (a_fp8) return out_fp8 ? launch_mx_quant<true, 2>(p, st) : launch_mx_quant<true, 1>(p, st);
+  return out_fp8 ? launch_mx_quant<false, 2>(p, st) : launch_mx_quant<false, 1>(p, st);
 }
 
 hipError_t launch_qgemm_mx(bool a_fp8, const uint8_t* a_q, const uint8_t* a_s, const uint8_t* w_q,

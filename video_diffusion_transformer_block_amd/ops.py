@@ -92,9 +92,10 @@ class MXTensor:
 
 
 def hadamard_quantize(x: torch.Tensor, had_block: int = 64, fmt: str = "nvfp4", amax=None,
-                      stats: bool = False, out=None):
+                      stats: bool = False, out=None, gelu: bool = False):
     """Block Hadamard transform of bf16 rows + NVFP4, INT8, MXFP4 or MXFP8
-    quantization (or bf16 rounding).
+    quantization (or bf16 rounding).  gelu: the rows are first mapped
+    through the feed-forward's GELU (fp32, rounded to bf16).
     amax (NVFP4 only): a float or a 1-element device tensor to use as the
     tensor amax instead of computing it, or the string "given" to use the
     value already in out.ts[0].  out: a previously returned NVFP4Tensor /
@@ -104,7 +105,7 @@ def hadamard_quantize(x: torch.Tensor, had_block: int = 64, fmt: str = "nvfp4", 
         raise ValueError("x must be a 2-D tensor with unit column stride")
     M, K = x.shape
     dev = x.device
-    flags = L.STATS if stats else 0
+    flags = (L.STATS if stats else 0) | (L.GELU if gelu else 0)
     st = torch.empty(4, dtype=torch.float64, device=dev) if stats else None
     nbytes = L.lib().vdtq_workspace_bytes(L.OP_HADAMARD_QUANTIZE, M, K)
     ws = workspace(dev, nbytes)
@@ -231,6 +232,32 @@ def qgemm_mx(a: MXTensor, w: MXTensor, bias: Optional[torch.Tensor] = None,
                              L.OUT_BF16 if out_dtype == "bf16" else L.OUT_F32, M, N, K, _p(ws), ws.numel(),
                              _stream(a.q.device)))
     return y
+
+
+def qgemm_mx_quant(a: MXTensor, w: MXTensor, bias: Optional[torch.Tensor] = None, out_fmt: str = "mxfp4",
+                   had_block: int = 64, gelu: bool = True, out: Optional[MXTensor] = None) -> MXTensor:
+    """qgemm_mx with a quantizing epilogue: the bf16 product (plus bias),
+    optionally through GELU, Hadamard-transformed in blocks of had_block and
+    MX-encoded as the next linear's activation (FFN-up feeding FFN-down)."""
+    if w.fmt != "mxfp4":
+        raise ValueError("MX weights must be mxfp4")
+    if out_fmt not in ("mxfp4", "mxfp8"):
+        raise ValueError(f"out_fmt {out_fmt!r}")
+    M = a.q.shape[0]
+    K = a.q.shape[1] * (2 if a.fmt == "mxfp4" else 1)
+    N = w.q.shape[0]
+    if w.q.shape[1] * 2 != K:
+        raise ValueError("K mismatch between activations and weights")
+    dev = a.q.device
+    if out is None:
+        q = torch.empty((M, N // 2 if out_fmt == "mxfp4" else N), dtype=torch.uint8, device=dev)
+        s = torch.empty((M, N // 32), dtype=torch.uint8, device=dev)
+        out = MXTensor(q, s, out_fmt)
+    L.check(L.lib().qgemm_mx_quant(L.FMT_MXFP4 if a.fmt == "mxfp4" else L.FMT_MXFP8, _p(a.q), _p(a.scales),
+                                   _p(w.q), _p(w.scales), _p(bias), had_block,
+                                   L.FMT_MXFP4 if out_fmt == "mxfp4" else L.FMT_MXFP8, L.GELU if gelu else 0,
+                                   _p(out.q), _p(out.scales), M, N, K, _stream(dev)))
+    return out
 
 
 def block_stats(inp: torch.Tensor, out: torch.Tensor, dprev: Optional[torch.Tensor] = None,
