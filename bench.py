@@ -259,6 +259,7 @@ def main():
         del src, dst
 
     bsroof = measure_block_stats(torch, V, X["qkv"], Y["ffn_down"], M * hidden, args.steps)
+    ffn_fusion = measure_ffn_fusion(torch, V, X, WM, M, args.steps) if want_mx else None
 
     dyn = None if args.no_dyn else measure_dyn(torch, V, synth)
     cpu = None if args.no_cpu_baseline else cpu_baseline(host, M, args.cpu_rows)
@@ -285,6 +286,7 @@ def main():
         "quantize_roofline": qroof,
         "mx_gemm_roofline": mx_roof or None,
         "block_stats_roofline": bsroof,
+        "ffn_fusion": ffn_fusion,
         "sweeps": {k: {"tops": round(v["tops"], 2), "ms_per_step": round(v["ms_per_step"], 4),
                        "gemm_tflops": round(total_flops / (sum(d["gemm_ms"] for d in v["per_linear"].values())
                                                            * 1e-3) / 1e12, 1),
@@ -564,6 +566,51 @@ def measure_quantize(torch, V, X, M, steps, with_mx=False):
                                   "grid_work_items": hq_grid_work_items(M, K, fmt)}
             del g
     return out
+
+
+def measure_ffn_fusion(torch, V, X, WM, M, steps):
+    """FFN-up feeding FFN-down at the 5B shape (17776 x 3072 -> 12288, MXFP4
+    weights, bias): the unfused chain qgemm_mx (bf16 Y) -> hadamard_quantize
+    (GELU, Hadamard 64, MXFP4) against qgemm_mx_quant, which never writes Y;
+    for MXFP8 activations (the W4A6 mix's FFN-up format) and MXFP4.  Each
+    part is timed alone too (HIP events around 10 launches, median)."""
+    N = WM["ffn_up"].q.shape[0]
+    gen = torch.Generator(device=X["ffn_up"].device).manual_seed(77)
+    bias = torch.randn(N, generator=gen, device=X["ffn_up"].device) * 0.1
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=X["ffn_up"].device)
+    w = WM["ffn_up"]
+
+    def timed(fn, reps=10):
+        fn()
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(max(3, steps // 4)):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1) / reps)
+        return round(1e3 * float(np.median(times)), 1)
+
+    res = {"workload": f"FFN-up {M}x3072 -> {N} + bias, GELU, Hadamard 64, MXFP4 FFN-down activation",
+           "bf16_round_trip_bytes": 4 * M * N}
+    q = V.hadamard_quantize(y, HAD_BLOCK, "mxfp4")
+    res["quant_us"] = timed(lambda: V.hadamard_quantize(y, HAD_BLOCK, "mxfp4", out=q))
+    res["quant_gelu_us"] = timed(lambda: V.hadamard_quantize(y, HAD_BLOCK, "mxfp4", gelu=True, out=q))
+    for afmt in ("mxfp8", "mxfp4"):
+        a = V.hadamard_quantize(X["ffn_up"], HAD_BLOCK, afmt)
+        qf = V.qgemm_mx_quant(a, w, bias, "mxfp4", gelu=True)
+        gemm = timed(lambda: V.qgemm_mx(a, w, bias, "bf16", y=y))
+        chain = timed(lambda: (V.qgemm_mx(a, w, bias, "bf16", y=y),
+                               V.hadamard_quantize(y, HAD_BLOCK, "mxfp4", gelu=True, out=q)))
+        fused = timed(lambda: V.qgemm_mx_quant(a, w, bias, "mxfp4", gelu=True, out=qf))
+        res[afmt] = {"gemm_bf16_us": gemm, "unfused_us": chain, "fused_us": fused,
+                     "speedup": round(chain / fused, 3)}
+        print(f"[bench] ffn fusion {afmt}: gemm {gemm} us, chain {chain} us, fused {fused} us", file=sys.stderr,
+              flush=True)
+    return res
 
 
 def cpu_baseline(host, M, rows):

@@ -83,7 +83,7 @@ int hadamard_quantize(const void* x_dev, int64_t M, int64_t K, int64_t ldx, int 
     return fail(VDTQ_EINVAL, "hadamard_quantize: NVFP4 needs an aligned tensor_scale (float[2])");
   if ((flags & VDTQ_STATS) && (!stats_dev || !aligned(stats_dev, 8)))
     return fail(VDTQ_EINVAL, "hadamard_quantize: VDTQ_STATS needs an aligned stats buffer (double[4])");
-  const bool need_ws = (flags & VDTQ_STATS) || (fmt == VDTQ_FMT_NVFP4 && !(flags & VDTQ_AMAX_GIVEN));
+  const bool need_ws = (flags & (VDTQ_STATS | VDTQ_GELU)) || (fmt == VDTQ_FMT_NVFP4 && !(flags & VDTQ_AMAX_GIVEN));
   if (need_ws) {
     const size_t need = vdtq::hq_workspace_bytes(M, K);
     if (!ws_dev || !aligned(ws_dev, 16) || ws_bytes < need)

@@ -68,25 +68,33 @@ constexpr int kGeluPosN = (int)(kGeluPosEnd - kGeluLo);
 constexpr int kGeluTabN = kGeluPosN + (int)(kGeluNegEnd - kGeluLo);
 constexpr int kGeluTabBytes = ((2 * kGeluTabN + 15) / 16) * 16;
 
+// Table entry i (0 <= i < kGeluTabN).
+__device__ __forceinline__ uint16_t gelu_table_entry(int i) {
+  const uint32_t b = i < kGeluPosN ? kGeluLo + i : (0x8000u | (kGeluLo + (i - kGeluPosN)));
+  return (uint16_t)f32_to_bf16_bits(gelu_fp32(__uint_as_float(b << 16)));
+}
+
 // Fills the table; every thread of the workgroup takes part (a barrier
 // must follow before the first lookup).
 __device__ __forceinline__ void gelu_table_build(uint16_t* tab) {
-  for (int i = threadIdx.x; i < kGeluTabN; i += blockDim.x) {
-    const uint32_t b = i < kGeluPosN ? kGeluLo + i : (0x8000u | (kGeluLo + (i - kGeluPosN)));
-    tab[i] = (uint16_t)f32_to_bf16_bits(gelu_fp32(__uint_as_float(b << 16)));
-  }
+  for (int i = threadIdx.x; i < kGeluTabN; i += blockDim.x) tab[i] = gelu_table_entry(i);
 }
 
-// RNE_bf16(gelu_fp32(x)) for the bf16 bits b of a finite x.
+// RNE_bf16(gelu_fp32(x)) for the bf16 bits b of a finite x.  Below the
+// table, x / 2 is exact for exponent fields >= 2 (one less in the exponent
+// field); smaller inputs round (rare: a divergent branch).
 __device__ __forceinline__ uint32_t gelu_bf16_bits(uint32_t b, const uint16_t* tab) {
   const uint32_t mag = b & 0x7FFFu;
-  const bool neg = (b & 0x8000u) != 0;
-  const bool in_tab = mag >= kGeluLo && mag < (neg ? kGeluNegEnd : kGeluPosEnd);
-  const uint32_t idx = mag - kGeluLo + (neg ? (uint32_t)kGeluPosN : 0u);
-  const uint32_t t = tab[in_tab ? idx : 0u];
-  if (in_tab) return t;
-  if (mag < kGeluLo) return f32_to_bf16_bits(__uint_as_float(b << 16) * 0.5f);
-  return neg ? 0x8000u : b;
+  const bool neg = b > 0x7FFFu;
+  const uint32_t idx = mag - kGeluLo;                       // wraps below the table
+  const bool in_tab = idx < (neg ? kGeluNegEnd - kGeluLo : kGeluPosEnd - kGeluLo);
+  const uint32_t t = tab[in_tab ? idx + (neg ? (uint32_t)kGeluPosN : 0u) : 0u];
+  uint32_t r = neg ? 0x8000u : b;                           // above the table
+  if (mag < kGeluLo) {
+    r = b - 0x80u;
+    if (mag < 0x100u) r = f32_to_bf16_bits(__uint_as_float(b << 16) * 0.5f);
+  }
+  return in_tab ? t : r;
 }
 
 // ---------------------------------------------------------------- Hadamard

@@ -33,8 +33,9 @@
 //     hardware (E2M1 saturates by itself; E4M3 is clamped to +-448 first,
 //     the conversion itself does not saturate).  No tensor scale, one pass.
 //   * GELU prologue (flag 4; the FFN-down input taken straight from FFN-up's
-//     bf16 output): each staged element goes through the fp32 GELU of
-//     hadamard_common.h and back to bf16 in LDS, before anything else.
+//     bf16 output): each element is replaced by the bf16 GELU of
+//     hadamard_common.h (a table of the non-trivial inputs, written once
+//     per call and copied into LDS) before anything else.
 //   * Statistics: fp32 over a thread's 64 elements, fp64 across threads and
 //     workgroups in a fixed order (bit-reproducible, no float atomics).
 #include <algorithm>
@@ -61,6 +62,7 @@ struct HQParams {
   double* stats_part;         // [grid][4] partial statistics
   unsigned flags;
   int32_t flat;               // ldx == K and K % 64 == 0: chunk g starts at element 64 g
+  const uint16_t* gtab;       // GELU table in the workspace (flag 4)
 };
 
 __device__ __forceinline__ void divmod_cpr(int64_t g, const HQParams& p, int& row, int& col) {
@@ -146,38 +148,36 @@ __device__ __forceinline__ void stage(const HQParams& p, uint4* lds, int& my_row
   }
 }
 
-// With the GELU flag (4) the kernels are launched with the GELU table in
-// dynamic LDS (gelu_lds); gelu_begin fills it before staging, gelu_chunk
-// maps this thread's staged chunk through it in place (the thread touches
-// only its own LDS slots) before load_chunk widens it.
+// With the GELU flag (4) a one-block-per-256-entries kernel first writes the
+// GELU table to the workspace; each quantize workgroup copies it into
+// dynamic LDS (gelu_lds) before staging; load_chunk maps each staged
+// element through it as it widens the chunk.
 extern __shared__ __attribute__((aligned(16))) uint16_t gelu_lds[];
 
-__device__ __forceinline__ void gelu_begin(unsigned flags) {
-  if (flags & 4u) gelu_table_build(gelu_lds);
+__global__ __launch_bounds__(256) void gelu_table_kernel(uint16_t* tab) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < kGeluTabN) tab[i] = gelu_table_entry(i);
 }
 
-__device__ __forceinline__ void gelu_chunk(uint4* lds, unsigned flags) {
-  if (!(flags & 4u)) return;
-  const int t = threadIdx.x;
-#pragma unroll
-  for (int jj = 0; jj < 8; ++jj) {
-    uint4& slot = lds[t * 8 + (jj ^ (t & 7))];
-    const uint4 w = slot;
-    const uint32_t in[4] = {w.x, w.y, w.z, w.w};
-    uint32_t out[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      out[i] = gelu_bf16_bits(in[i] & 0xFFFFu, gelu_lds) | (gelu_bf16_bits(in[i] >> 16, gelu_lds) << 16);
-    slot = make_uint4(out[0], out[1], out[2], out[3]);
-  }
+__device__ __forceinline__ void gelu_begin(const HQParams& p) {
+  if (!(p.flags & 4u)) return;
+  for (int i = threadIdx.x; i < kGeluTabBytes / 16; i += HQ_THREADS)
+    reinterpret_cast<uint4*>(gelu_lds)[i] = reinterpret_cast<const uint4*>(p.gtab)[i];
 }
 
-// Reads this thread's chunk from LDS and widens bf16 -> fp32.
-__device__ __forceinline__ void load_chunk(const uint4* lds, float (&v)[64]) {
+// Reads this thread's chunk from LDS and widens bf16 -> fp32 (through the
+// GELU table first with flag 4).
+__device__ __forceinline__ uint32_t gelu_word(uint32_t w) {
+  return gelu_bf16_bits(w & 0xFFFFu, gelu_lds) | (gelu_bf16_bits(w >> 16, gelu_lds) << 16);
+}
+
+__device__ __forceinline__ void load_chunk(const uint4* lds, float (&v)[64], unsigned flags) {
   const int t = threadIdx.x;
+  const bool gelu = (flags & 4u) != 0;
 #pragma unroll
   for (int jj = 0; jj < 8; ++jj) {
     uint4 w = lds[t * 8 + (jj ^ (t & 7))];
+    if (gelu) w = make_uint4(gelu_word(w.x), gelu_word(w.y), gelu_word(w.z), gelu_word(w.w));
     v[8 * jj + 0] = bf16_lo(w.x); v[8 * jj + 1] = bf16_hi(w.x);
     v[8 * jj + 2] = bf16_lo(w.y); v[8 * jj + 3] = bf16_hi(w.y);
     v[8 * jj + 4] = bf16_lo(w.z); v[8 * jj + 5] = bf16_hi(w.z);
@@ -236,12 +236,11 @@ __global__ __launch_bounds__(HQ_THREADS) void hq_amax_kernel(HQParams p) {
   __shared__ float wred[HQ_THREADS / 64];
   int row, col;
   bool valid;
-  gelu_begin(p.flags);
+  gelu_begin(p);
   stage<false>(p, lds, row, col, valid);
   __syncthreads();
   float v[64];
-  gelu_chunk(lds, p.flags);
-  load_chunk(lds, v);
+  load_chunk(lds, v, p.flags);
   fwht<B>(v);
   normalise<B>(v);
   float m = 0.0f;
@@ -328,12 +327,11 @@ __global__ __launch_bounds__(HQ_THREADS) void hq_nvfp4_kernel(HQParams p) {
   }
   int row, col;
   bool valid;
-  gelu_begin(p.flags);
+  gelu_begin(p);
   stage<false>(p, lds, row, col, valid);
   __syncthreads();
   float v[64];
-  gelu_chunk(lds, p.flags);
-  load_chunk(lds, v);
+  load_chunk(lds, v, p.flags);
   const int nvalid = valid ? min(64, p.K - col * 64) : 0;
   const bool want_stats = (p.flags & 2u) != 0;
   float mx = 0.0f, sx = 0.0f;
@@ -397,12 +395,11 @@ __global__ __launch_bounds__(HQ_THREADS) void hq_int8_kernel(HQParams p) {
   if (threadIdx.x < p.rows_per_wg) rowmax[threadIdx.x] = 0u;
   int row, col;
   bool valid;
-  gelu_begin(p.flags);
+  gelu_begin(p);
   stage<true>(p, lds, row, col, valid);
   __syncthreads();
   float v[64];
-  gelu_chunk(lds, p.flags);
-  load_chunk(lds, v);
+  load_chunk(lds, v, p.flags);
   const int nvalid = valid ? min(64, p.K - col * 64) : 0;
   const bool want_stats = (p.flags & 2u) != 0;
   float mx = 0.0f, sx = 0.0f;
@@ -458,12 +455,11 @@ __global__ __launch_bounds__(HQ_THREADS) void hq_bf16_kernel(HQParams p) {
   __shared__ uint4 lds[HQ_THREADS * 8];
   int row, col;
   bool valid;
-  gelu_begin(p.flags);
+  gelu_begin(p);
   stage<false>(p, lds, row, col, valid);
   __syncthreads();
   float v[64];
-  gelu_chunk(lds, p.flags);
-  load_chunk(lds, v);
+  load_chunk(lds, v, p.flags);
   const int nvalid = valid ? min(64, p.K - col * 64) : 0;
   const bool want_stats = (p.flags & 2u) != 0;
   float mx = 0.0f, sx = 0.0f;
@@ -499,12 +495,11 @@ __global__ __launch_bounds__(HQ_THREADS) void hq_mx_kernel(HQParams p) {
   __shared__ uint4 lds[HQ_THREADS * 8];
   int row, col;
   bool valid;
-  gelu_begin(p.flags);
+  gelu_begin(p);
   stage<false>(p, lds, row, col, valid);
   __syncthreads();
   float v[64];
-  gelu_chunk(lds, p.flags);
-  load_chunk(lds, v);
+  load_chunk(lds, v, p.flags);
   const int nvalid = valid ? min(64, p.K - col * 64) : 0;
   const bool want_stats = (p.flags & 2u) != 0;
   float mx = 0.0f, sx = 0.0f;
@@ -562,13 +557,17 @@ static hipError_t launch_b(const HQParams& p, int fmt, bool amax_given, int grid
   return hipGetLastError();
 }
 
-size_t hq_workspace_bytes(int64_t M, int64_t K) {
+// Workspace: per-workgroup amax partials (float), statistics partials
+// (double[4]), then the GELU table.
+static size_t hq_partials_bytes(int64_t M, int64_t K) {
   if (M <= 0 || K <= 0) return 256;
   const int64_t cpr = (K + 63) / 64;
   // the largest grid of either format: flat chunks, or one row per group
   const int64_t grid = std::max<int64_t>((M * cpr + HQ_THREADS - 1) / HQ_THREADS, M);
   return (size_t)(((grid * 4 + 63) / 64) * 64 + grid * 4 * 8);
 }
+
+size_t hq_workspace_bytes(int64_t M, int64_t K) { return hq_partials_bytes(M, K) + kGeluTabBytes; }
 
 hipError_t launch_hadamard_quantize(const void* x, int64_t M, int64_t K, int64_t ldx, int b, int fmt,
                                     unsigned flags, void* q, void* scales, float* ts,
@@ -599,6 +598,8 @@ hipError_t launch_hadamard_quantize(const void* x, int64_t M, int64_t K, int64_t
   const int64_t grid_cap = std::max<int64_t>((M * p.cpr + HQ_THREADS - 1) / HQ_THREADS, M);
   p.amax_part = reinterpret_cast<float*>(wsb);
   p.stats_part = reinterpret_cast<double*>(wsb + ((grid_cap * 4 + 63) / 64) * 64);
+  uint16_t* gtab = reinterpret_cast<uint16_t*>(wsb + hq_partials_bytes(M, K));
+  p.gtab = gtab;
 
   if (M == 0) {
     if (fmt == 0) {
@@ -609,6 +610,11 @@ hipError_t launch_hadamard_quantize(const void* x, int64_t M, int64_t K, int64_t
     }
     if (want_stats) hipLaunchKernelGGL(hq_stats_final_kernel, dim3(1), dim3(kFinalThreads), 0, st, p.stats_part, 0, stats);
     return hipGetLastError();
+  }
+  if (flags & 4u) {
+    hipLaunchKernelGGL(gelu_table_kernel, dim3((kGeluTabN + 255) / 256), dim3(256), 0, st, gtab);
+    const hipError_t et = hipGetLastError();
+    if (et != hipSuccess) return et;
   }
   hipError_t e;
   switch (b) {

@@ -132,7 +132,7 @@ __device__ __forceinline__ void quant_store_tile(const GemmParams& p, const floa
   // the same wave reads back what it wrote (LDS operations of a wave run in order)
   const bool gelu = (p.qflags & 4u) != 0;
   const int half = lane & 1;
-#pragma unroll 1
+#pragma unroll 2
   for (int it = 0; it < 4; ++it) {
     const int lrow = 32 * it + (lane >> 1);
     float v[64];
