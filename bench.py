@@ -510,17 +510,31 @@ def measure_block_stats(torch, V, inp, out, n, steps):
 
 def hq_grid_work_items(M, K, fmt):
     """Work-items of one quantize launch, as the library's launcher sizes it:
-    one 64-element chunk per thread for NVFP4 and MX; for INT8, max(1, 256 /
-    chunks per row) whole rows per 256-thread group.  Keys the counter record."""
+    one 64-element chunk per thread for NVFP4 and MX; for INT8, whole rows
+    per group of int8_threads(chunks per row) threads.  Keys the counter
+    record."""
     cpr = (K + 63) // 64
     if fmt != "int8":
         return -(-M * cpr // 256) * 256
-    rpw = max(1, 256 // cpr)
-    return -(-M // rpw) * 256
+    threads = int8_threads(cpr)
+    rpw = max(1, threads // cpr)
+    return -(-M // rpw) * threads
+
+
+def int8_threads(cpr):
+    """Workgroup size of the INT8 quantize kernel for rows of cpr chunks of
+    64 (the library's rule: the T in {64, 128, 192, 256} whose whole rows
+    leave the fewest lanes idle, the larger T on ties)."""
+    best, best_use = 256, 0.0
+    for t in (256, 192, 128, 64):
+        rows = t // cpr
+        if rows >= 1 and rows * cpr / t > best_use + 1e-12:
+            best, best_use = t, rows * cpr / t
+    return best
 
 
 QUANT_BYTES = {"nvfp4": 2 + 0.5 + 1 / 16, "int8": 3.0, "mxfp4": 2 + 0.5 + 1 / 32, "mxfp8": 2 + 1 + 1 / 32}
-QUANT_KERNEL = {"nvfp4": "hq_nvfp4_kernel<64>", "int8": "hq_int8_kernel<64>",
+QUANT_KERNEL = {"nvfp4": "hq_nvfp4_kernel<64>", "int8": "hq_int8_kernel<64, 192>",
                 "mxfp4": "hq_mx_kernel<64, false>", "mxfp8": "hq_mx_kernel<64, true>"}
 
 

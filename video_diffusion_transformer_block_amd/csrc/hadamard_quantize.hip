@@ -75,11 +75,11 @@ __device__ __forceinline__ void divmod_cpr(int64_t g, const HQParams& p, int& ro
 }
 
 // ---------------------------------------------------------------- staging
-// Loads the workgroup's 256 chunks into LDS (zeros where the chunk or the
-// 8-element slot lies outside X) and returns this thread's own chunk
-// coordinates.  ROWS: chunks are rows_per_wg whole rows; otherwise the
-// workgroup owns flat chunk ids [256 wg, 256 wg + 256).
-template <bool ROWS>
+// Loads the workgroup's T chunks (T = its thread count) into LDS (zeros
+// where the chunk or the 8-element slot lies outside X) and returns this
+// thread's own chunk coordinates.  ROWS: chunks are rows_per_wg whole rows;
+// otherwise the workgroup owns flat chunk ids [T wg, T wg + T).
+template <bool ROWS, int T = HQ_THREADS>
 __device__ __forceinline__ void stage(const HQParams& p, uint4* lds, int& my_row, int& my_col,
                                       bool& my_valid) {
   const int t = threadIdx.x;
@@ -90,19 +90,19 @@ __device__ __forceinline__ void stage(const HQParams& p, uint4* lds, int& my_row
   if (p.flat) {
     // contiguous whole-chunk rows: the workgroup's chunks are one contiguous
     // run starting at chunk g0, so loads need no row / column arithmetic
-    const int chunk_limit = ROWS ? p.rows_per_wg * p.cpr : HQ_THREADS;
-    const int64_t g0 = ROWS ? (int64_t)wg * p.rows_per_wg * p.cpr : (int64_t)wg * HQ_THREADS;
+    const int chunk_limit = ROWS ? p.rows_per_wg * p.cpr : T;
+    const int64_t g0 = ROWS ? (int64_t)wg * p.rows_per_wg * p.cpr : (int64_t)wg * T;
     const int64_t left = p.total_chunks - g0;
     const int lim = (int)min<int64_t>(chunk_limit, left);
     const uint16_t* base = p.x + (g0 + c0) * 64 + 8 * j;
     uint4 buf[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      buf[i] = (c0 + 32 * i < lim) ? *reinterpret_cast<const uint4*>(base + i * (32 * 64))
+      buf[i] = (c0 + (T / 8) * i < lim) ? *reinterpret_cast<const uint4*>(base + i * ((T / 8) * 64))
                                    : make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int c = c0 + 32 * i;
+      const int c = c0 + (T / 8) * i;
       lds[c * 8 + (j ^ (c & 7))] = buf[i];
     }
     if (ROWS) {
@@ -119,23 +119,23 @@ __device__ __forceinline__ void stage(const HQParams& p, uint4* lds, int& my_row
     divmod_cpr(c0, p, row, col);
     row += wg * p.rows_per_wg;
   } else {
-    divmod_cpr((int64_t)wg * HQ_THREADS + c0, p, row, col);
+    divmod_cpr((int64_t)wg * T + c0, p, row, col);
   }
-  const int chunk_limit = ROWS ? p.rows_per_wg * p.cpr : HQ_THREADS;
+  const int chunk_limit = ROWS ? p.rows_per_wg * p.cpr : T;
   uint4 buf[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const int c = c0 + 32 * i;
+    const int c = c0 + (T / 8) * i;
     const int e = col * 64 + 8 * j;
     const bool ok = (c < chunk_limit) && (row < p.M) && (e < p.K);
     buf[i] = ok ? *reinterpret_cast<const uint4*>(p.x + (int64_t)row * p.ldx + e)
                 : make_uint4(0u, 0u, 0u, 0u);
-    col += 32;
+    col += T / 8;
     while (col >= p.cpr) { col -= p.cpr; ++row; }
   }
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const int c = c0 + 32 * i;
+    const int c = c0 + (T / 8) * i;
     lds[c * 8 + (j ^ (c & 7))] = buf[i];
   }
   if (ROWS) {
@@ -143,7 +143,7 @@ __device__ __forceinline__ void stage(const HQParams& p, uint4* lds, int& my_row
     my_row += wg * p.rows_per_wg;
     my_valid = (t < chunk_limit) && (my_row < p.M);
   } else {
-    divmod_cpr((int64_t)wg * HQ_THREADS + t, p, my_row, my_col);
+    divmod_cpr((int64_t)wg * T + t, p, my_row, my_col);
     my_valid = my_row < p.M;
   }
 }
@@ -161,7 +161,7 @@ __global__ __launch_bounds__(256) void gelu_table_kernel(uint16_t* tab) {
 
 __device__ __forceinline__ void gelu_begin(const HQParams& p) {
   if (!(p.flags & 4u)) return;
-  for (int i = threadIdx.x; i < kGeluTabBytes / 16; i += HQ_THREADS)
+  for (int i = threadIdx.x; i < kGeluTabBytes / 16; i += blockDim.x)
     reinterpret_cast<uint4*>(gelu_lds)[i] = reinterpret_cast<const uint4*>(p.gtab)[i];
 }
 
@@ -171,8 +171,8 @@ __device__ __forceinline__ uint32_t gelu_word(uint32_t w) {
   return gelu_bf16_bits(w & 0xFFFFu, gelu_lds) | (gelu_bf16_bits(w >> 16, gelu_lds) << 16);
 }
 
-__device__ __forceinline__ void load_chunk(const uint4* lds, float (&v)[64], unsigned flags) {
-  const int t = threadIdx.x;
+__device__ __forceinline__ void load_chunk(const uint4* lds, float (&v)[64], unsigned flags,
+                                           int t = threadIdx.x) {
   const bool gelu = (flags & 4u) != 0;
 #pragma unroll
   for (int jj = 0; jj < 8; ++jj) {
@@ -211,8 +211,9 @@ __device__ __forceinline__ void input_stats(const float (&v)[64], int nvalid, fl
 
 // Sum / max of four per-thread values over the workgroup, fp64, fixed order;
 // thread 0 writes them to part[4].
+template <int T = HQ_THREADS>
 __device__ void wg_stats_write(double mx, double sx, double my, double sy, double* part) {
-  __shared__ double red[4][HQ_THREADS / 64];
+  __shared__ double red[4][T / 64];
   mx = wave_max_d(mx);
   sx = wave_sum(sx);
   my = wave_max_d(my);
@@ -222,7 +223,7 @@ __device__ void wg_stats_write(double mx, double sx, double my, double sy, doubl
   __syncthreads();
   if (threadIdx.x == 0) {
     double a = red[0][0], b = red[1][0], c = red[2][0], d = red[3][0];
-    for (int i = 1; i < HQ_THREADS / 64; ++i) {
+    for (int i = 1; i < T / 64; ++i) {
       a = fmax(a, red[0][i]); b += red[1][i]; c = fmax(c, red[2][i]); d += red[3][i];
     }
     part[0] = a; part[1] = b; part[2] = c; part[3] = d;
@@ -311,6 +312,39 @@ __global__ __launch_bounds__(kFinalThreads) void hq_stats_final_kernel(const dou
   }
 }
 
+// NVFP4 encoding of a thread's 64 transformed register values: per 16-group
+// the E4M3 scale byte (byte g of sbytes) and 16 E2M1 codes (words 2g, 2g+1);
+// with want_stats, max|y| and sum|y| over the first nvalid values are folded
+// into my / sy.
+template <int B>
+__device__ __forceinline__ void nvfp4_encode64(const float (&v)[64], const float* inv_tab, bool ok, float d,
+                                               bool want_stats, int nvalid, uint32_t (&words)[8],
+                                               uint32_t& sbytes, float& my, float& sy) {
+  sbytes = 0;
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    float av = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) av = fmaxf(av, fabsf(v[16 * g + e]));
+    const float ag = av * yfac<B>();                 // exact (power of two)
+    uint32_t s8 = ok ? e4m3_encode_pos(ag / d) : 0u;
+    const float inv = inv_tab[s8];                  // 0 exactly when s_dec == 0
+    const bool nz = inv != 0.0f;
+    const uint32_t w0 = pack8_e2m1(&v[16 * g], inv, HadScale<B>::inv);
+    const uint32_t w1 = pack8_e2m1(&v[16 * g + 8], inv, HadScale<B>::inv);
+    words[2 * g] = nz ? w0 : 0u;
+    words[2 * g + 1] = nz ? w1 : 0u;
+    sbytes |= s8 << (8 * g);
+    if (want_stats && 16 * g < nvalid) {
+      my = fmaxf(my, ag);
+      float s = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s = s + fabsf(v[16 * g + e]);
+      sy = sy + s * yfac<B>();
+    }
+  }
+}
+
 // ---------------------------------------------------------------- NVFP4 pass
 template <int B>
 __global__ __launch_bounds__(HQ_THREADS) void hq_nvfp4_kernel(HQParams p) {
@@ -343,30 +377,9 @@ __global__ __launch_bounds__(HQ_THREADS) void hq_nvfp4_kernel(HQParams p) {
   if (blockIdx.x == 0 && threadIdx.x == 0) p.ts[1] = gs;
 
   uint32_t words[8];
-  uint32_t sbytes = 0;
+  uint32_t sbytes;
   float my = 0.0f, sy = 0.0f;
-#pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    float av = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) av = fmaxf(av, fabsf(v[16 * g + e]));
-    const float ag = av * yfac<B>();                 // exact (power of two)
-    uint32_t s8 = ok ? e4m3_encode_pos(ag / d) : 0u;
-    const float inv = inv_tab[s8];                  // 0 exactly when s_dec == 0
-    const bool nz = inv != 0.0f;
-    const uint32_t w0 = pack8_e2m1(&v[16 * g], inv, HadScale<B>::inv);
-    const uint32_t w1 = pack8_e2m1(&v[16 * g + 8], inv, HadScale<B>::inv);
-    words[2 * g] = nz ? w0 : 0u;
-    words[2 * g + 1] = nz ? w1 : 0u;
-    sbytes |= s8 << (8 * g);
-    if (want_stats && 16 * g < nvalid) {
-      my = fmaxf(my, ag);
-      float s = 0.0f;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) s = s + fabsf(v[16 * g + e]);
-      sy = sy + s * yfac<B>();
-    }
-  }
+  nvfp4_encode64<B>(v, inv_tab, ok, d, want_stats, nvalid, words, sbytes, my, sy);
 
   if (valid) {
     uint8_t* qrow = p.q + (int64_t)row * (p.K / 2) + col * 32;
@@ -375,28 +388,33 @@ __global__ __launch_bounds__(HQ_THREADS) void hq_nvfp4_kernel(HQParams p) {
       reinterpret_cast<uint4*>(qrow)[0] = make_uint4(words[0], words[1], words[2], words[3]);
       reinterpret_cast<uint4*>(qrow)[1] = make_uint4(words[4], words[5], words[6], words[7]);
     } else {
-      for (int g = 0; 16 * g < nvalid; ++g)
-        reinterpret_cast<uint2*>(qrow)[g] = make_uint2(words[2 * g], words[2 * g + 1]);
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        if (16 * g < nvalid) reinterpret_cast<uint2*>(qrow)[g] = make_uint2(words[2 * g], words[2 * g + 1]);
     }
     if (nvalid == 64 && (p.K % 64) == 0) {
       *reinterpret_cast<uint32_t*>(srow) = sbytes;
     } else {
-      for (int g = 0; 16 * g < nvalid; ++g) srow[g] = (uint8_t)(sbytes >> (8 * g));
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        if (16 * g < nvalid) srow[g] = (uint8_t)(sbytes >> (8 * g));
     }
   }
   if (want_stats) wg_stats_write(mx, sx, my, sy, p.stats_part + 4 * (int64_t)blockIdx.x);
 }
 
 // ---------------------------------------------------------------- INT8 pass
-template <int B>
-__global__ __launch_bounds__(HQ_THREADS) void hq_int8_kernel(HQParams p) {
-  __shared__ uint4 lds[HQ_THREADS * 8];
-  __shared__ uint32_t rowmax[HQ_THREADS];
+// T threads per workgroup, rows_per_wg * cpr <= T chunks (the launcher picks
+// T in {64, 128, 192, 256} so that few lanes idle).
+template <int B, int T>
+__global__ __launch_bounds__(T) void hq_int8_kernel(HQParams p) {
+  __shared__ uint4 lds[T * 8];
+  __shared__ uint32_t rowmax[T];
   if (threadIdx.x < p.rows_per_wg) rowmax[threadIdx.x] = 0u;
   int row, col;
   bool valid;
   gelu_begin(p);
-  stage<true>(p, lds, row, col, valid);
+  stage<true, T>(p, lds, row, col, valid);
   __syncthreads();
   float v[64];
   load_chunk(lds, v, p.flags);
@@ -443,7 +461,7 @@ __global__ __launch_bounds__(HQ_THREADS) void hq_int8_kernel(HQParams p) {
   if (want_stats) {
     float my = valid ? ay : 0.0f;
     for (int i = 0; i < 64; ++i) sv = sv + ((i < nvalid) ? fabsf(v[i]) : 0.0f);
-    wg_stats_write(mx, sx, my, (double)(sv * yfac<B>()), p.stats_part + 4 * (int64_t)blockIdx.x);
+    wg_stats_write<T>(mx, sx, my, (double)(sv * yfac<B>()), p.stats_part + 4 * (int64_t)blockIdx.x);
   }
 }
 
@@ -536,6 +554,21 @@ __global__ __launch_bounds__(HQ_THREADS) void hq_mx_kernel(HQParams p) {
 }
 
 // ---------------------------------------------------------------- launcher
+// INT8 workgroup size for rows of cpr chunks (cpr <= 256): the T in
+// {64, 128, 192, 256} whose floor(T / cpr) whole rows leave the fewest lanes
+// idle, the larger T on ties.
+static int hq_int8_threads(int cpr) {
+  int best = 256;
+  double best_use = 0.0;
+  for (int T = 256; T >= 64; T -= 64) {
+    const int rows = T / cpr;
+    if (rows < 1) continue;
+    const double use = (double)(rows * cpr) / T;
+    if (use > best_use + 1e-12) { best_use = use; best = T; }
+  }
+  return best;
+}
+
 template <int B>
 static hipError_t launch_b(const HQParams& p, int fmt, bool amax_given, int grid, hipStream_t st) {
   const size_t shm = (p.flags & 4u) ? (size_t)kGeluTabBytes : 0;   // the GELU table
@@ -546,7 +579,11 @@ static hipError_t launch_b(const HQParams& p, int fmt, bool amax_given, int grid
     }
     hipLaunchKernelGGL(hq_nvfp4_kernel<B>, dim3(grid), dim3(HQ_THREADS), shm, st, p);
   } else if (fmt == 1) {
-    hipLaunchKernelGGL(hq_int8_kernel<B>, dim3(grid), dim3(HQ_THREADS), shm, st, p);
+    const int T = hq_int8_threads(p.cpr);
+    if (T == 64) hipLaunchKernelGGL((hq_int8_kernel<B, 64>), dim3(grid), dim3(64), shm, st, p);
+    else if (T == 128) hipLaunchKernelGGL((hq_int8_kernel<B, 128>), dim3(grid), dim3(128), shm, st, p);
+    else if (T == 192) hipLaunchKernelGGL((hq_int8_kernel<B, 192>), dim3(grid), dim3(192), shm, st, p);
+    else hipLaunchKernelGGL((hq_int8_kernel<B, 256>), dim3(grid), dim3(256), shm, st, p);
   } else if (fmt == 2) {
     hipLaunchKernelGGL(hq_bf16_kernel<B>, dim3(grid), dim3(HQ_THREADS), shm, st, p);
   } else if (fmt == 3) {
@@ -591,7 +628,7 @@ hipError_t launch_hadamard_quantize(const void* x, int64_t M, int64_t K, int64_t
   if (fmt != 1) {
     grid = (int)((p.total_chunks + HQ_THREADS - 1) / HQ_THREADS);
   } else {
-    p.rows_per_wg = std::max(1, HQ_THREADS / p.cpr);
+    p.rows_per_wg = std::max(1, hq_int8_threads(p.cpr) / p.cpr);
     grid = (int)((M + p.rows_per_wg - 1) / p.rows_per_wg);
   }
   char* wsb = static_cast<char*>(ws);

@@ -8,6 +8,21 @@
 
 namespace vdtq {
 
+// Compute units of the current device, cached per device; `fallback` when
+// the query fails.
+inline int device_cu_count(int fallback = 256) {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return fallback;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      return fallback;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
 size_t hq_workspace_bytes(int64_t M, int64_t K);
 hipError_t launch_hadamard_quantize(const void* x, int64_t M, int64_t K, int64_t ldx, int b, int fmt,
                                     unsigned flags, void* q, void* scales, float* ts,

@@ -7,6 +7,7 @@
 #include <algorithm>
 
 #include "device_common.h"
+#include "launch.h"
 #include "lds_dma.h"
 
 namespace vdtq {
@@ -224,17 +225,6 @@ inline void plan_pipe(GemmParams& p, int cus, int& dp_grid, int& sk_grid) {
 }
 
 // Compute units of the current device (cached per device).
-inline int cu_count() {
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return kGemmMaxGrid;
-  if (cached[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-      n = kGemmMaxGrid;
-    cached[dev] = n;
-  }
-  return cached[dev];
-}
+inline int cu_count() { return device_cu_count(kGemmMaxGrid); }
 
 }  // namespace vdtq
