@@ -534,7 +534,7 @@ def int8_threads(cpr):
 
 
 QUANT_BYTES = {"nvfp4": 2 + 0.5 + 1 / 16, "int8": 3.0, "mxfp4": 2 + 0.5 + 1 / 32, "mxfp8": 2 + 1 + 1 / 32}
-QUANT_KERNEL = {"nvfp4": "hq_nvfp4_kernel<64>", "int8": "hq_int8_kernel<64, 192>",
+QUANT_KERNEL = {"nvfp4": "hq_nvfp4_kernel<64, false>", "int8": "hq_int8_kernel<64, 192>",
                 "mxfp4": "hq_mx_kernel<64, false>", "mxfp8": "hq_mx_kernel<64, true>"}
 
 

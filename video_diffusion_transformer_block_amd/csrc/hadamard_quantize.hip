@@ -346,7 +346,9 @@ __device__ __forceinline__ void nvfp4_encode64(const float (&v)[64], const float
 }
 
 // ---------------------------------------------------------------- NVFP4 pass
-template <int B>
+// STATS: the fused statistics (flag 2) are compiled in only where asked for,
+// so the plain pass fits four waves per SIMD.
+template <int B, bool STATS>
 __global__ __launch_bounds__(HQ_THREADS) void hq_nvfp4_kernel(HQParams p) {
   __shared__ uint4 lds[HQ_THREADS * 8];
   __shared__ float inv_tab[128];
@@ -367,7 +369,7 @@ __global__ __launch_bounds__(HQ_THREADS) void hq_nvfp4_kernel(HQParams p) {
   float v[64];
   load_chunk(lds, v, p.flags);
   const int nvalid = valid ? min(64, p.K - col * 64) : 0;
-  const bool want_stats = (p.flags & 2u) != 0;
+  const bool want_stats = STATS && (p.flags & 2u) != 0;
   float mx = 0.0f, sx = 0.0f;
   if (want_stats) input_stats(v, nvalid, mx, sx);
   fwht<B>(v);
@@ -381,7 +383,14 @@ __global__ __launch_bounds__(HQ_THREADS) void hq_nvfp4_kernel(HQParams p) {
   float my = 0.0f, sy = 0.0f;
   nvfp4_encode64<B>(v, inv_tab, ok, d, want_stats, nvalid, words, sbytes, my, sy);
 
-  if (valid) {
+  if (valid && p.flat) {
+    // contiguous whole chunks: chunk g's codes at 32 g, its scales at 4 g
+    // (a workgroup-uniform base plus a 32-bit lane offset)
+    const int64_t wg0 = (int64_t)blockIdx.x * HQ_THREADS;
+    reinterpret_cast<uint4*>(p.q + wg0 * 32)[2 * threadIdx.x] = make_uint4(words[0], words[1], words[2], words[3]);
+    reinterpret_cast<uint4*>(p.q + wg0 * 32)[2 * threadIdx.x + 1] = make_uint4(words[4], words[5], words[6], words[7]);
+    reinterpret_cast<uint32_t*>(p.scales)[wg0 + threadIdx.x] = sbytes;
+  } else if (valid) {
     uint8_t* qrow = p.q + (int64_t)row * (p.K / 2) + col * 32;
     uint8_t* srow = reinterpret_cast<uint8_t*>(p.scales) + (int64_t)row * (p.K / 16) + col * 4;
     if (nvalid == 64 && (p.K % 32) == 0) {
@@ -577,7 +586,10 @@ static hipError_t launch_b(const HQParams& p, int fmt, bool amax_given, int grid
       hipLaunchKernelGGL(hq_amax_kernel<B>, dim3(grid), dim3(HQ_THREADS), shm, st, p);
       hipLaunchKernelGGL(hq_amax_final_kernel, dim3(1), dim3(kFinalThreads), 0, st, p.amax_part, grid, p.ts);
     }
-    hipLaunchKernelGGL(hq_nvfp4_kernel<B>, dim3(grid), dim3(HQ_THREADS), shm, st, p);
+    if (p.flags & 2u)
+      hipLaunchKernelGGL((hq_nvfp4_kernel<B, true>), dim3(grid), dim3(HQ_THREADS), shm, st, p);
+    else
+      hipLaunchKernelGGL((hq_nvfp4_kernel<B, false>), dim3(grid), dim3(HQ_THREADS), shm, st, p);
   } else if (fmt == 1) {
     const int T = hq_int8_threads(p.cpr);
     if (T == 64) hipLaunchKernelGGL((hq_int8_kernel<B, 64>), dim3(grid), dim3(64), shm, st, p);
