@@ -515,7 +515,7 @@ def hq_grid_work_items(M, K, fmt):
     record."""
     cpr = (K + 63) // 64
     if fmt != "int8":
-        return -(-M * cpr // 256) * 256
+        return -(-M * cpr // 128) * 128
     threads = int8_threads(cpr)
     rpw = max(1, threads // cpr)
     return -(-M // rpw) * threads

@@ -9,22 +9,24 @@
 // ratio of the input); fused into one pass as §4 / §四 describe.
 //
 // Design (HBM-bound pass, 2 B/element in, 0.5625 (NVFP4) or 1 (INT8) out):
-//   * A 256-thread workgroup owns 256 "chunks" of 64 consecutive elements of
-//     a row.  The chunks are staged through LDS with fully coalesced 16-byte
-//     loads (a wavefront reads 1 KB contiguous per instruction) and an XOR
-//     swizzle, so that each thread then reads its own 128-byte chunk without
-//     bank conflicts.
+//   * A 128-thread workgroup owns 128 "chunks" of 64 consecutive elements of
+//     a row (small workgroups: 16 KB of LDS each, so registers set the
+//     occupancy, and a short last wave).  The chunks are staged through LDS
+//     with fully coalesced 16-byte loads (a wavefront reads 1 KB contiguous
+//     per instruction) and an XOR swizzle, so that each thread then reads its
+//     own 128-byte chunk without bank conflicts.
 //   * Every thread keeps its 64 values in registers and runs the butterflies
 //     h = 1, 2, ..., min(b, 64)/2 in fp32 with no data exchange; for b = 128
 //     and 256 the remaining stages pair neighbouring lanes with one shuffle.
 //   * A 16-element NVFP4 group lies inside a thread, so group maxima are
-//     register-local.  Each group costs two correctly rounded divisions (the
-//     E4M3 scale and its reciprocal); each element costs one multiply and
-//     half of a hardware E2M1 conversion (v_cvt_scalef32_pk_fp4_f32, whose
-//     power-of-two scale operand also absorbs the 1/sqrt(b) normalisation
-//     when b is a power of four).
-//   * INT8: a workgroup owns whole rows; the row maximum is combined with
-//     LDS atomic max on the float bits (order independent), and rint is the
+//     register-local.  Each group costs one correctly rounded division (the
+//     E4M3 scale) and a table read (its reciprocal); each element costs one
+//     multiply and half of a hardware E2M1 conversion
+//     (v_cvt_scalef32_pk_fp4_f32, whose power-of-two scale operand also
+//     absorbs the 1/sqrt(b) normalisation when b is a power of four).
+//   * INT8: a workgroup owns whole rows (64 to 256 threads, sized so that
+//     few lanes idle); the row maximum is combined with LDS atomic max on
+//     the float bits (order independent), and rint is the
 //     2^23-magic-number add whose low byte is the two's complement code.
 //   * MX (OCP Microscaling v1.0 conversion; the variant of NVFP4 / INT8 for
 //     block-scaled matrix instructions): a thread's chunk is two 32-element
@@ -46,7 +48,7 @@
 
 namespace vdtq {
 
-constexpr int HQ_THREADS = 256;
+constexpr int HQ_THREADS = 128;
 
 struct HQParams {
   const uint16_t* x;
