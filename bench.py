@@ -523,14 +523,10 @@ def hq_grid_work_items(M, K, fmt):
 
 def int8_threads(cpr):
     """Workgroup size of the INT8 quantize kernel for rows of cpr chunks of
-    64 (the library's rule: the T in {64, 128, 192, 256} whose whole rows
-    leave the fewest lanes idle, the larger T on ties)."""
-    best, best_use = 256, 0.0
-    for t in (256, 192, 128, 64):
-        rows = t // cpr
-        if rows >= 1 and rows * cpr / t > best_use + 1e-12:
-            best, best_use = t, rows * cpr / t
-    return best
+    64 (the library's rule: 192 threads when their whole rows leave fewer
+    lanes idle than 256 threads' do, else 256)."""
+    r192, r256 = 192 // cpr, 256 // cpr
+    return 192 if r192 >= 1 and r192 * cpr * 256 > r256 * cpr * 192 else 256
 
 
 QUANT_BYTES = {"nvfp4": 2 + 0.5 + 1 / 16, "int8": 3.0, "mxfp4": 2 + 0.5 + 1 / 32, "mxfp8": 2 + 1 + 1 / 32}

@@ -24,8 +24,8 @@
 //     multiply and half of a hardware E2M1 conversion
 //     (v_cvt_scalef32_pk_fp4_f32, whose power-of-two scale operand also
 //     absorbs the 1/sqrt(b) normalisation when b is a power of four).
-//   * INT8: a workgroup owns whole rows (64 to 256 threads, sized so that
-//     few lanes idle); the row maximum is combined with LDS atomic max on
+//   * INT8: a workgroup owns whole rows (192 or 256 threads, whichever
+//     leaves fewer lanes idle); the row maximum is combined with LDS atomic max on
 //     the float bits (order independent), and rint is the
 //     2^23-magic-number add whose low byte is the two's complement code.
 //   * MX (OCP Microscaling v1.0 conversion; the variant of NVFP4 / INT8 for
@@ -416,7 +416,7 @@ __global__ __launch_bounds__(HQ_THREADS) void hq_nvfp4_kernel(HQParams p) {
 
 // ---------------------------------------------------------------- INT8 pass
 // T threads per workgroup, rows_per_wg * cpr <= T chunks (the launcher picks
-// T in {64, 128, 192, 256} so that few lanes idle).
+// T = 192 or 256, whichever leaves fewer lanes idle).
 template <int B, int T>
 __global__ __launch_bounds__(T) void hq_int8_kernel(HQParams p) {
   __shared__ uint4 lds[T * 8];
@@ -565,19 +565,13 @@ __global__ __launch_bounds__(HQ_THREADS) void hq_mx_kernel(HQParams p) {
 }
 
 // ---------------------------------------------------------------- launcher
-// INT8 workgroup size for rows of cpr chunks (cpr <= 256): the T in
-// {64, 128, 192, 256} whose floor(T / cpr) whole rows leave the fewest lanes
-// idle, the larger T on ties.
+// INT8 workgroup size for rows of cpr chunks (cpr <= 256): 192 threads when
+// floor(192 / cpr) whole rows leave fewer lanes idle than floor(256 / cpr)
+// rows in 256 threads, else 256 (64 or 128 threads never do better than 256,
+// which holds twice or four times their rows).
 static int hq_int8_threads(int cpr) {
-  int best = 256;
-  double best_use = 0.0;
-  for (int T = 256; T >= 64; T -= 64) {
-    const int rows = T / cpr;
-    if (rows < 1) continue;
-    const double use = (double)(rows * cpr) / T;
-    if (use > best_use + 1e-12) { best_use = use; best = T; }
-  }
-  return best;
+  const int r192 = 192 / cpr, r256 = 256 / cpr;
+  return (r192 >= 1 && r192 * cpr * 256 > r256 * cpr * 192) ? 192 : 256;
 }
 
 template <int B>
@@ -593,11 +587,10 @@ static hipError_t launch_b(const HQParams& p, int fmt, bool amax_given, int grid
     else
       hipLaunchKernelGGL((hq_nvfp4_kernel<B, false>), dim3(grid), dim3(HQ_THREADS), shm, st, p);
   } else if (fmt == 1) {
-    const int T = hq_int8_threads(p.cpr);
-    if (T == 64) hipLaunchKernelGGL((hq_int8_kernel<B, 64>), dim3(grid), dim3(64), shm, st, p);
-    else if (T == 128) hipLaunchKernelGGL((hq_int8_kernel<B, 128>), dim3(grid), dim3(128), shm, st, p);
-    else if (T == 192) hipLaunchKernelGGL((hq_int8_kernel<B, 192>), dim3(grid), dim3(192), shm, st, p);
-    else hipLaunchKernelGGL((hq_int8_kernel<B, 256>), dim3(grid), dim3(256), shm, st, p);
+    if (hq_int8_threads(p.cpr) == 192)
+      hipLaunchKernelGGL((hq_int8_kernel<B, 192>), dim3(grid), dim3(192), shm, st, p);
+    else
+      hipLaunchKernelGGL((hq_int8_kernel<B, 256>), dim3(grid), dim3(256), shm, st, p);
   } else if (fmt == 2) {
     hipLaunchKernelGGL(hq_bf16_kernel<B>, dim3(grid), dim3(HQ_THREADS), shm, st, p);
   } else if (fmt == 3) {
