@@ -262,6 +262,7 @@ def main():
     ffn_fusion = measure_ffn_fusion(torch, V, X, WM, M, args.steps) if want_mx else None
 
     dyn = None if args.no_dyn else measure_dyn(torch, V, synth)
+    dmpq = measure_dmpq(V)
     cpu = None if args.no_cpu_baseline else cpu_baseline(host, M, args.cpu_rows)
 
     line = {
@@ -294,9 +295,53 @@ def main():
                                          for n, d in v["per_linear"].items()}}
                    for k, v in results.items()},
         "dyn_schedule": dyn,
+        "dmpq_step": dmpq,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line))
+
+
+def measure_dmpq(V, blocks=30, steps=50, reps=20):
+    """The host scheduler alone: dmpq_step over 30 blocks x 50 steps of
+    seeded statistics (Gamma around the threshold, delta similarity around
+    tau, an occasional outlier spike), repeated; microseconds per call
+    through the ctypes binding, next to the cost of a trivial call through
+    the same binding (vdtq_outlier_ratio), which bounds the marshalling."""
+    rng = np.random.default_rng(9)
+    n = blocks * steps
+    g = 0.1 * np.exp(rng.normal(0.0, 0.5, n))
+    r = 0.05 * np.exp(rng.normal(0.0, 0.7, n))
+    stats = []
+    for i in range(n):
+        sin2 = 1.0e4
+        sd2 = (g[i] ** 2) * sin2
+        sp2 = 1.0e2
+        sdd2 = (r[i] ** 2) * sp2
+        stats.append([sd2, sin2, sdd2, sp2, 30.0, 1.0e4, 31.0, 1.0e4])
+    ratio = np.where(rng.random(n) < 0.01, 1.0e4, 10.0)
+    params = V.dmpq_params(gamma=0.1, tau=0.05, tau_acc=0.15, rho=1000.0)
+    acts = [0, 0, 0, 0]
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        states = [V.dmpq_state() for _ in range(blocks)]
+        last = [None] * blocks
+        for t in range(steps):
+            for b in range(blocks):
+                i = t * blocks + b
+                a = V.dmpq_step(params, states[b], last[b], float(ratio[i]))
+                acts[a] += 1
+                last[b] = None if a == 0 else stats[i]
+    dt = time.perf_counter() - t0
+    calls = reps * n
+    t1 = time.perf_counter()
+    for i in range(calls):
+        V.outlier_ratio(30.0, 1.0e4, 1000)
+    dt_floor = time.perf_counter() - t1
+    return {"us_per_call": round(1e6 * dt / calls, 3), "calls": calls,
+            "trivial_binding_call_us": round(1e6 * dt_floor / calls, 3),
+            "actions": {"skip": acts[0], "nvfp4": acts[1], "int8": acts[2], "bf16": acts[3]},
+            "note": "host only, through the ctypes binding (8 statistics marshalled per call); "
+                    "the C function itself is a few comparisons per call"}
 
 
 def measure_dyn(torch, V, synth, blocks=30, steps=50, M=4446, hidden=1920):
