@@ -259,6 +259,7 @@ def main():
         del src, dst
 
     bsroof = measure_block_stats(torch, V, X["qkv"], Y["ffn_down"], M * hidden, args.steps)
+    bf16ctx = measure_bf16_context(torch, X, host, linears, M, args.steps, up)
     ffn_fusion = measure_ffn_fusion(torch, V, X, WM, M, args.steps) if want_mx else None
 
     dyn = None if args.no_dyn else measure_dyn(torch, V, synth)
@@ -287,6 +288,7 @@ def main():
         "quantize_roofline": qroof,
         "mx_gemm_roofline": mx_roof or None,
         "block_stats_roofline": bsroof,
+        "bf16_context": bf16ctx,
         "ffn_fusion": ffn_fusion,
         "sweeps": {k: {"tops": round(v["tops"], 2), "ms_per_step": round(v["ms_per_step"], 4),
                        "gemm_tflops": round(total_flops / (sum(d["gemm_ms"] for d in v["per_linear"].values())
@@ -515,6 +517,38 @@ def gemm_call_traffic(rec, afmt):
                 if name.startswith(f"qgemm_pipe_kernel<{afmt}, false"):
                     calls += e["dispatches"]
     return round(total / calls) if calls else None
+
+
+def measure_bf16_context(torch, X, host, linears, M, steps, up):
+    """Context row, not a target: the four linears as plain bf16 GEMMs in
+    torch (hipBLASLt), Y = X W^T with the unquantized bf16 weights, the
+    weight operand made contiguous as [K, N] first.  HIP events around 10
+    launches, median per linear."""
+    per = {}
+    total_ms, total_flops = 0.0, 0.0
+    for name, K, N in linears:
+        wt = up(host[name][1]).t().contiguous()          # [K, N]
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=X[name].device)
+        torch.mm(X[name], wt, out=y)
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(max(3, steps // 4)):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(10):
+                torch.mm(X[name], wt, out=y)
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1) / 10)
+        ms = float(np.median(times))
+        f = 2.0 * M * N * K
+        per[name] = {"ms": round(ms, 4), "tflops": round(f / (ms * 1e-3) / 1e12, 1)}
+        total_ms += ms
+        total_flops += f
+        del wt, y
+    return {"what": "torch.mm bf16 (hipBLASLt), unquantized weights, same shapes; context only",
+            "per_linear": per, "gemm_ms": round(total_ms, 4),
+            "tops": round(total_flops / (total_ms * 1e-3) / 1e12, 1)}
 
 
 def measure_block_stats(torch, V, inp, out, n, steps):
