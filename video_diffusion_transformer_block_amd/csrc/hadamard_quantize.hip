@@ -83,9 +83,8 @@ __device__ __forceinline__ void divmod_cpr(int64_t g, const HQParams& p, int& ro
 // otherwise the workgroup owns flat chunk ids [T wg, T wg + T).
 template <bool ROWS, int T = HQ_THREADS>
 __device__ __forceinline__ void stage(const HQParams& p, uint4* lds, int& my_row, int& my_col,
-                                      bool& my_valid) {
+                                      bool& my_valid, int wg = blockIdx.x) {
   const int t = threadIdx.x;
-  const int wg = blockIdx.x;
   const int j = t & 7;
   int row, col;
   int c0 = t >> 3;
@@ -233,6 +232,10 @@ __device__ void wg_stats_write(double mx, double sx, double my, double sy, doubl
 }
 
 // ---------------------------------------------------------------- amax pre-pass
+// The workgroups walk the tensor from its end (workgroup i takes tile
+// G - 1 - i): the quantize pass that follows starts at the front, which is
+// then what the last-level cache holds.  The maximum does not depend on the
+// order.
 template <int B>
 __global__ __launch_bounds__(HQ_THREADS) void hq_amax_kernel(HQParams p) {
   __shared__ uint4 lds[HQ_THREADS * 8];
@@ -240,7 +243,7 @@ __global__ __launch_bounds__(HQ_THREADS) void hq_amax_kernel(HQParams p) {
   int row, col;
   bool valid;
   gelu_begin(p);
-  stage<false>(p, lds, row, col, valid);
+  stage<false>(p, lds, row, col, valid, (int)(gridDim.x - 1 - blockIdx.x));
   __syncthreads();
   float v[64];
   load_chunk(lds, v, p.flags);
