@@ -106,6 +106,28 @@ def mfma_table(path: str, simds: int = 1024, xcds: int = 8) -> str:
     return "\n".join(out)
 
 
+def l2_table(path: str) -> str:
+    """Per (kernel, grid): L2 (TCC) hits and misses per dispatch, summed over
+    the channels, and the hit rate = hits / (hits + misses)."""
+    per = collections.defaultdict(lambda: collections.defaultdict(list))
+    for r in csv.DictReader(open(path)):
+        n = short_name(r["Kernel_Name"])
+        if "FillFunctor" in n or "copyBuffer" in n:
+            continue
+        per[(n, int(r["Grid_Size"]))][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    out = ["| kernel | grid (work-items) | dispatches | L2 hits (M) | L2 misses (M) | hit rate % |",
+           "|---|---|---|---|---|---|"]
+    for k, c in sorted(per.items()):
+        hits = c.get("TCC_HIT_sum") or c.get("TCC_HIT")
+        miss = c.get("TCC_MISS_sum") or c.get("TCC_MISS")
+        if not hits or not miss:
+            continue
+        h, m = _mean(hits), _mean(miss)
+        rate = 100.0 * h / (h + m) if h + m else 0.0
+        out.append(f"| {k[0]} | {k[1]} | {len(hits)} | {h / 1e6:.2f} | {m / 1e6:.2f} | {rate:.1f} |")
+    return "\n".join(out)
+
+
 def _counter_values(path: str, counter: str):
     """Counter values (KiB) per dispatch, keyed by (kernel name, grid size in
     work-items)."""
@@ -186,6 +208,8 @@ def main(argv=None):
     t.add_argument("csv")
     mf = sub.add_parser("mfma")
     mf.add_argument("csv")
+    l2 = sub.add_parser("l2")
+    l2.add_argument("csv")
     b = sub.add_parser("traffic")
     b.add_argument("fetch_csv")
     b.add_argument("write_csv")
@@ -199,6 +223,8 @@ def main(argv=None):
         print(trace_table(args.csv))
     elif args.cmd == "mfma":
         print(mfma_table(args.csv))
+    elif args.cmd == "l2":
+        print(l2_table(args.csv))
     else:
         rec = traffic(args.fetch_csv, args.write_csv, args.copy_bytes, args.copy_kernel)
         with open(args.out, "w") as fh:
