@@ -68,6 +68,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=8192)
     ap.add_argument("--no-dyn", action="store_true", help="skip the closed-loop schedule measurement")
+    ap.add_argument("--no-stress", action="store_true", help="skip the 1080p FFN measurement")
     ap.add_argument("--sweeps", default=",".join(SWEEPS),
                     help="comma-separated subset of " + ",".join(SWEEPS) + " (the first listed is the headline)")
     ap.add_argument("--calibration-copy", action="store_true",
@@ -260,6 +261,7 @@ def main():
 
     bsroof = measure_block_stats(torch, V, X["qkv"], Y["ffn_down"], M * hidden, args.steps)
     bf16ctx = measure_bf16_context(torch, X, host, linears, M, args.steps, up)
+    stress = None if args.no_stress else measure_1080p(torch, V, args.steps)
     ffn_fusion = measure_ffn_fusion(torch, V, X, WM, M, args.steps) if want_mx else None
 
     dyn = None if args.no_dyn else measure_dyn(torch, V, synth)
@@ -289,6 +291,7 @@ def main():
         "mx_gemm_roofline": mx_roof or None,
         "block_stats_roofline": bsroof,
         "bf16_context": bf16ctx,
+        "stress_1080p": stress,
         "ffn_fusion": ffn_fusion,
         "sweeps": {k: {"tops": round(v["tops"], 2), "ms_per_step": round(v["ms_per_step"], 4),
                        "gemm_tflops": round(total_flops / (sum(d["gemm_ms"] for d in v["per_linear"].values())
@@ -517,6 +520,83 @@ def gemm_call_traffic(rec, afmt):
                 if name.startswith(f"qgemm_pipe_kernel<{afmt}, false"):
                     calls += e["dispatches"]
     return round(total / calls) if calls else None
+
+
+def measure_1080p(torch, V, steps, M=13 * 68 * 120 + 226, hidden=3072, ffn=12288):
+    """The 1080p stress workload: 49 frames at 1088x1920 -> 106080 latent
+    tokens + 226 text tokens, hidden 3072, FFN 3072 -> 12288 -> 3072.  Each
+    FFN linear runs both ways: NVFP4 quantize (tensor amax computed) + W4A4,
+    and INT8 quantize + W4A8; each quantize pass is also timed alone with the
+    amax supplied.  Activations are Laplace(0, 1) with 0.5% of the channels
+    x30, weights N(0, 0.02), drawn by torch's seeded GPU generator (the
+    parity tests take the numpy recipe on sampled rows).  HIP events around
+    3 launches, median."""
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+
+    def laplace(shape, seed):
+        gen.manual_seed(seed)
+        x = torch.empty(shape, device=dev).exponential_(generator=gen)
+        x -= torch.empty(shape, device=dev).exponential_(generator=gen)
+        return x
+
+    def activations(K, seed):
+        x = laplace((M, K), seed)
+        gen.manual_seed(seed + 1)
+        ch = torch.randperm(K, generator=gen, device=dev)[:round(0.005 * K)]
+        x[:, ch] *= 30.0
+        return x.to(torch.bfloat16)
+
+    def timed(fn, reps=3):
+        fn()
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(max(3, steps // 6)):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1) / reps)
+        return float(np.median(times))
+
+    res = {"workload": f"1080p FFN: M={M} tokens (13x68x120 + 226), {hidden} -> {ffn} -> {hidden}, "
+                       "Laplace(0,1) activations with 0.5% channels x30, N(0,0.02) weights (torch generator)"}
+    for name, K, N, seed in (("ffn_up", hidden, ffn, 7100), ("ffn_down", ffn, hidden, 7200)):
+        x = activations(K, seed)
+        gen.manual_seed(seed + 2)
+        w = (torch.randn((N, K), generator=gen, device=dev) * 0.02).to(torch.bfloat16)
+        wq = V.hadamard_quantize(w, HAD_BLOCK, "nvfp4")
+        del w
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        flops = 2.0 * M * N * K
+        e = {}
+        a4 = V.hadamard_quantize(x, HAD_BLOCK, "nvfp4")
+        a8 = V.hadamard_quantize(x, HAD_BLOCK, "int8")
+        q4 = timed(lambda: V.hadamard_quantize(x, HAD_BLOCK, "nvfp4", amax="given", out=a4))
+        q4c = timed(lambda: V.hadamard_quantize(x, HAD_BLOCK, "nvfp4", out=a4))
+        q8 = timed(lambda: V.hadamard_quantize(x, HAD_BLOCK, "int8", out=a8))
+        g4 = timed(lambda: V.qgemm_w4a4(a4, wq, None, "bf16", y=y))
+        g8 = timed(lambda: V.qgemm_w4a8(a8, wq, None, "bf16", y=y))
+        elems = M * K
+        e["quantize_nvfp4"] = {"us": round(1e3 * q4, 1), "gbs": round(QUANT_BYTES["nvfp4"] * elems / (q4 * 1e-3) / 1e9, 1),
+                               "frac_hbm": round(QUANT_BYTES["nvfp4"] * elems / (q4 * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+        e["quantize_nvfp4_amax_computed_us"] = round(1e3 * q4c, 1)
+        b8 = (QUANT_BYTES["int8"] + 4.0 / K) * elems
+        e["quantize_int8"] = {"us": round(1e3 * q8, 1), "gbs": round(b8 / (q8 * 1e-3) / 1e9, 1),
+                              "frac_hbm": round(b8 / (q8 * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+        e["w4a4"] = {"ms": round(g4, 4), "tflops": round(flops / (g4 * 1e-3) / 1e12, 1),
+                     "frac_fp16_peak": round(flops / (g4 * 1e-3) / 1e12 / PEAK_FP16_MFMA_TFLOPS, 4)}
+        e["w4a8"] = {"ms": round(g8, 4), "tflops": round(flops / (g8 * 1e-3) / 1e12, 1),
+                     "frac_fp16_peak": round(flops / (g8 * 1e-3) / 1e12 / PEAK_FP16_MFMA_TFLOPS, 4)}
+        res[name] = e
+        del x, wq, y, a4, a8
+        torch.cuda.empty_cache()
+        print(f"[bench] 1080p {name}: nvfp4 quant {e['quantize_nvfp4']['us']} us, int8 quant "
+              f"{e['quantize_int8']['us']} us, W4A4 {e['w4a4']['tflops']} / W4A8 {e['w4a8']['tflops']} TFLOP/s",
+              file=sys.stderr, flush=True)
+    return res
 
 
 def measure_bf16_context(torch, X, host, linears, M, steps, up):
