@@ -25,8 +25,8 @@
 //     (v_cvt_scalef32_pk_fp4_f32, whose power-of-two scale operand also
 //     absorbs the 1/sqrt(b) normalisation when b is a power of four).
 //   * INT8: a workgroup owns whole rows (192 or 256 threads, whichever
-//     leaves fewer lanes idle); the row maximum is combined with LDS atomic max on
-//     the float bits (order independent), and rint is the
+//     leaves fewer lanes idle); the row maximum is combined with LDS atomic
+//     max on the float bits (order independent), and rint is the
 //     2^23-magic-number add whose low byte is the two's complement code.
 //   * MX (OCP Microscaling v1.0 conversion; the variant of NVFP4 / INT8 for
 //     block-scaled matrix instructions): a thread's chunk is two 32-element
@@ -172,8 +172,8 @@ __device__ __forceinline__ uint32_t gelu_word(uint32_t w) {
   return gelu_bf16_bits(w & 0xFFFFu, gelu_lds) | (gelu_bf16_bits(w >> 16, gelu_lds) << 16);
 }
 
-__device__ __forceinline__ void load_chunk(const uint4* lds, float (&v)[64], unsigned flags,
-                                           int t = threadIdx.x) {
+__device__ __forceinline__ void load_chunk(const uint4* lds, float (&v)[64], unsigned flags) {
+  const int t = threadIdx.x;
   const bool gelu = (flags & 4u) != 0;
 #pragma unroll
   for (int jj = 0; jj < 8; ++jj) {
