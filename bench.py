@@ -21,7 +21,16 @@ seeded synthetic bf16 (Laplace(0,1) with 0.5% of the channels x30), resident
 in HBM before the timed region; weights are random N(0, 0.02) prepared
 offline (Hadamard-rotated + NVFP4) before timing.
 
+Besides the step, the JSON line carries: the dominant GEMM call against the
+fp16 MFMA peak (roofline, with counter traffic while the committed record
+matches the sources), each quantize pass against HBM peak, the MX GEMMs
+against their own peaks, block_stats against HBM peak, the same four GEMMs
+in bf16 through torch / hipBLASLt (context), the 1080p FFN stress shape,
+the fused FFN-up -> FFN-down epilogue, the closed-loop schedule study, the
+host cost of dmpq_step, and the CPU oracle on a bounded sample.
+
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline]
+                       [--no-dyn] [--no-stress] [--sweeps a,b,...]
 """
 from __future__ import annotations
 
