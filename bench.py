@@ -208,22 +208,24 @@ def main():
     kern = {}
     for name, d in head["per_linear"].items():
         k = GEMM_OF[d["fmt"]]
-        kk = kern.setdefault(k, {"ms": 0.0, "flops": 0.0, "launches": 0})
+        kk = kern.setdefault(k, {"ms": 0.0, "flops": 0.0, "launches": 0, "shapes": []})
         kk["ms"] += d["gemm_ms"]
         kk["flops"] += flops[name]
         kk["launches"] += 1
+        kk["shapes"].append(next((K, N) for n, K, N in linears if n == name))
     dom = max(kern, key=lambda k: kern[k]["ms"])
     dk = kern[dom]
     achieved = dk["flops"] / (dk["ms"] * 1e-3) / 1e12
     # HBM bytes per call of the dominant GEMM from the committed counter runs
     # (FETCH_SIZE + WRITE_SIZE, copy-calibrated), while its sources match.  A
     # call is one data-parallel kernel plus, when the last wave is split along
-    # K, the slice kernel and the reduce kernel: all of them are summed and
-    # divided by the number of calls (= data-parallel dispatches).
+    # K, the slice kernel and the reduce kernel: the dispatches of exactly
+    # those grids are summed per call and averaged over the step's calls.
     from video_diffusion_transformer_block_amd import profiling
     rec = profiling.load_traffic(os.path.join(ROOT, "profiles", "traffic_5b_mixed.json"))
     afmt = {"qgemm_w4a4": 0, "qgemm_w4a8": 1}.get(dom)
-    traffic = gemm_call_traffic(rec, afmt) if rec is not None and afmt is not None else None
+    traffic = (gemm_call_traffic(rec, afmt, M, dk["shapes"])
+               if rec is not None and afmt is not None else None)
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1),
                 "peak": PEAK_FP16_MFMA_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_FP16_MFMA_TFLOPS, 4), "traffic": traffic,
@@ -517,18 +519,48 @@ def measure_dyn(torch, V, synth, blocks=30, steps=50, M=4446, hidden=1920):
                             "bf16_cache_bytes_per_block": M * hidden * 2}}
 
 
-def gemm_call_traffic(rec, afmt):
+def gemm_call_grids(M, N, K, cus=256):
+    """Work-items of the kernels of one pipelined GEMM call, as the library's
+    launcher plans it (256 x 256 tiles, 256-thread workgroups, at most one
+    workgroup per CU): the data-parallel kernel, and for a split last wave
+    the K-slice kernel and the reduce kernel (64 workgroups per tile)."""
+    tiles = -(-M // 256) * -(-N // 256)
+    nk = K // 128
+    g = max(1, min(cus, 256))
+    left = tiles % g
+    slices = min(g // left, nk) if left else 0
+    slice_nk = -(-nk // slices) if slices else 0
+    if slices:
+        slices = -(-nk // slice_nk)
+    split = slices >= 2 and slice_nk + 3 < nk
+    sk = left if split else 0
+    return {"dp": (tiles - sk) * 256, "sk": sk * slices * 256 if split else 0, "reduce": sk * 64 * 256}
+
+
+def gemm_call_traffic(rec, afmt, M, shapes):
     """Mean FETCH+WRITE bytes per GEMM call of activation format afmt (0
-    NVFP4, 1 INT8) in a counter record: every dispatch of that format's GEMM
-    kernels summed, over the number of data-parallel dispatches (one per call)."""
-    total, calls = 0.0, 0
-    for name, k in rec["kernels"].items():
-        if name.startswith(f"qgemm_pipe_kernel<{afmt}, ") or name == f"qgemm_reduce_kernel<{afmt}>":
-            for e in k["grids"].values():
-                total += e["bytes"] * e["dispatches"]
-                if name.startswith(f"qgemm_pipe_kernel<{afmt}, false"):
-                    calls += e["dispatches"]
-    return round(total / calls) if calls else None
+    NVFP4, 1 INT8) over the calls of the given (K, N) shapes at M tokens:
+    per call, the record's per-dispatch bytes of its data-parallel, K-slice
+    and reduce grids (None when a grid is missing from the record)."""
+    k = rec["kernels"]
+
+    def grid_bytes(prefix, grid):
+        for name, e in k.items():
+            if name.startswith(prefix) and str(grid) in e["grids"]:
+                return e["grids"][str(grid)]["bytes"]
+        return None
+
+    per_call = []
+    for K, N in shapes:
+        g = gemm_call_grids(M, N, K)
+        parts = [grid_bytes(f"qgemm_pipe_kernel<{afmt}, false", g["dp"])]
+        if g["sk"]:
+            parts += [grid_bytes(f"qgemm_pipe_kernel<{afmt}, true", g["sk"]),
+                      grid_bytes(f"qgemm_reduce_kernel<{afmt}>", g["reduce"])]
+        if any(b is None for b in parts):
+            return None
+        per_call.append(sum(parts))
+    return round(sum(per_call) / len(per_call)) if per_call else None
 
 
 def measure_1080p(torch, V, steps, M=13 * 68 * 120 + 226, hidden=3072, ffn=12288):
