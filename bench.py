@@ -193,12 +193,18 @@ def main():
         torch.cuda.synchronize()
         wall = time.perf_counter() - tw
         ms = ev0.elapsed_time(ev1) / args.steps
+        # per-step times on the GPU timeline: from one step's first event to
+        # the next step's (the last step ends at ev1)
+        nlin = len(linears)
+        starts = [rec[i * nlin][2] for i in range(args.steps)] + [ev1]
+        step_ms = np.array([starts[i].elapsed_time(starts[i + 1]) for i in range(args.steps)])
+        pct = {f"p{q}": round(float(np.percentile(step_ms, q)), 4) for q in (10, 50, 90)}
         per = {}
         for name, fmt, e0, e1, e2 in rec:
             d = per.setdefault(name, {"fmt": fmt, "quant_ms": 0.0, "gemm_ms": 0.0})
             d["quant_ms"] += e0.elapsed_time(e1) / args.steps
             d["gemm_ms"] += e1.elapsed_time(e2) / args.steps
-        results[sweep] = {"ms_per_step": ms, "wall_ms_per_step": 1e3 * wall / args.steps,
+        results[sweep] = {"ms_per_step": ms, "wall_ms_per_step": 1e3 * wall / args.steps, "step_ms_pct": pct,
                           "tops": total_flops / (ms * 1e-3) / 1e12, "per_linear": per}
         print(f"[bench] {sweep}: {ms:.3f} ms/step, {results[sweep]['tops']:.1f} TOPS", file=sys.stderr,
               flush=True)
@@ -304,7 +310,9 @@ def main():
         "bf16_context": bf16ctx,
         "stress_1080p": stress,
         "ffn_fusion": ffn_fusion,
+        "step_ms_pct": head["step_ms_pct"],
         "sweeps": {k: {"tops": round(v["tops"], 2), "ms_per_step": round(v["ms_per_step"], 4),
+                       "step_ms_pct": v["step_ms_pct"],
                        "gemm_tflops": round(total_flops / (sum(d["gemm_ms"] for d in v["per_linear"].values())
                                                            * 1e-3) / 1e12, 1),
                        "per_linear_ms": {n: [round(d["quant_ms"], 4), round(d["gemm_ms"], 4)]
