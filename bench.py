@@ -739,25 +739,29 @@ def int8_threads(cpr):
 
 QUANT_BYTES = {"nvfp4": 2 + 0.5 + 1 / 16, "int8": 3.0, "mxfp4": 2 + 0.5 + 1 / 32, "mxfp8": 2 + 1 + 1 / 32}
 QUANT_KERNEL = {"nvfp4": "hq_nvfp4_kernel<64, false>", "int8": "hq_int8_kernel<64, 192>",
+                "nvfp4_amax": "hq_amax_kernel<64> + hq_amax_final_kernel + hq_nvfp4_kernel<64, false>",
                 "mxfp4": "hq_mx_kernel<64, false>", "mxfp8": "hq_mx_kernel<64, true>"}
 
 
 def measure_quantize(torch, V, X, M, steps, with_mx=False):
     """hadamard_quantize with the tensor amax supplied (the single fused
-    kernel).  The launches are captured in a graph and replayed, so the
-    per-launch time (HIP events around the replays / launches) excludes host
-    launch gaps.  The 3072-wide inputs rotate over the three K=3072
-    activations (327 MB of bf16 per rotation, above the 256 MB last-level
-    cache); the 12288-wide FFN-down input is 437 MB."""
+    kernel), and NVFP4 with the tensor amax computed (pre-pass, its final
+    reduction and the pass: 2 more bytes per element, key nvfp4_amax).  The
+    launches are captured in a graph and replayed, so the per-launch time
+    (HIP events around the replays / launches) excludes host launch gaps.
+    The 3072-wide inputs rotate over the three K=3072 activations (327 MB of
+    bf16 per rotation, above the 256 MB last-level cache); the 12288-wide
+    FFN-down input is 437 MB."""
     out = {}
     for K, names in ((3072, ["qkv", "out", "ffn_up"]), (12288, ["ffn_down"])):
         elems = M * K
-        for fmt in ("nvfp4", "int8") + (("mxfp4", "mxfp8") if with_mx else ()):
-            bpe = QUANT_BYTES[fmt]
+        for key in ("nvfp4", "nvfp4_amax", "int8") + (("mxfp4", "mxfp8") if with_mx else ()):
+            fmt = "nvfp4" if key == "nvfp4_amax" else key
+            bpe = QUANT_BYTES[fmt] + (2.0 if key == "nvfp4_amax" else 0.0)
             extra = 0 if fmt == "nvfp4" else 4 * M / elems
             # buffers allocated (and the tensor amax written) before capture
             outs = [V.hadamard_quantize(X[n], HAD_BLOCK, fmt) for n in names]
-            amax = "given" if fmt == "nvfp4" else None
+            amax = "given" if key == "nvfp4" else None
             n_launch = 12
             torch.cuda.synchronize()
             g = torch.cuda.CUDAGraph()
@@ -777,11 +781,15 @@ def measure_quantize(torch, V, X, M, steps, with_mx=False):
                 times.append(e0.elapsed_time(e1) / n_launch)
             us = 1e3 * float(np.median(times))
             gbs = (bpe + extra) * elems / (us * 1e-6) / 1e9
-            out[f"{fmt}_K{K}"] = {"bound": "hbm", "kernel": QUANT_KERNEL[fmt], "achieved": round(gbs, 1),
+            out[f"{key}_K{K}"] = {"bound": "hbm", "kernel": QUANT_KERNEL[key], "achieved": round(gbs, 1),
                                   "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                                   "traffic": None, "avg_launch_us": round(us, 2),
                                   "bytes_per_launch": (bpe + extra) * elems, "shape": [M, K],
                                   "grid_work_items": hq_grid_work_items(M, K, fmt)}
+            if key == "nvfp4_amax":
+                out[f"{key}_K{K}"]["note"] = ("algorithmic bytes (2 reads of X): the pass re-reads the tensor the "
+                                              "pre-pass just read, and up to 256 MB of that comes from the "
+                                              "last-level cache, not HBM")
             del g
     return out
 
