@@ -80,10 +80,16 @@ __device__ __forceinline__ void divmod_cpr(int64_t g, const HQParams& p, int& ro
 // Loads the workgroup's T chunks (T = its thread count) into LDS (zeros
 // where the chunk or the 8-element slot lies outside X) and returns this
 // thread's own chunk coordinates.  ROWS: chunks are rows_per_wg whole rows;
-// otherwise the workgroup owns flat chunk ids [T wg, T wg + T).
-template <bool ROWS, int T = HQ_THREADS>
+// otherwise the workgroup owns flat chunk ids [T wg, T wg + T).  mid() runs
+// after the global loads are issued and before their data is needed, so
+// independent set-up work overlaps their latency.
+struct NoMid {
+  __device__ void operator()() const {}
+};
+
+template <bool ROWS, int T = HQ_THREADS, class Mid = NoMid>
 __device__ __forceinline__ void stage(const HQParams& p, uint4* lds, int& my_row, int& my_col,
-                                      bool& my_valid, int wg = blockIdx.x) {
+                                      bool& my_valid, int wg = blockIdx.x, Mid mid = Mid()) {
   const int t = threadIdx.x;
   const int j = t & 7;
   int row, col;
@@ -101,6 +107,7 @@ __device__ __forceinline__ void stage(const HQParams& p, uint4* lds, int& my_row
     for (int i = 0; i < 8; ++i)
       buf[i] = (c0 + (T / 8) * i < lim) ? *reinterpret_cast<const uint4*>(base + i * ((T / 8) * 64))
                                    : make_uint4(0u, 0u, 0u, 0u);
+    mid();
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int c = c0 + (T / 8) * i;
@@ -134,6 +141,7 @@ __device__ __forceinline__ void stage(const HQParams& p, uint4* lds, int& my_row
     col += T / 8;
     while (col >= p.cpr) { col -= p.cpr; ++row; }
   }
+  mid();
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int c = c0 + (T / 8) * i;
@@ -357,19 +365,23 @@ template <int B, bool STATS>
 __global__ __launch_bounds__(HQ_THREADS) void hq_nvfp4_kernel(HQParams p) {
   __shared__ uint4 lds[HQ_THREADS * 8];
   __shared__ float inv_tab[128];
-  const float amax = p.ts[0];
-  const bool ok = nvfp4_amax_ok(amax);
-  const float gs = ok ? amax / 2688.0f : 1.0f;
-  // RN(1 / s_dec) for every E4M3 code (s_dec = RN(e4m3 * gs), 0 -> 0): the
-  // per-group reciprocal becomes a table read
-  if (threadIdx.x < 128) {
+  float amax = 0.0f, gs = 1.0f;
+  bool ok = false;
+  // under the chunk loads: the tensor scale, and RN(1 / s_dec) for every
+  // E4M3 code (s_dec = RN(e4m3 * gs), 0 -> 0), so that the per-group
+  // reciprocal is a table read (one entry per thread)
+  static_assert(HQ_THREADS == 128, "one reciprocal-table entry per thread");
+  auto scale_setup = [&]() {
+    amax = p.ts[0];
+    ok = nvfp4_amax_ok(amax);
+    gs = ok ? amax / 2688.0f : 1.0f;
     const float sd = e4m3_decode_pos(threadIdx.x) * gs;
     inv_tab[threadIdx.x] = sd != 0.0f ? 1.0f / sd : 0.0f;
-  }
+  };
   int row, col;
   bool valid;
   gelu_begin(p);
-  stage<false>(p, lds, row, col, valid);
+  stage<false>(p, lds, row, col, valid, blockIdx.x, scale_setup);
   __syncthreads();
   float v[64];
   load_chunk(lds, v, p.flags);
