@@ -159,8 +159,9 @@ __device__ __forceinline__ void stage(const HQParams& p, uint4* lds, int& my_row
 
 // With the GELU flag (4) a one-block-per-256-entries kernel first writes the
 // GELU table to the workspace; each quantize workgroup copies it into
-// dynamic LDS (gelu_lds) before staging; load_chunk maps each staged
-// element through it as it widens the chunk.
+// dynamic LDS (gelu_lds) while its chunk loads are in flight (the stage()
+// hook); load_chunk maps each staged element through it as it widens the
+// chunk.
 extern __shared__ __attribute__((aligned(16))) uint16_t gelu_lds[];
 
 __global__ __launch_bounds__(256) void gelu_table_kernel(uint16_t* tab) {
@@ -250,8 +251,7 @@ __global__ __launch_bounds__(HQ_THREADS) void hq_amax_kernel(HQParams p) {
   __shared__ float wred[HQ_THREADS / 64];
   int row, col;
   bool valid;
-  gelu_begin(p);
-  stage<false>(p, lds, row, col, valid, (int)(gridDim.x - 1 - blockIdx.x));
+  stage<false>(p, lds, row, col, valid, (int)(gridDim.x - 1 - blockIdx.x), [&]() { gelu_begin(p); });
   __syncthreads();
   float v[64];
   load_chunk(lds, v, p.flags);
@@ -380,8 +380,10 @@ __global__ __launch_bounds__(HQ_THREADS) void hq_nvfp4_kernel(HQParams p) {
   };
   int row, col;
   bool valid;
-  gelu_begin(p);
-  stage<false>(p, lds, row, col, valid, blockIdx.x, scale_setup);
+  stage<false>(p, lds, row, col, valid, blockIdx.x, [&]() {
+    gelu_begin(p);
+    scale_setup();
+  });
   __syncthreads();
   float v[64];
   load_chunk(lds, v, p.flags);
@@ -439,8 +441,7 @@ __global__ __launch_bounds__(T) void hq_int8_kernel(HQParams p) {
   if (threadIdx.x < p.rows_per_wg) rowmax[threadIdx.x] = 0u;
   int row, col;
   bool valid;
-  gelu_begin(p);
-  stage<true, T>(p, lds, row, col, valid);
+  stage<true, T>(p, lds, row, col, valid, blockIdx.x, [&]() { gelu_begin(p); });
   __syncthreads();
   float v[64];
   load_chunk(lds, v, p.flags);
@@ -499,8 +500,7 @@ __global__ __launch_bounds__(HQ_THREADS) void hq_bf16_kernel(HQParams p) {
   __shared__ uint4 lds[HQ_THREADS * 8];
   int row, col;
   bool valid;
-  gelu_begin(p);
-  stage<false>(p, lds, row, col, valid);
+  stage<false>(p, lds, row, col, valid, blockIdx.x, [&]() { gelu_begin(p); });
   __syncthreads();
   float v[64];
   load_chunk(lds, v, p.flags);
@@ -539,8 +539,7 @@ __global__ __launch_bounds__(HQ_THREADS) void hq_mx_kernel(HQParams p) {
   __shared__ uint4 lds[HQ_THREADS * 8];
   int row, col;
   bool valid;
-  gelu_begin(p);
-  stage<false>(p, lds, row, col, valid);
+  stage<false>(p, lds, row, col, valid, blockIdx.x, [&]() { gelu_begin(p); });
   __syncthreads();
   float v[64];
   load_chunk(lds, v, p.flags);
