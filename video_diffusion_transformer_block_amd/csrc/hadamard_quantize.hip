@@ -87,6 +87,10 @@ struct NoMid {
   __device__ void operator()() const {}
 };
 
+// Word 3 of a raw (unstrided, unswizzled) CDNA buffer resource: 32-bit data
+// format, the one untyped loads need to read anything but zeros.
+constexpr int kRawBufferWord3 = 0x00020000;
+
 template <bool ROWS, int T = HQ_THREADS, class Mid = NoMid>
 __device__ __forceinline__ void stage(const HQParams& p, uint4* lds, int& my_row, int& my_col,
                                       bool& my_valid, int wg = blockIdx.x, Mid mid = Mid()) {
@@ -101,12 +105,19 @@ __device__ __forceinline__ void stage(const HQParams& p, uint4* lds, int& my_row
     const int64_t g0 = ROWS ? (int64_t)wg * p.rows_per_wg * p.cpr : (int64_t)wg * T;
     const int64_t left = p.total_chunks - g0;
     const int lim = (int)min<int64_t>(chunk_limit, left);
-    const uint16_t* base = p.x + (g0 + c0) * 64 + 8 * j;
+    // The run is read through a buffer resource of lim chunks: the hardware
+    // returns zeros past its end, so the eight loads need no branch and no
+    // merge with a zero value (which made the compiler wait for the first
+    // loads before issuing the rest).
+    const __amdgpu_buffer_rsrc_t run = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(p.x + g0 * 64), (short)0, lim * 128, kRawBufferWord3);
+    const uint32_t off = (uint32_t)(c0 * 128 + 16 * j);
     uint4 buf[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      buf[i] = (c0 + (T / 8) * i < lim) ? *reinterpret_cast<const uint4*>(base + i * ((T / 8) * 64))
-                                   : make_uint4(0u, 0u, 0u, 0u);
+    for (int i = 0; i < 8; ++i) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(run, off + i * ((T / 8) * 128), 0, 0);
+      buf[i] = make_uint4(v[0], v[1], v[2], v[3]);
+    }
     mid();
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -438,10 +449,14 @@ template <int B, int T>
 __global__ __launch_bounds__(T) void hq_int8_kernel(HQParams p) {
   __shared__ uint4 lds[T * 8];
   __shared__ uint32_t rowmax[T];
-  if (threadIdx.x < p.rows_per_wg) rowmax[threadIdx.x] = 0u;
   int row, col;
   bool valid;
-  stage<true, T>(p, lds, row, col, valid, blockIdx.x, [&]() { gelu_begin(p); });
+  // the row maxima are cleared while the chunk loads are in flight; the
+  // barrier after staging orders the clear before the atomics
+  stage<true, T>(p, lds, row, col, valid, blockIdx.x, [&]() {
+    gelu_begin(p);
+    if (threadIdx.x < p.rows_per_wg) rowmax[threadIdx.x] = 0u;
+  });
   __syncthreads();
   float v[64];
   load_chunk(lds, v, p.flags);
