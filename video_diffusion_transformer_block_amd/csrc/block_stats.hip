@@ -9,8 +9,10 @@
 // metrics are an extra pass whose cost must stay small).
 //
 // HBM-bound: 8 bytes per element (in, out, Delta_prev read; Delta_new
-// written).  Each thread handles 8 elements per step with 16-byte accesses in
-// a grid-stride loop over a grid sized from n only, accumulates in fp64, and
+// written).  Each thread handles 4 x 8 elements per step with 16-byte
+// buffer accesses (all twelve loads in flight at once), two steps per
+// workgroup in a grid-stride loop over a grid sized from n only, accumulates
+// in fp64, and
 // the workgroup / grid reductions run in a fixed order: the eight results are
 // bit-identical from run to run.
 //
@@ -22,79 +24,106 @@
 // instead of 8.  Four consecutive lanes hold one 32-element block (8
 // elements each), combine its maximum with two lane exchanges, and write 32
 // contiguous code bytes.
+#include <algorithm>
+
 #include "device_common.h"
 #include "launch.h"
 
 namespace vdtq {
 
 constexpr int BS_THREADS = 256;
-constexpr int BS_MAX_GRID = 4096;
+constexpr int BS_UNROLL = 4;                     // 16-byte vectors per thread and step (bf16 pass)
+constexpr int BS_STEPS = 2;                      // steps per workgroup (fewer partials to combine)
+constexpr int BS_MAX_GRID = 8192;
 
-static int bs_grid(int64_t n) {
-  int64_t vecs = (n + 7) / 8;
-  int64_t g = (vecs + BS_THREADS - 1) / BS_THREADS;
+// Workgroups of a launch: per_thread vectors for each of its threads, at
+// most BS_MAX_GRID (the loops are grid-stride); the bf16 pass takes
+// BS_STEPS steps of BS_UNROLL vectors per thread, the MXFP8 pass one vector.
+static int bs_grid(int64_t n, int per_thread = BS_UNROLL * BS_STEPS) {
+  const int64_t vecs = (n + 7) / 8, per_wg = (int64_t)BS_THREADS * per_thread;
+  int64_t g = (vecs + per_wg - 1) / per_wg;
   if (g > BS_MAX_GRID) g = BS_MAX_GRID;
   return (int)(g < 1 ? 1 : g);
 }
+static int bs_grid_mx8(int64_t n) { return std::min(bs_grid(n, 1), 4096); }
 
 struct Acc8 {
   double d2 = 0, i2 = 0, dd2 = 0, p2 = 0, si = 0, so = 0;
   float mi = 0.0f, mo = 0.0f;
 };
 
-__device__ __forceinline__ void acc_one(Acc8& a, float xi, float xo, bool has_prev, float dp,
-                                        uint32_t& dnew_bits) {
+// The squares of fp32 and bf16 values are exact in fp64, so each fma below
+// rounds once, as the separate product and sum would.
+template <bool HAS_PREV>
+__device__ __forceinline__ void acc_one(Acc8& a, float xi, float xo, float dp, uint32_t& dnew_bits) {
   const float d = xo - xi;                       // fp32 RN
   dnew_bits = f32_to_bf16_bits(d);
   const double dd = (double)d, ii = (double)xi;
-  a.d2 += dd * dd;
-  a.i2 += ii * ii;
-  if (has_prev) {
+  a.d2 = fma(dd, dd, a.d2);
+  a.i2 = fma(ii, ii, a.i2);
+  if (HAS_PREV) {
     const double dn = (double)__uint_as_float(dnew_bits << 16);
     const double pp = (double)dp;
-    const double df = dn - pp;                   // exact in fp64
+    const double df = dn - pp;                   // fp64 RN
     a.dd2 += df * df;
-    a.p2 += pp * pp;
+    a.p2 = fma(pp, pp, a.p2);
   }
   const float ai = fabsf(xi), ao = fabsf(xo);
   a.mi = fmaxf(a.mi, ai);
   a.mo = fmaxf(a.mo, ao);
-  a.si += (double)ai;
+  a.si += fabs(ii);
   a.so += (double)ao;
 }
 
+template <bool HAS_PREV>
 __global__ __launch_bounds__(BS_THREADS) void block_stats_kernel(const uint16_t* in, const uint16_t* out,
                                                                  const uint16_t* dprev, uint16_t* dnew,
                                                                  int64_t n, double* part) {
   Acc8 a;
-  const bool has_prev = dprev != nullptr;
   const int64_t nvec = n / 8;
-  const int64_t stride = (int64_t)gridDim.x * BS_THREADS;
-  for (int64_t v = (int64_t)blockIdx.x * BS_THREADS + threadIdx.x; v < nvec; v += stride) {
-    const uint4 wi = reinterpret_cast<const uint4*>(in)[v];
-    const uint4 wo = reinterpret_cast<const uint4*>(out)[v];
-    uint4 wp = make_uint4(0u, 0u, 0u, 0u);
-    if (has_prev) wp = reinterpret_cast<const uint4*>(dprev)[v];
-    const uint32_t ii[4] = {wi.x, wi.y, wi.z, wi.w};
-    const uint32_t oo[4] = {wo.x, wo.y, wo.z, wo.w};
-    const uint32_t pp[4] = {wp.x, wp.y, wp.z, wp.w};
-    uint32_t res[4];
+  // Each step covers BS_UNROLL * BS_THREADS consecutive vectors through
+  // buffer resources bounded at the end of the data: every load of the step
+  // is issued before the first is used, vectors past the end read as zeros
+  // (which add nothing to any sum or maximum) and their stores are dropped.
+  // An absent Delta_prev or Delta_new gets an empty resource.
+  constexpr int kSpan = BS_THREADS * BS_UNROLL;
+  const int64_t step = (int64_t)gridDim.x * kSpan;
+  const uint32_t lane = threadIdx.x * 16u;
+  for (int64_t vb = (int64_t)blockIdx.x * kSpan; vb < nvec; vb += step) {
+    const uint32_t bytes = (uint32_t)min<int64_t>(nvec - vb, kSpan) * 16u;
+    const __amdgpu_buffer_rsrc_t ri = raw_buffer(in + vb * 8, bytes);
+    const __amdgpu_buffer_rsrc_t ro = raw_buffer(out + vb * 8, bytes);
+    const __amdgpu_buffer_rsrc_t rp = raw_buffer(HAS_PREV ? dprev + vb * 8 : in, HAS_PREV ? bytes : 0u);
+    const __amdgpu_buffer_rsrc_t rn = raw_buffer(dnew ? dnew + vb * 8 : in, dnew ? bytes : 0u);
+    uint4 wi[BS_UNROLL], wo[BS_UNROLL], wp[BS_UNROLL];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      uint32_t b0, b1;
-      acc_one(a, bf16_lo(ii[k]), bf16_lo(oo[k]), has_prev, bf16_lo(pp[k]), b0);
-      acc_one(a, bf16_hi(ii[k]), bf16_hi(oo[k]), has_prev, bf16_hi(pp[k]), b1);
-      res[k] = b0 | (b1 << 16);
+    for (int u = 0; u < BS_UNROLL; ++u) {
+      wi[u] = buffer_load16(ri, lane + u * BS_THREADS * 16);
+      wo[u] = buffer_load16(ro, lane + u * BS_THREADS * 16);
+      wp[u] = buffer_load16(rp, lane + u * BS_THREADS * 16);
     }
-    if (dnew) reinterpret_cast<uint4*>(dnew)[v] = make_uint4(res[0], res[1], res[2], res[3]);
+#pragma unroll
+    for (int u = 0; u < BS_UNROLL; ++u) {
+      const uint32_t ii[4] = {wi[u].x, wi[u].y, wi[u].z, wi[u].w};
+      const uint32_t oo[4] = {wo[u].x, wo[u].y, wo[u].z, wo[u].w};
+      const uint32_t pp[4] = {wp[u].x, wp[u].y, wp[u].z, wp[u].w};
+      uint32_t res[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        uint32_t b0, b1;
+        acc_one<HAS_PREV>(a, bf16_lo(ii[k]), bf16_lo(oo[k]), bf16_lo(pp[k]), b0);
+        acc_one<HAS_PREV>(a, bf16_hi(ii[k]), bf16_hi(oo[k]), bf16_hi(pp[k]), b1);
+        res[k] = b0 | (b1 << 16);
+      }
+      buffer_store16(rn, lane + u * BS_THREADS * 16, make_uint4(res[0], res[1], res[2], res[3]));
+    }
   }
   // scalar tail (n % 8 elements), taken by the first workgroup's first lanes
   if (blockIdx.x == 0 && threadIdx.x < (n & 7)) {
     const int64_t i = nvec * 8 + threadIdx.x;
     uint32_t b;
-    const float pv = has_prev ? __uint_as_float((uint32_t)dprev[i] << 16) : 0.0f;
-    acc_one(a, __uint_as_float((uint32_t)in[i] << 16), __uint_as_float((uint32_t)out[i] << 16),
-            has_prev, pv, b);
+    const float pv = HAS_PREV ? __uint_as_float((uint32_t)dprev[i] << 16) : 0.0f;
+    acc_one<HAS_PREV>(a, __uint_as_float((uint32_t)in[i] << 16), __uint_as_float((uint32_t)out[i] << 16), pv, b);
     if (dnew) dnew[i] = (uint16_t)b;
   }
 
@@ -224,15 +253,29 @@ __global__ __launch_bounds__(BS_THREADS) void block_stats_mx8_kernel(const uint1
 
 constexpr int kBsFinalThreads = 1024;
 
+// Fixed-order sum (maxima for entries 4 and 6) of the per-workgroup
+// partials.  Each thread keeps 4 partials (16 loads) in flight; reads past
+// nparts are zeros, neutral for these non-negative sums and maxima.
 __global__ __launch_bounds__(kBsFinalThreads) void block_stats_final_kernel(const double* part, int nparts,
                                                                             double* stats) {
   __shared__ double red[8][kBsFinalThreads / 64];
+  constexpr int U = 4;
+  const __amdgpu_buffer_rsrc_t r = raw_buffer(part, (uint32_t)nparts * 64u);
   double vals[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int i = threadIdx.x; i < nparts; i += kBsFinalThreads) {
-    const double4 lo = reinterpret_cast<const double4*>(part)[2 * i];
-    const double4 hi = reinterpret_cast<const double4*>(part)[2 * i + 1];
-    vals[0] += lo.x; vals[1] += lo.y; vals[2] += lo.z; vals[3] += lo.w;
-    vals[4] = fmax(vals[4], hi.x); vals[5] += hi.y; vals[6] = fmax(vals[6], hi.z); vals[7] += hi.w;
+  for (int base = 0; base < nparts; base += U * kBsFinalThreads) {
+    uint4 w[U][4];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        w[u][q] = buffer_load16(r, (uint32_t)(base + u * kBsFinalThreads + threadIdx.x) * 64u + 16u * q);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      vals[0] += u2d(w[u][0].x, w[u][0].y); vals[1] += u2d(w[u][0].z, w[u][0].w);
+      vals[2] += u2d(w[u][1].x, w[u][1].y); vals[3] += u2d(w[u][1].z, w[u][1].w);
+      vals[4] = fmax(vals[4], u2d(w[u][2].x, w[u][2].y)); vals[5] += u2d(w[u][2].z, w[u][2].w);
+      vals[6] = fmax(vals[6], u2d(w[u][3].x, w[u][3].y)); vals[7] += u2d(w[u][3].z, w[u][3].w);
+    }
   }
 #pragma unroll
   for (int k = 0; k < 8; ++k) vals[k] = (k == 4 || k == 6) ? wave_max_d(vals[k]) : wave_sum(vals[k]);
@@ -249,15 +292,22 @@ __global__ __launch_bounds__(kBsFinalThreads) void block_stats_final_kernel(cons
   }
 }
 
-size_t bs_workspace_bytes(int64_t n) { return (size_t)bs_grid(n) * 8 * sizeof(double); }
+size_t bs_workspace_bytes(int64_t n) {
+  return (size_t)std::max(bs_grid(n), bs_grid_mx8(n)) * 8 * sizeof(double);
+}
 
 hipError_t launch_block_stats(const void* in, const void* out, const void* dprev, void* dnew,
                               int64_t n, double* stats, void* ws, hipStream_t st) {
   const int grid = bs_grid(n);
   double* part = static_cast<double*>(ws);
-  hipLaunchKernelGGL(block_stats_kernel, dim3(grid), dim3(BS_THREADS), 0, st,
-                     static_cast<const uint16_t*>(in), static_cast<const uint16_t*>(out),
-                     static_cast<const uint16_t*>(dprev), static_cast<uint16_t*>(dnew), n, part);
+  if (dprev)
+    hipLaunchKernelGGL(block_stats_kernel<true>, dim3(grid), dim3(BS_THREADS), 0, st,
+                       static_cast<const uint16_t*>(in), static_cast<const uint16_t*>(out),
+                       static_cast<const uint16_t*>(dprev), static_cast<uint16_t*>(dnew), n, part);
+  else
+    hipLaunchKernelGGL(block_stats_kernel<false>, dim3(grid), dim3(BS_THREADS), 0, st,
+                       static_cast<const uint16_t*>(in), static_cast<const uint16_t*>(out), nullptr,
+                       static_cast<uint16_t*>(dnew), n, part);
   hipLaunchKernelGGL(block_stats_final_kernel, dim3(1), dim3(kBsFinalThreads), 0, st, part, grid, stats);
   return hipGetLastError();
 }
@@ -265,8 +315,8 @@ hipError_t launch_block_stats(const void* in, const void* out, const void* dprev
 hipError_t launch_block_stats_mx8(const void* in, const void* out, const uint8_t* dprev_q, const uint8_t* dprev_s,
                                   uint8_t* dnew_q, uint8_t* dnew_s, int64_t n, double* stats, void* ws,
                                   hipStream_t st) {
-  // same grid (and workspace) as the bf16 pass: a multiple of 4 lanes per block
-  const int grid = bs_grid(n);
+  // whole workgroups of 256 lanes: a multiple of 4 lanes per block
+  const int grid = bs_grid_mx8(n);
   double* part = static_cast<double*>(ws);
   hipLaunchKernelGGL(block_stats_mx8_kernel, dim3(grid), dim3(BS_THREADS), 0, st,
                      static_cast<const uint16_t*>(in), static_cast<const uint16_t*>(out), dprev_q, dprev_s,

@@ -22,6 +22,33 @@ typedef float float2v __attribute__((ext_vector_type(2)));
 // scales derived from smaller maxima would leave the fp32 normal range.
 constexpr float kZeroLimit = 0x1p-100f;
 
+// Raw (unstrided, unswizzled) buffer resources over [p, p + bytes): the
+// hardware's range check makes loads past the end read zeros and drops
+// stores past it, so bounded accesses need no branch.  Word 3 selects the
+// 32-bit data format, which untyped accesses need to move anything.
+constexpr int kRawBufferWord3 = 0x00020000;
+typedef uint32_t uint4v __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_buffer(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, kRawBufferWord3);
+}
+__device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const uint4v v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ float buffer_load4f(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+__device__ __forceinline__ void buffer_store16(__amdgpu_buffer_rsrc_t r, uint32_t off, uint4 w) {
+  const uint4v v = {w.x, w.y, w.z, w.w};
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
+}
+
+// The double whose bits are (hi:lo).
+__device__ __forceinline__ double u2d(uint32_t lo, uint32_t hi) {
+  return __hiloint2double((int)hi, (int)lo);
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 

@@ -87,10 +87,6 @@ struct NoMid {
   __device__ void operator()() const {}
 };
 
-// Word 3 of a raw (unstrided, unswizzled) CDNA buffer resource: 32-bit data
-// format, the one untyped loads need to read anything but zeros.
-constexpr int kRawBufferWord3 = 0x00020000;
-
 template <bool ROWS, int T = HQ_THREADS, class Mid = NoMid>
 __device__ __forceinline__ void stage(const HQParams& p, uint4* lds, int& my_row, int& my_col,
                                       bool& my_valid, int wg = blockIdx.x, Mid mid = Mid()) {
@@ -109,15 +105,11 @@ __device__ __forceinline__ void stage(const HQParams& p, uint4* lds, int& my_row
     // returns zeros past its end, so the eight loads need no branch and no
     // merge with a zero value (which made the compiler wait for the first
     // loads before issuing the rest).
-    const __amdgpu_buffer_rsrc_t run = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(p.x + g0 * 64), (short)0, lim * 128, kRawBufferWord3);
+    const __amdgpu_buffer_rsrc_t run = raw_buffer(p.x + g0 * 64, (uint32_t)lim * 128u);
     const uint32_t off = (uint32_t)(c0 * 128 + 16 * j);
     uint4 buf[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const auto v = __builtin_amdgcn_raw_buffer_load_b128(run, off + i * ((T / 8) * 128), 0, 0);
-      buf[i] = make_uint4(v[0], v[1], v[2], v[3]);
-    }
+    for (int i = 0; i < 8; ++i) buf[i] = buffer_load16(run, off + i * ((T / 8) * 128));
     mid();
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -282,21 +274,23 @@ __global__ __launch_bounds__(HQ_THREADS) void hq_amax_kernel(HQParams p) {
 }
 
 // One workgroup of kFinalThreads: amax_T = max of the partial maxima;
-// writes {amax_T, gs}.  Four independent loads in flight per thread.
+// writes {amax_T, gs}.  Each thread keeps 16 loads in flight; reads past n
+// are zeros, neutral for a maximum of non-negative values.
 constexpr int kFinalThreads = 1024;
 
 __global__ __launch_bounds__(kFinalThreads) void hq_amax_final_kernel(const float* part, int n, float* ts) {
   __shared__ float wred[kFinalThreads / 64];
-  float m0 = 0.0f, m1 = 0.0f, m2 = 0.0f, m3 = 0.0f;
-  int i = threadIdx.x;
-  for (; i + 3 * kFinalThreads < n; i += 4 * kFinalThreads) {
-    m0 = fmaxf(m0, part[i]);
-    m1 = fmaxf(m1, part[i + kFinalThreads]);
-    m2 = fmaxf(m2, part[i + 2 * kFinalThreads]);
-    m3 = fmaxf(m3, part[i + 3 * kFinalThreads]);
+  constexpr int U = 16;
+  const __amdgpu_buffer_rsrc_t r = raw_buffer(part, (uint32_t)n * 4u);
+  float m = 0.0f;
+  for (int base = 0; base < n; base += U * kFinalThreads) {
+    float x[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) x[u] = buffer_load4f(r, (uint32_t)(base + u * kFinalThreads + threadIdx.x) * 4u);
+#pragma unroll
+    for (int u = 0; u < U; ++u) m = fmaxf(m, x[u]);
   }
-  for (; i < n; i += kFinalThreads) m0 = fmaxf(m0, part[i]);
-  float m = wave_max(fmaxf(fmaxf(m0, m1), fmaxf(m2, m3)));
+  m = wave_max(m);
   if ((threadIdx.x & 63) == 0) wred[threadIdx.x >> 6] = m;
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -312,16 +306,29 @@ __global__ void hq_gs_only_kernel(float* ts) {
   if (threadIdx.x == 0) ts[1] = nvfp4_gs(ts[0]);
 }
 
-// Final fp64 reduction of the per-workgroup statistics (fixed order).
+// Final fp64 reduction of the per-workgroup statistics {max, sum, max, sum}
+// (fixed order).  Each thread keeps 4 partials (8 loads) in flight; reads
+// past n are zeros, neutral for these non-negative maxima and sums.
 __global__ __launch_bounds__(kFinalThreads) void hq_stats_final_kernel(const double* part, int n, double* out) {
   __shared__ double red[4][kFinalThreads / 64];
+  constexpr int U = 4;
+  const __amdgpu_buffer_rsrc_t r = raw_buffer(part, (uint32_t)n * 32u);
   double a = 0.0, b = 0.0, c = 0.0, d = 0.0;
-  for (int i = threadIdx.x; i < n; i += kFinalThreads) {
-    const double4 v = reinterpret_cast<const double4*>(part)[i];
-    a = fmax(a, v.x);
-    b += v.y;
-    c = fmax(c, v.z);
-    d += v.w;
+  for (int base = 0; base < n; base += U * kFinalThreads) {
+    uint4 w[U][2];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t off = (uint32_t)(base + u * kFinalThreads + threadIdx.x) * 32u;
+      w[u][0] = buffer_load16(r, off);
+      w[u][1] = buffer_load16(r, off + 16u);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      a = fmax(a, u2d(w[u][0].x, w[u][0].y));
+      b += u2d(w[u][0].z, w[u][0].w);
+      c = fmax(c, u2d(w[u][1].x, w[u][1].y));
+      d += u2d(w[u][1].z, w[u][1].w);
+    }
   }
   a = wave_max_d(a); b = wave_sum(b); c = wave_max_d(c); d = wave_sum(d);
   const int w = threadIdx.x >> 6;
