@@ -709,7 +709,8 @@ def measure_block_stats(torch, V, inp, out, n, steps):
             times.append(e0.elapsed_time(e1) / 20)
         us = 1e3 * float(np.median(times))
         gbs = bpe * n / (us * 1e-6) / 1e9
-        res[cache] = {"bound": "hbm", "kernel": "block_stats_kernel" if cache == "bf16" else "block_stats_mx8_kernel",
+        res[cache] = {"bound": "hbm", "kernel": ("block_stats_kernel<true> + block_stats_final_kernel" if cache == "bf16"
+                                                else "block_stats_mx8_kernel + block_stats_final_kernel"),
                       "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                       "avg_launch_us": round(us, 2), "bytes_per_launch": bpe * n,
                       "cache_bytes": n * (2 if cache == "bf16" else 1 + 1 / 32)}
