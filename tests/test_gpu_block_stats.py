@@ -39,6 +39,28 @@ def F32(bits):
     return (bits.astype(np.uint32) << 16).view(np.float32)
 
 
+@pytest.mark.parametrize("n", [1000, 65536 + 3, 4446 * 1920])
+@pytest.mark.parametrize("with_prev", [False, True])
+def test_without_delta(n, with_prev):
+    """No Delta_new buffer: nothing is written (the inputs keep their bits)
+    and the eight statistics equal those of the call that writes Delta_new."""
+    need_gpu()
+    log(f"block_stats without Delta_new n={n} dprev={with_prev}")
+    inp = synth.to_bf16_bits(RNG.laplace(size=n).astype(np.float32))
+    out = synth.to_bf16_bits(RNG.laplace(size=n).astype(np.float32) * 0.1 + F32(inp))
+    dprev = synth.to_bf16_bits(RNG.standard_normal(n).astype(np.float32) * 0.1) if with_prev else None
+    di, do = dev_bf16(inp), dev_bf16(out)
+    dp = dev_bf16(dprev) if with_prev else None
+    _, st_ref = V.block_stats(di, do, dp)
+    none, st = V.block_stats(di, do, dp, write_delta=False)
+    torch.cuda.synchronize()
+    assert none is None
+    assert np.array_equal(host_bits(di), inp) and np.array_equal(host_bits(do), out)
+    if with_prev:
+        assert np.array_equal(host_bits(dp), dprev)
+    assert np.array_equal(st.cpu().numpy(), st_ref.cpu().numpy())
+
+
 def test_closed_forms_on_gpu():
     need_gpu()
     x = RNG.integers(-16, 17, size=(64, 96)).astype(np.float32).ravel() * 8
