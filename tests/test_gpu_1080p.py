@@ -15,7 +15,8 @@ import torch
 import synth
 import video_diffusion_transformer_block_amd as V
 from oracle import gemm as G, hadamard as H, quant as Q
-from helpers import bf16_values, dev_bf16, host_bits, need_gpu, rel_fro, log
+from helpers import (assert_elementwise, bf16_values, dev_bf16, host_bits, need_gpu, rel_fro, log,
+                     terms_w4a4, terms_w4a8)
 
 pytestmark = pytest.mark.gpu
 B = 64
@@ -34,6 +35,8 @@ def test_1080p_ffn_sampled(name, K, N):
     a8 = V.hadamard_quantize(xd, B, "int8")
     y4 = V.qgemm_w4a4(a4, wd, None, "bf16")
     y8 = V.qgemm_w4a8(a8, wd, None, "bf16")
+    f4 = V.qgemm_w4a4(a4, wd, None, "f32")[torch.from_numpy(rows).cuda()]
+    f8 = V.qgemm_w4a8(a8, wd, None, "f32")[torch.from_numpy(rows).cuda()]
     torch.cuda.synchronize()
     log("  library done; oracle on sampled rows")
 
@@ -58,10 +61,22 @@ def test_1080p_ffn_sampled(name, K, N):
     assert np.array_equal(a8.q.cpu().numpy()[rows], r8["q"])
     assert np.array_equal(s8[rows].view(np.uint32), r8["scales"].view(np.uint32))
 
-    # GEMM outputs on the sampled rows
-    _, o4 = G.qgemm_w4a4(r4["q"], r4["scales"], r4["gs"], wq_o, ws_o, wgs_o, None, "bf16")
-    _, o8 = G.qgemm_w4a8(r8["q"], r8["scales"], wq_o, ws_o, wgs_o, None, "bf16")
-    e4 = rel_fro(bf16_values(host_bits(y4)[rows]), bf16_values(o4))
-    e8 = rel_fro(bf16_values(host_bits(y8)[rows]), bf16_values(o8))
-    log(f"  w4a4 rel {e4:.2e}  w4a8 rel {e8:.2e}")
+    # GEMM outputs on the sampled rows: bf16 and f32, each element within the
+    # fp32-summation bound, f32 also within 1e-5 relative Frobenius
+    x4, o4 = G.qgemm_w4a4(r4["q"], r4["scales"], r4["gs"], wq_o, ws_o, wgs_o, None, "bf16")
+    x8, o8 = G.qgemm_w4a8(r8["q"], r8["scales"], wq_o, ws_o, wgs_o, None, "bf16")
+    t4 = terms_w4a4(r4["q"], r4["scales"], r4["gs"], wq_o, ws_o, wgs_o, None)
+    t8 = terms_w4a8(r8["q"], r8["scales"], wq_o, ws_o, wgs_o, None)
+    g4, g8 = bf16_values(host_bits(y4)[rows]), bf16_values(host_bits(y8)[rows])
+    e4 = rel_fro(g4, bf16_values(o4))
+    e8 = rel_fro(g8, bf16_values(o8))
+    assert_elementwise(g4, x4, t4, K, "bf16", "w4a4 bf16")
+    assert_elementwise(g8, x8, t8, K, "bf16", "w4a8 bf16")
+    h4, h8 = f4.cpu().numpy(), f8.cpu().numpy()
+    q4 = assert_elementwise(h4, x4, t4, K, "f32", "w4a4 f32")
+    q8 = assert_elementwise(h8, x8, t8, K, "f32", "w4a8 f32")
+    ef4, ef8 = rel_fro(h4, x4), rel_fro(h8, x8)
+    log(f"  w4a4 rel {e4:.2e} / f32 {ef4:.2e} (err/bound {q4:.3f})  w4a8 rel {e8:.2e} / f32 {ef8:.2e} "
+        f"(err/bound {q8:.3f})")
     assert e4 <= 2e-3 and e8 <= 2e-3
+    assert ef4 < 1e-5 and ef8 < 1e-5

@@ -10,7 +10,7 @@ import torch
 import synth
 import video_diffusion_transformer_block_amd as V
 from oracle import formats as F, gemm as G, quant as Q
-from helpers import bf16_values, dev_bf16, host_bits, need_gpu, rel_fro, log
+from helpers import assert_elementwise, bf16_values, dev_bf16, host_bits, need_gpu, rel_fro, log, terms_mx
 
 pytestmark = pytest.mark.gpu
 RNG = np.random.Generator(np.random.PCG64(51))
@@ -108,6 +108,8 @@ def check_gemm(x_bits, w_bits, b=64, bias=True, rows=None, out_dtypes=("bf16", "
     for fmt in fmts:
         ref = Q.hadamard_quantize(x_bits[sel], b, fmt)
         ad = V.hadamard_quantize(xd, b, fmt)
+        assert np.array_equal(ad.q.cpu().numpy()[sel], ref["q"]) and np.array_equal(ad.scales.cpu().numpy()[sel], ref["scales"])
+        terms = terms_mx(ref["q"], ref["scales"], fmt, wq_o, ws_o, bias_h)
         for od in out_dtypes:
             y = V.qgemm_mx(ad, wd, bias_d, od)
             torch.cuda.synchronize()
@@ -117,7 +119,8 @@ def check_gemm(x_bits, w_bits, b=64, bias=True, rows=None, out_dtypes=("bf16", "
             else:
                 got, want = y.cpu().numpy()[sel], e64
             err = rel_fro(got, want)
-            log(f"  {fmt} {od}: rel {err:.2e}")
+            qb = assert_elementwise(got, e64, terms, K, od, f"{fmt} {od}")
+            log(f"  {fmt} {od}: rel {err:.2e} (max err/bound {qb:.3f})")
             assert err <= TOL, err
             if od == "f32":
                 assert err < 1e-5, err
@@ -188,7 +191,7 @@ def test_gemm_cogvideox_5b_sampled(name):
     M = synth.TOKENS_2B_5B
     K, N = {n: (k, nn) for n, k, nn in synth.block_linears(3072)}[name]
     x, w = synth.layer_inputs(M, name, K, N)
-    check_gemm(x, w, rows=synth.row_sample(M, 48), out_dtypes=("bf16",))
+    check_gemm(x, w, rows=synth.row_sample(M, 48), out_dtypes=("bf16", "f32"))
 
 
 def test_gemm_two_waves_and_split_tail():
@@ -198,7 +201,7 @@ def test_gemm_two_waves_and_split_tail():
     M, N, K = 2000, 19200, 1024
     x = synth.to_bf16_bits(RNG.laplace(size=(M, K)).astype(np.float32))
     w = synth.to_bf16_bits(RNG.standard_normal((N, K)).astype(np.float32) * 0.02)
-    check_gemm(x, w, rows=synth.row_sample(M, 96), out_dtypes=("bf16",))
+    check_gemm(x, w, rows=synth.row_sample(M, 96), out_dtypes=("bf16", "f32"))
 
 
 @pytest.mark.parametrize("fmt", ["mxfp4", "mxfp8"])

@@ -1,6 +1,8 @@
 """GPU parity of qgemm_w4a4 / qgemm_w4a8 against the oracle: relative
 Frobenius error <= 2e-3 (bf16 compared with the oracle's bf16 rounding; f32
-with its exact value), and the W4A8 integer accumulator bit-exact."""
+with its exact value, where it must also be <= 1e-5), every element within
+the fp32-summation bound of helpers.assert_elementwise, and the W4A8 integer
+accumulator bit-exact."""
 import numpy as np
 import pytest
 import torch
@@ -8,7 +10,8 @@ import torch
 import synth
 import video_diffusion_transformer_block_amd as V
 from oracle import formats as F, gemm as G, quant as Q
-from helpers import bf16_values, dev_bf16, host_bits, need_gpu, rel_fro, log
+from helpers import (assert_elementwise, bf16_values, dev_bf16, host_bits, need_gpu, rel_fro, log,
+                     terms_w4a4, terms_w4a8)
 
 pytestmark = pytest.mark.gpu
 RNG = np.random.Generator(np.random.PCG64(22))
@@ -44,6 +47,12 @@ def check_layer(x_bits, w_bits, b=64, bias=True, rows=None, out_dtypes=("bf16", 
     a8 = Q.hadamard_quantize(x_bits[sel], b, "int8")
     ad4 = V.hadamard_quantize(xd, b, "nvfp4")
     ad8 = V.hadamard_quantize(xd, b, "int8")
+    # the activation codes themselves are checked bit for bit on the same rows
+    assert np.array_equal(ad4.q.cpu().numpy()[sel], a4["q"]) and np.array_equal(ad4.scales.cpu().numpy()[sel], a4["scales"])
+    assert np.array_equal(ad8.q.cpu().numpy()[sel], a8["q"])
+    assert np.array_equal(ad8.scales.cpu().numpy()[sel].view(np.uint32), a8["scales"].view(np.uint32))
+    t4 = terms_w4a4(a4["q"], a4["scales"], a4["gs"], wq_o, ws_o, wgs_o, bias_h)
+    t8 = terms_w4a8(a8["q"], a8["scales"], wq_o, ws_o, wgs_o, bias_h)
     for od in out_dtypes:
         y4 = V.qgemm_w4a4(ad4, wd, bias_d, od)
         y8 = V.qgemm_w4a8(ad8, wd, bias_d, od)
@@ -57,7 +66,9 @@ def check_layer(x_bits, w_bits, b=64, bias=True, rows=None, out_dtypes=("bf16", 
             g4 = y4.cpu().numpy()[sel]; g8 = y8.cpu().numpy()[sel]
             w4, w8 = e4, e8
         err4, err8 = rel_fro(g4, w4), rel_fro(g8, w8)
-        log(f"  {od}: w4a4 rel {err4:.2e}  w4a8 rel {err8:.2e}")
+        q4 = assert_elementwise(g4, e4, t4, K, od, f"w4a4 {od}")
+        q8 = assert_elementwise(g8, e8, t8, K, od, f"w4a8 {od}")
+        log(f"  {od}: w4a4 rel {err4:.2e} (max err/bound {q4:.3f})  w4a8 rel {err8:.2e} (max err/bound {q8:.3f})")
         assert err4 <= TOL and err8 <= TOL, (err4, err8)
         if od == "f32":
             assert err4 < 1e-5 and err8 < 1e-5   # only fp32 accumulation order differs
@@ -137,6 +148,8 @@ def test_w4a4_full_scale_range_exact(lo, hi):
         assert np.array_equal(got, want)
     else:
         assert rel_fro(got, want) < 1e-6
+        t = terms_w4a4(F.pack_nibbles(ac), as_, 1.0, F.pack_nibbles(wc), ws, 1.0, None)
+        assert_elementwise(got, want, t, K, "f32", "full scale range")
 
 
 @pytest.mark.parametrize("name", ["qkv", "out", "ffn_up", "ffn_down"])
@@ -145,7 +158,7 @@ def test_cogvideox_5b_linears_sampled(name):
     M = synth.TOKENS_2B_5B
     K, N = {n: (k, nn) for n, k, nn in synth.block_linears(3072)}[name]
     x, w = synth.layer_inputs(M, name, K, N)
-    check_layer(x, w, rows=synth.row_sample(M, 48), out_dtypes=("bf16",))
+    check_layer(x, w, rows=synth.row_sample(M, 48), out_dtypes=("bf16", "f32"))
 
 
 @pytest.mark.parametrize("name", ["qkv", "out", "ffn_up", "ffn_down"])
@@ -155,7 +168,7 @@ def test_cogvideox_2b_linears_sampled(name):
     M = synth.TOKENS_2B_5B
     K, N = {n: (k, nn) for n, k, nn in synth.block_linears(1920)}[name]
     x, w = synth.layer_inputs(M, name, K, N)
-    check_layer(x, w, rows=synth.row_sample(M, 48), out_dtypes=("bf16",))
+    check_layer(x, w, rows=synth.row_sample(M, 48), out_dtypes=("bf16", "f32"))
 
 
 @pytest.mark.parametrize("M,N,K", [(1000, 700, 1024), (300, 260, 3072), (17, 2000, 2048), (4400, 4400, 1536)])

@@ -13,9 +13,31 @@ pytestmark = pytest.mark.gpu
 RNG = np.random.Generator(np.random.PCG64(21))
 
 
+def oracle_every_row(x_bits, b, chunk=2048):
+    """The tensor amax and the four outlier statistics over every row of a
+    large input, from the oracle's transform chunk by chunk (the maxima
+    combine exactly, the fp64 sums in row-chunk order)."""
+    M = x_bits.shape[0]
+    amax = np.float32(0)
+    st = np.zeros(4)
+    for r0 in range(0, M, chunk):
+        xc = x_bits[r0:r0 + chunk]
+        y = H.block_hadamard_bf16(xc, b)
+        amax = max(amax, np.float32(np.abs(y).max()) if y.size else np.float32(0))
+        c = Q.activation_stats(xc, y)
+        st = np.array([max(st[0], c[0]), st[1] + c[1], max(st[2], c[2]), st[3] + c[3]])
+    return amax, st
+
+
+def check_stats(got, want):
+    assert got[0] == want[0] and got[2] == want[2], (got, want)
+    assert np.allclose(got[[1, 3]], want[[1, 3]], rtol=1e-5, atol=0), (got, want)
+
+
 def run_and_compare(x_bits, b, fmt, amax=None, stats=True, ldx_pad=0, rows=None):
     M, K = x_bits.shape
-    log(f"hq case M={M} K={K} b={b} fmt={fmt} amax={amax} pad={ldx_pad}")
+    log(f"hq case M={M} K={K} b={b} fmt={fmt} amax={amax} pad={ldx_pad} stats={stats} "
+        f"rows={'all' if rows is None else len(rows)}")
     if ldx_pad:
         big = np.zeros((M, K + ldx_pad), np.uint16)
         big[:, :K] = x_bits
@@ -25,15 +47,12 @@ def run_and_compare(x_bits, b, fmt, amax=None, stats=True, ldx_pad=0, rows=None)
     r = V.hadamard_quantize(xd, had_block=b, fmt=fmt, amax=amax, stats=stats)
     torch.cuda.synchronize()
     sel = np.arange(M) if rows is None else rows
+    # the tensor amax and the statistics need every row; the codes are row-local
+    full = oracle_every_row(x_bits, b) if rows is not None else None
     if fmt == "nvfp4":
-        # the tensor amax needs every row; the codes are row-local
         ya = None
         if amax is None:
-            amax_o = np.float32(0)
-            for r0 in range(0, M, 4096):
-                y = H.block_hadamard_bf16(x_bits[r0:r0 + 4096], b)
-                amax_o = max(amax_o, np.float32(np.abs(y).max()) if y.size else np.float32(0))
-            ya = amax_o
+            ya = full[0] if full is not None else oracle_every_row(x_bits, b)[0]
         ref = Q.hadamard_quantize(x_bits[sel], b, "nvfp4", amax=ya if amax is None else amax)
         ts = r.ts.cpu().numpy()
         assert ts[0] == ref["amax"] or (np.isnan(ts[0]) and np.isnan(ref["amax"])), (ts, ref["amax"])
@@ -48,11 +67,8 @@ def run_and_compare(x_bits, b, fmt, amax=None, stats=True, ldx_pad=0, rows=None)
         s = r.scales.cpu().numpy()[sel]
         assert np.array_equal(s.view(np.uint32), ref["scales"].view(np.uint32))
         assert np.array_equal(q, ref["q"])
-    if stats and rows is None:
-        st = r.stats.cpu().numpy()
-        want = ref["stats"]
-        assert st[0] == want[0] and st[2] == want[2], (st, want)
-        assert np.allclose(st[[1, 3]], want[[1, 3]], rtol=1e-5, atol=0), (st, want)
+    if stats:
+        check_stats(r.stats.cpu().numpy(), ref["stats"] if rows is None else full[1])
     return r
 
 
@@ -135,7 +151,7 @@ def test_cogvideox_5b_shapes_sampled(fmt, K):
     M = synth.TOKENS_2B_5B
     name = "ffn_down" if K == 12288 else "qkv"
     x, _ = synth.layer_inputs(M, name, K, 16)
-    run_and_compare(x, 64, fmt, rows=synth.row_sample(M, 256), stats=False)
+    run_and_compare(x, 64, fmt, rows=synth.row_sample(M, 256), stats=True)
 
 
 @pytest.mark.parametrize("fmt,K", [("nvfp4", 1920), ("int8", 1920), ("nvfp4", 7680), ("int8", 7680)])
@@ -145,4 +161,43 @@ def test_cogvideox_2b_shapes_sampled(fmt, K):
     M = synth.TOKENS_2B_5B
     name = "ffn_down" if K == 7680 else "qkv"
     x, _ = synth.layer_inputs(M, name, K, 16)
-    run_and_compare(x, 64, fmt, rows=synth.row_sample(M, 256), stats=False)
+    run_and_compare(x, 64, fmt, rows=synth.row_sample(M, 256), stats=True)
+
+
+@pytest.mark.parametrize("K", [3072, 12288])
+def test_fused_stats_5b_every_format(K):
+    """The fused statistics at the 5B shapes in every activation format
+    (NVFP4, INT8, BF16, MXFP4, MXFP8), against the oracle over every row.
+    These grids hold 4444 to 26664 workgroup partials, more than one pass of
+    the final reduction's 4096-partial loop; the codes of the BF16 and MX
+    formats are compared on sampled rows as well."""
+    need_gpu()
+    M = synth.TOKENS_2B_5B
+    name = "ffn_down" if K == 12288 else "qkv"
+    x, _ = synth.layer_inputs(M, name, K, 16)
+    amax_o, want = oracle_every_row(x, 64)
+    rows = synth.row_sample(M, 64)
+    xd = dev_bf16(x)
+    for fmt in ("nvfp4", "int8", "bf16", "mxfp4", "mxfp8"):
+        log(f"stats 5B K={K} fmt={fmt}")
+        r = V.hadamard_quantize(xd, 64, fmt, stats=True)
+        torch.cuda.synchronize()
+        check_stats(r.stats.cpu().numpy(), want)
+        if fmt == "nvfp4":
+            assert r.ts.cpu().numpy()[0] == amax_o
+        if fmt in ("bf16", "mxfp4", "mxfp8"):
+            ref = Q.hadamard_quantize(x[rows], 64, fmt)
+            if fmt == "bf16":
+                assert np.array_equal(r.q.view(torch.int16).cpu().numpy().view(np.uint16)[rows], ref["q"])
+            else:
+                assert np.array_equal(r.q.cpu().numpy()[rows], ref["q"])
+                assert np.array_equal(r.scales.cpu().numpy()[rows], ref["scales"])
+
+
+def test_fused_stats_more_partials_than_one_pass_all_rows():
+    """M = 12000, K = 3072: 4500 NVFP4 and 3000 INT8 workgroup partials;
+    codes and statistics compared on every row."""
+    need_gpu()
+    x = synth.laplace_activations(12000, 3072, 77, 78)
+    for fmt in ("nvfp4", "int8"):
+        run_and_compare(x, 64, fmt, stats=True)

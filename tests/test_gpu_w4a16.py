@@ -10,7 +10,7 @@ import torch
 import synth
 import video_diffusion_transformer_block_amd as V
 from oracle import gemm as G, hadamard as H, quant as Q
-from helpers import bf16_values, dev_bf16, host_bits, need_gpu, rel_fro, log
+from helpers import assert_elementwise, bf16_values, dev_bf16, host_bits, need_gpu, rel_fro, log, terms_w4a16
 
 pytestmark = pytest.mark.gpu
 RNG = np.random.Generator(np.random.PCG64(31))
@@ -46,6 +46,7 @@ def check_w4a16(x_bits, w_bits, b=64, bias=True, rows=None, out_dtypes=("bf16", 
     bias_d = torch.from_numpy(bias_h).cuda() if bias else None
     a = check_bf16_pass(x_bits, b, rows=rows)
     a_ref = Q.hadamard_quantize(x_bits[sel], b, "bf16")["q"]
+    terms = terms_w4a16(a_ref, wq_o, ws_o, wgs_o, bias_h)
     for od in out_dtypes:
         y = V.qgemm_w4a16(a, wd, bias_d, od)
         torch.cuda.synchronize()
@@ -55,7 +56,8 @@ def check_w4a16(x_bits, w_bits, b=64, bias=True, rows=None, out_dtypes=("bf16", 
         else:
             got, want = y.cpu().numpy()[sel], e64
         err = rel_fro(got, want)
-        log(f"  {od}: rel {err:.2e}")
+        qb = assert_elementwise(got, e64, terms, K, od, f"w4a16 {od}")
+        log(f"  {od}: rel {err:.2e} (max err/bound {qb:.3f})")
         assert err <= TOL, err
         if od == "f32":
             assert err < 1e-5
@@ -119,10 +121,10 @@ def test_w4a16_rejects_k_not_multiple_of_64():
         V.qgemm_w4a16(a, w)
 
 
-@pytest.mark.parametrize("name", ["qkv", "ffn_down"])
+@pytest.mark.parametrize("name", ["qkv", "out", "ffn_up", "ffn_down"])
 def test_w4a16_cogvideox_5b_sampled(name):
     need_gpu()
     M = synth.TOKENS_2B_5B
     K, N = {n: (k, nn) for n, k, nn in synth.block_linears(3072)}[name]
     x, w = synth.layer_inputs(M, name, K, N)
-    check_w4a16(x, w, rows=synth.row_sample(M, 48), out_dtypes=("bf16",))
+    check_w4a16(x, w, rows=synth.row_sample(M, 48), out_dtypes=("bf16", "f32"))
