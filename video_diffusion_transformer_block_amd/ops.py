@@ -21,11 +21,58 @@ def _stream(dev: torch.device):
     return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
 
 
+# Device type every tensor handed to the library must have (the CPU tests of
+# the argument checks below substitute "cpu" and a library stub).
+_DEVICE_TYPE = "cuda"
+
+
 def _require(t: torch.Tensor, dtype, name: str):
-    if not t.is_cuda:
+    if not torch.is_tensor(t) or t.device.type != _DEVICE_TYPE:
         raise ValueError(f"{name} must be a device tensor")
     if t.dtype != dtype:
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _buf(t, name: str, dtype, shape, dev: torch.device):
+    """A caller-given buffer the library reads or writes as a dense row-major
+    array: it must be a contiguous tensor of exactly `shape` and `dtype` on
+    `dev`, or the kernel would read or write past it."""
+    _require(t, dtype, name)
+    if t.device != dev:
+        raise ValueError(f"{name} is on {t.device}, expected {dev}")
+    if tuple(t.shape) != tuple(int(v) for v in shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _flat(t, name: str, dtype, n: int, dev: torch.device):
+    """A caller-given buffer read or written as n consecutive elements."""
+    _require(t, dtype, name)
+    if t.device != dev:
+        raise ValueError(f"{name} is on {t.device}, expected {dev}")
+    if t.numel() != n or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous tensor of {n} elements, got shape {tuple(t.shape)}")
+    return t
+
+
+def _nvfp4(t: "NVFP4Tensor", name: str, R: int, K: int, dev: torch.device):
+    _buf(t.q, f"{name}.q", torch.uint8, (R, K // 2), dev)
+    _buf(t.scales, f"{name}.scales", torch.uint8, (R, K // 16), dev)
+    _buf(t.ts, f"{name}.ts", torch.float32, (2,), dev)
+
+
+def _mx(t: "MXTensor", name: str, R: int, K: int, dev: torch.device):
+    if t.fmt not in ("mxfp4", "mxfp8"):
+        raise ValueError(f"{name}.fmt {t.fmt!r}")
+    _buf(t.q, f"{name}.q", torch.uint8, (R, K // 2 if t.fmt == "mxfp4" else K), dev)
+    _buf(t.scales, f"{name}.scales", torch.uint8, (R, K // 32), dev)
+
+
+def _bias(bias, N: int, dev: torch.device):
+    if bias is not None:
+        _buf(bias, "bias", torch.float32, (N,), dev)
 
 
 _ws = {}
@@ -105,6 +152,10 @@ def hadamard_quantize(x: torch.Tensor, had_block: int = 64, fmt: str = "nvfp4", 
         raise ValueError("x must be a 2-D tensor with unit column stride")
     M, K = x.shape
     dev = x.device
+    if K % 16:
+        raise ValueError(f"K = {K} is not a multiple of 16")
+    if out is not None and stats and out.stats is not None:
+        _buf(out.stats, "out.stats", torch.float64, (4,), dev)
     flags = (L.STATS if stats else 0) | (L.GELU if gelu else 0)
     st = torch.empty(4, dtype=torch.float64, device=dev) if stats else None
     nbytes = L.lib().vdtq_workspace_bytes(L.OP_HADAMARD_QUANTIZE, M, K)
@@ -113,6 +164,7 @@ def hadamard_quantize(x: torch.Tensor, had_block: int = 64, fmt: str = "nvfp4", 
         st = out.stats
     if fmt == "nvfp4":
         if out is not None:
+            _nvfp4(out, "out", M, K, dev)
             q, s, ts = out.q, out.scales, out.ts
         else:
             q = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
@@ -129,6 +181,8 @@ def hadamard_quantize(x: torch.Tensor, had_block: int = 64, fmt: str = "nvfp4", 
         if amax is not None:
             raise ValueError("amax applies to nvfp4 only")
         if out is not None:
+            _buf(out.q, "out.q", torch.int8, (M, K), dev)
+            _buf(out.scales, "out.scales", torch.float32, (M,), dev)
             q, s = out.q, out.scales
         else:
             q = torch.empty((M, K), dtype=torch.int8, device=dev)
@@ -138,6 +192,8 @@ def hadamard_quantize(x: torch.Tensor, had_block: int = 64, fmt: str = "nvfp4", 
     elif fmt == "bf16":
         if amax is not None:
             raise ValueError("amax applies to nvfp4 only")
+        if out is not None:
+            _buf(out.q, "out.q", torch.bfloat16, (M, K), dev)
         q = out.q if out is not None else torch.empty((M, K), dtype=torch.bfloat16, device=dev)
         s = ts = None
         fcode = L.FMT_BF16
@@ -145,6 +201,9 @@ def hadamard_quantize(x: torch.Tensor, had_block: int = 64, fmt: str = "nvfp4", 
         if amax is not None:
             raise ValueError("amax applies to nvfp4 only")
         if out is not None:
+            if getattr(out, "fmt", fmt) != fmt:
+                raise ValueError(f"out holds {out.fmt}, asked for {fmt}")
+            _mx(MXTensor(out.q, out.scales, fmt), "out", M, K, dev)
             q, s = out.q, out.scales
         else:
             q = torch.empty((M, K // 2 if fmt == "mxfp4" else K), dtype=torch.uint8, device=dev)
@@ -165,18 +224,31 @@ def hadamard_quantize(x: torch.Tensor, had_block: int = 64, fmt: str = "nvfp4", 
 
 
 def _out(M, N, out_dtype, dev, y):
-    if y is not None:
-        return y
-    return torch.empty((M, N), dtype=torch.bfloat16 if out_dtype == "bf16" else torch.float32, device=dev)
+    """The GEMM output: a caller-given y must be [M, N] of the output dtype
+    on `dev` with unit column stride (its row stride is passed as ldy)."""
+    if out_dtype not in ("bf16", "f32"):
+        raise ValueError(f"out_dtype {out_dtype!r}")
+    dt = torch.bfloat16 if out_dtype == "bf16" else torch.float32
+    if y is None:
+        return torch.empty((M, N), dtype=dt, device=dev)
+    _require(y, dt, "y")
+    if y.device != dev:
+        raise ValueError(f"y is on {y.device}, expected {dev}")
+    if tuple(y.shape) != (M, N) or (M > 0 and N > 0 and (y.stride(1) != 1 or y.stride(0) < N)):
+        raise ValueError(f"y must be [{M}, {N}] with unit column stride, got shape {tuple(y.shape)} "
+                         f"strides {tuple(y.stride())}")
+    return y
 
 
 def qgemm_w4a4(a: NVFP4Tensor, w: NVFP4Tensor, bias: Optional[torch.Tensor] = None,
                out_dtype: str = "bf16", y: Optional[torch.Tensor] = None) -> torch.Tensor:
     M, K = a.q.shape[0], a.q.shape[1] * 2
     N = w.q.shape[0]
-    if w.q.shape[1] * 2 != K:
-        raise ValueError("K mismatch between activations and weights")
-    y = _out(M, N, out_dtype, a.q.device, y)
+    dev = a.q.device
+    _nvfp4(a, "a", M, K, dev)
+    _nvfp4(w, "w", N, K, dev)
+    _bias(bias, N, dev)
+    y = _out(M, N, out_dtype, dev, y)
     ws = gemm_workspace(a.q.device, M, N)
     L.check(L.lib().qgemm_w4a4(_p(a.q), _p(a.scales), _p(a.ts), _p(w.q), _p(w.scales), _p(w.ts), _p(bias),
                                _p(y), y.stride(0), L.OUT_BF16 if out_dtype == "bf16" else L.OUT_F32,
@@ -188,9 +260,12 @@ def qgemm_w4a8(a: INT8Tensor, w: NVFP4Tensor, bias: Optional[torch.Tensor] = Non
                out_dtype: str = "bf16", y: Optional[torch.Tensor] = None) -> torch.Tensor:
     M, K = a.q.shape
     N = w.q.shape[0]
-    if w.q.shape[1] * 2 != K:
-        raise ValueError("K mismatch between activations and weights")
-    y = _out(M, N, out_dtype, a.q.device, y)
+    dev = a.q.device
+    _buf(a.q, "a.q", torch.int8, (M, K), dev)
+    _buf(a.scales, "a.scales", torch.float32, (M,), dev)
+    _nvfp4(w, "w", N, K, dev)
+    _bias(bias, N, dev)
+    y = _out(M, N, out_dtype, dev, y)
     ws = gemm_workspace(a.q.device, M, N)
     L.check(L.lib().qgemm_w4a8(_p(a.q), _p(a.scales), _p(w.q), _p(w.scales), _p(w.ts), _p(bias),
                                _p(y), y.stride(0), L.OUT_BF16 if out_dtype == "bf16" else L.OUT_F32,
@@ -206,9 +281,10 @@ def qgemm_w4a16(a: BF16Tensor, w: NVFP4Tensor, bias: Optional[torch.Tensor] = No
         raise ValueError("a.q must be a contiguous [M, K] tensor")
     M, K = a.q.shape
     N = w.q.shape[0]
-    if w.q.shape[1] * 2 != K:
-        raise ValueError("K mismatch between activations and weights")
-    y = _out(M, N, out_dtype, a.q.device, y)
+    dev = a.q.device
+    _nvfp4(w, "w", N, K, dev)
+    _bias(bias, N, dev)
+    y = _out(M, N, out_dtype, dev, y)
     L.check(L.lib().qgemm_w4a16(_p(a.q), _p(w.q), _p(w.scales), _p(w.ts), _p(bias), _p(y), y.stride(0),
                                 L.OUT_BF16 if out_dtype == "bf16" else L.OUT_F32, M, N, K,
                                 _stream(a.q.device)))
@@ -223,9 +299,11 @@ def qgemm_mx(a: MXTensor, w: MXTensor, bias: Optional[torch.Tensor] = None,
     M = a.q.shape[0]
     K = a.q.shape[1] * (2 if a.fmt == "mxfp4" else 1)
     N = w.q.shape[0]
-    if w.q.shape[1] * 2 != K:
-        raise ValueError("K mismatch between activations and weights")
-    y = _out(M, N, out_dtype, a.q.device, y)
+    dev = a.q.device
+    _mx(a, "a", M, K, dev)
+    _mx(w, "w", N, K, dev)
+    _bias(bias, N, dev)
+    y = _out(M, N, out_dtype, dev, y)
     ws = gemm_workspace(a.q.device, M, N)
     L.check(L.lib().qgemm_mx(L.FMT_MXFP4 if a.fmt == "mxfp4" else L.FMT_MXFP8, _p(a.q), _p(a.scales), _p(w.q),
                              _p(w.scales), _p(bias), _p(y), y.stride(0),
@@ -246,9 +324,15 @@ def qgemm_mx_quant(a: MXTensor, w: MXTensor, bias: Optional[torch.Tensor] = None
     M = a.q.shape[0]
     K = a.q.shape[1] * (2 if a.fmt == "mxfp4" else 1)
     N = w.q.shape[0]
-    if w.q.shape[1] * 2 != K:
-        raise ValueError("K mismatch between activations and weights")
     dev = a.q.device
+    _mx(a, "a", M, K, dev)
+    _mx(w, "w", N, K, dev)
+    if bias is not None:
+        _bias(bias, N, dev)
+    if out is not None:
+        if out.fmt != out_fmt:
+            raise ValueError(f"out holds {out.fmt}, asked for {out_fmt}")
+        _mx(out, "out", M, N, dev)
     if out is None:
         q = torch.empty((M, N // 2 if out_fmt == "mxfp4" else N), dtype=torch.uint8, device=dev)
         s = torch.empty((M, N // 32), dtype=torch.uint8, device=dev)
@@ -269,6 +353,14 @@ def block_stats(inp: torch.Tensor, out: torch.Tensor, dprev: Optional[torch.Tens
         raise ValueError("inp/out must be contiguous tensors of one shape")
     n = inp.numel()
     dev = inp.device
+    if out.device != dev:
+        raise ValueError("inp and out must be on one device")
+    if dprev is not None:
+        _flat(dprev, "dprev", torch.bfloat16, n, dev)
+    if dnew is not None:
+        _flat(dnew, "dnew", torch.bfloat16, n, dev)
+        if dprev is not None and n > 0 and dnew.data_ptr() == dprev.data_ptr():
+            raise ValueError("dnew must not alias dprev")
     if dnew is None and write_delta:
         dnew = torch.empty_like(inp)
     st = torch.empty(8, dtype=torch.float64, device=dev)
@@ -289,6 +381,18 @@ def block_stats_mx8(inp: torch.Tensor, out: torch.Tensor, dprev: Optional[MXTens
         raise ValueError("inp/out must be contiguous tensors of one shape")
     n = inp.numel()
     dev = inp.device
+    if out.device != dev:
+        raise ValueError("inp and out must be on one device")
+    if n % 32:
+        raise ValueError(f"n = {n} is not a multiple of 32")
+    for name, d in (("dprev", dprev), ("dnew", dnew)):
+        if d is not None:
+            if d.fmt != "mxfp8":
+                raise ValueError(f"{name} must be an mxfp8 MXTensor")
+            _flat(d.q, f"{name}.q", torch.uint8, n, dev)
+            _flat(d.scales, f"{name}.scales", torch.uint8, n // 32, dev)
+    if dprev is not None and dnew is not None and n > 0 and dnew.q.data_ptr() == dprev.q.data_ptr():
+        raise ValueError("dnew must not alias dprev")
     if dnew is None and write_delta:
         dnew = MXTensor(torch.empty(n, dtype=torch.uint8, device=dev),
                         torch.empty(n // 32, dtype=torch.uint8, device=dev), "mxfp8")
