@@ -434,6 +434,28 @@ double vdtq_outlier_ratio(double max_abs, double sum_abs, int64_t n);
  */
 double dmpq_budget_gamma(const double* gammas, int32_t n, double avg_bits);
 
+/*
+ * dmpq_depth_params -- one block's scheduler parameters under a depth-aware
+ * caching profile.
+ *
+ * Defined by: [yly] §五 (blocks at different depths of the transformer have
+ * different temporal stability, the basis the page gives for a layered,
+ * adaptive caching policy) over the skip rule of dmpq_step ([gist] §2.B).
+ *
+ * *out = *base except that, with d = depth / (n_blocks - 1) (0 when
+ * n_blocks == 1) and s = s_shallow + (s_deep - s_shallow) * d (double,
+ * in that order), out->tau = base->tau * s and out->tau_acc =
+ * base->tau_acc * s: the skip thresholds move linearly with relative
+ * depth from s_shallow at the first block to s_deep at the last.  gamma,
+ * rho, tau_u and warmup are copied unchanged.  s_shallow = s_deep = 1 gives
+ * *base back.  out may alias base.
+ * Errors: VDTQ_EINVAL for a null pointer, n_blocks <= 0, depth outside
+ * [0, n_blocks), or a factor that is negative or not finite (out untouched).
+ * Pure host code; allocates nothing.
+ */
+int dmpq_depth_params(const vdtq_dmpq_params* base, int32_t depth, int32_t n_blocks,
+                      double s_shallow, double s_deep, vdtq_dmpq_params* out);
+
 #ifdef __cplusplus
 }
 #endif

@@ -27,7 +27,7 @@ One call per block per denoising step:
 from __future__ import annotations
 
 import math
-from dataclasses import dataclass
+from dataclasses import dataclass, replace
 
 from .stats import gamma as _gamma, delta_change as _delta_change
 
@@ -103,3 +103,28 @@ def budget_gamma(gammas, avg_bits: float) -> float:
     k = max(0, min(n, k))
     return math.inf if k == 0 else g[k - 1]
 
+
+def depth_params(p: Params, depth: int, n_blocks: int, s_shallow: float, s_deep: float) -> Params:
+    """Depth-aware caching thresholds.  [yly] §五: blocks at different depths
+    of the transformer show different temporal stability, which the page
+    offers as the basis of a layered caching policy; it gives no formula.
+
+    Reading: a block's two skip thresholds (tau and tau_acc) are the common
+    ones scaled by a factor that moves linearly with the block's relative
+    depth d = depth / (n_blocks - 1) (d = 0 for a single block), from
+    s_shallow at the first block to s_deep at the last:
+        s = s_shallow + (s_deep - s_shallow) * d
+        tau_b = tau * s,  tau_acc_b = tau_acc * s
+    in float64, in that order.  A factor above 1 lets a block skip more
+    (and drift further before a refresh), below 1 less, 0 never.  The
+    precision thresholds (gamma, rho, tau_u) and warmup are unchanged: the
+    page ties depth to temporal redundancy only.  s_shallow = s_deep = 1 is
+    the uniform scheduler."""
+    if n_blocks <= 0 or not 0 <= depth < n_blocks:
+        raise ValueError("depth outside [0, n_blocks)")
+    for v in (s_shallow, s_deep):
+        if not (math.isfinite(v) and v >= 0.0):
+            raise ValueError("depth factors must be finite and >= 0")
+    d = 0.0 if n_blocks == 1 else float(depth) / float(n_blocks - 1)
+    s = s_shallow + (s_deep - s_shallow) * d
+    return replace(p, tau=p.tau * s, tau_acc=p.tau_acc * s)

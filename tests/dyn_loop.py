@@ -47,10 +47,15 @@ def _step_gammas(last, gamma_of_state):
     return out
 
 
-def oracle_loop(w, params: OD.Params, record=None, budget=None):
+def oracle_loop(w, params: OD.Params, record=None, budget=None, profile=None):
     """Returns (actions int[B, T], stats dict (b, t) -> float64[8]).
     budget: average activation bits of the bit-budget mode (each step's
-    Gamma threshold from the oracle's budget_gamma), or None."""
+    Gamma threshold from the oracle's budget_gamma), or None.
+    profile: (s_shallow, s_deep) of the depth-aware skip thresholds (each
+    block's parameters from the oracle's depth_params), or None.
+    record(b, t, action, ratio, params, state_before, last_stats) sees every
+    decision with the block's parameters, its state before the call and the
+    statistics passed in."""
     B, T = w.blocks, w.steps
     acts = np.zeros((B, T), np.int32)
     stats = {}
@@ -68,7 +73,9 @@ def oracle_loop(w, params: OD.Params, record=None, budget=None):
             x = _spiked(w, b, t, x)
             _, rs = OS.block_stats(x, x)
             ratio = OS.outlier_ratio(rs[4], rs[5], n)
-            a = OD.dmpq_step(p_t, st[b], last[b], ratio)
+            p_tb = p_t if profile is None else OD.depth_params(p_t, b, B, *profile)
+            before, last_before = dataclasses.replace(st[b]), last[b]
+            a = OD.dmpq_step(p_tb, st[b], last[b], ratio)
             acts[b, t] = a
             if a == OD.SKIP:
                 out = F.f32_to_bf16((F.bf16_to_f32(x) + F.bf16_to_f32(cache[b])).astype(np.float32))
@@ -80,17 +87,19 @@ def oracle_loop(w, params: OD.Params, record=None, budget=None):
                 last[b] = s
                 cache[b] = dnew
             if record is not None:
-                record(b, t, a, ratio)
+                record(b, t, a, ratio, p_tb, before, last_before)
             x = out
     return acts, stats
 
 
-def gpu_loop(w, params, sample=(), on_sample=None, budget=None):
+def gpu_loop(w, params, sample=(), on_sample=None, budget=None, profile=None):
     """The same loop through libvdtq: block_stats on the device, dmpq_step in
     the library's C code.  Delta_{b,t} is formed on the device from the same
     seeded fields.  For (b, t) in `sample`, on_sample(b, t, in, out, cache,
     dnew, stats) receives the device operands (cache None on a block's first
-    computed step) and the statistics the library returned."""
+    computed step) and the statistics the library returned.  profile: as
+    for oracle_loop, each block's parameters from the library's
+    dmpq_depth_params."""
     import torch
     import video_diffusion_transformer_block_amd as V
 
@@ -120,7 +129,8 @@ def gpu_loop(w, params, sample=(), on_sample=None, budget=None):
             _, rs = V.block_stats(x, x)
             rs = rs.cpu().numpy()
             ratio = V.outlier_ratio(rs[4], rs[5], n)
-            a = V.dmpq_step(p_t, st[b], last[b], ratio)
+            p_tb = p_t if profile is None else V.dmpq_depth_params(p_t, b, B, *profile)
+            a = V.dmpq_step(p_tb, st[b], last[b], ratio)
             acts[b, t] = a
             if a == V.ACT_SKIP:
                 out = (x.float() + cache[b].float()).to(torch.bfloat16)

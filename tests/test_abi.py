@@ -261,3 +261,26 @@ def test_dmpq_budget_gamma_matches_oracle():
         assert V.dmpq_budget_gamma(g, bits) == D.budget_gamma(g, bits), (trial, n, bits)
     assert V.dmpq_budget_gamma([0.2, 0.1], math.nan) == math.inf
     assert V.lib().dmpq_budget_gamma(None, 4, 6.0) == math.inf
+
+
+def test_dmpq_depth_params_matches_oracle():
+    """The C depth profile equals the oracle's bit for bit (same float64
+    steps), for random bases, depths and factors, and rejects bad input."""
+    rng = np.random.Generator(np.random.PCG64(91))
+    for _ in range(500):
+        n = int(rng.integers(1, 64))
+        depth = int(rng.integers(0, n))
+        s0, s1 = (float(v) for v in rng.uniform(0, 3, 2))
+        base = dict(gamma=float(rng.uniform(0, 1)), tau=float(rng.uniform(0, 0.2)),
+                    tau_acc=float(rng.uniform(0, 0.5)), rho=float(rng.uniform(1, 500)),
+                    tau_u=float(rng.choice([math.inf, rng.uniform(0, 1)])), warmup=int(rng.integers(0, 5)))
+        got = V.dmpq_depth_params(V.dmpq_params(**base), depth, n, s0, s1)
+        want = D.depth_params(D.Params(**base), depth, n, s0, s1)
+        assert (got.gamma, got.tau, got.tau_acc, got.rho, got.tau_u, got.warmup) == \
+               (want.gamma, want.tau, want.tau_acc, want.rho, want.tau_u, want.warmup)
+    base = V.dmpq_params()
+    out = L.DmpqParams()
+    for args in ((-1, 4, 1.0, 1.0), (4, 4, 1.0, 1.0), (0, 0, 1.0, 1.0), (0, 4, -0.5, 1.0),
+                 (0, 4, 1.0, math.inf), (0, 4, math.nan, 1.0)):
+        assert V.lib().dmpq_depth_params(ctypes.byref(base), *args, ctypes.byref(out)) == L.EINVAL
+    assert V.lib().dmpq_depth_params(None, 0, 1, 1.0, 1.0, ctypes.byref(out)) == L.EINVAL

@@ -80,3 +80,61 @@ def test_closed_loop_full_size_sampled():
     log(f"  actions skip/nvfp4/int8/bf16 = {counts.tolist()}, checked {len(checked)}")
     assert (counts > 0).all()
     assert len(checked) >= 8
+
+
+def _decision_margins(w, p, profile):
+    """Oracle loop with every compared quantity's relative distance to its
+    threshold: r_last vs tau_b (and acc + r vs tau_acc_b where r < tau_b),
+    Gamma_{t-1} vs gamma, the outlier ratio vs rho."""
+    import math
+    mins = {"tau": math.inf, "tau_acc": math.inf, "gamma": math.inf, "rho": math.inf}
+
+    def rec(b, t, a, ratio, pb, before, last):
+        r, has_d2, acc, g, hg = before.r_last, before.has_d2, before.acc, before.gamma_prev, before.has_gamma
+        if last is not None:
+            g, hg = OS.gamma(last), True
+            if before.has_d1:
+                r = OS.delta_change(last)
+            has_d2, acc = before.has_d1, 0.0
+        if t >= pb.warmup and has_d2 and math.isfinite(r):
+            mins["tau"] = min(mins["tau"], abs(r - pb.tau) / pb.tau)
+            if r < pb.tau:
+                mins["tau_acc"] = min(mins["tau_acc"], abs(acc + r - pb.tau_acc) / pb.tau_acc)
+        if a != OD.SKIP:
+            mins["rho"] = min(mins["rho"], abs(ratio - pb.rho) / pb.rho)
+            if hg and math.isfinite(g):
+                mins["gamma"] = min(mins["gamma"], abs(g - pb.gamma) / pb.gamma)
+
+    acts, stats = dyn_loop.oracle_loop(w, p, record=rec, profile=profile)
+    return acts, stats, mins
+
+
+def test_closed_loop_depth_profile_matches_oracle():
+    """Depth-aware caching thresholds: tau and tau_acc scaled from 1/2 at the
+    first block to 3/2 at the last (dmpq_depth_params in C, depth_params in
+    the oracle).  Every compared statistic stays at least 1e-4 (relative)
+    from its block's threshold on the oracle side, ten times the statistics
+    tolerance, so the 1500 actions must be identical; the profile moves
+    skips from the shallow third of the blocks to the deep third."""
+    need_gpu()
+    w = synth.DynWorkload(M=35)
+    p = dict(gamma=0.1, tau=0.05, tau_acc=0.15, rho=400.0)
+    prof = (0.5, 1.5)
+    want_acts, want_stats, mins = _decision_margins(w, OD.Params(**p), prof)
+    log(f"  depth profile margins {mins}")
+    assert min(mins.values()) >= 1e-4
+    got_acts, got_stats = dyn_loop.gpu_loop(w, V.dmpq_params(**p), profile=prof)
+    bad = np.argwhere(got_acts != want_acts)
+    assert len(bad) == 0, f"first differing (block, step): {bad[:5].tolist()}"
+    for k in want_stats:
+        same_stats(got_stats[k], want_stats[k])
+    counts = np.bincount(got_acts.ravel(), minlength=4)
+    uni, _ = dyn_loop.oracle_loop(w, OD.Params(**p))
+    third = w.blocks // 3
+    sk = (got_acts == OD.SKIP).sum(1)
+    sk_u = (uni == OD.SKIP).sum(1)
+    log(f"  depth profile actions skip/nvfp4/int8/bf16 = {counts.tolist()}; skips by depth third "
+        f"{[int(sk[:third].sum()), int(sk[third:2 * third].sum()), int(sk[2 * third:].sum())]} (uniform "
+        f"{[int(sk_u[:third].sum()), int(sk_u[third:2 * third].sum()), int(sk_u[2 * third:].sum())]})")
+    assert (counts > 0).all()
+    assert sk[:third].sum() < sk_u[:third].sum() and sk[2 * third:].sum() > sk_u[2 * third:].sum()

@@ -19,7 +19,7 @@ OP_HADAMARD_QUANTIZE, OP_BLOCK_STATS, OP_QGEMM = 0, 1, 2
 
 # every extern "C" symbol include/vdtq.h declares
 EXPORTED = ["vdtq_last_error", "vdtq_version", "vdtq_workspace_bytes", "hadamard_quantize",
-            "qgemm_w4a4", "qgemm_w4a8", "qgemm_w4a16", "qgemm_mx", "qgemm_mx_quant", "block_stats", "block_stats_mx8", "dmpq_state_init", "dmpq_step", "dmpq_budget_gamma",
+            "qgemm_w4a4", "qgemm_w4a8", "qgemm_w4a16", "qgemm_mx", "qgemm_mx_quant", "block_stats", "block_stats_mx8", "dmpq_state_init", "dmpq_step", "dmpq_budget_gamma", "dmpq_depth_params",
             "vdtq_outlier_ratio"]
 
 
@@ -87,6 +87,9 @@ def lib() -> ctypes.CDLL:
             L.dmpq_step.restype = i32
             L.dmpq_step.argtypes = [ctypes.POINTER(DmpqParams), ctypes.POINTER(DmpqState),
                                     ctypes.POINTER(ctypes.c_double), dbl, ctypes.POINTER(ctypes.c_int)]
+            L.dmpq_depth_params.restype = i32
+            L.dmpq_depth_params.argtypes = [ctypes.POINTER(DmpqParams), i32, i32, dbl, dbl,
+                                            ctypes.POINTER(DmpqParams)]
             L.vdtq_outlier_ratio.restype = dbl
             L.vdtq_outlier_ratio.argtypes = [dbl, dbl, i64]
             _lib = L

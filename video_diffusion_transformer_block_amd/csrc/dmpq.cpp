@@ -78,4 +78,20 @@ double dmpq_budget_gamma(const double* gammas, int32_t n, double avg_bits) {
   return INFINITY;   // unreachable for comparable values
 }
 
+// Depth-aware caching profile (youleyou.com article §五: temporal stability
+// differs with block depth): the skip thresholds scale linearly with the
+// block's relative depth.
+int dmpq_depth_params(const vdtq_dmpq_params* base, int32_t depth, int32_t n_blocks, double s_shallow,
+                      double s_deep, vdtq_dmpq_params* out) {
+  if (!base || !out || n_blocks <= 0 || depth < 0 || depth >= n_blocks) return VDTQ_EINVAL;
+  if (!isfinite(s_shallow) || !isfinite(s_deep) || s_shallow < 0.0 || s_deep < 0.0) return VDTQ_EINVAL;
+  const double d = n_blocks == 1 ? 0.0 : (double)depth / (double)(n_blocks - 1);
+  const double s = s_shallow + (s_deep - s_shallow) * d;
+  vdtq_dmpq_params r = *base;
+  r.tau = base->tau * s;
+  r.tau_acc = base->tau_acc * s;
+  *out = r;
+  return VDTQ_OK;
+}
+
 }  // extern "C"

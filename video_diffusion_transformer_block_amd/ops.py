@@ -413,6 +413,17 @@ def dmpq_budget_gamma(gammas, avg_bits: float = 6.0) -> float:
     return float(L.lib().dmpq_budget_gamma(arr, len(g), float(avg_bits)))
 
 
+def dmpq_depth_params(base: L.DmpqParams, depth: int, n_blocks: int, s_shallow: float,
+                      s_deep: float) -> L.DmpqParams:
+    """Host call: block `depth` of `n_blocks`' parameters under a depth-aware
+    caching profile (tau and tau_acc scaled linearly with relative depth,
+    from s_shallow at the first block to s_deep at the last)."""
+    out = L.DmpqParams()
+    L.check(L.lib().dmpq_depth_params(ctypes.byref(base), int(depth), int(n_blocks), float(s_shallow),
+                                      float(s_deep), ctypes.byref(out)))
+    return out
+
+
 def dmpq_params(gamma=0.1, tau=0.05, tau_acc=0.15, rho=50.0, tau_u=math.inf, warmup=2) -> L.DmpqParams:
     return L.DmpqParams(gamma, tau, tau_acc, rho, tau_u, warmup, 0)
 
