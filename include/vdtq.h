@@ -168,6 +168,34 @@ int hadamard_quantize(const void* x_dev, int64_t M, int64_t K, int64_t ldx,
                       void* stream);
 
 /*
+ * hadamard_quantize_noalloc -- hadamard_quantize without a workspace
+ * argument, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ *
+ * Same operation, arguments, outputs and errors as hadamard_quantize, minus
+ * ws_dev/ws_bytes.  The per-workgroup partials and the GELU table live in a
+ * library-owned device array of VDTQ_NOALLOC_SCRATCH_BYTES, one per GPU,
+ * held from the first call on that GPU until the process ends; the call
+ * allocates nothing (no hipMalloc, hipFree or allocating library routine).
+ * Everything in that array is written before it is read within a call, so
+ * no state carries over between calls; but every call on one GPU shares the
+ * array, so calls that overlap in time on one GPU (different streams, or
+ * host threads racing on one device) race on it and give undefined
+ * results.  Calls on one stream run in order and are safe.
+ * Errors: those of hadamard_quantize; VDTQ_EUNSUPPORTED when the call would
+ * need more than VDTQ_NOALLOC_SCRATCH_BYTES
+ * (vdtq_workspace_bytes(VDTQ_OP_HADAMARD_QUANTIZE, M, K) above it: about
+ * 36 bytes per 8192 elements or per row, whichever is more, i.e. up to
+ * about 1.9e9 elements or 233k rows); VDTQ_EHIP if the array's device
+ * address cannot be obtained.
+ */
+#define VDTQ_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+int hadamard_quantize_noalloc(const void* x_dev, int64_t M, int64_t K, int64_t ldx,
+                              int had_block, int fmt, unsigned flags, void* q_dev,
+                              void* scales_dev, float* tensor_scale_dev,
+                              double* stats_dev, void* stream);
+
+/*
  * qgemm_w4a4 -- Y = gs_a * gs_w * (A_hat W_hat^T) + bias with NVFP4
  * activations A [M][K] and NVFP4 weights W [N][K] (both rotated by the same
  * block Hadamard transform along K, so Y is the linear layer's output).

@@ -74,6 +74,39 @@ def test_hadamard_quantize_rejects(kw, code):
     assert V.lib().vdtq_last_error()
 
 
+@pytest.mark.parametrize("kw,code", [
+    (dict(K=15), L.EINVAL), (dict(b=48), L.EINVAL), (dict(x=None), L.EINVAL), (dict(x=FAKE8), L.EINVAL),
+    (dict(fmt=1, flags=1), L.EINVAL), (dict(ts=None), L.EINVAL), (dict(flags=2, st=None), L.EINVAL),
+    (dict(fmt=1, K=16384 + 64, ldx=16448), L.EUNSUPPORTED),
+])
+def test_hadamard_quantize_noalloc_rejects_like_the_workspace_call(kw, code):
+    """The allocation-free entry point shares hadamard_quantize's checks."""
+    a = dict(x=FAKE, M=4, K=64, ldx=64, b=64, fmt=0, flags=0, q=FAKE, s=FAKE, ts=FAKE, st=None)
+    a.update(kw)
+    rc = V.lib().hadamard_quantize_noalloc(a["x"], a["M"], a["K"], a["ldx"], a["b"], a["fmt"], a["flags"], a["q"],
+                                           a["s"], a["ts"], a["st"], None)
+    assert rc == code and V.lib().vdtq_last_error()
+
+
+@pytest.mark.parametrize("M,K,fmt", [(250000, 3072, 1), (240000, 64, 0), (17776 * 12, 12288, 0)])
+def test_hadamard_quantize_noalloc_rejects_beyond_its_scratch(M, K, fmt):
+    """Sizes whose partials exceed the static scratch array are refused
+    before anything runs (no device is needed to see it)."""
+    lib = V.lib()
+    assert lib.vdtq_workspace_bytes(L.OP_HADAMARD_QUANTIZE, M, K) > L.NOALLOC_SCRATCH_BYTES
+    rc = lib.hadamard_quantize_noalloc(FAKE, M, K, K, 64, fmt, 0, FAKE, FAKE, FAKE, None, None)
+    assert rc == L.EUNSUPPORTED and b"maximum" in lib.vdtq_last_error()
+
+
+def test_noalloc_scratch_bound_is_the_header_constant():
+    src = open(HEADER).read()
+    m = re.search(r"#define VDTQ_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", src)
+    assert m and int(m.group(1)) << int(m.group(2)) == L.NOALLOC_SCRATCH_BYTES
+    # the 5B and 1080p shapes of the block fit
+    for M, K in ((17776, 3072), (17776, 12288), (106306, 3072), (106306, 12288)):
+        assert V.lib().vdtq_workspace_bytes(L.OP_HADAMARD_QUANTIZE, M, K) <= L.NOALLOC_SCRATCH_BYTES
+
+
 def _gemm(fn, **kw):
     a = dict(aq=FAKE, as_=FAKE, ats=FAKE, wq=FAKE, ws=FAKE, wts=FAKE, bias=None, y=FAKE, ldy=64, od=0,
              M=8, N=64, K=64, gws=FAKE, gwsb=1 << 28)

@@ -16,9 +16,10 @@ OUT_BF16, OUT_F32 = 0, 1
 AMAX_GIVEN, STATS, GELU = 1, 2, 4
 ACT_SKIP, ACT_NVFP4, ACT_INT8, ACT_BF16 = 0, 1, 2, 3
 OP_HADAMARD_QUANTIZE, OP_BLOCK_STATS, OP_QGEMM = 0, 1, 2
+NOALLOC_SCRATCH_BYTES = 8 << 20      # VDTQ_NOALLOC_SCRATCH_BYTES
 
 # every extern "C" symbol include/vdtq.h declares
-EXPORTED = ["vdtq_last_error", "vdtq_version", "vdtq_workspace_bytes", "hadamard_quantize",
+EXPORTED = ["vdtq_last_error", "vdtq_version", "vdtq_workspace_bytes", "hadamard_quantize", "hadamard_quantize_noalloc",
             "qgemm_w4a4", "qgemm_w4a8", "qgemm_w4a16", "qgemm_mx", "qgemm_mx_quant", "block_stats", "block_stats_mx8", "dmpq_state_init", "dmpq_step", "dmpq_budget_gamma", "dmpq_depth_params",
             "vdtq_outlier_ratio"]
 
@@ -66,6 +67,8 @@ def lib() -> ctypes.CDLL:
             L.vdtq_workspace_bytes.argtypes = [i32, i64, i64]
             L.hadamard_quantize.restype = i32
             L.hadamard_quantize.argtypes = [vp, i64, i64, i64, i32, i32, u32, vp, vp, vp, vp, vp, sz, vp]
+            L.hadamard_quantize_noalloc.restype = i32
+            L.hadamard_quantize_noalloc.argtypes = [vp, i64, i64, i64, i32, i32, u32, vp, vp, vp, vp, vp]
             L.qgemm_w4a4.restype = i32
             L.qgemm_w4a4.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i32, i64, i64, i64, vp, sz, vp]
             L.qgemm_w4a16.restype = i32

@@ -52,9 +52,11 @@ size_t vdtq_workspace_bytes(int op, int64_t M, int64_t K) {
   return 0;
 }
 
-int hadamard_quantize(const void* x_dev, int64_t M, int64_t K, int64_t ldx, int had_block, int fmt,
-                      unsigned flags, void* q_dev, void* scales_dev, float* tensor_scale_dev,
-                      double* stats_dev, void* ws_dev, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+// Every check of hadamard_quantize's arguments except the workspace.
+static int hq_check(const void* x_dev, int64_t M, int64_t K, int64_t ldx, int had_block, int fmt,
+                    unsigned flags, void* q_dev, void* scales_dev, float* tensor_scale_dev, double* stats_dev) {
   if (M < 0 || M > kI32) return fail(VDTQ_EINVAL, "hadamard_quantize: M=%lld out of range", (long long)M);
   if (K <= 0 || K > kI32 || K % 16) return fail(VDTQ_EINVAL, "hadamard_quantize: K=%lld must be a positive multiple of 16", (long long)K);
   if (had_block != 16 && had_block != 32 && had_block != 64 && had_block != 128 && had_block != 256)
@@ -83,6 +85,16 @@ int hadamard_quantize(const void* x_dev, int64_t M, int64_t K, int64_t ldx, int 
     return fail(VDTQ_EINVAL, "hadamard_quantize: NVFP4 needs an aligned tensor_scale (float[2])");
   if ((flags & VDTQ_STATS) && (!stats_dev || !aligned(stats_dev, 8)))
     return fail(VDTQ_EINVAL, "hadamard_quantize: VDTQ_STATS needs an aligned stats buffer (double[4])");
+  return VDTQ_OK;
+}
+
+extern "C" {
+
+int hadamard_quantize(const void* x_dev, int64_t M, int64_t K, int64_t ldx, int had_block, int fmt,
+                      unsigned flags, void* q_dev, void* scales_dev, float* tensor_scale_dev,
+                      double* stats_dev, void* ws_dev, size_t ws_bytes, void* stream) {
+  const int rc = hq_check(x_dev, M, K, ldx, had_block, fmt, flags, q_dev, scales_dev, tensor_scale_dev, stats_dev);
+  if (rc != VDTQ_OK) return rc;
   const bool need_ws = (flags & (VDTQ_STATS | VDTQ_GELU)) || (fmt == VDTQ_FMT_NVFP4 && !(flags & VDTQ_AMAX_GIVEN));
   if (need_ws) {
     const size_t need = vdtq::hq_workspace_bytes(M, K);
@@ -93,6 +105,24 @@ int hadamard_quantize(const void* x_dev, int64_t M, int64_t K, int64_t ldx, int 
                                                 tensor_scale_dev, stats_dev, ws_dev,
                                                 static_cast<hipStream_t>(stream));
   return hip_status(e, "hadamard_quantize launch");
+}
+
+int hadamard_quantize_noalloc(const void* x_dev, int64_t M, int64_t K, int64_t ldx, int had_block, int fmt,
+                              unsigned flags, void* q_dev, void* scales_dev, float* tensor_scale_dev,
+                              double* stats_dev, void* stream) {
+  const int rc = hq_check(x_dev, M, K, ldx, had_block, fmt, flags, q_dev, scales_dev, tensor_scale_dev, stats_dev);
+  if (rc != VDTQ_OK) return rc;
+  const size_t need = vdtq::hq_workspace_bytes(M, K);
+  if (need > VDTQ_NOALLOC_SCRATCH_BYTES)
+    return fail(VDTQ_EUNSUPPORTED,
+                "hadamard_quantize_noalloc: M=%lld K=%lld needs %zu bytes of scratch, above the %zu-byte maximum",
+                (long long)M, (long long)K, need, (size_t)VDTQ_NOALLOC_SCRATCH_BYTES);
+  void* scratch = nullptr;
+  hipError_t e = vdtq::hq_noalloc_scratch(&scratch);
+  if (e != hipSuccess) return hip_status(e, "hadamard_quantize_noalloc: scratch address");
+  e = vdtq::launch_hadamard_quantize(x_dev, M, K, ldx, had_block, fmt, flags, q_dev, scales_dev, tensor_scale_dev,
+                                     stats_dev, scratch, static_cast<hipStream_t>(stream));
+  return hip_status(e, "hadamard_quantize_noalloc launch");
 }
 
 static int qgemm_check(const char* name, const void* a_q, const void* a_s, const void* w_q, const void* w_s,

@@ -41,6 +41,9 @@
 //   * Statistics: fp32 over a thread's 64 elements, fp64 across threads and
 //     workgroups in a fixed order (bit-reproducible, no float atomics).
 #include <algorithm>
+#include <mutex>
+
+#include "../../include/vdtq.h"
 
 #include "device_common.h"
 #include "hadamard_common.h"
@@ -648,6 +651,34 @@ static size_t hq_partials_bytes(int64_t M, int64_t K) {
 }
 
 size_t hq_workspace_bytes(int64_t M, int64_t K) { return hq_partials_bytes(M, K) + kGeluTabBytes; }
+
+// ------------------------------------------------ allocation-free scratch
+// The workspace of hadamard_quantize_noalloc: a device array per GPU, in the
+// code object (no allocation call), holding the partials and the GELU table
+// exactly as a caller-given workspace would.  Host code never passes the
+// array's name to a kernel (on the host it is only a stand-in symbol): it
+// uses the device address hipGetSymbolAddress returns for the current
+// device, looked up on the first call on each device and kept.
+static __device__ __align__(256) uint8_t scratch[VDTQ_NOALLOC_SCRATCH_BYTES];
+
+hipError_t hq_noalloc_scratch(void** ptr) {
+  static std::mutex mu;
+  static void* addr[64] = {nullptr};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_hadamard_quantize(const void* x, int64_t M, int64_t K, int64_t ldx, int b, int fmt,
                                     unsigned flags, void* q, void* scales, float* ts,

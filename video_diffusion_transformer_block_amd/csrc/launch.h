@@ -28,6 +28,10 @@ hipError_t launch_hadamard_quantize(const void* x, int64_t M, int64_t K, int64_t
                                     unsigned flags, void* q, void* scales, float* ts,
                                     double* stats, void* ws, hipStream_t st);
 
+// Device address of this GPU's allocation-free scratch array
+// (VDTQ_NOALLOC_SCRATCH_BYTES, 256-byte aligned), looked up once per device.
+hipError_t hq_noalloc_scratch(void** ptr);
+
 size_t qgemm_workspace_bytes(int64_t M, int64_t N);
 hipError_t launch_qgemm(int afmt, const void* a_q, const void* a_s, const float* a_ts,
                         const uint8_t* w_q, const uint8_t* w_s, const float* w_ts,
