@@ -205,6 +205,9 @@ int hadamard_quantize_noalloc(const void* x_dev, int64_t M, int64_t K, int64_t l
  *
  * A_hat = e2m1(code) * e4m3(scale) per element (exact), W_hat likewise;
  * products and sums in fp32 (any order), result rounded to out_dtype.
+ * Scale bytes are non-negative E4M3 values (0x00 .. 0x7E), as
+ * hadamard_quantize writes them; a byte with the sign bit set gives
+ * unspecified (memory-safe) results.
  *
  * a_q_dev  uint8 [M][K/2]   a_s_dev uint8 [M][K/16]   a_ts_dev float[2] {amax, gs}
  * w_q_dev  uint8 [N][K/2]   w_s_dev uint8 [N][K/16]   w_ts_dev float[2] {amax, gs}

@@ -530,8 +530,13 @@ void qgemm_pipe_kernel(GemmParams p) {
     for (int j = 0; j < 4; ++j)
       sw[j] = *reinterpret_cast<const uint2*>(st + P::A_CODES + P::A_SC + P::W_CODES + (wn * 128 + 32 * j + r32) * 8);
   };
-  // scale pair of chunk c for this lane half: groups 4c + 2h, 4c + 2h + 1
-  auto scale_of = [&](const uint2& s8, int c) { return scale_pair_bits((c ? s8.y : s8.x) >> (16 * h)); };
+  // scale pair of chunk c for this lane half: groups 4c + 2h, 4c + 2h + 1.
+  // One byte permute moves bytes 2h and 2h + 1 of the chunk's dword into
+  // bytes 0 and 2 (zeros elsewhere) and one shift by 7 makes each 16-bit
+  // half the fp16 scale * 2^-8 of scale_pair_bits, for scale bytes with the
+  // sign bit clear (every scale the quantizer writes is >= 0).
+  const uint32_t ssel = 0x0C000C00u | ((2u * (uint32_t)h + 1u) << 16) | (2u * (uint32_t)h);
+  auto scale_of = [&](const uint2& s8, int c) { return __builtin_amdgcn_perm(0u, c ? s8.y : s8.x, ssel) << 7; };
 
   auto decode = [&](const Raw<A8>& R, const uint2 (&sa)[4], const uint2 (&sw)[4], int c, int s,
                     half8 (&af)[4], half8 (&bf)[4]) {
