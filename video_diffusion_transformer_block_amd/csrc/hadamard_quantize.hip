@@ -502,7 +502,27 @@ __global__ __launch_bounds__(T) void hq_int8_kernel(HQParams p) {
     uint32_t hi = __builtin_amdgcn_perm(b3, b2, 0x0c0c0400u);
     words[w] = ok ? (lo | (hi << 16)) : 0u;
   }
-  if (valid) {
+  if (p.flat) {
+    // The workgroup's codes are one contiguous run of its chunks (64 bytes
+    // each).  They leave through LDS so that every store instruction writes
+    // consecutive 16-byte vectors, not 16 bytes every 64.  The staging buffer
+    // is free: every thread read its chunk before the row-maximum barrier.
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      lds[4 * t + (i ^ (t & 3))] = make_uint4(words[4 * i], words[4 * i + 1], words[4 * i + 2], words[4 * i + 3]);
+    __syncthreads();
+    const int64_t g0 = (int64_t)blockIdx.x * p.rows_per_wg * p.cpr;
+    const int lim = (int)min<int64_t>((int64_t)p.rows_per_wg * p.cpr, p.total_chunks - g0);
+    uint4* dst = reinterpret_cast<uint4*>(p.q + g0 * 64);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int v16 = t + T * i;                       // 16-byte vector of the run
+      const int c = v16 >> 2, jj = v16 & 3;
+      if (v16 < 4 * lim) dst[v16] = lds[4 * c + (jj ^ (c & 3))];
+    }
+    if (valid && col == 0) reinterpret_cast<float*>(p.scales)[row] = s;
+  } else if (valid) {
     int8_t* qrow = reinterpret_cast<int8_t*>(p.q) + (int64_t)row * p.K + col * 64;
     for (int g = 0; g < 4; ++g)
       if (16 * g < nvalid)
@@ -578,7 +598,26 @@ __global__ __launch_bounds__(HQ_THREADS) void hq_mx_kernel(HQParams p) {
   uint32_t sbytes;
   mx_encode64<B, FP8>(v, words, sbytes);
 
-  if (valid) {
+  if (FP8 && p.flat) {
+    // E4M3 codes, 64 bytes per chunk: the workgroup's run leaves through LDS
+    // so that every store instruction writes consecutive 16-byte vectors
+    const int t = threadIdx.x;
+    __syncthreads();                                     // every chunk has been read from lds
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      lds[4 * t + (i ^ (t & 3))] = make_uint4(words[4 * i], words[4 * i + 1], words[4 * i + 2], words[4 * i + 3]);
+    __syncthreads();
+    const int64_t g0 = (int64_t)blockIdx.x * HQ_THREADS;
+    const int lim = (int)min<int64_t>(HQ_THREADS, p.total_chunks - g0);
+    uint4* dst = reinterpret_cast<uint4*>(p.q + g0 * 64);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int v16 = t + HQ_THREADS * i;
+      const int c = v16 >> 2, jj = v16 & 3;
+      if (v16 < 4 * lim) dst[v16] = lds[4 * c + (jj ^ (c & 3))];
+    }
+    if (valid) *reinterpret_cast<uint16_t*>(reinterpret_cast<uint8_t*>(p.scales) + (g0 + t) * 2) = (uint16_t)sbytes;
+  } else if (valid) {
     constexpr int BYTES = FP8 ? 64 : 32;                      // code bytes per chunk
     uint4* qrow = reinterpret_cast<uint4*>(p.q + (int64_t)row * (FP8 ? p.K : p.K / 2) + col * BYTES);
     uint8_t* srow = reinterpret_cast<uint8_t*>(p.scales) + (int64_t)row * (p.K / 32) + col * 2;
