@@ -23,7 +23,8 @@ offline (Hadamard-rotated + NVFP4) before timing.
 
 Besides the step, the JSON line carries: the dominant GEMM call against the
 fp16 MFMA peak (roofline, with counter traffic while the committed record
-matches the sources), each quantize pass against HBM peak, the MX GEMMs
+matches the sources), each quantize pass against HBM peak and against a
+plain streaming pass of the same bytes and launch size, the MX GEMMs
 against their own peaks, block_stats against HBM peak, the same four GEMMs
 in bf16 through torch / hipBLASLt (context), the 1080p FFN stress shape,
 the fused FFN-up -> FFN-down epilogue, the closed-loop schedule study, the
@@ -35,6 +36,7 @@ Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline]
 from __future__ import annotations
 
 import argparse
+import gc
 import json
 import math
 import os
@@ -117,6 +119,10 @@ def main():
         X[name], W[name] = up(x), V.hadamard_quantize(up(w), HAD_BLOCK, "nvfp4")  # offline weight prep
         if want_mx:
             WM[name] = V.hadamard_quantize(up(w), HAD_BLOCK, "mxfp4")
+    # the block's input: in the model the QKV linear reads LayerNorm(block
+    # input), another tensor, so block_stats reads a buffer of its own and
+    # does not warm the caches for the next step's QKV quantize
+    Xblk = X["qkv"].clone()
     dprev = torch.zeros((M, hidden), dtype=torch.bfloat16, device=dev)
     dnew = torch.empty_like(dprev)
     Y = {name: torch.empty((M, N), dtype=torch.bfloat16, device=dev) for name, K, N in linears}
@@ -151,7 +157,7 @@ def main():
             if rec is not None:
                 e2.record()
                 rec.append((name, fmt, e0, e1, e2))
-        _, st = V.block_stats(X["qkv"], Y["ffn_down"], dprev, dnew)
+        _, st = V.block_stats(Xblk, Y["ffn_down"], dprev, dnew)
         # The 8 statistics go to pinned host memory without blocking; the host
         # scheduler runs on them while the GPU works on the next step, as it
         # does when a model has more than one block.
@@ -183,6 +189,10 @@ def main():
         drain()
         torch.cuda.synchronize()
         rec = []
+        # no Python garbage collection inside the timed region: a collection
+        # pause on the host would leave the GPU idle between launches
+        gc.collect()
+        gc.disable()
         ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         tw = time.perf_counter()
         ev0.record()
@@ -192,6 +202,7 @@ def main():
         drain()
         torch.cuda.synchronize()
         wall = time.perf_counter() - tw
+        gc.enable()
         ms = ev0.elapsed_time(ev1) / args.steps
         # per-step times on the GPU timeline: from one step's first event to
         # the next step's (the last step ends at ev1)
@@ -276,7 +287,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    bsroof = measure_block_stats(torch, V, X["qkv"], Y["ffn_down"], M * hidden, args.steps)
+    bsroof = measure_block_stats(torch, V, Xblk, Y["ffn_down"], M * hidden, args.steps)
     bf16ctx = measure_bf16_context(torch, X, host, linears, M, args.steps, up)
     stress = None if args.no_stress else measure_1080p(torch, V, args.steps)
     ffn_fusion = measure_ffn_fusion(torch, V, X, WM, M, args.steps) if want_mx else None
@@ -323,6 +334,24 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(line))
+
+
+def bench_lib():
+    """libvdtq_bench.so: plain streaming passes that move a launch's bytes
+    with no arithmetic (the measured ceilings); not part of the library."""
+    import ctypes
+    path = os.path.join(ROOT, "video_diffusion_transformer_block_amd", "libvdtq_bench.so")
+    L = ctypes.CDLL(path)
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    L.vdtq_bench_stream_rows.restype = i32
+    L.vdtq_bench_stream_rows.argtypes = [vp, i64, i64, i32, i32, i32, vp, vp, vp, vp]
+    L.vdtq_bench_stream_3r1w.restype = i32
+    L.vdtq_bench_stream_3r1w.argtypes = [vp, vp, vp, vp, i64, vp]
+    return L
+
+
+# bytes a quantize launch writes per 64-element chunk (codes, scales) and per row
+STREAM_SHAPE = {"nvfp4": (32, 4, 0), "int8": (64, 0, 4), "mxfp4": (32, 2, 0), "mxfp8": (64, 2, 0)}
 
 
 def measure_dmpq(V, blocks=30, steps=50, reps=20):
@@ -382,8 +411,10 @@ def measure_dyn(torch, V, synth, blocks=30, steps=50, M=4446, hidden=1920):
     delta cache in MXFP8 (block_stats_mx8; a skipped block adds the
     dequantized cached delta); and once in bit-budget mode (each step's
     Gamma threshold from dmpq_budget_gamma for an average of 6 activation
-    bits over the ranked blocks).  Times are HIP events around each computed
-    block's quantize + GEMM."""
+    bits over the ranked blocks); and once with depth-aware skip thresholds
+    (tau and tau_acc scaled from 1/2 at the first block to 3/2 at the last,
+    dmpq_depth_params).  Times are HIP events around each computed block's
+    quantize + GEMM."""
     dev = torch.device("cuda:0")
     gen = torch.Generator(device=dev)
 
@@ -427,7 +458,7 @@ def measure_dyn(torch, V, synth, blocks=30, steps=50, M=4446, hidden=1920):
                 gs.append(states[b].gamma_prev)
         return V.dmpq_budget_gamma(gs, avg_bits)
 
-    def run(params, cache_fmt="bf16", budget=None):
+    def run(params, cache_fmt="bf16", budget=None, profile=None):
         states = [V.dmpq_state() for _ in range(blocks)]
         last = [None] * blocks
         cache = [None] * blocks
@@ -453,7 +484,8 @@ def measure_dyn(torch, V, synth, blocks=30, steps=50, M=4446, hidden=1920):
                     x[:, spike] = (x[:, spike].float() * 300.0).to(torch.bfloat16)
                 _, rs = V.block_stats(x, x, write_delta=False)
                 rs = rs.cpu().numpy()
-                act = V.dmpq_step(p_t, states[b], last[b], V.outlier_ratio(rs[4], rs[5], M * hidden))
+                p_tb = p_t if profile is None else V.dmpq_depth_params(p_t, b, blocks, *profile)
+                act = V.dmpq_step(p_tb, states[b], last[b], V.outlier_ratio(rs[4], rs[5], M * hidden))
                 acts.append(act)
                 if act == V.ACT_SKIP:
                     counts["skip"] += 1
@@ -499,12 +531,20 @@ def measure_dyn(torch, V, synth, blocks=30, steps=50, M=4446, hidden=1920):
     c8, per8, total8, wall8, acts8 = run(p_dyn, "mxfp8")
     same = float(np.mean(np.array(acts) == np.array(acts8)))
     cb, perb, totalb, wallb, _ = run(p_dyn, budget=6.0)
+    depth_prof = (0.5, 1.5)
+    cd, perd, totald, walld, actsd = run(p_dyn, profile=depth_prof)
+
+    def skips_by_third(a):
+        sk = (np.array(a).reshape(steps, blocks) == V.ACT_SKIP).sum(0)
+        th = blocks // 3
+        return [int(sk[:th].sum()), int(sk[th:2 * th].sum()), int(sk[2 * th:].sum())]
 
     def avg_bits(c):
         n = c["nvfp4"] + c["int8"] + c["bf16"]
         return round((4 * c["nvfp4"] + 8 * c["int8"] + 16 * c["bf16"]) / n, 3) if n else None
     print(f"[bench] dyn schedule: actions {counts}, linear path {total:.1f} ms vs {rtotal:.1f} ms all-BF16; "
-          f"MXFP8 cache: actions {c8}, {100 * same:.1f}% of decisions unchanged; budget 6 bits: actions {cb}",
+          f"MXFP8 cache: actions {c8}, {100 * same:.1f}% of decisions unchanged; budget 6 bits: actions {cb}; "
+          f"depth profile {depth_prof}: actions {cd}",
           file=sys.stderr, flush=True)
     return {"workload": f"closed loop, {blocks} blocks x {steps} steps, M={M}, hidden {hidden}, "
                         f"QKV {hidden}->{3 * hidden} at the scheduled precision",
@@ -521,6 +561,11 @@ def measure_dyn(torch, V, synth, blocks=30, steps=50, M=4446, hidden=1920):
                             "avg_quantized_bits": round((4 * cb["nvfp4"] + 8 * cb["int8"]) / max(1, cb["nvfp4"] + cb["int8"]), 3),
                             "linear_ms_total": round(totalb, 2),
                             "linear_speedup_vs_all_bf16": round(rtotal / totalb, 3) if totalb else None},
+            "skips_by_depth_third": skips_by_third(acts),
+            "depth_profile": {"tau_scale_shallow_to_deep": list(depth_prof), "actions": cd,
+                              "skips_by_depth_third": skips_by_third(actsd),
+                              "avg_activation_bits": avg_bits(cd), "linear_ms_total": round(totald, 2),
+                              "linear_speedup_vs_all_bf16": round(rtotal / totald, 3) if totald else None},
             "mxfp8_cache": {"actions": c8, "linear_ms_total": round(total8, 2),
                             "same_action_fraction": round(same, 4),
                             "cache_bytes_per_block": M * hidden * (1 + 1 / 32),
@@ -709,11 +754,38 @@ def measure_block_stats(torch, V, inp, out, n, steps):
             times.append(e0.elapsed_time(e1) / 20)
         us = 1e3 * float(np.median(times))
         gbs = bpe * n / (us * 1e-6) / 1e9
+        if cache == "bf16":
+            # the same bytes through a plain streaming pass (3 reads, 1 write)
+            import ctypes
+            BL = bench_lib()
+            dsink = torch.empty_like(d0)
+            st = lambda: ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+            ptr = lambda t: ctypes.c_void_p(t.data_ptr())
+            srun = lambda a, b: BL.vdtq_bench_stream_3r1w(ptr(inp), ptr(out), ptr(a), ptr(b), n, st())
+            srun(d0, dsink)
+            torch.cuda.synchronize()
+            stimes = []
+            for _ in range(max(3, steps // 4)):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for i in range(20):
+                    srun(d0, dsink) if i % 2 == 0 else srun(dsink, d0)
+                e1.record()
+                torch.cuda.synchronize()
+                stimes.append(e0.elapsed_time(e1) / 20)
+            cus = 1e3 * float(np.median(stimes))
+            del dsink
         res[cache] = {"bound": "hbm", "kernel": ("block_stats_kernel<true> + block_stats_final_kernel" if cache == "bf16"
                                                 else "block_stats_mx8_kernel + block_stats_final_kernel"),
                       "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                       "avg_launch_us": round(us, 2), "bytes_per_launch": bpe * n,
                       "cache_bytes": n * (2 if cache == "bf16" else 1 + 1 / 32)}
+        if cache == "bf16":
+            res[cache]["ceiling"] = {"what": "plain streaming pass, 3 bf16 reads + 1 write of n, no arithmetic",
+                                     "avg_launch_us": round(cus, 2),
+                                     "achieved": round(bpe * n / (cus * 1e-6) / 1e9, 1),
+                                     "frac": round(bpe * n / (cus * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+            res[cache]["frac_of_ceiling"] = round(cus / us, 4)
     return res
 
 
@@ -750,48 +822,83 @@ def measure_quantize(torch, V, X, M, steps, with_mx=False):
     reduction and the pass: 2 more bytes per element, key nvfp4_amax).  The
     launches are captured in a graph and replayed, so the per-launch time
     (HIP events around the replays / launches) excludes host launch gaps.
-    The 3072-wide inputs rotate over the three K=3072 activations (327 MB of
-    bf16 per rotation, above the 256 MB last-level cache); the 12288-wide
-    FFN-down input is 437 MB."""
+    Each shape rotates over distinct copies of its inputs totalling at least
+    1 GB (ten 109 MB copies of the three K = 3072 activations, three of the
+    437 MB FFN-down input), four times the 256 MB last-level cache, so every
+    launch reads its input from HBM.  Beside each pass, `ceiling` times a
+    plain streaming kernel that moves exactly the same bytes per launch with
+    no arithmetic (same grid shape of one 64-element chunk per thread, same
+    rotation, same graph replay): the rate this launch size allows."""
+    import ctypes
+    BL = bench_lib()
     out = {}
+    stream = lambda: ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     for K, names in ((3072, ["qkv", "out", "ffn_up"]), (12288, ["ffn_down"])):
         elems = M * K
+        n_copies = max(3, -(-int(1.0e9) // (2 * elems)))
+        srcs = [X[names[i % len(names)]].clone() for i in range(n_copies)]
+        n_launch = 2 * n_copies
         for key in ("nvfp4", "nvfp4_amax", "int8") + (("mxfp4", "mxfp8") if with_mx else ()):
             fmt = "nvfp4" if key == "nvfp4_amax" else key
             bpe = QUANT_BYTES[fmt] + (2.0 if key == "nvfp4_amax" else 0.0)
             extra = 0 if fmt == "nvfp4" else 4 * M / elems
             # buffers allocated (and the tensor amax written) before capture
-            outs = [V.hadamard_quantize(X[n], HAD_BLOCK, fmt) for n in names]
+            outs = [V.hadamard_quantize(x, HAD_BLOCK, fmt) for x in srcs]
             amax = "given" if key == "nvfp4" else None
-            n_launch = 12
-            torch.cuda.synchronize()
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                for i in range(n_launch):
-                    j = i % len(names)
-                    V.hadamard_quantize(X[names[j]], HAD_BLOCK, fmt, amax=amax, out=outs[j])
-            g.replay()
-            torch.cuda.synchronize()
-            times = []
-            for _ in range(max(3, steps // 4)):
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record()
-                g.replay()
-                e1.record()
+
+            def replay_us(launch):
                 torch.cuda.synchronize()
-                times.append(e0.elapsed_time(e1) / n_launch)
-            us = 1e3 * float(np.median(times))
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    for i in range(n_launch):
+                        launch(i % n_copies)
+                g.replay()
+                torch.cuda.synchronize()
+                times = []
+                for _ in range(max(3, steps // 4)):
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record()
+                    g.replay()
+                    e1.record()
+                    torch.cuda.synchronize()
+                    times.append(e0.elapsed_time(e1) / n_launch)
+                del g
+                return 1e3 * float(np.median(times))
+
+            us = replay_us(lambda j: V.hadamard_quantize(srcs[j], HAD_BLOCK, fmt, amax=amax, out=outs[j]))
             gbs = (bpe + extra) * elems / (us * 1e-6) / 1e9
-            out[f"{key}_K{K}"] = {"bound": "hbm", "kernel": QUANT_KERNEL[key], "achieved": round(gbs, 1),
-                                  "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
-                                  "traffic": None, "avg_launch_us": round(us, 2),
-                                  "bytes_per_launch": (bpe + extra) * elems, "shape": [M, K],
-                                  "grid_work_items": hq_grid_work_items(M, K, fmt)}
+            e = {"bound": "hbm", "kernel": QUANT_KERNEL[key], "achieved": round(gbs, 1),
+                 "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                 "traffic": None, "avg_launch_us": round(us, 2),
+                 "bytes_per_launch": (bpe + extra) * elems, "shape": [M, K],
+                 "grid_work_items": hq_grid_work_items(M, K, fmt),
+                 "rotation": f"{n_copies} distinct inputs, {n_copies * 2 * elems / 1e9:.2f} GB"}
             if key == "nvfp4_amax":
-                out[f"{key}_K{K}"]["note"] = ("algorithmic bytes (2 reads of X): the pass re-reads the tensor the "
-                                              "pre-pass just read, and up to 256 MB of that comes from the "
-                                              "last-level cache, not HBM")
-            del g
+                e["note"] = ("algorithmic bytes (2 reads of X): the pass re-reads the tensor the pre-pass just "
+                             "read, and up to 256 MB of that comes from the last-level cache, not HBM")
+            else:
+                cb, sb, rb = STREAM_SHAPE[fmt]
+                chunks = elems // 64
+                q = torch.empty(chunks * cb, dtype=torch.uint8, device=srcs[0].device)
+                sc = torch.empty(max(1, chunks * sb), dtype=torch.uint8, device=srcs[0].device)
+                rw = torch.empty(M, dtype=torch.int32, device=srcs[0].device)
+
+                def stream_launch(j):
+                    rc = BL.vdtq_bench_stream_rows(ctypes.c_void_p(srcs[j].data_ptr()), M, K, cb, sb, rb,
+                                                   ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(sc.data_ptr()),
+                                                   ctypes.c_void_p(rw.data_ptr()), stream())
+                    assert rc == 0, rc
+                cus = replay_us(stream_launch)
+                cgbs = (bpe + extra) * elems / (cus * 1e-6) / 1e9
+                e["ceiling"] = {"what": "plain streaming pass, same bytes and launch size, no arithmetic",
+                                "avg_launch_us": round(cus, 2), "achieved": round(cgbs, 1),
+                                "frac": round(cgbs / PEAK_HBM_GBS, 4)}
+                e["frac_of_ceiling"] = round(cus / us, 4)
+                del q, sc, rw
+            out[f"{key}_K{K}"] = e
+            del outs
+        del srcs
+        torch.cuda.empty_cache()
     return out
 
 

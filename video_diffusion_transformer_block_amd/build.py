@@ -20,6 +20,9 @@ CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libvdtq.so")
+# plain streaming passes the benchmark times as ceilings (not the library's ABI)
+BENCH_LIB = os.path.join(HERE, "libvdtq_bench.so")
+BENCH_SOURCES = ["bench_stream.hip"]
 SOURCES = ["hadamard_quantize.hip", "qgemm.hip", "qgemm_mx.hip", "qgemm_w4a16.hip", "block_stats.hip", "api.cpp",
            "dmpq.cpp"]
 
@@ -42,18 +45,24 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(len(SOURCES), 8)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, out: str) -> None:
+    tmp = out + ".tmp"
     cmd = [HIPCC, "-shared", f"--offload-arch={ARCH}", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + BENCH_SOURCES
+    with ThreadPoolExecutor(max_workers=min(len(srcs), 8)) as ex:
+        objs = list(ex.map(_compile, srcs))
+    _link(objs[:len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], BENCH_LIB)
     if verbose:
-        print("built", LIB)
+        print("built", LIB, "and", BENCH_LIB)
     return LIB
 
 
