@@ -361,7 +361,14 @@ int qgemm_mx_quant(int a_fmt, const uint8_t* a_q_dev, const uint8_t* a_s_dev,
  *   order (bit-identical across runs).
  * in_dev, out_dev, dprev_dev, dnew_dev: bf16 [n] (dnew may not alias dprev)
  * n >= 0 (n == 0 writes zeros).
- * ws_dev: vdtq_workspace_bytes(VDTQ_OP_BLOCK_STATS, n, 1) bytes.
+ * ws_dev: vdtq_workspace_bytes(VDTQ_OP_BLOCK_STATS, n, 1) bytes, 16-byte
+ *   aligned.  Its first 4 bytes are a completion counter (the last
+ *   workgroup to finish reduces the per-workgroup partials, in a fixed
+ *   order): they must be zero before the first call that uses the
+ *   workspace, and every completed call leaves them zero.  Use this
+ *   workspace for block_stats / block_stats_mx8 calls only (other entry
+ *   points write theirs from the start); calls sharing it run in stream
+ *   order.
  */
 int block_stats(const void* in_dev, const void* out_dev,
                 const void* dprev_dev, void* dnew_dev, int64_t n,
@@ -387,7 +394,7 @@ int block_stats(const void* in_dev, const void* out_dev,
  *                aligned) and uint8 E8M0 [n/32], both NULL when there is none
  * dnew_q_dev, dnew_s_dev  the new delta, same layout; both NULL to skip the
  *                write; must not alias dprev
- * ws_dev: vdtq_workspace_bytes(VDTQ_OP_BLOCK_STATS, n, 1) bytes.
+ * ws_dev: as for block_stats (zeroed completion counter first).
  * Errors: VDTQ_EINVAL for n not a multiple of 32, a null or misaligned
  * pointer, codes without scales (or the reverse), aliasing, or a short
  * workspace.

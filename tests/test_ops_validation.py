@@ -35,6 +35,7 @@ def stub(monkeypatch):
     monkeypatch.setattr(O, "_stream", lambda dev: None)
     monkeypatch.setattr(O, "_ws", {})
     monkeypatch.setattr(O, "_gemm_ws", {})
+    monkeypatch.setattr(O, "_bs_ws", {})
     return s
 
 

@@ -89,6 +89,22 @@ def workspace(device: torch.device, nbytes: int) -> torch.Tensor:
     return buf
 
 
+_bs_ws = {}
+
+
+def stats_workspace(device: torch.device, nbytes: int) -> torch.Tensor:
+    """Per-device workspace of block_stats / block_stats_mx8, zero-filled when
+    allocated: it holds the calls' completion counter, which must be zero
+    before the first call and which every call leaves at zero (so it is not
+    shared with the other entry points' workspace)."""
+    key = torch.device(device).index
+    buf = _bs_ws.get(key)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.zeros(max(nbytes, 4096), dtype=torch.uint8, device=device)
+        _bs_ws[key] = buf
+    return buf
+
+
 _gemm_ws = {}
 
 
@@ -364,7 +380,7 @@ def block_stats(inp: torch.Tensor, out: torch.Tensor, dprev: Optional[torch.Tens
     if dnew is None and write_delta:
         dnew = torch.empty_like(inp)
     st = torch.empty(8, dtype=torch.float64, device=dev)
-    ws = workspace(dev, L.lib().vdtq_workspace_bytes(L.OP_BLOCK_STATS, n, 1))
+    ws = stats_workspace(dev, L.lib().vdtq_workspace_bytes(L.OP_BLOCK_STATS, n, 1))
     L.check(L.lib().block_stats(_p(inp), _p(out), _p(dprev), _p(dnew), n, _p(st), _p(ws), ws.numel(),
                                 _stream(dev)))
     return dnew, st
@@ -397,7 +413,7 @@ def block_stats_mx8(inp: torch.Tensor, out: torch.Tensor, dprev: Optional[MXTens
         dnew = MXTensor(torch.empty(n, dtype=torch.uint8, device=dev),
                         torch.empty(n // 32, dtype=torch.uint8, device=dev), "mxfp8")
     st = torch.empty(8, dtype=torch.float64, device=dev)
-    ws = workspace(dev, L.lib().vdtq_workspace_bytes(L.OP_BLOCK_STATS, n, 1))
+    ws = stats_workspace(dev, L.lib().vdtq_workspace_bytes(L.OP_BLOCK_STATS, n, 1))
     L.check(L.lib().block_stats_mx8(_p(inp), _p(out), _p(dprev.q if dprev else None),
                                     _p(dprev.scales if dprev else None), _p(dnew.q if dnew else None),
                                     _p(dnew.scales if dnew else None), n, _p(st), _p(ws), ws.numel(),
