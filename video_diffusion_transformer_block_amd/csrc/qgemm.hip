@@ -352,9 +352,11 @@ void qgemm_kernel(GemmParams p) {
 //     own loads of the next stage (vmcnt) and for its LDS reads of the current
 //     one (lgkmcnt), so after the barrier the next stage is complete and the
 //     current buffer is free for the stage three ahead;
-//   * a step-level software pipeline: the 16 MFMAs of step s are interleaved
-//     (sched_group_barrier) with the decode of step s+1 and the LDS reads of
-//     the next chunk, so the VALU work hides under the MFMAs.
+//   * a step-level software pipeline scheduled by hand: each of the 16
+//     MFMAs of step s is followed by a quarter fragment of the decode of
+//     step s+1 (two conversions, two multiplies) and at most one LDS read
+//     or scale operation, held together by sched_barrier, so the VALU work
+//     runs under the MFMAs instead of in bursts between them.
 // PAIRS (K % 256 == 0): the E4M3 scales of two consecutive stages (16
 // contiguous bytes per row) arrive in one 16-byte load per row, into a
 // double-buffered pair region after the ring, instead of two 4-byte loads
@@ -562,30 +564,6 @@ void qgemm_pipe_kernel(GemmParams p) {
   };
 
   float16v acc[4][4];
-
-  // D = W_frag x A_frag^T: each accumulator tile is a 32 x 32 block of Y^T,
-  // so a lane holds one token row and, per register group of 4, four
-  // consecutive output features (vector stores in the epilogue)
-  auto mfma16 = [&](const half8 (&af)[4], const half8 (&bf)[4]) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[j], af[i], acc[i][j], 0, 0, 0);
-  };
-  // interleave: each MFMA followed by a few VALU (decode) and, when present,
-  // one LDS read
-  auto interleave = [&]() {
-#pragma unroll
-    for (int x = 0; x < 16; ++x) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
-    }
-    // each step is its own scheduling region: nothing migrates between steps
-    __builtin_amdgcn_sched_barrier(0);
-  };
-
   int tile, kb, ke;
   if constexpr (SPLIT) {
     tile = (int)(blockIdx.x % p.sk_tiles);
@@ -629,26 +607,131 @@ void qgemm_pipe_kernel(GemmParams p) {
   read_scales(kb, sa, sw);
   decode(R0, sa, sw, 0, 0, fa, fb);
 
+  // ---- the main loop, scheduled by hand.  A step is 16 MFMAs; after MFMA
+  // x comes piece x of the decode of the next step's operands (fragment
+  // x / 2 of 4 A + 4 W, elements 4 (x % 2) .. +3: two conversions and two
+  // multiplies) and at most one LDS read or scale operation, and a
+  // sched_barrier keeps each MFMA with its slot.  One wave runs per SIMD,
+  // so the matrix core stays busy only if no run of VALU work outlasts an
+  // MFMA and no MFMAs are issued back to back.
+  //
+  // Scale registers of a chunk: per fragment f (A 0-3, W 4-7) lo = the fp16
+  // scale pair bits (the group of steps 0-1 in the low half) and hi = the
+  // group of steps 2-3 moved to the low half.
+  uint32_t S0lo[8], S0hi[8], S1lo[8], S1hi[8];
+  auto scale_lo = [&](const uint2 (&xa)[4], const uint2 (&xw)[4], int c, int f, uint32_t (&lo)[8]) {
+    if (f < 4) {
+      if (!A8) lo[f] = scale_of(xa[f], c);
+    } else {
+      lo[f] = scale_of(xw[f - 4], c);
+    }
+  };
+  auto scale_hi = [&](int f, const uint32_t (&lo)[8], uint32_t (&hi)[8]) {
+    if (f >= 4 || !A8) hi[f] = lo[f] >> 16;
+  };
+#pragma unroll
+  for (int f = 0; f < 8; ++f) {
+    scale_lo(sa, sw, 0, f, S0lo);
+    scale_hi(f, S0lo, S0hi);
+  }
+  // piece x of the decode of step s of a chunk (codes R, scales lo / hi)
+  auto piece = [&](const Raw<A8>& R, int s, const uint32_t (&lo)[8], const uint32_t (&hi)[8], half8 (&NA)[4],
+                   half8 (&NB)[4], int x) {
+    const int f = x >> 1, h2 = x & 1;
+    if (A8 && f < 4) {
+      const uint4& v = R.a[f][s >> 1];
+      const uint32_t w = h2 ? ((s & 1) ? v.w : v.y) : ((s & 1) ? v.z : v.x);
+      const half2v bias = {(_Float16)1152.0f, (_Float16)1152.0f};
+      const uint32_t x0 = w ^ 0x80808080u;
+      const half2v p0 = __builtin_bit_cast(half2v, __builtin_amdgcn_perm(0x64646464u, x0, 0x04010400u)) - bias;
+      const half2v p1 = __builtin_bit_cast(half2v, __builtin_amdgcn_perm(0x64646464u, x0, 0x04030402u)) - bias;
+      NA[f][4 * h2 + 0] = p0[0]; NA[f][4 * h2 + 1] = p0[1];
+      NA[f][4 * h2 + 2] = p1[0]; NA[f][4 * h2 + 3] = p1[1];
+    } else {
+      const half2v sp = __builtin_bit_cast(half2v, s < 2 ? lo[f] : hi[f]);
+      const half2v sc = {sp[0], sp[0]};
+      const uint4& v = f < 4 ? R.a[f][0] : R.w[f - 4];
+      const uint32_t w = s == 0 ? v.x : s == 1 ? v.y : s == 2 ? v.z : v.w;
+      // (the byte index of the conversion is an immediate)
+      const half2v p0 = (h2 ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 2)
+                            : __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 0)) * sc;
+      const half2v p1 = (h2 ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 3)
+                            : __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 1)) * sc;
+      half8& o = f < 4 ? NA[f] : NB[f - 4];
+      o[4 * h2 + 0] = p0[0]; o[4 * h2 + 1] = p0[1];
+      o[4 * h2 + 2] = p1[0]; o[4 * h2 + 3] = p1[1];
+    }
+  };
+  // one LDS read of chunk c's codes of stage kt: A fragment reads first
+  // (INT8: two per fragment), then the four W fragments
+  constexpr int NAR = A8 ? 8 : 4;
+  auto read_code = [&](int kt, int c, Raw<A8>& R, int r) {
+    const uint8_t* st = smem + ring(kt) * P::STAGE;
+    const int qd = 2 * c + h;
+    if (r < NAR) {
+      if (A8) {
+        const int i = r >> 1, half = r & 1;
+        R.a[i][half] = *reinterpret_cast<const uint4*>(st + i8_quad_off(wm * 128 + 32 * i + r32, 2 * qd + half));
+      } else {
+        R.a[r][0] = *reinterpret_cast<const uint4*>(st + fp4_quad_off(wm * 128 + 32 * r + r32, qd));
+      }
+    } else {
+      const int j = r - NAR;
+      R.w[j] = *reinterpret_cast<const uint4*>(st + P::A_CODES + P::A_SC + fp4_quad_off(wn * 128 + 32 * j + r32, qd));
+    }
+  };
+  // one LDS read of the 8 scale bytes of fragment f (A 0-3, W 4-7) of stage kt
+  auto read_scale = [&](int kt, int f, uint2 (&xa)[4], uint2 (&xw)[4]) {
+    if (f < 4 && A8) {
+      xa[f] = make_uint2(0u, 0u);
+      return;
+    }
+    const int row = (f < 4 ? wm : wn) * 128 + 32 * (f & 3) + r32;
+    const uint8_t* src;
+    if (PAIRS) {
+      const uint8_t* ps = smem + P::PAIR_BASE + ((kt >> 1) & 1) * P::PAIR_SLOT + (kt & 1) * 8;
+      src = f < 4 ? ps + row * 16 : ps + P::PAIR_A + row * 16;
+    } else {
+      const uint8_t* st = smem + ring(kt) * P::STAGE;
+      src = f < 4 ? st + P::A_CODES + row * 8 : st + P::A_CODES + P::A_SC + P::W_CODES + row * 8;
+    }
+    (f < 4 ? xa[f] : xw[f - 4]) = *reinterpret_cast<const uint2*>(src);
+  };
+  // The decoded fragments are materialised where this is called: without it
+  // the compiler sinks a step's decode past the branches of the mid-stage
+  // wait (into another basic block, out of reach of sched_barrier).
+  auto pin = [](half8 (&A)[4], half8 (&B)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(A[i]), "+v"(B[i]));
+  };
+  auto step = [&](const half8 (&CA)[4], const half8 (&CB)[4], auto&& work) {
+#pragma unroll
+    for (int x = 0; x < 16; ++x) {
+      acc[x >> 2][x & 3] = __builtin_amdgcn_mfma_f32_32x32x16_f16(CB[x & 3], CA[x >> 2], acc[x >> 2][x & 3], 0, 0, 0);
+      work(x);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
   // Every step has the same shape; past the last stage the reads of the
   // "next" stage hit a stale ring slot and the extra decode is discarded.
   for (int kt = kb; kt < ke; ++kt) {
-    // step 0 | decode step 1
-    decode(R0, sa, sw, 0, 1, ga, gb);
-    mfma16(fa, fb);
-    interleave();
-    // step 1 | read chunk 1 codes, decode step 2
-    read_codes(kt, 1, R1);
-    decode(R0, sa, sw, 0, 2, fa, fb);
-    mfma16(ga, gb);
-    interleave();
-    // step 2 | decode step 3
-    decode(R0, sa, sw, 0, 3, ga, gb);
-    mfma16(fa, fb);
-    interleave();
-    // step 3 | decode step 4 (chunk 1)
-    decode(R1, sa, sw, 1, 0, fa, fb);
-    mfma16(ga, gb);
-    interleave();
+    // step 0 | decode chunk 0 step 1
+    step(fa, fb, [&](int x) { piece(R0, 1, S0lo, S0hi, ga, gb, x); });
+    // step 1 | decode chunk 0 step 2; read chunk 1 codes
+    step(ga, gb, [&](int x) {
+      piece(R0, 2, S0lo, S0hi, fa, fb, x);
+      if (x < NAR + 4) read_code(kt, 1, R1, x);
+    });
+    // step 2 | decode chunk 0 step 3; chunk 1 scale registers
+    step(fa, fb, [&](int x) {
+      piece(R0, 3, S0lo, S0hi, ga, gb, x);
+      if (x < 8) scale_lo(sa, sw, 1, x, S1lo);
+      else scale_hi(x - 8, S1lo, S1hi);
+    });
+    // step 3 | decode chunk 1 step 0
+    step(ga, gb, [&](int x) { piece(R1, 0, S1lo, S1hi, fa, fb, x); });
+    pin(fa, fb);
     // mid-stage barrier: next stage complete (only stage kt+2's loads may
     // still be in flight), this buffer free
     if (kt + 2 < ke) {
@@ -659,26 +742,27 @@ void qgemm_pipe_kernel(GemmParams p) {
     }
     wait_lgkm_barrier();
     if (kt + 3 < ke) issue_stage(kt + 3);
-    // step 4 | read stage kt+1 scales, decode step 5
-    read_scales(kt + 1, na, nw);
-    decode(R1, sa, sw, 1, 1, ga, gb);
-    mfma16(fa, fb);
-    interleave();
-    // step 5 | read stage kt+1 chunk 0 codes, decode step 6
-    read_codes(kt + 1, 0, R0);
-    decode(R1, sa, sw, 1, 2, fa, fb);
-    mfma16(ga, gb);
-    interleave();
-    // step 6 | decode step 7
-    decode(R1, sa, sw, 1, 3, ga, gb);
-    mfma16(fa, fb);
-    interleave();
+    // step 4 | decode chunk 1 step 1; read stage kt+1's scales
+    step(fa, fb, [&](int x) {
+      piece(R1, 1, S1lo, S1hi, ga, gb, x);
+      if (x < 8) read_scale(kt + 1, x, na, nw);
+    });
+    // step 5 | decode chunk 1 step 2; read stage kt+1's chunk 0 codes
+    step(ga, gb, [&](int x) {
+      piece(R1, 2, S1lo, S1hi, fa, fb, x);
+      if (x < NAR + 4) read_code(kt + 1, 0, R0, x);
+    });
+    // step 6 | decode chunk 1 step 3; stage kt+1's chunk 0 scale registers
+    step(fa, fb, [&](int x) {
+      piece(R1, 3, S1lo, S1hi, ga, gb, x);
+      if (x < 8) scale_lo(na, nw, 0, x, S0lo);
+      else scale_hi(x - 8, S0lo, S0hi);
+    });
     // step 7 | decode step 0 of stage kt+1
 #pragma unroll
     for (int i = 0; i < 4; ++i) { sa[i] = na[i]; sw[i] = nw[i]; }
-    decode(R0, sa, sw, 0, 0, fa, fb);
-    mfma16(ga, gb);
-    interleave();
+    step(ga, gb, [&](int x) { piece(R0, 0, S0lo, S0hi, fa, fb, x); });
+    pin(fa, fb);
   }
 
   if constexpr (SPLIT) {
