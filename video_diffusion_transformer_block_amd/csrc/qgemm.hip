@@ -380,7 +380,12 @@ struct Pipe {
   static constexpr int PAIR_SLOT = PAIR_A + PAIR_W;
   static constexpr int PAIR_BASE = NS * STAGE;
   static constexpr int NPAIR = (PAIR_A ? 1 : 0) + (PAIR_W ? 1 : 0);   // pair loads per wave
-  static constexpr int LDS = NS * STAGE + 2 * PAIR_SLOT;
+  // a 1 KB LDS landing area per wave for the loads of stages past the last:
+  // every stage issues the same loads (no branch), those past the end
+  // read valid addresses and land here
+  static constexpr int DUMMY = NS * STAGE + 2 * PAIR_SLOT;
+  static constexpr int NDMA = LPS + NPAIR;             // loads per wave and stage, scale pair included
+  static constexpr int LDS = DUMMY + 4 * 1024;
 };
 
 // per-chunk raw operands of one lane: codes for its 4 A and 4 W sub-blocks
@@ -461,30 +466,43 @@ void qgemm_pipe_kernel(GemmParams p) {
   const uint32_t wvu = __builtin_amdgcn_readfirstlane(wv);
   // ring slot of stage kt: counted from the first stage of the segment
   int kbase = 0;
+  int tile, kb, ke;
   auto ring = [&](int kt) { return (kt - kbase) % P::NS; };
-  auto issue_stage = [&](int kt) {
+  // Load u (0 .. NDMA-1) of stage kt, branch-free: a stage past the last
+  // reads stage ke-1's addresses into this wave's landing area, and the
+  // scale-pair loads go out every stage, to the landing area unless the
+  // stage is even or the segment's first (the pair (kt & ~1, kt | 1)).
+  const uint32_t dummy = lds0 + P::DUMMY + wvu * 1024;
+  // (the destination is chosen by masks, not branches: the step stays one
+  // basic block, so its schedule holds)
+  auto pick = [&](uint32_t m, uint32_t target) { return dummy + ((target - dummy) & m); };
+  auto issue_one = [&](int kt, int u) {
+    const uint32_t live = 0u - (uint32_t)(kt < ke);
+    const int ks = min(kt, ke - 1);
     const uint32_t st = lds0 + (uint32_t)ring(kt) * P::STAGE;
-    const int k0 = kt * BK;
-    const uint8_t* abase = aq + (A8 ? k0 : k0 / 2);
-    const uint8_t* asbase = as + k0 / 16;
-    const uint8_t* wbase = p.w_q + k0 / 2;
-    const uint8_t* wsbase = p.w_s + k0 / 16;
-#pragma unroll
-    for (int u = 0; u < P::NA; ++u) dma16(abase, offA[u], st + (wvu * P::NA + u) * 1024);
-#pragma unroll
-    for (int u = 0; u < P::NAS; ++u) dma4(asbase, offAS[u], st + P::A_CODES + (wvu * P::NAS + u) * 256);
-#pragma unroll
-    for (int u = 0; u < P::NW; ++u) dma16(wbase, offW[u], st + P::A_CODES + P::A_SC + (wvu * P::NW + u) * 1024);
-#pragma unroll
-    for (int u = 0; u < P::NWS; ++u)
-      dma4(wsbase, offWS[u], st + P::A_CODES + P::A_SC + P::W_CODES + (wvu * P::NWS + u) * 256);
-    // the scale pair (kt & ~1, kt | 1), with the even stage or a segment's first
-    if (PAIRS && ((kt & 1) == 0 || kt == kbase)) {
-      const int pr = kt >> 1;
+    const int k0 = ks * BK;
+    if (u < P::NA) {
+      dma16(aq + (A8 ? k0 : k0 / 2), offA[u], pick(live, st + (wvu * P::NA + u) * 1024));
+    } else if (u < P::NA + P::NAS) {
+      const int v = u - P::NA;
+      dma4(as + k0 / 16, offAS[v], pick(live, st + P::A_CODES + (wvu * P::NAS + v) * 256));
+    } else if (u < P::NA + P::NAS + P::NW) {
+      const int v = u - P::NA - P::NAS;
+      dma16(p.w_q + k0 / 2, offW[v], pick(live, st + P::A_CODES + P::A_SC + (wvu * P::NW + v) * 1024));
+    } else if (u < P::LPS) {
+      const int v = u - P::NA - P::NAS - P::NW;
+      dma4(p.w_s + k0 / 16, offWS[v], pick(live, st + P::A_CODES + P::A_SC + P::W_CODES + (wvu * P::NWS + v) * 256));
+    } else if (PAIRS) {
+      const uint32_t real = live & (0u - (uint32_t)(((kt & 1) == 0) | (kt == kbase)));
+      const int pr = ks >> 1;
       const uint32_t ps = lds0 + P::PAIR_BASE + (uint32_t)(pr & 1) * P::PAIR_SLOT + wvu * 64 * 16;
-      if (P::PAIR_A) dma16(as + 16 * pr, offAP, ps);
-      dma16(p.w_s + 16 * pr, offWP, ps + P::PAIR_A);
+      if (P::PAIR_A && u == P::LPS) dma16(as + 16 * pr, offAP, pick(real, ps));
+      else dma16(p.w_s + 16 * pr, offWP, pick(real, ps + P::PAIR_A));
     }
+  };
+  auto issue_stage = [&](int kt) {
+#pragma unroll
+    for (int u = 0; u < P::NDMA; ++u) issue_one(kt, u);
   };
 
   // ---- LDS read offsets of this lane's fragments (within a stage)
@@ -564,7 +582,6 @@ void qgemm_pipe_kernel(GemmParams p) {
   };
 
   float16v acc[4][4];
-  int tile, kb, ke;
   if constexpr (SPLIT) {
     tile = (int)(blockIdx.x % p.sk_tiles);
     const int sl = (int)(blockIdx.x / p.sk_tiles);
@@ -584,20 +601,12 @@ void qgemm_pipe_kernel(GemmParams p) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-  // ---- prologue: stages kb..kb+2 in flight, wait for stage kb
-  // (loads still allowed in flight: those of stages kb+1 and kb+2, a scale
-  // pair with whichever of them is even)
+  // ---- prologue: stages kb..kb+2 in flight (those past the end land in
+  // the landing area), wait for stage kb
   issue_stage(kb);
-  if (ke - kb > 1) issue_stage(kb + 1);
-  if (ke - kb > 2) issue_stage(kb + 2);
-  if (ke - kb > 2) {
-    wait_vm<2 * P::LPS + P::NPAIR>();
-  } else if (ke - kb > 1) {
-    if (PAIRS && ((kb + 1) & 1) == 0) wait_vm<P::LPS + P::NPAIR>();
-    else wait_vm<P::LPS>();
-  } else {
-    wait_vm<0>();
-  }
+  issue_stage(kb + 1);
+  issue_stage(kb + 2);
+  wait_vm<2 * P::NDMA>();
   wait_lgkm_barrier();
 
   Raw<A8> R0, R1;
@@ -697,13 +706,6 @@ void qgemm_pipe_kernel(GemmParams p) {
     }
     (f < 4 ? xa[f] : xw[f - 4]) = *reinterpret_cast<const uint2*>(src);
   };
-  // The decoded fragments are materialised where this is called: without it
-  // the compiler sinks a step's decode past the branches of the mid-stage
-  // wait (into another basic block, out of reach of sched_barrier).
-  auto pin = [](half8 (&A)[4], half8 (&B)[4]) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(A[i]), "+v"(B[i]));
-  };
   auto step = [&](const half8 (&CA)[4], const half8 (&CB)[4], auto&& work) {
 #pragma unroll
     for (int x = 0; x < 16; ++x) {
@@ -731,21 +733,16 @@ void qgemm_pipe_kernel(GemmParams p) {
     });
     // step 3 | decode chunk 1 step 0
     step(ga, gb, [&](int x) { piece(R1, 0, S1lo, S1hi, fa, fb, x); });
-    pin(fa, fb);
     // mid-stage barrier: next stage complete (only stage kt+2's loads may
     // still be in flight), this buffer free
-    if (kt + 2 < ke) {
-      if (PAIRS && ((kt + 2) & 1) == 0) wait_vm<P::LPS + P::NPAIR>();
-      else wait_vm<P::LPS>();
-    } else {
-      wait_vm<0>();
-    }
+    wait_vm<P::NDMA>();
     wait_lgkm_barrier();
-    if (kt + 3 < ke) issue_stage(kt + 3);
-    // step 4 | decode chunk 1 step 1; read stage kt+1's scales
+    // step 4 | decode chunk 1 step 1; read stage kt+1's scales; issue the
+    // loads of stage kt+3 into the buffer just freed
     step(fa, fb, [&](int x) {
       piece(R1, 1, S1lo, S1hi, ga, gb, x);
       if (x < 8) read_scale(kt + 1, x, na, nw);
+      if (x < P::NDMA) issue_one(kt + 3, x);
     });
     // step 5 | decode chunk 1 step 2; read stage kt+1's chunk 0 codes
     step(ga, gb, [&](int x) {
@@ -762,8 +759,10 @@ void qgemm_pipe_kernel(GemmParams p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) { sa[i] = na[i]; sw[i] = nw[i]; }
     step(ga, gb, [&](int x) { piece(R0, 0, S0lo, S0hi, fa, fb, x); });
-    pin(fa, fb);
   }
+  // the loads of the stages past the end must land before the workgroup's
+  // LDS is released or reused
+  wait_vm<0>();
 
   if constexpr (SPLIT) {
     // partial sums of this K slice; the reduce kernel finishes the tile
