@@ -264,14 +264,18 @@ int qgemm_w4a8(const int8_t* a_q_dev, const float* a_s_dev,
  *          4-byte aligned)
  * bias_dev float [N] or NULL; y_dev out_dtype [M][ldy], ldy >= N
  * M, N >= 0 (0 is a no-op); K > 0, multiple of 16.
- * Errors: VDTQ_EINVAL as for the other GEMMs; VDTQ_EUNSUPPORTED when K is
- * not a multiple of 64 or an operand reaches 4 GB.  No workspace.
+ * ws_dev/ws_bytes  workspace of vdtq_workspace_bytes(VDTQ_OP_QGEMM, M, N)
+ *          bytes, 256-byte aligned, as for qgemm_w4a4 (partial sums of the
+ *          tiles of a partial last wave, split along K).
+ * Errors: VDTQ_EINVAL as for the other GEMMs (a short workspace included);
+ * VDTQ_EUNSUPPORTED when K is not a multiple of 64 or an operand reaches
+ * 4 GB.
  */
 int qgemm_w4a16(const void* a_dev, const uint8_t* w_q_dev,
                 const uint8_t* w_s_dev, const float* w_ts_dev,
                 const float* bias_dev, void* y_dev, int64_t ldy,
                 int out_dtype, int64_t M, int64_t N, int64_t K,
-                void* stream);
+                void* ws_dev, size_t ws_bytes, void* stream);
 
 /*
  * qgemm_mx -- the MX-native variant of qgemm_w4a4 / qgemm_w4a8:

@@ -142,17 +142,19 @@ def test_qgemm_empty_is_noop():
 
 
 def _a16(**kw):
-    a = dict(a=FAKE, wq=FAKE, ws=FAKE, wts=FAKE, bias=None, y=FAKE, ldy=64, od=0, M=8, N=64, K=128)
+    a = dict(a=FAKE, wq=FAKE, ws=FAKE, wts=FAKE, bias=None, y=FAKE, ldy=64, od=0, M=8, N=64, K=128, gws=FAKE,
+             gwsb=1 << 28)
     a.update(kw)
     return V.lib().qgemm_w4a16(a["a"], a["wq"], a["ws"], a["wts"], a["bias"], a["y"], a["ldy"], a["od"],
-                               a["M"], a["N"], a["K"], None)
+                               a["M"], a["N"], a["K"], a["gws"], a["gwsb"], None)
 
 
 @pytest.mark.parametrize("kw,code", [
     (dict(K=0), L.EINVAL), (dict(K=40), L.EINVAL), (dict(M=-1), L.EINVAL), (dict(ldy=10), L.EINVAL),
     (dict(od=2), L.EINVAL), (dict(a=None), L.EINVAL), (dict(wq=None), L.EINVAL), (dict(wts=None), L.EINVAL),
     (dict(y=None), L.EINVAL), (dict(a=FAKE8), L.EINVAL), (dict(K=96), L.EUNSUPPORTED),
-    (dict(M=1 << 20, K=1 << 11), L.EUNSUPPORTED),
+    (dict(M=1 << 20, K=1 << 11), L.EUNSUPPORTED), (dict(gws=None), L.EINVAL), (dict(gwsb=4096), L.EINVAL),
+    (dict(gws=FAKE8), L.EINVAL),
 ])
 def test_qgemm_w4a16_rejects(kw, code):
     assert _a16(**kw) == code

@@ -72,7 +72,7 @@ def lib() -> ctypes.CDLL:
             L.qgemm_w4a4.restype = i32
             L.qgemm_w4a4.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i32, i64, i64, i64, vp, sz, vp]
             L.qgemm_w4a16.restype = i32
-            L.qgemm_w4a16.argtypes = [vp, vp, vp, vp, vp, vp, i64, i32, i64, i64, i64, vp]
+            L.qgemm_w4a16.argtypes = [vp, vp, vp, vp, vp, vp, i64, i32, i64, i64, i64, vp, sz, vp]
             L.qgemm_mx.restype = i32
             L.qgemm_mx.argtypes = [i32, vp, vp, vp, vp, vp, vp, i64, i32, i64, i64, i64, vp, sz, vp]
             L.qgemm_mx_quant.restype = i32

@@ -181,7 +181,7 @@ int qgemm_w4a8(const int8_t* a_q_dev, const float* a_s_dev, const uint8_t* w_q_d
 
 int qgemm_w4a16(const void* a_dev, const uint8_t* w_q_dev, const uint8_t* w_s_dev, const float* w_ts_dev,
                 const float* bias_dev, void* y_dev, int64_t ldy, int out_dtype, int64_t M, int64_t N, int64_t K,
-                void* stream) {
+                void* ws_dev, size_t ws_bytes, void* stream) {
   const char* name = "qgemm_w4a16";
   if (M < 0 || M > kI32 || N < 0 || N > kI32) return fail(VDTQ_EINVAL, "%s: M=%lld N=%lld out of range", name, (long long)M, (long long)N);
   if (K <= 0 || K > kI32 || K % 16) return fail(VDTQ_EINVAL, "%s: K=%lld must be a positive multiple of 16", name, (long long)K);
@@ -196,8 +196,10 @@ int qgemm_w4a16(const void* a_dev, const uint8_t* w_q_dev, const uint8_t* w_s_de
   if (M * K * 2 >= (int64_t(1) << 32) || N * K / 2 >= (int64_t(1) << 32))
     return fail(VDTQ_EUNSUPPORTED, "%s: operands of 4 GB or more", name);
   if (((M + 255) / 256) * ((N + 255) / 256) > kI32) return fail(VDTQ_EUNSUPPORTED, "%s: too many output tiles", name);
+  const int rc = qgemm_ws_check(name, M, N, ws_dev, ws_bytes);
+  if (rc != VDTQ_OK) return rc;
   hipError_t e = vdtq::launch_qgemm_w4a16(a_dev, w_q_dev, w_s_dev, w_ts_dev, bias_dev, y_dev, ldy, out_dtype, M, N,
-                                          K, static_cast<hipStream_t>(stream));
+                                          K, ws_dev, static_cast<hipStream_t>(stream));
   return hip_status(e, "qgemm_w4a16 launch");
 }
 

@@ -40,7 +40,7 @@ hipError_t launch_qgemm(int afmt, const void* a_q, const void* a_s, const float*
 
 hipError_t launch_qgemm_w4a16(const void* a, const uint8_t* w_q, const uint8_t* w_s, const float* w_ts,
                               const float* bias, void* y, int64_t ldy, int out_dtype, int64_t M, int64_t N,
-                              int64_t K, hipStream_t st);
+                              int64_t K, void* ws, hipStream_t st);
 
 hipError_t launch_qgemm_mx(bool a_fp8, const uint8_t* a_q, const uint8_t* a_s, const uint8_t* w_q,
                            const uint8_t* w_s, const float* bias, void* y, int64_t ldy, int out_dtype, int64_t M,

@@ -103,11 +103,13 @@ __device__ __forceinline__ void emit4(const GemmParams& p, bool vec, int row, in
 }
 
 // Output scale of a row: NVFP4 (AFMT 0) the two tensor scales, INT8 (1) the
-// row's token scale times the weight tensor scale, MX (2) none.
+// row's token scale times the weight tensor scale, MX (2) none, bf16
+// activations (3, the W4A16 fallback) the weight tensor scale.
 template <int AFMT>
 __device__ __forceinline__ float row_alpha(const GemmParams& p, int row) {
   if constexpr (AFMT == 0) return p.a_ts[1] * p.w_ts[1];
   else if constexpr (AFMT == 1) return static_cast<const float*>(p.a_s)[row] * p.w_ts[1];
+  else if constexpr (AFMT == 3) return p.w_ts[1];
   else return 1.0f;
 }
 
@@ -197,7 +199,8 @@ __global__ __launch_bounds__(256) void qgemm_reduce_kernel(GemmParams p) {
   emit4(p, out_vec_ok(p), row, col, row_alpha<AFMT>(p, row), sum.x, sum.y, sum.z, sum.w);
 }
 
-// Work split of a pipelined call on `cus` compute units.  Whole waves of
+// Work split of a pipelined call on `cus` compute units, K in stages of
+// `bk` (128 for the 4/8-bit activations, 64 for bf16).  Whole waves of
 // tiles go to the data-parallel kernel.  The tiles of a last, partial wave
 // (all tiles when there are fewer than CUs) are split into `slices` K slices,
 // at most one workgroup per CU in all, when that is estimated to finish
@@ -206,10 +209,10 @@ __global__ __launch_bounds__(256) void qgemm_reduce_kernel(GemmParams p) {
 // pass, against nk.
 constexpr int kSplitOverhead = 3;
 
-inline void plan_pipe(GemmParams& p, int cus, int& dp_grid, int& sk_grid) {
+inline void plan_pipe(GemmParams& p, int cus, int& dp_grid, int& sk_grid, int bk = BK) {
   p.tiles_m = (p.M + 255) / 256;
   p.tiles_n = (p.N + 255) / 256;
-  p.nk = p.K / BK;
+  p.nk = p.K / bk;
   const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n;
   const int G = std::max(1, std::min(cus, kGemmMaxGrid));
   const int64_t left = tiles % G;

@@ -11,24 +11,34 @@
 // product runs on v_mfma_f32_32x32x16_bf16 with fp32 accumulation; gs_w and
 // the bias are applied in the epilogue.
 //
-// Data flow: one 256 x 256 output tile per 256-thread workgroup (4 waves,
-// 2 x 2, each 128 x 128 = 4 x 4 MFMA tiles, accumulators holding Y^T tiles
-// as in the NVFP4/INT8 kernels).  K in stages of 64 (a stage of A is 256 rows
-// x 128 bytes of bf16), direct-to-LDS loads into a 3-deep ring issued two
-// stages ahead, one barrier per stage.  Within a stage, lane half h and step
-// s (0..3) cover k = 32 h + 8 s .. +8 for both operands: A is read as one
-// 16-byte quad per row and step; W as one 16-byte quad (32 codes) per row and
-// stage, decoded 8 codes per step: fp4 -> fp32 pairs (hardware conversion),
-// times the group's E4M3 scale (exact), -> bf16 pairs.
+// Data flow: the tile, work split, reduce pass and LDS-staged bf16 epilogue
+// of the NVFP4/INT8 kernels (qgemm_common.h): one 256 x 256 output tile per
+// 256-thread workgroup (4 waves, 2 x 2, each 128 x 128 = 4 x 4 MFMA tiles,
+// accumulators holding Y^T tiles), whole waves of tiles data-parallel, the
+// tiles of a partial last wave split into K slices.  K in stages of 64 (a
+// stage of A is 256 rows x 128 bytes of bf16), direct-to-LDS loads into a
+// 3-deep ring issued two stages ahead, one barrier per stage.  Within a
+// stage, lane half h and step s (0..3) cover k = 32 h + 8 s .. +8 for both
+// operands: A is read as one 16-byte quad per row and step; W as one 16-byte
+// quad (32 codes) per row and stage, decoded 8 codes per step: fp4 -> fp32
+// pairs (hardware conversion), times the group's E4M3 scale (exact), ->
+// bf16 pairs (2 VALU per element: gfx950 has no packed bf16 multiply).
+//
+// The main loop is scheduled by hand, as in qgemm.hip: each MFMA of a step
+// is followed by one eighth of the next step's W decode (two elements) and
+// at most one LDS read and one stage load, held together by sched_barrier.
+// Reads: step 0 reads A of step 2, step 1 A of step 3; after the barrier,
+// step 2 reads the next stage's W codes and scales and issues the loads of
+// the stage three ahead, step 3 reads the next stage's A of steps 0 and 1.
 #include "device_common.h"
 #include "launch.h"
 #include "lds_dma.h"
+#include "qgemm_common.h"
 
 namespace vdtq {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
-constexpr int A16_THREADS = 256;
 constexpr int A16_BK = 64;
 constexpr int A16_NS = 3;
 constexpr int A16_A = 256 * 128;      // A bytes per stage
@@ -36,55 +46,39 @@ constexpr int A16_W = 256 * 32;       // W code bytes per stage
 constexpr int A16_WS = 256 * 4;       // W scale bytes per stage
 constexpr int A16_STAGE = A16_A + A16_W + A16_WS;
 constexpr int A16_LPS = 8 + 2 + 1;    // loads per wave and stage
-
-struct A16Params {
-  const uint8_t* a;                   // bf16 [M][K]
-  const uint8_t* w_q;
-  const uint8_t* w_s;
-  const float* w_ts;
-  const float* bias;
-  void* y;
-  int64_t ldy;
-  int32_t M, N, K;
-  int32_t out_f32;
-  int32_t tiles_m, tiles_n;
-};
+constexpr int A16_DUMMY = A16_NS * A16_STAGE;   // landing area (1 KB per wave) of loads past the last stage
+constexpr int A16_LDS = (A16_DUMMY + 4096 > 4 * 32768) ? A16_DUMMY + 4096 : 4 * 32768;
 
 // LDS layout of a stage: A rows of 8 quads (16 B) stored at quad position
 // q ^ (row & 7); W rows of 2 quads, unswizzled; W scales 4 bytes per row.
 __device__ __forceinline__ int a16_quad_off(int row, int q) { return row * 128 + 16 * (q ^ (row & 7)); }
 
-// 8 codes (one dword) times the group scale -> 8 exact bf16 values.
-__device__ __forceinline__ bf16x8 dec_fp4x8_bf16(uint32_t w, float sc) {
-  bf16x8 r;
-#pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    float2v f;
-    switch (b) {
-      case 0: f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0); break;
-      case 1: f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1); break;
-      case 2: f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2); break;
-      default: f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3); break;
-    }
-    r[2 * b] = (__bf16)(f[0] * sc);
-    r[2 * b + 1] = (__bf16)(f[1] * sc);
-  }
-  return r;
-}
-
-__global__ __launch_bounds__(A16_THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void qgemm_a16_kernel(A16Params p) {
+template <bool SPLIT>
+__global__ __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void qgemm_a16_kernel(GemmParams p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wv = t >> 6;
   const int wm = wv >> 1, wn = wv & 1;
   const int r32 = lane & 31, h = lane >> 5;
-  int tm, tn;
-  tile_coords(xcd_range_id(blockIdx.x, gridDim.x), p.tiles_m, p.tiles_n, tm, tn);
-  const int m0 = tm * 256, n0 = tn * 256;
   const int K = p.K;
-  const int nk = K / A16_BK;
+  const uint8_t* a_bf = static_cast<const uint8_t*>(p.a_q);
+
+  int tile, kb, ke;
+  if constexpr (SPLIT) {
+    tile = (int)(blockIdx.x % p.sk_tiles);
+    const int sl = (int)(blockIdx.x / p.sk_tiles);
+    kb = sl * p.slice_nk;
+    ke = min(p.nk, kb + p.slice_nk);
+  } else {
+    tile = p.sk_tiles + xcd_range_id(blockIdx.x, gridDim.x);
+    kb = 0;
+    ke = p.nk;
+  }
+  int tm, tn;
+  tile_coords(tile, p.tiles_m, p.tiles_n, tm, tn);
+  const int m0 = tm * 256, n0 = tn * 256;
 
   // DMA sources at k0 = 0 (32-bit byte offsets, checked on the host)
   uint32_t offA[8], offW[2];
@@ -103,14 +97,22 @@ void qgemm_a16_kernel(A16Params p) {
 
   const uint32_t lds0 = (uint32_t)(size_t)(lds_void_t*)smem;
   const uint32_t wvu = __builtin_amdgcn_readfirstlane(wv);
+  auto ring = [&](int kt) { return (kt - kb) % A16_NS; };
+  // Load u (0 .. A16_LPS-1) of stage kt, branch-free: a stage past the last
+  // reads stage ke-1's addresses into this wave's landing area.
+  const uint32_t dummy = lds0 + A16_DUMMY + wvu * 1024;
+  auto issue_one = [&](int kt, int u) {
+    const uint32_t live = 0u - (uint32_t)(kt < ke);
+    const int k0 = min(kt, ke - 1) * A16_BK;
+    const uint32_t st = lds0 + (uint32_t)ring(kt) * A16_STAGE;
+    auto pick = [&](uint32_t target) { return dummy + ((target - dummy) & live); };
+    if (u < 8) dma16(a_bf + 2 * k0, offA[u], pick(st + (wvu * 8 + u) * 1024));
+    else if (u < 10) dma16(p.w_q + k0 / 2, offW[u - 8], pick(st + A16_A + (wvu * 2 + (u - 8)) * 1024));
+    else dma4(p.w_s + k0 / 16, offWS, pick(st + A16_A + A16_W + wvu * 256));
+  };
   auto issue_stage = [&](int kt) {
-    const uint32_t st = lds0 + (uint32_t)(kt % A16_NS) * A16_STAGE;
-    const int k0 = kt * A16_BK;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) dma16(p.a + 2 * k0, offA[u], st + (wvu * 8 + u) * 1024);
-#pragma unroll
-    for (int u = 0; u < 2; ++u) dma16(p.w_q + k0 / 2, offW[u], st + A16_A + (wvu * 2 + u) * 1024);
-    dma4(p.w_s + k0 / 16, offWS, st + A16_A + A16_W + wvu * 256);
+    for (int u = 0; u < A16_LPS; ++u) issue_one(kt, u);
   };
 
   float16v acc[4][4];
@@ -121,160 +123,177 @@ void qgemm_a16_kernel(A16Params p) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-  // this lane's W quads and group scales of a stage
-  uint4 wq[4];
-  float wsc[4][2];
-  auto read_w = [&](int kt) {
-    const uint8_t* st = smem + (kt % A16_NS) * A16_STAGE;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int row = wn * 128 + 32 * j + r32;
-      wq[j] = *reinterpret_cast<const uint4*>(st + A16_A + row * 32 + 16 * h);
-      const uint32_t s4 = *reinterpret_cast<const uint32_t*>(st + A16_A + A16_W + row * 4);
-      // steps 0-1 use group 2h, steps 2-3 group 2h + 1
-      wsc[j][0] = e4m3_decode_pos((s4 >> (16 * h)) & 0xFFu);
-      wsc[j][1] = e4m3_decode_pos((s4 >> (16 * h + 8)) & 0xFFu);
+  // LDS reads of one fragment: A of step s, W codes, W scale dword (a lane's
+  // two groups: steps 0-1 use group 2h, steps 2-3 group 2h + 1)
+  auto read_a = [&](int kt, int s, int i, bf16x8& af) {
+    const uint8_t* st = smem + ring(kt) * A16_STAGE;
+    af = __builtin_bit_cast(bf16x8,
+                            *reinterpret_cast<const uint4*>(st + a16_quad_off(wm * 128 + 32 * i + r32, 4 * h + s)));
+  };
+  auto read_wq = [&](int kt, int j, uint4& q) {
+    const uint8_t* st = smem + ring(kt) * A16_STAGE;
+    q = *reinterpret_cast<const uint4*>(st + A16_A + (wn * 128 + 32 * j + r32) * 32 + 16 * h);
+  };
+  auto read_ws = [&](int kt, int j, uint32_t& s4) {
+    const uint8_t* st = smem + ring(kt) * A16_STAGE;
+    s4 = *reinterpret_cast<const uint32_t*>(st + A16_A + A16_W + (wn * 128 + 32 * j + r32) * 4);
+  };
+  // group g's E4M3 scale as fp32: the hardware fp8 conversion (exact for
+  // every E4M3 byte; no branch, which would split the step's schedule)
+  auto scale_of = [&](uint32_t s4, int g) {
+    const int v = (int)(s4 >> (16 * h));
+    return g ? __builtin_amdgcn_cvt_f32_fp8(v, 1) : __builtin_amdgcn_cvt_f32_fp8(v, 0);
+  };
+  // elements 2b, 2b + 1 of W fragment j at step s (codes q, group scale sc)
+  auto piece = [&](const uint4& q, float sc, int s, int b, bf16x8& out) {
+    const uint32_t w = s == 0 ? q.x : s == 1 ? q.y : s == 2 ? q.z : q.w;
+    float2v f;
+    switch (b) {
+      case 0: f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0); break;
+      case 1: f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1); break;
+      case 2: f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2); break;
+      default: f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3); break;
     }
+    out[2 * b] = (__bf16)(f[0] * sc);
+    out[2 * b + 1] = (__bf16)(f[1] * sc);
   };
-  // A fragments of step s read from LDS; W fragments decoded
-  auto read_a = [&](int kt, int s, bf16x8 (&af)[4]) {
-    const uint8_t* st = smem + (kt % A16_NS) * A16_STAGE;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = wm * 128 + 32 * i + r32;
-      af[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(st + a16_quad_off(row, 4 * h + s)));
-    }
-  };
-  auto decode_w = [&](int s, bf16x8 (&bf)[4]) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t w = s == 0 ? wq[j].x : s == 1 ? wq[j].y : s == 2 ? wq[j].z : wq[j].w;
-      bf[j] = dec_fp4x8_bf16(w, wsc[j][s >> 1]);
-    }
-  };
-  auto mfma16 = [&](const bf16x8 (&af)[4], const bf16x8 (&bf)[4]) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[j], af[i], acc[i][j], 0, 0, 0);
-  };
-  // each MFMA followed by a few VALU (decode) and, when present, one LDS read
-  auto interleave = [&]() {
+  auto step = [&](const bf16x8 (&CA)[4], const bf16x8 (&CB)[4], auto&& work) {
 #pragma unroll
     for (int x = 0; x < 16; ++x) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+      acc[x >> 2][x & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(CB[x & 3], CA[x >> 2], acc[x >> 2][x & 3], 0, 0, 0);
+      work(x);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_sched_barrier(0);
   };
 
-  // ---- prologue: stages 0..2 in flight, wait for stage 0
-  issue_stage(0);
-  if (nk > 1) issue_stage(1);
-  if (nk > 2) issue_stage(2);
-  if (nk > 2) wait_vm<2 * A16_LPS>();
-  else if (nk > 1) wait_vm<A16_LPS>();
-  else wait_vm<0>();
+  // ---- prologue: stages kb..kb+2 in flight, wait for stage kb
+  issue_stage(kb);
+  issue_stage(kb + 1);
+  issue_stage(kb + 2);
+  wait_vm<2 * A16_LPS>();
   wait_lgkm_barrier();
 
-  bf16x8 fa[4], fb[4], ga[4], gb[4];
-  read_w(0);
-  read_a(0, 0, fa);
-  decode_w(0, fb);
-
-  // Every step has the same shape: the MFMAs of step s run beside the LDS
-  // reads and W decode of step s+1.  The barrier sits before the last step:
-  // by then every read of this stage's slot has been issued (lgkmcnt(0)), so
-  // the slot takes the stage three ahead, and the next stage is complete, so
-  // the last step can prepare its first.  Past the last stage those reads hit
-  // a stale slot and are discarded.
-  for (int kt = 0; kt < nk; ++kt) {
-    // step 0 | step 1
-    read_a(kt, 1, ga);
-    decode_w(1, gb);
-    mfma16(fa, fb);
-    interleave();
-    // step 1 | step 2
-    read_a(kt, 2, fa);
-    decode_w(2, fb);
-    mfma16(ga, gb);
-    interleave();
-    // step 2 | step 3
-    read_a(kt, 3, ga);
-    decode_w(3, gb);
-    mfma16(fa, fb);
-    interleave();
-    // stage kt+1 complete (only stage kt+2's loads may be in flight), every
-    // wave done reading stage kt
-    if (kt + 2 < nk) wait_vm<A16_LPS>();
-    else wait_vm<0>();
-    wait_lgkm_barrier();
-    if (kt + 3 < nk) issue_stage(kt + 3);
-    // step 3 | step 0 of stage kt+1
-    read_w(kt + 1);
-    read_a(kt + 1, 0, fa);
-    decode_w(0, fb);
-    mfma16(ga, gb);
-    interleave();
+  bf16x8 A0[4], A1[4], A2[4], A3[4], B0[4], B1[4];
+  uint4 wq[4], wqn[4];
+  uint32_t ws4[4], ws4n[4];
+  float sc0[4], sc1[4], sn0[4], sn1[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    read_wq(kb, j, wq[j]);
+    read_ws(kb, j, ws4[j]);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    read_a(kb, 0, i, A0[i]);
+    read_a(kb, 1, i, A1[i]);
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    sc0[j] = scale_of(ws4[j], 0);
+    sc1[j] = scale_of(ws4[j], 1);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) piece(wq[j], sc0[j], 0, b, B0[j]);
   }
 
+  // Every stage has the same shape; past the last stage the reads of the
+  // "next" stage hit a stale slot (or the loads' landing area) and the
+  // extra decode is discarded.
+  for (int kt = kb; kt < ke; ++kt) {
+    // step 0 | W step 1; read A of step 2
+    step(A0, B0, [&](int x) {
+      piece(wq[x >> 2], sc0[x >> 2], 1, x & 3, B1[x >> 2]);
+      if (x < 4) read_a(kt, 2, x, A2[x]);
+    });
+    // step 1 | W step 2; read A of step 3
+    step(A1, B1, [&](int x) {
+      piece(wq[x >> 2], sc1[x >> 2], 2, x & 3, B0[x >> 2]);
+      if (x < 4) read_a(kt, 3, x, A3[x]);
+    });
+    // every read of stage kt is done and stage kt+1 has landed (only stage
+    // kt+2's loads may be in flight): the slot takes stage kt+3
+    wait_vm<A16_LPS>();
+    wait_lgkm_barrier();
+    // step 2 | W step 3; stage kt+1's W scales and codes; loads of stage kt+3
+    step(A2, B0, [&](int x) {
+      piece(wq[x >> 2], sc1[x >> 2], 3, x & 3, B1[x >> 2]);
+      if (x < 4) read_ws(kt + 1, x, ws4n[x]);
+      else if (x < 8) read_wq(kt + 1, x - 4, wqn[x - 4]);
+      else if (x < 12) sn0[x - 8] = scale_of(ws4n[x - 8], 0);
+      else sn1[x - 12] = scale_of(ws4n[x - 12], 1);
+      if (x < A16_LPS) issue_one(kt + 3, x);
+    });
+#pragma unroll
+    for (int j = 0; j < 4; ++j) asm volatile("" : "+v"(B1[j]));
+    // step 3 | W step 0 of stage kt+1; its A of steps 0 and 1
+    step(A3, B1, [&](int x) {
+      piece(wqn[x >> 2], sn0[x >> 2], 0, x & 3, B0[x >> 2]);
+      if (x < 4) read_a(kt + 1, 0, x, A0[x]);
+      else if (x < 8) read_a(kt + 1, 1, x - 4, A1[x - 4]);
+    });
+    // the decoded W of the next step is materialised here: otherwise the
+    // compiler sinks this step's decode past the loop latch, next to its use
+#pragma unroll
+    for (int j = 0; j < 4; ++j) asm volatile("" : "+v"(B0[j]));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      wq[j] = wqn[j];
+      sc0[j] = sn0[j];
+      sc1[j] = sn1[j];
+    }
+  }
+  // the loads of the stages past the end land before the LDS is reused
+  wait_vm<0>();
+
+  if constexpr (SPLIT) {
+    // partial sums of this K slice; the reduce kernel finishes the tile
+    float4* mine = part_slot(p, (int)(blockIdx.x / p.sk_tiles), tile) + wv * 64 * 64 + lane;
+#pragma unroll
+    for (int q = 0; q < 64; ++q) {
+      const int i = q >> 4, j = (q >> 2) & 3, g = q & 3;
+      mine[q * 64] = make_float4(acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
+    }
+    return;
+  }
+  // bf16 output in whole 16-byte chunks: through LDS (the ring is free)
+  if (staged_store_ok(p)) {
+    stage_store_tile<3, 1>(p, acc, smem, m0, n0);
+    return;
+  }
   // epilogue: tile (i, j), lane, register e -> token row m0 + wm*128 + 32 i
   // + lane%32, feature column n0 + wn*128 + 32 j + 8 (e/4) + 4 (lane/32) + e%4
-  const float alpha = p.w_ts[1];
-  const bool vec = (p.N % 4) == 0 && (p.ldy % 4) == 0 &&
-                   ((reinterpret_cast<uintptr_t>(p.y) & (p.out_f32 ? 15u : 7u)) == 0) &&
-                   (!p.bias || (reinterpret_cast<uintptr_t>(p.bias) & 15u) == 0);
+  const bool vec = out_vec_ok(p);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int row = m0 + wm * 128 + 32 * i + r32;
     if (row >= p.M) continue;
+    const float alpha = row_alpha<3>(p, row);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int col = n0 + wn * 128 + 32 * j + 8 * g + 4 * h;
-        float v[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) v[q] = acc[i][j][4 * g + q] * alpha;
-        if (vec && col + 4 <= p.N) {
-          if (p.bias) {
-            const float4 b = *reinterpret_cast<const float4*>(p.bias + col);
-            v[0] = v[0] + b.x; v[1] = v[1] + b.y; v[2] = v[2] + b.z; v[3] = v[3] + b.w;
-          }
-          if (p.out_f32) {
-            *reinterpret_cast<float4*>(static_cast<float*>(p.y) + (int64_t)row * p.ldy + col) =
-                make_float4(v[0], v[1], v[2], v[3]);
-          } else {
-            const uint32_t lo = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
-            const uint32_t hi = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
-            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.y) + (int64_t)row * p.ldy + col) =
-                make_uint2(lo, hi);
-          }
-        } else {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            if (col + q >= p.N) continue;
-            float x = v[q];
-            if (p.bias) x = x + p.bias[col + q];
-            if (p.out_f32)
-              static_cast<float*>(p.y)[(int64_t)row * p.ldy + col + q] = x;
-            else
-              static_cast<uint16_t*>(p.y)[(int64_t)row * p.ldy + col + q] = (uint16_t)f32_to_bf16_bits(x);
-          }
-        }
-      }
-    }
+      for (int g = 0; g < 4; ++g)
+        emit4(p, vec, row, n0 + wn * 128 + 32 * j + 8 * g + 4 * h, alpha, acc[i][j][4 * g], acc[i][j][4 * g + 1],
+              acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
   }
+}
+
+template <bool SPLIT>
+static hipError_t a16_set_lds() {
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&qgemm_a16_kernel<SPLIT>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, A16_LDS);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_qgemm_w4a16(const void* a, const uint8_t* w_q, const uint8_t* w_s, const float* w_ts,
                               const float* bias, void* y, int64_t ldy, int out_dtype, int64_t M, int64_t N,
-                              int64_t K, hipStream_t st) {
+                              int64_t K, void* ws, hipStream_t st) {
   if (M == 0 || N == 0) return hipSuccess;
-  A16Params p{};
-  p.a = static_cast<const uint8_t*>(a);
+  GemmParams p{};
+  p.a_q = a;
   p.w_q = w_q;
   p.w_s = w_s;
   p.w_ts = w_ts;
@@ -285,18 +304,25 @@ hipError_t launch_qgemm_w4a16(const void* a, const uint8_t* w_q, const uint8_t* 
   p.N = (int32_t)N;
   p.K = (int32_t)K;
   p.out_f32 = out_dtype == 1;
-  p.tiles_m = (int32_t)((M + 255) / 256);
-  p.tiles_n = (int32_t)((N + 255) / 256);
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&qgemm_a16_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, A16_NS * A16_STAGE);
+  p.part = static_cast<float*>(ws);
+  int dp_grid = 0, sk_grid = 0;
+  plan_pipe(p, cu_count(), dp_grid, sk_grid, A16_BK);
+  hipError_t e = a16_set_lds<false>();
+  if (e == hipSuccess) e = a16_set_lds<true>();
+  if (e != hipSuccess) return e;
+  if (dp_grid > 0) {
+    hipLaunchKernelGGL(qgemm_a16_kernel<false>, dim3(dp_grid), dim3(GT), (size_t)A16_LDS, st, p);
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
-    attr_set = true;
   }
-  hipLaunchKernelGGL(qgemm_a16_kernel, dim3(p.tiles_m * p.tiles_n), dim3(A16_THREADS),
-                     (size_t)A16_NS * A16_STAGE, st, p);
-  return hipGetLastError();
+  if (sk_grid > 0) {
+    hipLaunchKernelGGL(qgemm_a16_kernel<true>, dim3(sk_grid), dim3(GT), (size_t)A16_LDS, st, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((qgemm_reduce_kernel<3>), dim3(p.sk_tiles * 64), dim3(256), 0, st, p);
+    e = hipGetLastError();
+  }
+  return e;
 }
 
 }  // namespace vdtq

@@ -301,8 +301,9 @@ def qgemm_w4a16(a: BF16Tensor, w: NVFP4Tensor, bias: Optional[torch.Tensor] = No
     _nvfp4(w, "w", N, K, dev)
     _bias(bias, N, dev)
     y = _out(M, N, out_dtype, dev, y)
+    ws = gemm_workspace(dev, M, N)
     L.check(L.lib().qgemm_w4a16(_p(a.q), _p(w.q), _p(w.scales), _p(w.ts), _p(bias), _p(y), y.stride(0),
-                                L.OUT_BF16 if out_dtype == "bf16" else L.OUT_F32, M, N, K,
+                                L.OUT_BF16 if out_dtype == "bf16" else L.OUT_F32, M, N, K, _p(ws), ws.numel(),
                                 _stream(a.q.device)))
     return y
 
