@@ -45,8 +45,14 @@ def source_hash() -> str:
 
 
 def short_name(name: str) -> str:
-    n = name.replace("void ", "").replace("vdtq::", "")
-    return n.split("(")[0]
+    """Kernel name without return type, namespace and argument list; a
+    hipBLASLt (Tensile) kernel is named by its layout and macro tile."""
+    n = name.replace("void ", "").replace("vdtq::", "").replace("(anonymous namespace)::", "")
+    n = n.split("(")[0]
+    if n.startswith("Cijk_"):
+        tile = next((f for f in n.split("_") if f.startswith("MT")), "")
+        n = f"hipBLASLt {n.split('_')[1]} {tile}".rstrip()
+    return n
 
 
 def stats_table(path: str) -> str:
@@ -65,7 +71,7 @@ def trace_table(path: str) -> str:
     per = collections.defaultdict(list)
     for r in csv.DictReader(open(path)):
         n = short_name(r["Kernel_Name"])
-        if "FillFunctor" in n or "copyBuffer" in n:
+        if "FillFunctor" in n or "copyBuffer" in n or n.startswith("at::"):
             continue
         per[(n, int(r["Grid_Size_X"]))].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
     out = ["| kernel | grid (work-items) | dispatches | median us | min us | mean us |", "|---|---|---|---|---|---|"]
@@ -112,7 +118,7 @@ def l2_table(path: str) -> str:
     per = collections.defaultdict(lambda: collections.defaultdict(list))
     for r in csv.DictReader(open(path)):
         n = short_name(r["Kernel_Name"])
-        if "FillFunctor" in n or "copyBuffer" in n:
+        if "FillFunctor" in n or "copyBuffer" in n or n.startswith("at::"):
             continue
         per[(n, int(r["Grid_Size"]))][r["Counter_Name"]].append(float(r["Counter_Value"]))
     out = ["| kernel | grid (work-items) | dispatches | L2 hits (M) | L2 misses (M) | hit rate % |",
