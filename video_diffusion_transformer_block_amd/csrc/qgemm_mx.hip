@@ -31,7 +31,13 @@
 //     matrix instructions; the reads of the next step run under them;
 //   * scales: one dword per row and stage (4 blocks); a lane shifts its
 //     row's dword by 8 (l / 32) bits so that op_sel 0 / 2 picks its block of
-//     step 0 / 1;
+//     step 0 / 1.  With K % 512 == 0 (QUADS) a row's dwords of four
+//     consecutive stages are one 16-byte load per operand row, issued with
+//     every fourth stage into a double-buffered region after the ring (a
+//     scale load touches one row per lane, so per-stage 4-byte loads cost
+//     as many memory requests as the operand codes for a sixteenth of their
+//     bytes); each lane reads its rows' 16 bytes every stage and picks the
+//     stage's dword.  Otherwise each stage carries its own scale dwords;
 //   * the tile order, the split of a partial last wave into K slices, the
 //     reduce pass and the bf16 epilogue through LDS are those of the NVFP4 /
 //     INT8 kernel (qgemm_common.h).
@@ -59,18 +65,25 @@ typedef int int4v __attribute__((ext_vector_type(4)));
 constexpr int kMfmaFp8 = 0;
 constexpr int kMfmaFp4 = 4;
 
-template <bool A8>
+template <bool A8, bool QUADS>
 struct MxPipe {
   static constexpr int A_CODES = 256 * (A8 ? 128 : 64);   // code bytes per stage
   static constexpr int W_CODES = 256 * 64;
   static constexpr int A_SC = 256 * 4;                     // 4 E8M0 bytes per row and stage
   static constexpr int W_SC = 256 * 4;
-  static constexpr int STAGE = A_CODES + W_CODES + A_SC + W_SC;
-  static constexpr int NS = A8 ? 3 : 4;                     // 150 KB / 136 KB of LDS
+  static constexpr int STAGE = A_CODES + W_CODES + (QUADS ? 0 : A_SC + W_SC);
+  // ring depth: a third E4M3 stage measured no faster than two
+  static constexpr int NS = A8 ? (QUADS ? 2 : 3) : 4;
   static constexpr int NA = A_CODES / (4 * 1024);           // 16-byte loads per wave and stage
   static constexpr int NW = W_CODES / (4 * 1024);
-  static constexpr int LPS = NA + NW + 2;                   // + one scale load per operand
-  static constexpr int LDS = NS * STAGE;
+  // loads per stage as the waits count them: with QUADS the scale loads of
+  // every fourth stage are left out, so a wait for "n stages in flight"
+  // waits for at most n * LPS loads and is, if anything, stricter
+  static constexpr int LPS = NA + NW + (QUADS ? 0 : 2);
+  static constexpr int SQ = NS * STAGE;                      // scale quads: 2 buffers x (A, W) x 256 rows x 16 B
+  static constexpr int LDS = SQ + (QUADS ? 2 * 2 * 256 * 16 : 0);
+  // the quantizing epilogue stages 128 KB; its GELU table lies past that
+  static constexpr int GTAB = LDS > 131072 ? LDS : 131072;
 };
 
 // s_waitcnt vmcnt(n * LPS) for n whole stages left in flight (n <= 3)
@@ -172,10 +185,10 @@ __device__ __forceinline__ void quant_store_tile(const GemmParams& p, const floa
 // otherwise per-element stores.  QOUT 1 / 2: the quantizing epilogue with
 // MXFP4 / MXFP8 codes (the GELU table sits after the ring).  One epilogue
 // per instantiation keeps the accumulators in AGPRs until they are read.
-template <bool A8, bool SPLIT, bool STAGED, int QOUT = 0>
+template <bool A8, bool QUADS, bool SPLIT, bool STAGED, int QOUT = 0>
 __global__ __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void qgemm_mx_kernel(GemmParams p) {
-  using P = MxPipe<A8>;
+  using P = MxPipe<A8, QUADS>;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
   const int t = threadIdx.x;
@@ -239,8 +252,18 @@ void qgemm_mx_kernel(GemmParams p) {
     for (int u = 0; u < P::NA; ++u) dma16(abase, offA[u], st + (wvu * P::NA + u) * 1024);
 #pragma unroll
     for (int u = 0; u < P::NW; ++u) dma16(wbase, offW[u], st + P::A_CODES + (wvu * P::NW + u) * 1024);
-    dma4(as + k0 / 32, offAS, st + P::A_CODES + P::W_CODES + wvu * 256);
-    dma4(p.w_s + k0 / 32, offWS, st + P::A_CODES + P::W_CODES + P::A_SC + wvu * 256);
+    if constexpr (QUADS) {
+      // the 16 scale bytes of stages 4g .. 4g+3 per row, into buffer g % 2
+      // (a slice that starts inside a quad loads that quad first)
+      if ((kt & 3) == 0 || kt == kb) {
+        const uint32_t sq = lds0 + P::SQ + (uint32_t)((kt >> 2) & 1) * 8192u + wvu * 1024u;
+        dma16(as + (kt >> 2) * 16, offAS, sq);
+        dma16(p.w_s + (kt >> 2) * 16, offWS, sq + 4096u);
+      }
+    } else {
+      dma4(as + k0 / 32, offAS, st + P::A_CODES + P::W_CODES + wvu * 256);
+      dma4(p.w_s + k0 / 32, offWS, st + P::A_CODES + P::W_CODES + P::A_SC + wvu * 256);
+    }
   };
 
   const int r32 = lane & 31, h = lane >> 5;
@@ -267,13 +290,32 @@ void qgemm_mx_kernel(GemmParams p) {
   // the scale dwords of a stage (4 blocks of each fragment row); a lane uses
   // them shifted right by 8 (lane / 32) bits, so that byte 0 / 2 is its
   // block of step 0 / 1
-  auto read_scales = [&](int kt, uint32_t (&sa)[4], uint32_t (&sw)[4]) {
-    const uint8_t* st = smem + slot(kt) * P::STAGE + P::A_CODES + P::W_CODES;
+  // (with QUADS: the 16 bytes of the stage's quad; pick_scale takes the
+  // stage's dword)
+  using ScaleReg = std::conditional_t<QUADS, int4v, uint32_t>;
+  auto read_scales = [&](int kt, ScaleReg (&sa)[4], ScaleReg (&sw)[4]) {
+    if constexpr (QUADS) {
+      const uint8_t* sq = smem + P::SQ + ((kt >> 2) & 1) * 8192;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sa[i] = *reinterpret_cast<const uint32_t*>(st + 4 * (wm * 128 + 32 * i + r32));
+      for (int i = 0; i < 4; ++i) sa[i] = *reinterpret_cast<const int4v*>(sq + 16 * (wm * 128 + 32 * i + r32));
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      sw[j] = *reinterpret_cast<const uint32_t*>(st + P::A_SC + 4 * (wn * 128 + 32 * j + r32));
+      for (int j = 0; j < 4; ++j) sw[j] = *reinterpret_cast<const int4v*>(sq + 4096 + 16 * (wn * 128 + 32 * j + r32));
+    } else {
+      const uint8_t* st = smem + slot(kt) * P::STAGE + P::A_CODES + P::W_CODES;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sa[i] = *reinterpret_cast<const uint32_t*>(st + 4 * (wm * 128 + 32 * i + r32));
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        sw[j] = *reinterpret_cast<const uint32_t*>(st + P::A_SC + 4 * (wn * 128 + 32 * j + r32));
+    }
+  };
+  auto pick_scale = [&](const ScaleReg& r, int kt) -> uint32_t {
+    if constexpr (QUADS) {
+      const int j = kt & 3;
+      return (uint32_t)(j == 0 ? r[0] : j == 1 ? r[1] : j == 2 ? r[2] : r[3]);
+    } else {
+      return r;
+    }
   };
   const uint32_t hsh = 8 * h;
 
@@ -317,19 +359,20 @@ void qgemm_mx_kernel(GemmParams p) {
   for (int s = 0; s < pre; ++s) issue_stage(kb + s);
   if constexpr (QOUT != 0) {
     // filled under the first loads; the loop's barriers order it before use
-    if (p.qflags & 4u) gelu_table_build(reinterpret_cast<uint16_t*>(smem + P::LDS));
+    if (p.qflags & 4u) gelu_table_build(reinterpret_cast<uint16_t*>(smem + P::GTAB));
   }
   wait_stages<P::LPS>(pre - 1);
   wait_lgkm_barrier();
 
   MxFrag<A8> F0, F1;
-  uint32_t ra[4], rw[4], sa[4], sw[4];   // raw and shifted scale dwords
+  ScaleReg ra[4], rw[4];                 // scale dwords (or quads) as read
+  uint32_t sa[4], sw[4];                 // the stage's dwords, shifted
   read_scales(kb, ra, rw);
   read_frag(kb, 0, F0);
 
   for (int kt = kb; kt < ke; ++kt) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) { sa[i] = ra[i] >> hsh; sw[i] = rw[i] >> hsh; }
+    for (int i = 0; i < 4; ++i) { sa[i] = pick_scale(ra[i], kt) >> hsh; sw[i] = pick_scale(rw[i], kt) >> hsh; }
     // step 0 | read step 1
     read_frag(kt, 1, F1);
     mfma16(F0, sa, sw, std::integral_constant<int, 0>{});
@@ -360,7 +403,7 @@ void qgemm_mx_kernel(GemmParams p) {
   }
 
   if constexpr (QOUT != 0) {
-    quant_store_tile<QOUT == 2>(p, acc, smem, reinterpret_cast<const uint16_t*>(smem + P::LDS), m0, n0);
+    quant_store_tile<QOUT == 2>(p, acc, smem, reinterpret_cast<const uint16_t*>(smem + P::GTAB), m0, n0);
     return;
   }
   // bf16 output in whole 16-byte chunks: through LDS (the ring is free)
@@ -384,40 +427,45 @@ void qgemm_mx_kernel(GemmParams p) {
   }
 }
 
-template <bool A8, bool SPLIT, bool STAGED, int QOUT = 0>
+template <bool A8, bool QUADS, bool SPLIT, bool STAGED, int QOUT = 0>
+static size_t mx_lds_bytes() {
+  return QOUT ? (size_t)MxPipe<A8, QUADS>::GTAB + kGeluTabBytes : (size_t)MxPipe<A8, QUADS>::LDS;
+}
+
+template <bool A8, bool QUADS, bool SPLIT, bool STAGED, int QOUT = 0>
 static hipError_t set_mx_lds_attr() {
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&qgemm_mx_kernel<A8, SPLIT, STAGED, QOUT>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&qgemm_mx_kernel<A8, QUADS, SPLIT, STAGED, QOUT>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       MxPipe<A8>::LDS + (QOUT ? kGeluTabBytes : 0));
+                                       (int)mx_lds_bytes<A8, QUADS, SPLIT, STAGED, QOUT>());
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   return hipSuccess;
 }
 
-template <bool A8>
+template <bool A8, bool QUADS>
 static hipError_t launch_mx(GemmParams p, hipStream_t st) {
   int dp_grid = 0, sk_grid = 0;
   plan_pipe(p, cu_count(), dp_grid, sk_grid);
-  const size_t lds = (size_t)MxPipe<A8>::LDS;
+  const size_t lds = (size_t)MxPipe<A8, QUADS>::LDS;
   // the same test as the device-side staged_store_ok
   const bool staged = !p.out_f32 && (p.N % 8) == 0 && (p.ldy % 8) == 0 && (reinterpret_cast<uintptr_t>(p.y) & 15u) == 0 &&
                       (!p.bias || (reinterpret_cast<uintptr_t>(p.bias) & 15u) == 0);
-  hipError_t e = staged ? set_mx_lds_attr<A8, false, true>() : set_mx_lds_attr<A8, false, false>();
-  if (e == hipSuccess) e = set_mx_lds_attr<A8, true, false>();
+  hipError_t e = staged ? set_mx_lds_attr<A8, QUADS, false, true>() : set_mx_lds_attr<A8, QUADS, false, false>();
+  if (e == hipSuccess) e = set_mx_lds_attr<A8, QUADS, true, false>();
   if (e != hipSuccess) return e;
   if (dp_grid > 0) {
     if (staged)
-      hipLaunchKernelGGL((qgemm_mx_kernel<A8, false, true>), dim3(dp_grid), dim3(GT), lds, st, p);
+      hipLaunchKernelGGL((qgemm_mx_kernel<A8, QUADS, false, true>), dim3(dp_grid), dim3(GT), lds, st, p);
     else
-      hipLaunchKernelGGL((qgemm_mx_kernel<A8, false, false>), dim3(dp_grid), dim3(GT), lds, st, p);
+      hipLaunchKernelGGL((qgemm_mx_kernel<A8, QUADS, false, false>), dim3(dp_grid), dim3(GT), lds, st, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (sk_grid > 0) {
-    hipLaunchKernelGGL((qgemm_mx_kernel<A8, true, false>), dim3(sk_grid), dim3(GT), lds, st, p);
+    hipLaunchKernelGGL((qgemm_mx_kernel<A8, QUADS, true, false>), dim3(sk_grid), dim3(GT), lds, st, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((qgemm_reduce_kernel<2>), dim3(p.sk_tiles * 64), dim3(256), 0, st, p);
@@ -427,7 +475,7 @@ static hipError_t launch_mx(GemmParams p, hipStream_t st) {
 }
 
 // Quantizing variant: every tile in the data-parallel kernel (no K split).
-template <bool A8, int QOUT>
+template <bool A8, bool QUADS, int QOUT>
 static hipError_t launch_mx_quant(GemmParams p, hipStream_t st) {
   int dp_grid = 0, sk_grid = 0;
   plan_pipe(p, cu_count(), dp_grid, sk_grid);
@@ -435,12 +483,15 @@ static hipError_t launch_mx_quant(GemmParams p, hipStream_t st) {
   p.slices = 0;
   p.slice_nk = 0;
   dp_grid = p.tiles_m * p.tiles_n;
-  hipError_t e = set_mx_lds_attr<A8, false, false, QOUT>();
+  hipError_t e = set_mx_lds_attr<A8, QUADS, false, false, QOUT>();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((qgemm_mx_kernel<A8, false, false, QOUT>), dim3(dp_grid), dim3(GT),
-                     (size_t)MxPipe<A8>::LDS + kGeluTabBytes, st, p);
+  const size_t lds = mx_lds_bytes<A8, QUADS, false, false, QOUT>();
+  hipLaunchKernelGGL((qgemm_mx_kernel<A8, QUADS, false, false, QOUT>), dim3(dp_grid), dim3(GT), lds, st, p);
   return hipGetLastError();
 }
+
+// Scale quads need 16-byte aligned 16-byte runs in every scale row.
+static bool mx_quads(int64_t K) { return K % 512 == 0; }
 
 hipError_t launch_qgemm_mx_quant(bool a_fp8, const uint8_t* a_q, const uint8_t* a_s, const uint8_t* w_q,
                                  const uint8_t* w_s, const float* bias, bool out_fp8, bool gelu, uint8_t* q_out,
@@ -452,8 +503,12 @@ hipError_t launch_qgemm_mx_quant(bool a_fp8, const uint8_t* a_q, const uint8_t* 
   p.bias = bias; p.y = nullptr; p.ldy = 0;
   p.M = (int32_t)M; p.N = (int32_t)N; p.K = (int32_t)K;
   p.q_out = q_out; p.s_out = s_out; p.qflags = gelu ? 4u : 0u;
-  if (a_fp8) return out_fp8 ? launch_mx_quant<true, 2>(p, st) : launch_mx_quant<true, 1>(p, st);
-  return out_fp8 ? launch_mx_quant<false, 2>(p, st) : launch_mx_quant<false, 1>(p, st);
+  if (mx_quads(K)) {
+    if (a_fp8) return out_fp8 ? launch_mx_quant<true, true, 2>(p, st) : launch_mx_quant<true, true, 1>(p, st);
+    return out_fp8 ? launch_mx_quant<false, true, 2>(p, st) : launch_mx_quant<false, true, 1>(p, st);
+  }
+  if (a_fp8) return out_fp8 ? launch_mx_quant<true, false, 2>(p, st) : launch_mx_quant<true, false, 1>(p, st);
+  return out_fp8 ? launch_mx_quant<false, false, 2>(p, st) : launch_mx_quant<false, false, 1>(p, st);
 }
 
 hipError_t launch_qgemm_mx(bool a_fp8, const uint8_t* a_q, const uint8_t* a_s, const uint8_t* w_q,
@@ -467,7 +522,8 @@ hipError_t launch_qgemm_mx(bool a_fp8, const uint8_t* a_q, const uint8_t* a_s, c
   p.M = (int32_t)M; p.N = (int32_t)N; p.K = (int32_t)K;
   p.out_f32 = out_dtype == 1;
   p.part = static_cast<float*>(ws);
-  return a_fp8 ? launch_mx<true>(p, st) : launch_mx<false>(p, st);
+  if (mx_quads(K)) return a_fp8 ? launch_mx<true, true>(p, st) : launch_mx<false, true>(p, st);
+  return a_fp8 ? launch_mx<true, false>(p, st) : launch_mx<false, false>(p, st);
 }
 
 }  // namespace vdtq
