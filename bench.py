@@ -19,7 +19,9 @@ block-scaled MFMA) with the same 50/50 assignment, all-MXFP4 and all-MXFP8.
 value = sum of 2*M*N*K over the four linears / step time (TOPS).  Inputs are
 seeded synthetic bf16 (Laplace(0,1) with 0.5% of the channels x30), resident
 in HBM before the timed region; weights are random N(0, 0.02) prepared
-offline (Hadamard-rotated + NVFP4) before timing.
+offline (Hadamard-rotated + NVFP4) before timing.  The timed steps record
+no events inside them; the per-call times and the per-step spread come from
+a second pass of the same steps with HIP events around every call.
 
 Besides the step, the JSON line carries: the dominant GEMM call against the
 fp16 MFMA peak (roofline, with counter traffic while the committed record
@@ -30,7 +32,7 @@ in bf16 through torch / hipBLASLt (context), the 1080p FFN stress shape,
 the fused FFN-up -> FFN-down epilogue, the closed-loop schedule study, the
 host cost of dmpq_step, and the CPU oracle on a bounded sample.
 
-Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline]
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 10] [--no-cpu-baseline]
                        [--no-dyn] [--no-stress] [--sweeps a,b,...]
 """
 from __future__ import annotations
@@ -75,7 +77,7 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=8192)
     ap.add_argument("--no-dyn", action="store_true", help="skip the closed-loop schedule measurement")
@@ -188,16 +190,31 @@ def main():
             step(assign)
         drain()
         torch.cuda.synchronize()
-        rec = []
         # no Python garbage collection inside the timed region: a collection
         # pause on the host would leave the GPU idle between launches
         gc.collect()
         gc.disable()
+        # the breakdown pass: K steps with HIP events around every quantize
+        # and GEMM call.  Each event record leaves the GPU idle for a few us
+        # (about 65 us per step in all), so these steps run slower than the
+        # timed ones; the per-call times (which include one such gap each)
+        # and the per-step spread come from them.  It runs first: the GPU
+        # takes some tens of ms of this load to reach its steady clock.
+        rec = []
+        eb0, eb1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        eb0.record()
+        for _ in range(args.steps):
+            step(assign, rec)
+        eb1.record()
+        drain()
+        torch.cuda.synchronize()
+        ms_instr = eb0.elapsed_time(eb1) / args.steps
+        # the timed region: K whole steps with nothing recorded inside them
         ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         tw = time.perf_counter()
         ev0.record()
         for _ in range(args.steps):
-            step(assign, rec)
+            step(assign)
         ev1.record()
         drain()
         torch.cuda.synchronize()
@@ -205,9 +222,9 @@ def main():
         gc.enable()
         ms = ev0.elapsed_time(ev1) / args.steps
         # per-step times on the GPU timeline: from one step's first event to
-        # the next step's (the last step ends at ev1)
+        # the next step's (the last step ends at eb1)
         nlin = len(linears)
-        starts = [rec[i * nlin][2] for i in range(args.steps)] + [ev1]
+        starts = [rec[i * nlin][2] for i in range(args.steps)] + [eb1]
         step_ms = np.array([starts[i].elapsed_time(starts[i + 1]) for i in range(args.steps)])
         pct = {f"p{q}": round(float(np.percentile(step_ms, q)), 4) for q in (10, 50, 90)}
         per = {}
@@ -216,6 +233,7 @@ def main():
             d["quant_ms"] += e0.elapsed_time(e1) / args.steps
             d["gemm_ms"] += e1.elapsed_time(e2) / args.steps
         results[sweep] = {"ms_per_step": ms, "wall_ms_per_step": 1e3 * wall / args.steps, "step_ms_pct": pct,
+                          "instrumented_ms_per_step": ms_instr,
                           "tops": total_flops / (ms * 1e-3) / 1e12, "per_linear": per}
         print(f"[bench] {sweep}: {ms:.3f} ms/step, {results[sweep]['tops']:.1f} TOPS", file=sys.stderr,
               flush=True)
@@ -322,7 +340,11 @@ def main():
         "stress_1080p": stress,
         "ffn_fusion": ffn_fusion,
         "step_ms_pct": head["step_ms_pct"],
+        "step_ms_pct_note": "per-step spread and per-call times come from a second pass of the same steps with "
+                            "HIP events around every call (instrumented_ms_per_step); ms_per_step and value "
+                            "come from the steps timed without them",
         "sweeps": {k: {"tops": round(v["tops"], 2), "ms_per_step": round(v["ms_per_step"], 4),
+                       "instrumented_ms_per_step": round(v["instrumented_ms_per_step"], 4),
                        "step_ms_pct": v["step_ms_pct"],
                        "gemm_tflops": round(total_flops / (sum(d["gemm_ms"] for d in v["per_linear"].values())
                                                            * 1e-3) / 1e12, 1),

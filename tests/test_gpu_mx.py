@@ -223,6 +223,38 @@ def test_gemm_bf16_output_is_rounded_f32(fmt):
     assert np.array_equal(got, want), np.argwhere(got != want)[:5]
 
 
+@pytest.mark.parametrize("fmt", ["mxfp4", "mxfp8"])
+@pytest.mark.parametrize("with_bias", [True, False])
+def test_gemm_ragged_edges_padded_output(fmt, with_bias):
+    """561 tiles with ragged M and N (17 x 33 tiles of 4100 x 8200): 512 in
+    the data-parallel kernel, 49 in K slices.  The bf16 output, written into
+    a row-padded buffer whose padding must stay untouched, equals the RNE of
+    the fp32 output bit for bit, and rows of the first and last tile rows
+    meet the element-wise bar against the oracle."""
+    need_gpu()
+    M, N, K = 4100, 8200, 1024
+    x_bits = synth.to_bf16_bits(RNG.laplace(size=(M, K)).astype(np.float32))
+    w_bits = synth.to_bf16_bits(RNG.standard_normal((N, K)).astype(np.float32) * 0.02)
+    bias_h = RNG.standard_normal(N).astype(np.float32) if with_bias else None
+    log(f"mx ragged edges fmt={fmt} bias={with_bias}")
+    a = V.hadamard_quantize(dev_bf16(x_bits), 64, fmt)
+    wd = V.hadamard_quantize(dev_bf16(w_bits), 64, "mxfp4")
+    bias_d = torch.from_numpy(bias_h).cuda() if with_bias else None
+    big = torch.full((M, N + 24), -7.0, dtype=torch.bfloat16, device="cuda")
+    yb = V.qgemm_mx(a, wd, bias_d, "bf16", y=big[:, :N])
+    yf = V.qgemm_mx(a, wd, bias_d, "f32")
+    torch.cuda.synchronize()
+    got = host_bits(big)
+    assert np.array_equal(got[:, :N], F.f32_to_bf16(yf.cpu().numpy())), "bf16 != RNE(f32)"
+    assert (got[:, N:] == F.f32_to_bf16(np.float32(-7.0))).all(), "padding written"
+    rows = np.r_[0:3, 255:258, M - 4:M]
+    ref = Q.hadamard_quantize(x_bits[rows], 64, fmt)
+    wq_o, ws_o = Q.prepare_weight_mx(w_bits, 64)
+    e64, _ = G.qgemm_mx(ref["q"], ref["scales"], fmt, wq_o, ws_o, bias_h, "f32")
+    terms = terms_mx(ref["q"], ref["scales"], fmt, wq_o, ws_o, bias_h)
+    assert_elementwise(yf.cpu().numpy()[rows], e64, terms, K, "f32", f"ragged edges {fmt}")
+
+
 def test_gemm_rejects_unsupported_k():
     need_gpu()
     a = V.MXTensor(torch.zeros((4, 48), dtype=torch.uint8, device="cuda"),
