@@ -85,7 +85,7 @@ def test_w4a16_tiny_layer():
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 1, 64), (129, 33, 64), (300, 200, 320), (5, 300, 128),
-                                   (131, 257, 256), (600, 520, 1920)])
+                                   (131, 257, 256), (600, 520, 1920), (300, 260, 768)])
 def test_w4a16_ragged(M, N, K):
     need_gpu()
     x = synth.to_bf16_bits(RNG.laplace(size=(M, K)).astype(np.float32))

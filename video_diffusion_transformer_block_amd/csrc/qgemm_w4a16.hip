@@ -24,6 +24,13 @@
 // pairs (hardware conversion), times the group's E4M3 scale (exact), ->
 // bf16 pairs (2 VALU per element: gfx950 has no packed bf16 multiply).
 //
+// W scales: with K % 256 == 0 (QUADS) a row's scale bytes of four
+// consecutive stages are one 16-byte load per row, issued with every fourth
+// stage into a double-buffered region past the ring (a scale load touches
+// one row per lane: per-stage 4-byte loads cost as many memory requests as
+// all the stage's A for an eighth of its bytes); otherwise 4 bytes per row
+// with every stage.
+//
 // The main loop is scheduled by hand, as in qgemm.hip: each MFMA of a step
 // is followed by one eighth of the next step's W decode (two elements) and
 // at most one LDS read and one stage load, held together by sched_barrier.
@@ -44,18 +51,29 @@ constexpr int A16_NS = 3;
 constexpr int A16_A = 256 * 128;      // A bytes per stage
 constexpr int A16_W = 256 * 32;       // W code bytes per stage
 constexpr int A16_WS = 256 * 4;       // W scale bytes per stage
-constexpr int A16_STAGE = A16_A + A16_W + A16_WS;
-constexpr int A16_LPS = 8 + 2 + 1;    // loads per wave and stage
-constexpr int A16_DUMMY = A16_NS * A16_STAGE;   // landing area (1 KB per wave) of loads past the last stage
-constexpr int A16_LDS = (A16_DUMMY + 4096 > 4 * 32768) ? A16_DUMMY + 4096 : 4 * 32768;
+
+template <bool QUADS>
+struct A16Pipe {
+  static constexpr int STAGE = A16_A + A16_W + (QUADS ? 0 : A16_WS);
+  static constexpr int NLOAD = 8 + 2 + 1;           // load slots per wave and stage
+  // loads per stage as the waits count them: with QUADS the scale slot
+  // issues on every fourth stage only and is left out, so a wait for
+  // "n stages in flight" is, if anything, stricter
+  static constexpr int LPS = QUADS ? 8 + 2 : NLOAD;
+  static constexpr int DUMMY = A16_NS * STAGE;      // landing area (1 KB per wave) of loads past the last stage
+  static constexpr int SQ = DUMMY + 4096;           // scale quads: 2 buffers x 256 rows x 16 B
+  static constexpr int END = SQ + (QUADS ? 2 * 4096 : 0);
+  static constexpr int LDS = END > 4 * 32768 ? END : 4 * 32768;
+};
 
 // LDS layout of a stage: A rows of 8 quads (16 B) stored at quad position
 // q ^ (row & 7); W rows of 2 quads, unswizzled; W scales 4 bytes per row.
 __device__ __forceinline__ int a16_quad_off(int row, int q) { return row * 128 + 16 * (q ^ (row & 7)); }
 
-template <bool SPLIT>
+template <bool SPLIT, bool QUADS>
 __global__ __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void qgemm_a16_kernel(GemmParams p) {
+  using P = A16Pipe<QUADS>;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int t = threadIdx.x;
   const int lane = t & 63;
@@ -98,21 +116,30 @@ void qgemm_a16_kernel(GemmParams p) {
   const uint32_t lds0 = (uint32_t)(size_t)(lds_void_t*)smem;
   const uint32_t wvu = __builtin_amdgcn_readfirstlane(wv);
   auto ring = [&](int kt) { return (kt - kb) % A16_NS; };
-  // Load u (0 .. A16_LPS-1) of stage kt, branch-free: a stage past the last
-  // reads stage ke-1's addresses into this wave's landing area.
-  const uint32_t dummy = lds0 + A16_DUMMY + wvu * 1024;
+  // Load u (0 .. NLOAD-1) of stage kt, branch-free: a stage past the last
+  // reads stage ke-1's addresses into this wave's landing area.  The scale
+  // slot with QUADS loads the 16 bytes of stages 4g .. 4g+3 per row into
+  // buffer g % 2 on stage 4g (and on a slice's first stage), else nothing.
+  const uint32_t dummy = lds0 + P::DUMMY + wvu * 1024;
   auto issue_one = [&](int kt, int u) {
     const uint32_t live = 0u - (uint32_t)(kt < ke);
     const int k0 = min(kt, ke - 1) * A16_BK;
-    const uint32_t st = lds0 + (uint32_t)ring(kt) * A16_STAGE;
+    const uint32_t st = lds0 + (uint32_t)ring(kt) * P::STAGE;
     auto pick = [&](uint32_t target) { return dummy + ((target - dummy) & live); };
-    if (u < 8) dma16(a_bf + 2 * k0, offA[u], pick(st + (wvu * 8 + u) * 1024));
-    else if (u < 10) dma16(p.w_q + k0 / 2, offW[u - 8], pick(st + A16_A + (wvu * 2 + (u - 8)) * 1024));
-    else dma4(p.w_s + k0 / 16, offWS, pick(st + A16_A + A16_W + wvu * 256));
+    if (u < 8) {
+      dma16(a_bf + 2 * k0, offA[u], pick(st + (wvu * 8 + u) * 1024));
+    } else if (u < 10) {
+      dma16(p.w_q + k0 / 2, offW[u - 8], pick(st + A16_A + (wvu * 2 + (u - 8)) * 1024));
+    } else if constexpr (QUADS) {
+      if (kt < ke && ((kt & 3) == 0 || kt == kb))
+        dma16(p.w_s + (kt >> 2) * 16, offWS, lds0 + P::SQ + (uint32_t)((kt >> 2) & 1) * 4096u + wvu * 1024u);
+    } else {
+      dma4(p.w_s + k0 / 16, offWS, pick(st + A16_A + A16_W + wvu * 256));
+    }
   };
   auto issue_stage = [&](int kt) {
 #pragma unroll
-    for (int u = 0; u < A16_LPS; ++u) issue_one(kt, u);
+    for (int u = 0; u < P::NLOAD; ++u) issue_one(kt, u);
   };
 
   float16v acc[4][4];
@@ -126,17 +153,22 @@ void qgemm_a16_kernel(GemmParams p) {
   // LDS reads of one fragment: A of step s, W codes, W scale dword (a lane's
   // two groups: steps 0-1 use group 2h, steps 2-3 group 2h + 1)
   auto read_a = [&](int kt, int s, int i, bf16x8& af) {
-    const uint8_t* st = smem + ring(kt) * A16_STAGE;
+    const uint8_t* st = smem + ring(kt) * P::STAGE;
     af = __builtin_bit_cast(bf16x8,
                             *reinterpret_cast<const uint4*>(st + a16_quad_off(wm * 128 + 32 * i + r32, 4 * h + s)));
   };
   auto read_wq = [&](int kt, int j, uint4& q) {
-    const uint8_t* st = smem + ring(kt) * A16_STAGE;
+    const uint8_t* st = smem + ring(kt) * P::STAGE;
     q = *reinterpret_cast<const uint4*>(st + A16_A + (wn * 128 + 32 * j + r32) * 32 + 16 * h);
   };
   auto read_ws = [&](int kt, int j, uint32_t& s4) {
-    const uint8_t* st = smem + ring(kt) * A16_STAGE;
-    s4 = *reinterpret_cast<const uint32_t*>(st + A16_A + A16_W + (wn * 128 + 32 * j + r32) * 4);
+    if constexpr (QUADS) {
+      s4 = *reinterpret_cast<const uint32_t*>(smem + P::SQ + ((kt >> 2) & 1) * 4096 + (wn * 128 + 32 * j + r32) * 16 +
+                                              4 * (kt & 3));
+    } else {
+      const uint8_t* st = smem + ring(kt) * P::STAGE;
+      s4 = *reinterpret_cast<const uint32_t*>(st + A16_A + A16_W + (wn * 128 + 32 * j + r32) * 4);
+    }
   };
   // group g's E4M3 scale as fp32: the hardware fp8 conversion (exact for
   // every E4M3 byte; no branch, which would split the step's schedule)
@@ -170,7 +202,7 @@ void qgemm_a16_kernel(GemmParams p) {
   issue_stage(kb);
   issue_stage(kb + 1);
   issue_stage(kb + 2);
-  wait_vm<2 * A16_LPS>();
+  wait_vm<2 * P::LPS>();
   wait_lgkm_barrier();
 
   bf16x8 A0[4], A1[4], A2[4], A3[4], B0[4], B1[4];
@@ -211,7 +243,7 @@ void qgemm_a16_kernel(GemmParams p) {
     });
     // every read of stage kt is done and stage kt+1 has landed (only stage
     // kt+2's loads may be in flight): the slot takes stage kt+3
-    wait_vm<A16_LPS>();
+    wait_vm<P::LPS>();
     wait_lgkm_barrier();
     // step 2 | W step 3; stage kt+1's W scales and codes; loads of stage kt+3
     step(A2, B0, [&](int x) {
@@ -220,7 +252,7 @@ void qgemm_a16_kernel(GemmParams p) {
       else if (x < 8) read_wq(kt + 1, x - 4, wqn[x - 4]);
       else if (x < 12) sn0[x - 8] = scale_of(ws4n[x - 8], 0);
       else sn1[x - 12] = scale_of(ws4n[x - 12], 1);
-      if (x < A16_LPS) issue_one(kt + 3, x);
+      if (x < P::NLOAD) issue_one(kt + 3, x);
     });
 #pragma unroll
     for (int j = 0; j < 4; ++j) asm volatile("" : "+v"(B1[j]));
@@ -276,16 +308,37 @@ void qgemm_a16_kernel(GemmParams p) {
   }
 }
 
-template <bool SPLIT>
+template <bool SPLIT, bool QUADS>
 static hipError_t a16_set_lds() {
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&qgemm_a16_kernel<SPLIT>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, A16_LDS);
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&qgemm_a16_kernel<SPLIT, QUADS>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, A16Pipe<QUADS>::LDS);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   return hipSuccess;
+}
+
+template <bool QUADS>
+static hipError_t launch_a16(const GemmParams& p, int dp_grid, int sk_grid, hipStream_t st) {
+  const size_t lds = (size_t)A16Pipe<QUADS>::LDS;
+  hipError_t e = a16_set_lds<false, QUADS>();
+  if (e == hipSuccess) e = a16_set_lds<true, QUADS>();
+  if (e != hipSuccess) return e;
+  if (dp_grid > 0) {
+    hipLaunchKernelGGL((qgemm_a16_kernel<false, QUADS>), dim3(dp_grid), dim3(GT), lds, st, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (sk_grid > 0) {
+    hipLaunchKernelGGL((qgemm_a16_kernel<true, QUADS>), dim3(sk_grid), dim3(GT), lds, st, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((qgemm_reduce_kernel<3>), dim3(p.sk_tiles * 64), dim3(256), 0, st, p);
+    e = hipGetLastError();
+  }
+  return e;
 }
 
 hipError_t launch_qgemm_w4a16(const void* a, const uint8_t* w_q, const uint8_t* w_s, const float* w_ts,
@@ -307,22 +360,8 @@ hipError_t launch_qgemm_w4a16(const void* a, const uint8_t* w_q, const uint8_t* 
   p.part = static_cast<float*>(ws);
   int dp_grid = 0, sk_grid = 0;
   plan_pipe(p, cu_count(), dp_grid, sk_grid, A16_BK);
-  hipError_t e = a16_set_lds<false>();
-  if (e == hipSuccess) e = a16_set_lds<true>();
-  if (e != hipSuccess) return e;
-  if (dp_grid > 0) {
-    hipLaunchKernelGGL(qgemm_a16_kernel<false>, dim3(dp_grid), dim3(GT), (size_t)A16_LDS, st, p);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  if (sk_grid > 0) {
-    hipLaunchKernelGGL(qgemm_a16_kernel<true>, dim3(sk_grid), dim3(GT), (size_t)A16_LDS, st, p);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((qgemm_reduce_kernel<3>), dim3(p.sk_tiles * 64), dim3(256), 0, st, p);
-    e = hipGetLastError();
-  }
-  return e;
+  // scale quads need 16-byte aligned 16-byte runs in every scale row
+  return K % 256 == 0 ? launch_a16<true>(p, dp_grid, sk_grid, st) : launch_a16<false>(p, dp_grid, sk_grid, st);
 }
 
 }  // namespace vdtq
