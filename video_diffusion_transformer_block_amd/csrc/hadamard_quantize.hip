@@ -250,8 +250,10 @@ __device__ void wg_stats_write(double mx, double sx, double my, double sy, doubl
 // The workgroups walk the tensor from its end (workgroup i takes tile
 // G - 1 - i): the quantize pass that follows starts at the front, which is
 // then what the last-level cache holds.  The maximum does not depend on the
-// order.
-template <int B>
+// order.  STATS: the pass also takes the outlier statistics (it transforms
+// every value anyway), in the quantize pass's per-thread order (sums of 16
+// |y| per group); staged zeros pad the tail and add nothing to any of them.
+template <int B, bool STATS>
 __global__ __launch_bounds__(HQ_THREADS) void hq_amax_kernel(HQParams p) {
   __shared__ uint4 lds[HQ_THREADS * 8];
   __shared__ float wred[HQ_THREADS / 64];
@@ -261,11 +263,29 @@ __global__ __launch_bounds__(HQ_THREADS) void hq_amax_kernel(HQParams p) {
   __syncthreads();
   float v[64];
   load_chunk(lds, v, p.flags);
+  float mx = 0.0f, sx = 0.0f;
+  if (STATS) {
+    input_stats(v, 64, mx, sx);
+    // taken here, before the butterflies overwrite v (left to the scheduler,
+    // the input values were kept in a second set of registers)
+    asm volatile("" : "+v"(mx), "+v"(sx));
+  }
   fwht<B>(v);
   normalise<B>(v);
   float m = 0.0f;
 #pragma unroll
   for (int i = 0; i < 64; ++i) m = fmaxf(m, fabsf(v[i]));   // staged zeros pad the tail
+  float sy = 0.0f;
+  if (STATS) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      float s = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s = s + fabsf(v[16 * g + e]);
+      sy = sy + s * yfac<B>();
+    }
+  }
+  const float my = m * yfac<B>();                 // exact (power of two)
   m = wave_max(m);
   if ((threadIdx.x & 63) == 0) wred[threadIdx.x >> 6] = m;
   __syncthreads();
@@ -274,6 +294,7 @@ __global__ __launch_bounds__(HQ_THREADS) void hq_amax_kernel(HQParams p) {
     for (int i = 1; i < HQ_THREADS / 64; ++i) a = fmaxf(a, wred[i]);
     p.amax_part[blockIdx.x] = a * yfac<B>();
   }
+  if (STATS) wg_stats_write(mx, sx, my, sy, p.stats_part + 4 * (int64_t)blockIdx.x);
 }
 
 // One workgroup of kFinalThreads: amax_T = max of the partial maxima;
@@ -281,7 +302,7 @@ __global__ __launch_bounds__(HQ_THREADS) void hq_amax_kernel(HQParams p) {
 // are zeros, neutral for a maximum of non-negative values.
 constexpr int kFinalThreads = 1024;
 
-__global__ __launch_bounds__(kFinalThreads) void hq_amax_final_kernel(const float* part, int n, float* ts) {
+__device__ __forceinline__ void amax_final(const float* part, int n, float* ts) {
   __shared__ float wred[kFinalThreads / 64];
   constexpr int U = 16;
   const __amdgpu_buffer_rsrc_t r = raw_buffer(part, (uint32_t)n * 4u);
@@ -304,6 +325,10 @@ __global__ __launch_bounds__(kFinalThreads) void hq_amax_final_kernel(const floa
   }
 }
 
+__global__ __launch_bounds__(kFinalThreads) void hq_amax_final_kernel(const float* part, int n, float* ts) {
+  amax_final(part, n, ts);
+}
+
 // Writes gs for a caller-supplied amax (used when there are no rows).
 __global__ void hq_gs_only_kernel(float* ts) {
   if (threadIdx.x == 0) ts[1] = nvfp4_gs(ts[0]);
@@ -312,7 +337,7 @@ __global__ void hq_gs_only_kernel(float* ts) {
 // Final fp64 reduction of the per-workgroup statistics {max, sum, max, sum}
 // (fixed order).  Each thread keeps 4 partials (8 loads) in flight; reads
 // past n are zeros, neutral for these non-negative maxima and sums.
-__global__ __launch_bounds__(kFinalThreads) void hq_stats_final_kernel(const double* part, int n, double* out) {
+__device__ __forceinline__ void stats_final(const double* part, int n, double* out) {
   __shared__ double red[4][kFinalThreads / 64];
   constexpr int U = 4;
   const __amdgpu_buffer_rsrc_t r = raw_buffer(part, (uint32_t)n * 32u);
@@ -344,6 +369,17 @@ __global__ __launch_bounds__(kFinalThreads) void hq_stats_final_kernel(const dou
     }
     out[0] = x0; out[1] = x1; out[2] = x2; out[3] = x3;
   }
+}
+
+__global__ __launch_bounds__(kFinalThreads) void hq_stats_final_kernel(const double* part, int n, double* out) {
+  stats_final(part, n, out);
+}
+
+// Both reductions of an amax pre-pass that also took the statistics.
+__global__ __launch_bounds__(kFinalThreads) void hq_amax_stats_final_kernel(const float* apart, const double* spart,
+                                                                            int n, float* ts, double* out) {
+  amax_final(apart, n, ts);
+  stats_final(spart, n, out);
 }
 
 // NVFP4 encoding of a thread's 64 transformed register values: per 16-group
@@ -652,15 +688,28 @@ static int hq_int8_threads(int cpr) {
   return (r192 >= 1 && r192 * cpr * 256 > r256 * cpr * 192) ? 192 : 256;
 }
 
+// stats: where the statistics' final reduction goes (the partials are
+// written by this call's kernels).  NVFP4 with the tensor amax computed takes
+// them in the pre-pass and reduces both in one launch; otherwise the pass
+// takes them and the final kernel follows it.
 template <int B>
-static hipError_t launch_b(const HQParams& p, int fmt, bool amax_given, int grid, hipStream_t st) {
+static hipError_t launch_b(const HQParams& p, int fmt, bool amax_given, int grid, double* stats, hipStream_t st) {
   const size_t shm = (p.flags & 4u) ? (size_t)kGeluTabBytes : 0;   // the GELU table
-  if (fmt == 0) {
-    if (!amax_given) {
-      hipLaunchKernelGGL(hq_amax_kernel<B>, dim3(grid), dim3(HQ_THREADS), shm, st, p);
+  const bool want_stats = (p.flags & 2u) != 0;
+  if (fmt == 0 && !amax_given) {
+    if (want_stats) {
+      hipLaunchKernelGGL((hq_amax_kernel<B, true>), dim3(grid), dim3(HQ_THREADS), shm, st, p);
+      hipLaunchKernelGGL(hq_amax_stats_final_kernel, dim3(1), dim3(kFinalThreads), 0, st, p.amax_part, p.stats_part,
+                         grid, p.ts, stats);
+    } else {
+      hipLaunchKernelGGL((hq_amax_kernel<B, false>), dim3(grid), dim3(HQ_THREADS), shm, st, p);
       hipLaunchKernelGGL(hq_amax_final_kernel, dim3(1), dim3(kFinalThreads), 0, st, p.amax_part, grid, p.ts);
     }
-    if (p.flags & 2u)
+    hipLaunchKernelGGL((hq_nvfp4_kernel<B, false>), dim3(grid), dim3(HQ_THREADS), shm, st, p);
+    return hipGetLastError();
+  }
+  if (fmt == 0) {
+    if (want_stats)
       hipLaunchKernelGGL((hq_nvfp4_kernel<B, true>), dim3(grid), dim3(HQ_THREADS), shm, st, p);
     else
       hipLaunchKernelGGL((hq_nvfp4_kernel<B, false>), dim3(grid), dim3(HQ_THREADS), shm, st, p);
@@ -676,6 +725,7 @@ static hipError_t launch_b(const HQParams& p, int fmt, bool amax_given, int grid
   } else {
     hipLaunchKernelGGL((hq_mx_kernel<B, true>), dim3(grid), dim3(HQ_THREADS), shm, st, p);
   }
+  if (want_stats) hipLaunchKernelGGL(hq_stats_final_kernel, dim3(1), dim3(kFinalThreads), 0, st, p.stats_part, grid, stats);
   return hipGetLastError();
 }
 
@@ -766,20 +816,13 @@ hipError_t launch_hadamard_quantize(const void* x, int64_t M, int64_t K, int64_t
     const hipError_t et = hipGetLastError();
     if (et != hipSuccess) return et;
   }
-  hipError_t e;
   switch (b) {
-    case 16: e = launch_b<16>(p, fmt, amax_given, grid, st); break;
-    case 32: e = launch_b<32>(p, fmt, amax_given, grid, st); break;
-    case 64: e = launch_b<64>(p, fmt, amax_given, grid, st); break;
-    case 128: e = launch_b<128>(p, fmt, amax_given, grid, st); break;
-    default: e = launch_b<256>(p, fmt, amax_given, grid, st); break;
+    case 16: return launch_b<16>(p, fmt, amax_given, grid, stats, st);
+    case 32: return launch_b<32>(p, fmt, amax_given, grid, stats, st);
+    case 64: return launch_b<64>(p, fmt, amax_given, grid, stats, st);
+    case 128: return launch_b<128>(p, fmt, amax_given, grid, stats, st);
+    default: return launch_b<256>(p, fmt, amax_given, grid, stats, st);
   }
-  if (e != hipSuccess) return e;
-  if (want_stats) {
-    hipLaunchKernelGGL(hq_stats_final_kernel, dim3(1), dim3(kFinalThreads), 0, st, p.stats_part, grid, stats);
-    e = hipGetLastError();
-  }
-  return e;
 }
 
 }  // namespace vdtq
