@@ -170,7 +170,9 @@ def test_fused_stats_5b_every_format(K):
     (NVFP4, INT8, BF16, MXFP4, MXFP8), against the oracle over every row.
     These grids hold 4444 to 26664 workgroup partials, more than one pass of
     the final reduction's 4096-partial loop; the codes of the BF16 and MX
-    formats are compared on sampled rows as well."""
+    formats are compared on sampled rows as well.  NVFP4 runs twice: with
+    the tensor amax computed (the statistics come from the amax pre-pass)
+    and with it supplied (from the quantize pass)."""
     need_gpu()
     M = synth.TOKENS_2B_5B
     name = "ffn_down" if K == 12288 else "qkv"
@@ -185,6 +187,11 @@ def test_fused_stats_5b_every_format(K):
         check_stats(r.stats.cpu().numpy(), want)
         if fmt == "nvfp4":
             assert r.ts.cpu().numpy()[0] == amax_o
+            log(f"stats 5B K={K} fmt=nvfp4, amax supplied")
+            rg = V.hadamard_quantize(xd, 64, fmt, amax=float(amax_o), stats=True)
+            torch.cuda.synchronize()
+            check_stats(rg.stats.cpu().numpy(), want)
+            assert torch.equal(rg.q, r.q) and torch.equal(rg.scales, r.scales)
         if fmt in ("bf16", "mxfp4", "mxfp8"):
             ref = Q.hadamard_quantize(x[rows], 64, fmt)
             if fmt == "bf16":
