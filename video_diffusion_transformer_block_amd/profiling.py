@@ -89,7 +89,7 @@ def mfma_table(path: str, simds: int = 1024, xcds: int = 8) -> str:
     dur = collections.defaultdict(dict)
     for r in csv.DictReader(open(path)):
         n = short_name(r["Kernel_Name"])
-        if not (n.startswith("qgemm_pipe") or n.startswith("qgemm_mx")):
+        if not (n.startswith("qgemm_pipe") or n.startswith("qgemm_mx") or n.startswith("qgemm_a16")):
             continue
         k = (n, int(r["Grid_Size"]))
         per[k][r["Counter_Name"]].append(float(r["Counter_Value"]))
