@@ -123,7 +123,11 @@ size_t vdtq_workspace_bytes(int op, int64_t M, int64_t K);
  *     e + 127, element = nearest-even encoding of y / 2^e, saturating at 6
  *     or 448, sign copied.
  *
- * x_dev          bf16 [M][ldx], ldx >= K (elements)
+ * x_dev          bf16 [M][ldx], ldx >= K (elements); finite values whose
+ *                transform stays finite (a NaN or an infinity, in X or
+ *                from butterflies that overflow fp32, gives unspecified
+ *                codes, scales and statistics; every access still stays
+ *                inside the buffers)
  * M              rows (tokens), >= 0; M == 0 is a no-op (NVFP4 still writes
  *                the tensor scale {0, 1} unless AMAX_GIVEN)
  * K              columns, > 0, multiple of 16 and of had_block; for INT8,
