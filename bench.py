@@ -12,7 +12,8 @@ One step = one pass of the whole hot path over one block:
   with more than one block).
 The headline step uses the 50/50 NVFP4/INT8 assignment (QKV and FFN-down
 NVFP4, out-proj and FFN-up INT8), the W4A6 operating point of the pages; the
-all-NVFP4, all-INT8 and all-W4A16 sweeps are timed the same way after it,
+same point with the two formats swapped, the all-NVFP4, all-INT8 and
+all-W4A16 sweeps are timed the same way after it,
 then the MX-native variant (MXFP4 weights; MXFP4 / MXFP8 activations on the
 block-scaled MFMA) with the same 50/50 assignment, all-MXFP4 and all-MXFP8.
 
@@ -59,6 +60,8 @@ HAD_BLOCK = 64
 
 MIXED = {"qkv": "nvfp4", "out": "int8", "ffn_up": "int8", "ffn_down": "nvfp4"}
 SWEEPS = {"mixed_w4a6": MIXED,
+          # the same 50/50 point with the two formats swapped between the linears
+          "mixed_w4a6_swapped": {k: ("int8" if v == "nvfp4" else "nvfp4") for k, v in MIXED.items()},
           "all_w4a4": {k: "nvfp4" for k in MIXED},
           "all_w4a8": {k: "int8" for k in MIXED},
           # the full-precision fallback (bf16 activations, 4-bit weights) on every linear
@@ -349,7 +352,10 @@ def main():
                        "gemm_tflops": round(total_flops / (sum(d["gemm_ms"] for d in v["per_linear"].values())
                                                            * 1e-3) / 1e12, 1),
                        "per_linear_ms": {n: [round(d["quant_ms"], 4), round(d["gemm_ms"], 4)]
-                                         for n, d in v["per_linear"].items()}}
+                                         for n, d in v["per_linear"].items()},
+                       # the per-layer pipeline figure: 2MNK / (quantize + GEMM)
+                       "per_linear_tops": {n: round(flops[n] / ((d["quant_ms"] + d["gemm_ms"]) * 1e-3) / 1e12, 1)
+                                           for n, d in v["per_linear"].items()}}
                    for k, v in results.items()},
         "dyn_schedule": dyn,
         "dmpq_step": dmpq,

@@ -1,0 +1,135 @@
+"""The hot path captured in a HIP graph (torch.cuda.CUDAGraph).  A library
+call only enqueues kernels on the caller's stream: no allocation, memset or
+synchronisation inside it, and every workspace it reads is either written
+first in the same call or left as it found it (block_stats' completion
+counter).  So a whole step captures once and replays.  Each replay, with
+new input values and eager calls of the same entry points between replays,
+must give the eager results bit for bit: codes, scales, tensor scales,
+statistics, GEMM outputs (including a split last wave and its reduce pass)
+and the delta cache."""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+import video_diffusion_transformer_block_amd as V
+from video_diffusion_transformer_block_amd import _lib as L
+from helpers import need_gpu, log
+
+pytestmark = pytest.mark.gpu
+
+M, K, N, KD = 600, 2048, 768, 1536     # 3 x 3 output tiles: a partial wave, split along K
+
+
+def _laplace_bits(rng, shape, scale=1.0):
+    return synth.to_bf16_bits(rng.laplace(size=shape).astype(np.float32) * np.float32(scale))
+
+
+def _upload(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def _fill(dst, bits):
+    dst.copy_(_upload(bits))
+
+
+def _noalloc_nvfp4(x, q, s, ts, st):
+    rows, cols = x.shape
+    L.check(L.lib().hadamard_quantize_noalloc(
+        ctypes.c_void_p(x.data_ptr()), rows, cols, x.stride(0), 64, L.FMT_NVFP4, L.STATS,
+        ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(s.data_ptr()), ctypes.c_void_p(ts.data_ptr()),
+        ctypes.c_void_p(st.data_ptr()), ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)))
+
+
+def _step(x1, x2, xd, xin, xout, dprev, dnew, w1, w2, wd, wm, bias, na):
+    """One pass over every entry point; returns the tensors it wrote."""
+    a4 = V.hadamard_quantize(x1, 64, "nvfp4", stats=True)        # amax pre-pass + statistics
+    y4 = V.qgemm_w4a4(a4, w1, bias, "bf16")
+    a8 = V.hadamard_quantize(x2, 64, "int8", stats=True)
+    y8 = V.qgemm_w4a8(a8, w2, None, "f32")
+    ag = V.hadamard_quantize(xd, 64, "nvfp4", gelu=True)         # GELU table, then both passes
+    yd = V.qgemm_w4a4(ag, wd, None, "bf16")
+    ab = V.hadamard_quantize(x1, 64, "bf16")
+    yb = V.qgemm_w4a16(ab, w1, bias, "bf16")
+    am = V.hadamard_quantize(x2, 64, "mxfp8")
+    ym = V.qgemm_mx(am, wm, bias, "bf16")
+    _, st = V.block_stats(xin, xout, dprev, dnew)
+    _noalloc_nvfp4(x2, *na)
+    return {"a4.q": a4.q, "a4.s": a4.scales, "a4.ts": a4.ts, "a4.st": a4.stats, "y4": y4,
+            "a8.q": a8.q, "a8.s": a8.scales, "a8.st": a8.stats, "y8": y8,
+            "ag.q": ag.q, "ag.s": ag.scales, "ag.ts": ag.ts, "yd": yd,
+            "ab.q": ab.q, "yb": yb, "am.q": am.q, "am.s": am.scales, "ym": ym,
+            "dnew": dnew, "bs.st": st,
+            "na.q": na[0], "na.s": na[1], "na.ts": na[2], "na.st": na[3]}
+
+
+def _bits(t):
+    t = t.detach()
+    if t.dtype in (torch.float32, torch.int32):
+        return t.view(torch.int32)
+    if t.dtype == torch.float64:
+        return t.view(torch.int64)
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16)
+    return t
+
+
+def test_step_graph_replays():
+    need_gpu()
+    dev = torch.device("cuda:0")
+    rng = np.random.Generator(np.random.PCG64(77))
+    w = {name: V.hadamard_quantize(_upload(_laplace_bits(rng, (n, k), 0.02)), 64, "nvfp4")
+         for name, n, k in (("w1", N, K), ("w2", N, K), ("wd", N, KD))}
+    wm = V.hadamard_quantize(_upload(_laplace_bits(rng, (N, K), 0.02)), 64, "mxfp4")
+    bias = torch.from_numpy(rng.standard_normal(N).astype(np.float32)).to(dev)
+    x1 = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    x2 = torch.empty_like(x1)
+    xd = torch.empty((M, KD), dtype=torch.bfloat16, device=dev)
+    xin = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    xout = torch.empty_like(xin)
+    dprev = torch.empty_like(xin)
+    dnew = torch.empty_like(xin)
+    na = (torch.empty((M, K // 2), dtype=torch.uint8, device=dev),
+          torch.empty((M, K // 16), dtype=torch.uint8, device=dev),
+          torch.empty(2, dtype=torch.float32, device=dev),
+          torch.empty(4, dtype=torch.float64, device=dev))
+
+    def load(seed):
+        r = np.random.Generator(np.random.PCG64(1000 + seed))
+        _fill(x1, _laplace_bits(r, (M, K)))
+        _fill(x2, _laplace_bits(r, (M, K), 3.0))
+        _fill(xd, _laplace_bits(r, (M, KD), 2.0))
+        _fill(xin, _laplace_bits(r, (M, K)))
+        _fill(xout, _laplace_bits(r, (M, K)))
+        _fill(dprev, _laplace_bits(r, (M, K), 0.1))
+
+    args = (x1, x2, xd, xin, xout, dprev, dnew, w["w1"], w["w2"], w["wd"], wm, bias, na)
+    # eager warm-up: the binding's per-device workspaces exist before capture
+    load(0)
+    _step(*args)
+    torch.cuda.synchronize()
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        out = _step(*args)
+    torch.cuda.synchronize()
+
+    for rnd in range(1, 4):
+        log(f"graph replay {rnd}")
+        load(rnd)
+        g.replay()
+        torch.cuda.synchronize()
+        got = {k: v.clone() for k, v in out.items()}
+        # the eager reference on the same inputs, between this replay and the next
+        want = _step(x1, x2, xd, xin, xout, dprev, torch.empty_like(dnew), w["w1"], w["w2"], w["wd"], wm,
+                     bias, tuple(torch.empty_like(t) for t in na))
+        torch.cuda.synchronize()
+        for k in want:
+            assert torch.equal(_bits(got[k]), _bits(want[k])), f"replay {rnd}: {k} differs from the eager call"
+        # the replays see the new inputs: the GEMM outputs changed from round to round
+        if rnd > 1:
+            assert not torch.equal(_bits(got["y4"]), prev_y4)
+        prev_y4 = _bits(got["y4"]).clone()
+    del g
