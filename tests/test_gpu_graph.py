@@ -6,7 +6,8 @@ counter).  So a whole step captures once and replays.  Each replay, with
 new input values and eager calls of the same entry points between replays,
 must give the eager results bit for bit: codes, scales, tensor scales,
 statistics, GEMM outputs (including a split last wave and its reduce pass)
-and the delta cache."""
+and the delta cache.  Calls on two concurrent streams use workspaces of
+their own and give the results of the same calls made in sequence."""
 import ctypes
 
 import numpy as np
@@ -133,3 +134,40 @@ def test_step_graph_replays():
             assert not torch.equal(_bits(got["y4"]), prev_y4)
         prev_y4 = _bits(got["y4"]).clone()
     del g
+
+
+def test_concurrent_streams():
+    """Calls on two streams at once: the binding gives each stream its own
+    workspaces (amax partials, statistics partials, K-slice partial tiles,
+    the statistics completion counter), so the results equal those of the
+    same calls made one after another."""
+    need_gpu()
+    dev = torch.device("cuda:0")
+    rng = np.random.Generator(np.random.PCG64(78))
+    w = V.hadamard_quantize(_upload(_laplace_bits(rng, (N, K), 0.02)), 64, "nvfp4")
+    xs = [_upload(_laplace_bits(rng, (M, K), 1.0 + i)) for i in range(2)]
+    outs = [_upload(_laplace_bits(rng, (M, K))) for i in range(2)]
+
+    def chain(x, o):
+        a = V.hadamard_quantize(x, 64, "nvfp4", stats=True)
+        y = V.qgemm_w4a4(a, w, None, "f32")
+        _, st = V.block_stats(x, o, None, None)
+        return a, y, st
+
+    want = [chain(xs[i], outs[i]) for i in range(2)]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(device=dev) for _ in range(2)]
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream())
+    got = [None, None]
+    for rep in range(3):
+        log(f"two streams, round {rep}")
+        for i, s in enumerate(streams):
+            with torch.cuda.stream(s):
+                got[i] = chain(xs[i], outs[i])
+        torch.cuda.synchronize()
+        for i in range(2):
+            (a, y, st), (a0, y0, st0) = got[i], want[i]
+            for t, t0 in ((a.q, a0.q), (a.scales, a0.scales), (a.ts, a0.ts), (a.stats, a0.stats), (y, y0),
+                          (st, st0)):
+                assert torch.equal(_bits(t), _bits(t0)), f"stream {i}, round {rep}"

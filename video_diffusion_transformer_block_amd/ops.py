@@ -75,13 +75,19 @@ def _bias(bias, N: int, dev: torch.device):
         _buf(bias, "bias", torch.float32, (N,), dev)
 
 
+def _ws_key(device: torch.device):
+    """Workspaces are kept per (device, current stream): calls on one stream
+    run in order and may share one; calls on different streams never do."""
+    s = _stream(device)
+    return torch.device(device).index, (None if s is None else s.value)
+
+
 _ws = {}
 
 
 def workspace(device: torch.device, nbytes: int) -> torch.Tensor:
-    """A per-device scratch buffer reused by every call on that device (calls
-    on one stream run in order; do not share it across concurrent streams)."""
-    key = torch.device(device).index
+    """Scratch buffer of the calls on the current stream of `device`."""
+    key = _ws_key(device)
     buf = _ws.get(key)
     if buf is None or buf.numel() < nbytes:
         buf = torch.empty(max(nbytes, 4096), dtype=torch.uint8, device=device)
@@ -93,11 +99,11 @@ _bs_ws = {}
 
 
 def stats_workspace(device: torch.device, nbytes: int) -> torch.Tensor:
-    """Per-device workspace of block_stats / block_stats_mx8, zero-filled when
-    allocated: it holds the calls' completion counter, which must be zero
-    before the first call and which every call leaves at zero (so it is not
-    shared with the other entry points' workspace)."""
-    key = torch.device(device).index
+    """Workspace of block_stats / block_stats_mx8 on the current stream,
+    zero-filled when allocated: it holds the calls' completion counter, which
+    must be zero before the first call and which every call leaves at zero
+    (so it is not shared with the other entry points' workspace)."""
+    key = _ws_key(device)
     buf = _bs_ws.get(key)
     if buf is None or buf.numel() < nbytes:
         buf = torch.zeros(max(nbytes, 4096), dtype=torch.uint8, device=device)
@@ -109,9 +115,9 @@ _gemm_ws = {}
 
 
 def gemm_workspace(device: torch.device, M: int, N: int) -> torch.Tensor:
-    """Per-device GEMM workspace (fp32 partial tiles of K slices), reused by
-    every GEMM call on that device (calls on one stream run in order)."""
-    key = torch.device(device).index
+    """GEMM workspace (fp32 partial tiles of K slices) of the calls on the
+    current stream of `device`."""
+    key = _ws_key(device)
     nbytes = L.lib().vdtq_workspace_bytes(L.OP_QGEMM, M, N)
     buf = _gemm_ws.get(key)
     if buf is None or buf.numel() < nbytes:
