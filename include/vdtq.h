@@ -160,8 +160,8 @@ size_t vdtq_workspace_bytes(int op, int64_t M, int64_t K);
  *                VDTQ_STATS (x before, y after the transform), else ignored
  * ws_dev/ws_bytes  workspace of vdtq_workspace_bytes(VDTQ_OP_HADAMARD_QUANTIZE,
  *                M, K) bytes (needed for NVFP4 without AMAX_GIVEN, with
- *                VDTQ_STATS or with VDTQ_GELU, whose lookup table of the
- *                non-trivial bf16 inputs is written there first)
+ *                VDTQ_STATS or with VDTQ_GELU, whose lookup table over
+ *                the bf16 inputs is written there first)
  * Errors: VDTQ_EINVAL for null pointers, misalignment, bad sizes/flags or a
  * short workspace; VDTQ_EUNSUPPORTED for INT8 with K > 16384.
  */

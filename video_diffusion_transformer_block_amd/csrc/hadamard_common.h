@@ -56,22 +56,40 @@ __device__ __forceinline__ float gelu_fp32(float y) {
 }
 
 // The kernels apply GELU to bf16 inputs and keep a bf16 result, so it is a
-// function of 16 bits; they evaluate gelu_fp32 once per workgroup for the
-// inputs where it is not trivial and look the rest up.  Over all finite
-// bf16 x (checked exhaustively): RNE_bf16(gelu_fp32(x)) equals
-// RNE_bf16(x / 2) when |x| < 2^-9 (bits & 0x7fff below 0x3b00), x itself
-// when x >= 2.75 (0x4030), and -0 when x <= -10.0625 (0xc121).  The table
-// holds the positive inputs 0x3b00 .. 0x402f, then the negative ones
-// 0xbb00 .. 0xc120.  Inputs are finite.
-constexpr uint32_t kGeluLo = 0x3B00u, kGeluPosEnd = 0x4030u, kGeluNegEnd = 0x4121u;
-constexpr int kGeluPosN = (int)(kGeluPosEnd - kGeluLo);
-constexpr int kGeluTabN = kGeluPosN + (int)(kGeluNegEnd - kGeluLo);
+// function of 16 bits, and its sign is the input's (GELU(x) = x times a
+// positive factor; negative results that round to zero stay -0).  Over all
+// finite bf16 x (checked exhaustively): |RNE_bf16(gelu_fp32(x))| =
+// |RNE_bf16(x / 2)| when |x| < 2^-9 (magnitude bits below 0x3b00; for
+// magnitude bits >= 0x100 that is one less in the exponent field), |x| when
+// x >= 2.75 (0x4030), and 0 when x <= -10.0625 (0xc121).
+//
+// The lookup works on a 32-bit word of two bf16 values with packed 16-bit
+// arithmetic.  Each value's magnitude bits m select a table entry holding a
+// subtrahend s, and the result is sign | max(m - s, 0):
+//   index = min(m, 0x100) + clamp(m - (0x3b00 - 1), 0, 1570) + sign * 1827
+// selects, within the sign's 1827 entries:
+//   m itself for m < 0x100 (subnormal and the smallest normal inputs,
+//     whose halving rounds);
+//   0x100 for the rest below 0x3b00 (s = 0x80: one less in the exponent
+//     field; 0 stays 0 by the clamp at zero);
+//   0x101 + (m - 0x3b00) for 0x3b00 <= m < 0x4121 (s = m - |GELU|; 0 for
+//     the positive inputs from 0x4030 up, where GELU(x) = x);
+//   the last entry for m >= 0x4121 (0 for positive inputs, 0x7fff for
+//     negative ones, whose GELU is -0).
+constexpr int kGeluLo = 0x3B00, kGeluLim = 0x4121 - 0x3B00 + 1;   // clamp bound 1570
+constexpr int kGeluRegion = 0x101 + kGeluLim;                       // entries per sign
+constexpr int kGeluTabN = 2 * kGeluRegion;
 constexpr int kGeluTabBytes = ((2 * kGeluTabN + 15) / 16) * 16;
 
-// Table entry i (0 <= i < kGeluTabN).
+// Table entry i (0 <= i < kGeluTabN): the subtrahend of the inputs that
+// map to it, from one representative input.
 __device__ __forceinline__ uint16_t gelu_table_entry(int i) {
-  const uint32_t b = i < kGeluPosN ? kGeluLo + i : (0x8000u | (kGeluLo + (i - kGeluPosN)));
-  return (uint16_t)f32_to_bf16_bits(gelu_fp32(__uint_as_float(b << 16)));
+  const uint32_t sign = i >= kGeluRegion ? 0x8000u : 0u;
+  const int e = i - (sign ? kGeluRegion : 0);
+  if (sign && e == kGeluRegion - 1) return 0x7FFFu;                 // large negative: -0
+  const uint32_t m = e <= 0x100 ? (uint32_t)e : (uint32_t)(kGeluLo + (e - 0x101));
+  const uint32_t g = f32_to_bf16_bits(gelu_fp32(__uint_as_float((sign | m) << 16)));
+  return (uint16_t)(m - (g & 0x7FFFu));
 }
 
 // Fills the table; every thread of the workgroup takes part (a barrier
@@ -80,21 +98,23 @@ __device__ __forceinline__ void gelu_table_build(uint16_t* tab) {
   for (int i = threadIdx.x; i < kGeluTabN; i += blockDim.x) tab[i] = gelu_table_entry(i);
 }
 
-// RNE_bf16(gelu_fp32(x)) for the bf16 bits b of a finite x.  Below the
-// table, x / 2 is exact for exponent fields >= 2 (one less in the exponent
-// field); smaller inputs round (rare: a divergent branch).
-__device__ __forceinline__ uint32_t gelu_bf16_bits(uint32_t b, const uint16_t* tab) {
-  const uint32_t mag = b & 0x7FFFu;
-  const bool neg = b > 0x7FFFu;
-  const uint32_t idx = mag - kGeluLo;                       // wraps below the table
-  const bool in_tab = idx < (neg ? kGeluNegEnd - kGeluLo : kGeluPosEnd - kGeluLo);
-  const uint32_t t = tab[in_tab ? idx + (neg ? (uint32_t)kGeluPosN : 0u) : 0u];
-  uint32_t r = neg ? 0x8000u : b;                           // above the table
-  if (mag < kGeluLo) {
-    r = b - 0x80u;
-    if (mag < 0x100u) r = f32_to_bf16_bits(__uint_as_float(b << 16) * 0.5f);
-  }
-  return in_tab ? t : r;
+typedef short short2v __attribute__((ext_vector_type(2)));
+typedef unsigned short ushort2v __attribute__((ext_vector_type(2)));
+
+// RNE_bf16(gelu_fp32(x)) for both bf16 values of w (low half first), from
+// the table above (finite inputs).
+__device__ __forceinline__ uint32_t gelu_word(uint32_t w, const uint16_t* tab) {
+  const uint32_t mag = w & 0x7FFF7FFFu;
+  const ushort2v m = __builtin_bit_cast(ushort2v, mag);
+  short2v d = __builtin_bit_cast(short2v, mag) - (short2v)(short)(kGeluLo - 1);   // |d| < 2^15
+  d = __builtin_elementwise_max(__builtin_elementwise_min(d, (short2v)(short)kGeluLim), (short2v)(short)0);
+  const ushort2v sign = __builtin_bit_cast(ushort2v, w) >> (ushort2v)(unsigned short)15;
+  const ushort2v idx = __builtin_elementwise_min(m, (ushort2v)(unsigned short)0x100) +
+                       __builtin_bit_cast(ushort2v, d) + sign * (ushort2v)(unsigned short)kGeluRegion;
+  const uint32_t iw = __builtin_bit_cast(uint32_t, idx);
+  const ushort2v s = {tab[iw & 0xFFFFu], tab[iw >> 16]};
+  const uint32_t r = __builtin_bit_cast(uint32_t, __builtin_elementwise_sub_sat(m, s));
+  return r | (w & 0x80008000u);
 }
 
 // ---------------------------------------------------------------- Hadamard

@@ -36,8 +36,9 @@
 //     the conversion itself does not saturate).  No tensor scale, one pass.
 //   * GELU prologue (flag 4; the FFN-down input taken straight from FFN-up's
 //     bf16 output): each element is replaced by the bf16 GELU of
-//     hadamard_common.h (a table of the non-trivial inputs, written once
-//     per call and copied into LDS) before anything else.
+//     hadamard_common.h before anything else: a table of subtrahends
+//     (written once per call, copied into LDS) indexed two elements at a
+//     time with packed 16-bit arithmetic.
 //   * Statistics: fp32 over a thread's 64 elements, fp64 across threads and
 //     workgroups in a fixed order (bit-reproducible, no float atomics).
 #include <algorithm>
@@ -183,17 +184,15 @@ __device__ __forceinline__ void gelu_begin(const HQParams& p) {
 
 // Reads this thread's chunk from LDS and widens bf16 -> fp32 (through the
 // GELU table first with flag 4).
-__device__ __forceinline__ uint32_t gelu_word(uint32_t w) {
-  return gelu_bf16_bits(w & 0xFFFFu, gelu_lds) | (gelu_bf16_bits(w >> 16, gelu_lds) << 16);
-}
-
 __device__ __forceinline__ void load_chunk(const uint4* lds, float (&v)[64], unsigned flags) {
   const int t = threadIdx.x;
   const bool gelu = (flags & 4u) != 0;
 #pragma unroll
   for (int jj = 0; jj < 8; ++jj) {
     uint4 w = lds[t * 8 + (jj ^ (t & 7))];
-    if (gelu) w = make_uint4(gelu_word(w.x), gelu_word(w.y), gelu_word(w.z), gelu_word(w.w));
+    if (gelu)
+      w = make_uint4(gelu_word(w.x, gelu_lds), gelu_word(w.y, gelu_lds), gelu_word(w.z, gelu_lds),
+                     gelu_word(w.w, gelu_lds));
     v[8 * jj + 0] = bf16_lo(w.x); v[8 * jj + 1] = bf16_hi(w.x);
     v[8 * jj + 2] = bf16_lo(w.y); v[8 * jj + 3] = bf16_hi(w.y);
     v[8 * jj + 4] = bf16_lo(w.z); v[8 * jj + 5] = bf16_hi(w.z);

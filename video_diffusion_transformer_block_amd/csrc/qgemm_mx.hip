@@ -156,13 +156,9 @@ __device__ __forceinline__ void quant_store_tile(const GemmParams& p, const floa
       const uint32_t in[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        uint32_t lo = in[q] & 0xFFFFu, hi = in[q] >> 16;
-        if (gelu) {
-          lo = gelu_bf16_bits(lo, gtab);
-          hi = gelu_bf16_bits(hi, gtab);
-        }
-        v[8 * jj + 2 * q] = __uint_as_float(lo << 16);
-        v[8 * jj + 2 * q + 1] = __uint_as_float(hi << 16);
+        const uint32_t x = gelu ? gelu_word(in[q], gtab) : in[q];
+        v[8 * jj + 2 * q] = __uint_as_float(x << 16);
+        v[8 * jj + 2 * q + 1] = __uint_as_float(x & 0xFFFF0000u);
       }
     }
     fwht<64>(v);
