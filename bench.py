@@ -935,7 +935,9 @@ def measure_ffn_fusion(torch, V, X, WM, M, steps):
     weights, bias): the unfused chain qgemm_mx (bf16 Y) -> hadamard_quantize
     (GELU, Hadamard 64, MXFP4) against qgemm_mx_quant, which never writes Y;
     for MXFP8 activations (the W4A6 mix's FFN-up format) and MXFP4.  Each
-    part is timed alone too (HIP events around 10 launches, median)."""
+    part is timed alone too (HIP events around 10 launches, median).  Also
+    FFN-down's NVFP4 quantize of the same Y (tensor amax computed) with and
+    without GELU."""
     N = WM["ffn_up"].q.shape[0]
     gen = torch.Generator(device=X["ffn_up"].device).manual_seed(77)
     bias = torch.randn(N, generator=gen, device=X["ffn_up"].device) * 0.1
@@ -961,6 +963,11 @@ def measure_ffn_fusion(torch, V, X, WM, M, steps):
     q = V.hadamard_quantize(y, HAD_BLOCK, "mxfp4")
     res["quant_us"] = timed(lambda: V.hadamard_quantize(y, HAD_BLOCK, "mxfp4", out=q))
     res["quant_gelu_us"] = timed(lambda: V.hadamard_quantize(y, HAD_BLOCK, "mxfp4", gelu=True, out=q))
+    # the headline format's FFN-down input in a model: NVFP4 with the tensor
+    # amax computed, both passes applying GELU
+    qn = V.hadamard_quantize(y, HAD_BLOCK, "nvfp4")
+    res["nvfp4_quant_us"] = timed(lambda: V.hadamard_quantize(y, HAD_BLOCK, "nvfp4", out=qn))
+    res["nvfp4_quant_gelu_us"] = timed(lambda: V.hadamard_quantize(y, HAD_BLOCK, "nvfp4", gelu=True, out=qn))
     for afmt in ("mxfp8", "mxfp4"):
         a = V.hadamard_quantize(X["ffn_up"], HAD_BLOCK, afmt)
         qf = V.qgemm_mx_quant(a, w, bias, "mxfp4", gelu=True)
