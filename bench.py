@@ -991,20 +991,27 @@ def cpu_baseline(host, M, rows):
     cores = len(os.sched_getaffinity(0))
     prepped = {n: Q.prepare_weight(w, HAD_BLOCK) for n, (x, w) in host.items()}
     t0 = time.perf_counter()
-    flops = 0.0
+    flops = elems = 0.0
+    tq = tg = 0.0
     for name, (x, w) in host.items():
         xs = x[:rows]
         wq, ws, wgs = prepped[name]
         fmt = MIXED[name]
+        t1 = time.perf_counter()
         a = Q.hadamard_quantize(xs, HAD_BLOCK, fmt)
+        t2 = time.perf_counter()
         if fmt == "nvfp4":
             G.qgemm_w4a4(a["q"], a["scales"], a["gs"], wq, ws, wgs, None, "bf16")
         else:
             G.qgemm_w4a8(a["q"], a["scales"], wq, ws, wgs, None, "bf16")
+        tq += t2 - t1
+        tg += time.perf_counter() - t2
         flops += 2.0 * rows * w.shape[0] * w.shape[1]
+        elems += xs.size
     dt = time.perf_counter() - t0
     return {"value": round(flops / dt / 1e12, 6), "unit": "TOPS", "cores": cores, "kind": "oracle",
             "seconds": round(dt, 2),
+            "quantize_elements_per_s": round(elems / tq, 1), "gemm_fp64_flop_per_s": round(flops / tg, 1),
             "sample": f"first {rows} of {M} tokens of each of the 4 linears (mixed W4A6 assignment), "
                       "quantize + GEMM; numpy float64 GEMM, weights decoded per call"}
 
