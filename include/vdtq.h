@@ -149,6 +149,12 @@ size_t vdtq_workspace_bytes(int op, int64_t M, int64_t K);
  *                feed-forward's activation: quantizing FFN-up's bf16 output
  *                for FFN-down ([gist] §4: quantization fused with the
  *                kernels around it).  The statistics then describe GELU(x).
+ *                The bf16 results come from a 7.3 KB lookup table in the
+ *                library's device memory, one per GPU: the first call with
+ *                VDTQ_GELU on a GPU builds it on `stream` and waits for it
+ *                (once per GPU and process); later calls only read it.  A
+ *                call on a capturing stream records the build into the
+ *                graph instead of waiting.
  * q_dev          NVFP4, MXFP4: uint8 [M][K/2]; INT8: int8 [M][K]; BF16:
  *                bf16 [M][K]; MXFP8: uint8 E4M3 [M][K]
  * scales_dev     NVFP4: uint8 E4M3 [M][K/16]; INT8: float [M]; MXFP4,
@@ -159,9 +165,8 @@ size_t vdtq_workspace_bytes(int op, int64_t M, int64_t K);
  * stats_dev      double[4] {max|x|, sum|x|, max|y|, sum|y|} when
  *                VDTQ_STATS (x before, y after the transform), else ignored
  * ws_dev/ws_bytes  workspace of vdtq_workspace_bytes(VDTQ_OP_HADAMARD_QUANTIZE,
- *                M, K) bytes (needed for NVFP4 without AMAX_GIVEN, with
- *                VDTQ_STATS or with VDTQ_GELU, whose lookup table over
- *                the bf16 inputs is written there first)
+ *                M, K) bytes (needed for NVFP4 without AMAX_GIVEN and with
+ *                VDTQ_STATS; otherwise ignored, may be NULL)
  * Errors: VDTQ_EINVAL for null pointers, misalignment, bad sizes/flags or a
  * short workspace; VDTQ_EUNSUPPORTED for INT8 with K > 16384.
  */
@@ -177,7 +182,7 @@ int hadamard_quantize(const void* x_dev, int64_t M, int64_t K, int64_t ldx,
  * graph capture, tight serving loops, harnesses that forbid hipMalloc).
  *
  * Same operation, arguments, outputs and errors as hadamard_quantize, minus
- * ws_dev/ws_bytes.  The per-workgroup partials and the GELU table live in a
+ * ws_dev/ws_bytes.  The per-workgroup partials live in a
  * library-owned device array of VDTQ_NOALLOC_SCRATCH_BYTES, one per GPU,
  * held from the first call on that GPU until the process ends; the call
  * allocates nothing (no hipMalloc, hipFree or allocating library routine).
@@ -342,7 +347,9 @@ int qgemm_mx(int a_fmt, const uint8_t* a_q_dev, const uint8_t* a_s_dev,
  *                (16-byte aligned)
  * s_out_dev      uint8 E8M0 [M][N/32] (4-byte aligned)
  * M, N, K        as for qgemm_mx; N a multiple of 64
- * No workspace: tiles are never split along K on this path.
+ * No workspace: tiles are never split along K on this path.  VDTQ_GELU
+ * uses the GPU's GELU table as hadamard_quantize does (built and waited for
+ * by the first call that needs it on the GPU).
  * Errors: VDTQ_EINVAL for bad formats or flags, N not a multiple of 64, K
  * not a multiple of 32, null or misaligned pointers; VDTQ_EUNSUPPORTED for
  * had_block other than 64, K not a multiple of 128 or an operand matrix of

@@ -58,8 +58,8 @@ def _hq(**kw):
     (dict(K=15), L.EINVAL), (dict(K=0), L.EINVAL), (dict(M=-1), L.EINVAL),
     (dict(b=48), L.EINVAL), (dict(b=512), L.EINVAL), (dict(K=96, ldx=96, b=64), L.EINVAL),
     (dict(ldx=60), L.EINVAL), (dict(ldx=68), L.EINVAL), (dict(fmt=5), L.EINVAL), (dict(fmt=-1), L.EINVAL),
-    (dict(flags=8), L.EINVAL), (dict(fmt=1, flags=1), L.EINVAL), (dict(fmt=1, flags=4, ws=None), L.EINVAL),
-    (dict(fmt=3, flags=4, wsb=256), L.EINVAL),
+    (dict(flags=8), L.EINVAL), (dict(fmt=1, flags=1), L.EINVAL), (dict(fmt=1, flags=2, ws=None), L.EINVAL),
+    (dict(fmt=3, flags=2, wsb=64), L.EINVAL),
     (dict(fmt=1, K=16384 + 64, ldx=16448), L.EUNSUPPORTED),
     (dict(x=None), L.EINVAL), (dict(q=None), L.EINVAL), (dict(x=FAKE8), L.EINVAL),
     (dict(ts=None), L.EINVAL), (dict(flags=2, st=None), L.EINVAL),

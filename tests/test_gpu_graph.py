@@ -1,6 +1,7 @@
 """The hot path captured in a HIP graph (torch.cuda.CUDAGraph).  A library
 call only enqueues kernels on the caller's stream: no allocation, memset or
-synchronisation inside it, and every workspace it reads is either written
+synchronisation inside it (the GPU's GELU table is built and waited for
+once, by the first call that needs it), and every workspace it reads is either written
 first in the same call or left as it found it (block_stats' completion
 counter).  So a whole step captures once and replays.  Each replay, with
 new input values and eager calls of the same entry points between replays,
@@ -171,3 +172,42 @@ def test_concurrent_streams():
             for t, t0 in ((a.q, a0.q), (a.scales, a0.scales), (a.ts, a0.ts), (a.stats, a0.stats), (y, y0),
                           (st, st0)):
                 assert torch.equal(_bits(t), _bits(t0)), f"stream {i}, round {rep}"
+
+
+_FIRST_GELU_UNDER_CAPTURE = r"""
+import sys
+import numpy as np
+import torch
+sys.path.insert(0, sys.argv[1])
+import video_diffusion_transformer_block_amd as V
+rng = np.random.Generator(np.random.PCG64(81))
+x = torch.from_numpy(rng.laplace(size=(96, 1024)).astype(np.float32) * 3).to(torch.bfloat16).cuda()
+q = V.hadamard_quantize(x, 64, "mxfp4")          # workspaces exist before capture; no GELU yet
+torch.cuda.synchronize()
+g = torch.cuda.CUDAGraph()
+with torch.cuda.graph(g):
+    out = V.hadamard_quantize(x, 64, "mxfp4", gelu=True)   # the process's first GELU call
+torch.cuda.synchronize()
+for _ in range(2):
+    g.replay()
+    torch.cuda.synchronize()
+    want = V.hadamard_quantize(x, 64, "mxfp4", gelu=True)  # eager: builds the table and waits
+    torch.cuda.synchronize()
+    assert torch.equal(out.q, want.q) and torch.equal(out.scales, want.scales)
+print("ok")
+"""
+
+
+def test_gelu_table_first_built_under_capture():
+    """The GPU's GELU table is built once per process by the first call that
+    needs it; when that call is being captured, the build goes into the
+    graph and the next eager call builds it again.  Run in a fresh process
+    so that the capture really is the first GELU call."""
+    need_gpu()
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", _FIRST_GELU_UNDER_CAPTURE, root], capture_output=True, text=True,
+                       timeout=240)
+    assert r.returncode == 0 and r.stdout.strip().endswith("ok"), r.stdout[-2000:] + r.stderr[-2000:]

@@ -95,7 +95,7 @@ int hadamard_quantize(const void* x_dev, int64_t M, int64_t K, int64_t ldx, int 
                       double* stats_dev, void* ws_dev, size_t ws_bytes, void* stream) {
   const int rc = hq_check(x_dev, M, K, ldx, had_block, fmt, flags, q_dev, scales_dev, tensor_scale_dev, stats_dev);
   if (rc != VDTQ_OK) return rc;
-  const bool need_ws = (flags & (VDTQ_STATS | VDTQ_GELU)) || (fmt == VDTQ_FMT_NVFP4 && !(flags & VDTQ_AMAX_GIVEN));
+  const bool need_ws = (flags & VDTQ_STATS) || (fmt == VDTQ_FMT_NVFP4 && !(flags & VDTQ_AMAX_GIVEN));
   if (need_ws) {
     const size_t need = vdtq::hq_workspace_bytes(M, K);
     if (!ws_dev || !aligned(ws_dev, 16) || ws_bytes < need)

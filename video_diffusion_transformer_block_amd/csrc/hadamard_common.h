@@ -92,12 +92,6 @@ __device__ __forceinline__ uint16_t gelu_table_entry(int i) {
   return (uint16_t)(m - (g & 0x7FFFu));
 }
 
-// Fills the table; every thread of the workgroup takes part (a barrier
-// must follow before the first lookup).
-__device__ __forceinline__ void gelu_table_build(uint16_t* tab) {
-  for (int i = threadIdx.x; i < kGeluTabN; i += blockDim.x) tab[i] = gelu_table_entry(i);
-}
-
 typedef short short2v __attribute__((ext_vector_type(2)));
 typedef unsigned short ushort2v __attribute__((ext_vector_type(2)));
 

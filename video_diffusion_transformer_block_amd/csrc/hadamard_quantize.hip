@@ -68,7 +68,7 @@ struct HQParams {
   double* stats_part;         // [grid][4] partial statistics
   unsigned flags;
   int32_t flat;               // ldx == K and K % 64 == 0: chunk g starts at element 64 g
-  const uint16_t* gtab;       // GELU table in the workspace (flag 4)
+  const uint16_t* gtab;       // the device's GELU table (flag 4)
 };
 
 __device__ __forceinline__ void divmod_cpr(int64_t g, const HQParams& p, int& row, int& col) {
@@ -164,11 +164,10 @@ __device__ __forceinline__ void stage(const HQParams& p, uint4* lds, int& my_row
   }
 }
 
-// With the GELU flag (4) a one-block-per-256-entries kernel first writes the
-// GELU table to the workspace; each quantize workgroup copies it into
-// dynamic LDS (gelu_lds) while its chunk loads are in flight (the stage()
-// hook); load_chunk maps each staged element through it as it widens the
-// chunk.
+// With the GELU flag (4) each quantize workgroup copies the GELU table from
+// the device's table (gelu_table below) into dynamic LDS (gelu_lds) while
+// its chunk loads are in flight (the stage() hook); load_chunk maps each
+// staged element through it as it widens the chunk.
 extern __shared__ __attribute__((aligned(16))) uint16_t gelu_lds[];
 
 __global__ __launch_bounds__(256) void gelu_table_kernel(uint16_t* tab) {
@@ -728,8 +727,8 @@ static hipError_t launch_b(const HQParams& p, int fmt, bool amax_given, int grid
   return hipGetLastError();
 }
 
-// Workspace: per-workgroup amax partials (float), statistics partials
-// (double[4]), then the GELU table.
+// Workspace: per-workgroup amax partials (float), then statistics partials
+// (double[4]).
 static size_t hq_partials_bytes(int64_t M, int64_t K) {
   if (M <= 0 || K <= 0) return 256;
   const int64_t cpr = (K + 63) / 64;
@@ -738,12 +737,51 @@ static size_t hq_partials_bytes(int64_t M, int64_t K) {
   return (size_t)(((grid * 4 + 63) / 64) * 64 + grid * 4 * 8);
 }
 
-size_t hq_workspace_bytes(int64_t M, int64_t K) { return hq_partials_bytes(M, K) + kGeluTabBytes; }
+size_t hq_workspace_bytes(int64_t M, int64_t K) { return hq_partials_bytes(M, K); }
+
+// ------------------------------------------------------------ GELU table
+// One table per GPU, in the code object: it depends on nothing but the GELU
+// definition, so it is built once per device and process, on the stream of
+// the first call that needs it, which waits for the build (afterwards every
+// kernel on any stream only reads it).  A call on a capturing stream may not
+// wait: it records the build into the graph (every replay rebuilds the same
+// values before using them) and leaves the table marked unbuilt.
+static __device__ __align__(16) uint16_t gelu_tab_dev[kGeluTabBytes / 2];
+
+hipError_t gelu_table(hipStream_t st, const uint16_t** tab) {
+  static std::mutex mu;
+  static void* addr[64] = {nullptr};
+  static bool built[64] = {false};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  e = hipStreamIsCapturing(st, &cs);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(gelu_tab_dev));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *tab = static_cast<const uint16_t*>(addr[dev]);
+  if (built[dev]) return hipSuccess;
+  hipLaunchKernelGGL(gelu_table_kernel, dim3((kGeluTabN + 255) / 256), dim3(256), 0, st,
+                     static_cast<uint16_t*>(addr[dev]));
+  e = hipGetLastError();
+  if (e != hipSuccess || cs != hipStreamCaptureStatusNone) return e;
+  e = hipStreamSynchronize(st);
+  if (e == hipSuccess) built[dev] = true;
+  return e;
+}
 
 // ------------------------------------------------ allocation-free scratch
 // The workspace of hadamard_quantize_noalloc: a device array per GPU, in the
-// code object (no allocation call), holding the partials and the GELU table
-// exactly as a caller-given workspace would.  Host code never passes the
+// code object (no allocation call), holding the partials exactly as a
+// caller-given workspace would.  Host code never passes the
 // array's name to a kernel (on the host it is only a stand-in symbol): it
 // uses the device address hipGetSymbolAddress returns for the current
 // device, looked up on the first call on each device and kept.
@@ -797,8 +835,6 @@ hipError_t launch_hadamard_quantize(const void* x, int64_t M, int64_t K, int64_t
   const int64_t grid_cap = std::max<int64_t>((M * p.cpr + HQ_THREADS - 1) / HQ_THREADS, M);
   p.amax_part = reinterpret_cast<float*>(wsb);
   p.stats_part = reinterpret_cast<double*>(wsb + ((grid_cap * 4 + 63) / 64) * 64);
-  uint16_t* gtab = reinterpret_cast<uint16_t*>(wsb + hq_partials_bytes(M, K));
-  p.gtab = gtab;
 
   if (M == 0) {
     if (fmt == 0) {
@@ -811,8 +847,7 @@ hipError_t launch_hadamard_quantize(const void* x, int64_t M, int64_t K, int64_t
     return hipGetLastError();
   }
   if (flags & 4u) {
-    hipLaunchKernelGGL(gelu_table_kernel, dim3((kGeluTabN + 255) / 256), dim3(256), 0, st, gtab);
-    const hipError_t et = hipGetLastError();
+    const hipError_t et = gelu_table(st, &p.gtab);
     if (et != hipSuccess) return et;
   }
   switch (b) {

@@ -32,6 +32,12 @@ hipError_t launch_hadamard_quantize(const void* x, int64_t M, int64_t K, int64_t
 // (VDTQ_NOALLOC_SCRATCH_BYTES, 256-byte aligned), looked up once per device.
 hipError_t hq_noalloc_scratch(void** ptr);
 
+// Device address of this GPU's GELU lookup table (hadamard_common.h), built
+// on `st` by the first call on the device, which then waits for it; a call
+// on a capturing stream records the build instead and leaves it to be done
+// again by the next call outside capture.
+hipError_t gelu_table(hipStream_t st, const uint16_t** tab);
+
 size_t qgemm_workspace_bytes(int64_t M, int64_t N);
 hipError_t launch_qgemm(int afmt, const void* a_q, const void* a_s, const float* a_ts,
                         const uint8_t* w_q, const uint8_t* w_s, const float* w_ts,

@@ -39,6 +39,7 @@ struct GemmParams {
   uint8_t* q_out;          // [M][N / 2] E2M1 or [M][N] E4M3 codes
   uint8_t* s_out;          // [M][N / 32] E8M0 scales
   uint32_t qflags;         // 4: GELU before the transform
+  const uint16_t* gtab;    // the device's GELU table (qflags 4)
 };
 
 // Partial tile of slice `sl` of split tile `tile`.  Layout inside a slot:

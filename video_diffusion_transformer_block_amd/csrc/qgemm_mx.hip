@@ -43,8 +43,9 @@
 //     INT8 kernel (qgemm_common.h).
 //   * quantizing epilogue (qgemm_mx_quant; FFN-up feeding FFN-down): the
 //     finished bf16 tile goes through LDS as in the bf16 epilogue, then each
-//     lane takes whole 64-element row chunks of it: GELU from a table that
-//     the workgroup fills while its first loads are in flight, the 64-point
+//     lane takes whole 64-element row chunks of it: GELU from the device's
+//     table, which the workgroup copies into LDS while its first loads are
+//     in flight, the 64-point
 //     Hadamard butterflies, the MX encoding; only codes and scales reach
 //     HBM.  Tiles are never split along K on this path (the epilogue needs
 //     the whole sum).
@@ -354,8 +355,11 @@ void qgemm_mx_kernel(GemmParams p) {
   const int pre = min(P::NS, ke - kb);
   for (int s = 0; s < pre; ++s) issue_stage(kb + s);
   if constexpr (QOUT != 0) {
-    // filled under the first loads; the loop's barriers order it before use
-    if (p.qflags & 4u) gelu_table_build(reinterpret_cast<uint16_t*>(smem + P::GTAB));
+    // copied under the first loads; the loop's barriers order it before use
+    if (p.qflags & 4u) {
+      for (int i = threadIdx.x; i < kGeluTabBytes / 16; i += GT)
+        reinterpret_cast<uint4*>(smem + P::GTAB)[i] = reinterpret_cast<const uint4*>(p.gtab)[i];
+    }
   }
   wait_stages<P::LPS>(pre - 1);
   wait_lgkm_barrier();
@@ -499,6 +503,10 @@ hipError_t launch_qgemm_mx_quant(bool a_fp8, const uint8_t* a_q, const uint8_t* 
   p.bias = bias; p.y = nullptr; p.ldy = 0;
   p.M = (int32_t)M; p.N = (int32_t)N; p.K = (int32_t)K;
   p.q_out = q_out; p.s_out = s_out; p.qflags = gelu ? 4u : 0u;
+  if (gelu) {
+    const hipError_t e = gelu_table(st, &p.gtab);
+    if (e != hipSuccess) return e;
+  }
   if (mx_quads(K)) {
     if (a_fp8) return out_fp8 ? launch_mx_quant<true, true, 2>(p, st) : launch_mx_quant<true, true, 1>(p, st);
     return out_fp8 ? launch_mx_quant<false, true, 2>(p, st) : launch_mx_quant<false, true, 1>(p, st);
