@@ -128,7 +128,9 @@ __device__ __forceinline__ bool staged_store_ok(const GemmParams& p) {
 // biased and rounded to bf16, to LDS (rows of 256 bytes, 16-byte chunk c of
 // row r at chunk position c ^ (r & 15): conflict-free writes), reads it back
 // as 16-byte row chunks and stores 4 whole 256-byte row segments per
-// instruction.  ROUNDS: the sub-tile goes through LDS in that many parts
+// instruction, marked non-temporal: the output is written once and is far
+// larger than the L2, so it should not evict the operand stripes the other
+// tiles of the XCD are still reading.  ROUNDS: the sub-tile goes through LDS in that many parts
 // (32 KB / ROUNDS per wave); the caller has finished every LDS read of the
 // ring, and smem holds at least 4 x 32 KB / ROUNDS bytes.
 template <int AFMT, int ROUNDS>
@@ -174,7 +176,8 @@ __device__ __forceinline__ void stage_store_tile(const GemmParams& p, const floa
       const int row = m0 + wm * 128 + 32 * rd * IPR + lrow;
       const int col = n0 + wn * 128 + 8 * c;
       if (row < p.M && col < p.N)
-        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.y) + (int64_t)row * p.ldy + col) = v;
+        __builtin_nontemporal_store(uint4v{v.x, v.y, v.z, v.w},
+                                    reinterpret_cast<uint4v*>(static_cast<uint16_t*>(p.y) + (int64_t)row * p.ldy + col));
     }
   }
 }
