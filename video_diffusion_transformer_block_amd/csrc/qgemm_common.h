@@ -3,6 +3,7 @@
 // parameters, the split of a partial last wave of tiles into K slices, the
 // deterministic reduce pass of those slices, and the output stores.
 #pragma once
+#include <type_traits>
 
 #include <algorithm>
 
@@ -149,37 +150,46 @@ __device__ __forceinline__ void stage_store_tile(const GemmParams& p, const floa
       bias[j][g] = p.bias ? *reinterpret_cast<const float4*>(p.bias + min(n0 + wn * 128 + 32 * j + 8 * g + 4 * h, p.N - 4))
                           : make_float4(0.f, 0.f, 0.f, 0.f);
   __syncthreads();   // every wave is past its last read of the ring
+  // without a bias the scaled sums are rounded as they are (as emit4 does)
+  auto body = [&](auto has_bias) {
+    constexpr bool HB = decltype(has_bias)::value;
 #pragma unroll
-  for (int rd = 0; rd < ROUNDS; ++rd) {
+    for (int rd = 0; rd < ROUNDS; ++rd) {
 #pragma unroll
-    for (int ii = 0; ii < IPR; ++ii) {
-      const int i = rd * IPR + ii;
-      const int lrow = 32 * ii + r32;                   // row within this round's part
-      const float alpha = row_alpha<AFMT>(p, min(m0 + wm * 128 + 32 * i + r32, p.M - 1));
+      for (int ii = 0; ii < IPR; ++ii) {
+        const int i = rd * IPR + ii;
+        const int lrow = 32 * ii + r32;                   // row within this round's part
+        const float alpha = row_alpha<AFMT>(p, min(m0 + wm * 128 + 32 * i + r32, p.M - 1));
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const float4 b = bias[j][g];
-          const float v0 = acc[i][j][4 * g] * alpha + b.x, v1 = acc[i][j][4 * g + 1] * alpha + b.y;
-          const float v2 = acc[i][j][4 * g + 2] * alpha + b.z, v3 = acc[i][j][4 * g + 3] * alpha + b.w;
-          const int c = (4 * j + g) ^ (lrow & 15);
-          *reinterpret_cast<uint2*>(reg + lrow * 256 + 16 * c + 8 * h) = make_uint2(bf16_pair(v0, v1), bf16_pair(v2, v3));
-        }
+          for (int g = 0; g < 4; ++g) {
+            float v0 = acc[i][j][4 * g] * alpha, v1 = acc[i][j][4 * g + 1] * alpha;
+            float v2 = acc[i][j][4 * g + 2] * alpha, v3 = acc[i][j][4 * g + 3] * alpha;
+            if constexpr (HB) {
+              const float4 b = bias[j][g];
+              v0 = v0 + b.x; v1 = v1 + b.y; v2 = v2 + b.z; v3 = v3 + b.w;
+            }
+            const int c = (4 * j + g) ^ (lrow & 15);
+            *reinterpret_cast<uint2*>(reg + lrow * 256 + 16 * c + 8 * h) = make_uint2(bf16_pair(v0, v1), bf16_pair(v2, v3));
+          }
+      }
+      // the same wave reads back what it wrote (LDS operations of a wave run in order)
+      const int c = lane & 15;
+#pragma unroll
+      for (int it = 0; it < 8 * IPR; ++it) {
+        const int lrow = 4 * it + (lane >> 4);
+        const uint4 v = *reinterpret_cast<const uint4*>(reg + lrow * 256 + 16 * (c ^ (lrow & 15)));
+        const int row = m0 + wm * 128 + 32 * rd * IPR + lrow;
+        const int col = n0 + wn * 128 + 8 * c;
+        if (row < p.M && col < p.N)
+          __builtin_nontemporal_store(uint4v{v.x, v.y, v.z, v.w},
+                                      reinterpret_cast<uint4v*>(static_cast<uint16_t*>(p.y) + (int64_t)row * p.ldy + col));
+      }
     }
-    // the same wave reads back what it wrote (LDS operations of a wave run in order)
-    const int c = lane & 15;
-#pragma unroll
-    for (int it = 0; it < 8 * IPR; ++it) {
-      const int lrow = 4 * it + (lane >> 4);
-      const uint4 v = *reinterpret_cast<const uint4*>(reg + lrow * 256 + 16 * (c ^ (lrow & 15)));
-      const int row = m0 + wm * 128 + 32 * rd * IPR + lrow;
-      const int col = n0 + wn * 128 + 8 * c;
-      if (row < p.M && col < p.N)
-        __builtin_nontemporal_store(uint4v{v.x, v.y, v.z, v.w},
-                                    reinterpret_cast<uint4v*>(static_cast<uint16_t*>(p.y) + (int64_t)row * p.ldy + col));
-    }
-  }
+  };
+  if (p.bias) body(std::true_type{});
+  else body(std::false_type{});
 }
 
 // Split tiles: out = alpha * (sum of the slices in slice order) + bias.

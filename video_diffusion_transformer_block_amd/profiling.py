@@ -32,8 +32,12 @@ import os
 import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-KERNEL_SOURCES = ["csrc/qgemm.hip", "csrc/qgemm_w4a16.hip", "csrc/hadamard_quantize.hip",
-                  "csrc/block_stats.hip", "csrc/device_common.h", "csrc/lds_dma.h"]
+# every device source a profiled kernel is built from (the kernels and the
+# headers they include): counters taken before a change to any of them no
+# longer describe the kernels
+KERNEL_SOURCES = ["csrc/qgemm.hip", "csrc/qgemm_mx.hip", "csrc/qgemm_w4a16.hip", "csrc/hadamard_quantize.hip",
+                  "csrc/block_stats.hip", "csrc/bench_stream.hip", "csrc/qgemm_common.h", "csrc/hadamard_common.h",
+                  "csrc/device_common.h", "csrc/lds_dma.h", "csrc/launch.h"]
 
 
 def source_hash() -> str:
