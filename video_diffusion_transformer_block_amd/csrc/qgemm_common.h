@@ -174,17 +174,30 @@ __device__ __forceinline__ void stage_store_tile(const GemmParams& p, const floa
             *reinterpret_cast<uint2*>(reg + lrow * 256 + 16 * c + 8 * h) = make_uint2(bf16_pair(v0, v1), bf16_pair(v2, v3));
           }
       }
-      // the same wave reads back what it wrote (LDS operations of a wave run in order)
+      // the same wave reads back what it wrote (LDS operations of a wave run
+      // in order).  Eight reads go out before their eight stores: each store
+      // sits behind its bounds branch, and a read issued after the previous
+      // store would wait out the LDS latency once per 16-byte chunk
       const int c = lane & 15;
+      const int col = n0 + wn * 128 + 8 * c;
+      const int row0 = m0 + wm * 128 + 32 * rd * IPR + (lane >> 4);
+      uint16_t* const y0 = static_cast<uint16_t*>(p.y) + (int64_t)row0 * p.ldy + col;
+      const int64_t rstep = 4 * p.ldy;                   // 4 rows per read
 #pragma unroll
-      for (int it = 0; it < 8 * IPR; ++it) {
-        const int lrow = 4 * it + (lane >> 4);
-        const uint4 v = *reinterpret_cast<const uint4*>(reg + lrow * 256 + 16 * (c ^ (lrow & 15)));
-        const int row = m0 + wm * 128 + 32 * rd * IPR + lrow;
-        const int col = n0 + wn * 128 + 8 * c;
-        if (row < p.M && col < p.N)
-          __builtin_nontemporal_store(uint4v{v.x, v.y, v.z, v.w},
-                                      reinterpret_cast<uint4v*>(static_cast<uint16_t*>(p.y) + (int64_t)row * p.ldy + col));
+      for (int b8 = 0; b8 < IPR; ++b8) {
+        uint4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int lrow = 4 * (8 * b8 + u) + (lane >> 4);
+          v[u] = *reinterpret_cast<const uint4*>(reg + lrow * 256 + 16 * (c ^ (lrow & 15)));
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int it = 8 * b8 + u;
+          if (row0 + 4 * it < p.M && col < p.N)
+            __builtin_nontemporal_store(uint4v{v[u].x, v[u].y, v[u].z, v[u].w},
+                                        reinterpret_cast<uint4v*>(y0 + it * rstep));
+        }
       }
     }
   };
