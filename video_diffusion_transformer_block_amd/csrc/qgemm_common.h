@@ -5,6 +5,7 @@
 #pragma once
 
 #include <algorithm>
+#include <type_traits>
 
 #include "device_common.h"
 #include "launch.h"
@@ -140,58 +141,75 @@ __device__ __forceinline__ void stage_store_tile(const GemmParams& p, const floa
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   const int wm = wv >> 1, wn = wv & 1, r32 = lane & 31, h = lane >> 5;
   uint8_t* reg = smem + wv * (32768 / ROUNDS);
-  // bias of this lane's 64 columns: 32 j + 8 g + 4 h .. +3 (of the wave's 128)
-  float4 bias[4][4];
+  // HB: add the bias (zeros where there is none).  The MX kernels take a
+  // second copy without it for calls with no bias: its 64 registers made
+  // their epilogue spill.  (For the NVFP4 / INT8 kernels a second copy
+  // made them spill instead, so they always add.)
+  auto body = [&](auto has_bias) {
+    constexpr bool HB = decltype(has_bias)::value;
+    // bias of this lane's 64 columns: 32 j + 8 g + 4 h .. +3 (of the wave's 128)
+    float4 bias[4][4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int g = 0; g < 4; ++g)
-      bias[j][g] = p.bias ? *reinterpret_cast<const float4*>(p.bias + min(n0 + wn * 128 + 32 * j + 8 * g + 4 * h, p.N - 4))
-                          : make_float4(0.f, 0.f, 0.f, 0.f);
-  __syncthreads();   // every wave is past its last read of the ring
+      for (int g = 0; g < 4; ++g)
+        bias[j][g] = HB && p.bias
+                         ? *reinterpret_cast<const float4*>(p.bias + min(n0 + wn * 128 + 32 * j + 8 * g + 4 * h, p.N - 4))
+                         : make_float4(0.f, 0.f, 0.f, 0.f);
+    __syncthreads();   // every wave is past its last read of the ring
 #pragma unroll
-  for (int rd = 0; rd < ROUNDS; ++rd) {
+    for (int rd = 0; rd < ROUNDS; ++rd) {
 #pragma unroll
-    for (int ii = 0; ii < IPR; ++ii) {
-      const int i = rd * IPR + ii;
-      const int lrow = 32 * ii + r32;                   // row within this round's part
-      const float alpha = row_alpha<AFMT>(p, min(m0 + wm * 128 + 32 * i + r32, p.M - 1));
+      for (int ii = 0; ii < IPR; ++ii) {
+        const int i = rd * IPR + ii;
+        const int lrow = 32 * ii + r32;                   // row within this round's part
+        const float alpha = row_alpha<AFMT>(p, min(m0 + wm * 128 + 32 * i + r32, p.M - 1));
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const float4 b = bias[j][g];
-          const float v0 = acc[i][j][4 * g] * alpha + b.x, v1 = acc[i][j][4 * g + 1] * alpha + b.y;
-          const float v2 = acc[i][j][4 * g + 2] * alpha + b.z, v3 = acc[i][j][4 * g + 3] * alpha + b.w;
-          const int c = (4 * j + g) ^ (lrow & 15);
-          *reinterpret_cast<uint2*>(reg + lrow * 256 + 16 * c + 8 * h) = make_uint2(bf16_pair(v0, v1), bf16_pair(v2, v3));
+          for (int g = 0; g < 4; ++g) {
+            float v0 = acc[i][j][4 * g] * alpha, v1 = acc[i][j][4 * g + 1] * alpha;
+            float v2 = acc[i][j][4 * g + 2] * alpha, v3 = acc[i][j][4 * g + 3] * alpha;
+            if constexpr (HB) {
+              const float4 b = bias[j][g];
+              v0 = v0 + b.x; v1 = v1 + b.y; v2 = v2 + b.z; v3 = v3 + b.w;
+            }
+            const int c = (4 * j + g) ^ (lrow & 15);
+            *reinterpret_cast<uint2*>(reg + lrow * 256 + 16 * c + 8 * h) = make_uint2(bf16_pair(v0, v1), bf16_pair(v2, v3));
+          }
+      }
+      // the same wave reads back what it wrote (LDS operations of a wave run
+      // in order).  Eight reads go out before their eight stores: each store
+      // sits behind its bounds branch, and a read issued after the previous
+      // store would wait out the LDS latency once per 16-byte chunk
+      const int c = lane & 15;
+      const int col = n0 + wn * 128 + 8 * c;
+      const int row0 = m0 + wm * 128 + 32 * rd * IPR + (lane >> 4);
+      uint16_t* const y0 = static_cast<uint16_t*>(p.y) + (int64_t)row0 * p.ldy + col;
+      const int64_t rstep = 4 * p.ldy;                   // 4 rows per read
+#pragma unroll
+      for (int b8 = 0; b8 < IPR; ++b8) {
+        uint4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int lrow = 4 * (8 * b8 + u) + (lane >> 4);
+          v[u] = *reinterpret_cast<const uint4*>(reg + lrow * 256 + 16 * (c ^ (lrow & 15)));
         }
-    }
-    // the same wave reads back what it wrote (LDS operations of a wave run
-    // in order).  Eight reads go out before their eight stores: each store
-    // sits behind its bounds branch, and a read issued after the previous
-    // store would wait out the LDS latency once per 16-byte chunk
-    const int c = lane & 15;
-    const int col = n0 + wn * 128 + 8 * c;
-    const int row0 = m0 + wm * 128 + 32 * rd * IPR + (lane >> 4);
-    uint16_t* const y0 = static_cast<uint16_t*>(p.y) + (int64_t)row0 * p.ldy + col;
-    const int64_t rstep = 4 * p.ldy;                   // 4 rows per read
 #pragma unroll
-    for (int b8 = 0; b8 < IPR; ++b8) {
-      uint4 v[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int lrow = 4 * (8 * b8 + u) + (lane >> 4);
-        v[u] = *reinterpret_cast<const uint4*>(reg + lrow * 256 + 16 * (c ^ (lrow & 15)));
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int it = 8 * b8 + u;
-        if (row0 + 4 * it < p.M && col < p.N)
-          __builtin_nontemporal_store(uint4v{v[u].x, v[u].y, v[u].z, v[u].w},
-                                      reinterpret_cast<uint4v*>(y0 + it * rstep));
+        for (int u = 0; u < 8; ++u) {
+          const int it = 8 * b8 + u;
+          if (row0 + 4 * it < p.M && col < p.N)
+            __builtin_nontemporal_store(uint4v{v[u].x, v[u].y, v[u].z, v[u].w},
+                                        reinterpret_cast<uint4v*>(y0 + it * rstep));
+        }
       }
     }
+  };
+  if constexpr (AFMT == 2) {
+    if (p.bias) body(std::true_type{});
+    else body(std::false_type{});
+  } else {
+    body(std::true_type{});
   }
 }
 
