@@ -141,10 +141,11 @@ __device__ __forceinline__ void stage_store_tile(const GemmParams& p, const floa
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   const int wm = wv >> 1, wn = wv & 1, r32 = lane & 31, h = lane >> 5;
   uint8_t* reg = smem + wv * (32768 / ROUNDS);
-  // HB: add the bias (zeros where there is none).  The MX kernels take a
-  // second copy without it for calls with no bias: its 64 registers made
-  // their epilogue spill.  (For the NVFP4 / INT8 kernels a second copy
-  // made them spill instead, so they always add.)
+  // HB: add the bias (zeros where there is none).  The NVFP4 and MX
+  // kernels take a second copy without it for calls with no bias (its 64
+  // registers made the MX epilogue spill); in the INT8 kernel, whose rows
+  // each load their own scale, a second copy made it spill instead, so it
+  // always adds.
   auto body = [&](auto has_bias) {
     constexpr bool HB = decltype(has_bias)::value;
     // bias of this lane's 64 columns: 32 j + 8 g + 4 h .. +3 (of the wave's 128)
@@ -205,7 +206,7 @@ __device__ __forceinline__ void stage_store_tile(const GemmParams& p, const floa
       }
     }
   };
-  if constexpr (AFMT == 2) {
+  if constexpr (AFMT == 0 || AFMT == 2) {
     if (p.bias) body(std::true_type{});
     else body(std::false_type{});
   } else {
