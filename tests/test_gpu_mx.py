@@ -204,15 +204,17 @@ def test_gemm_two_waves_and_split_tail():
     check_gemm(x, w, rows=synth.row_sample(M, 96), out_dtypes=("bf16", "f32"))
 
 
+@pytest.mark.parametrize("with_bias", [True, False])
 @pytest.mark.parametrize("fmt", ["mxfp4", "mxfp8"])
-def test_gemm_bf16_output_is_rounded_f32(fmt):
+def test_gemm_bf16_output_is_rounded_f32(fmt, with_bias):
     """The bf16 output is the fp32 output (same accumulation order) rounded
-    to nearest even, bit for bit: pins the epilogue's bf16 conversion."""
+    to nearest even, bit for bit: pins the epilogue's bf16 conversion, with
+    and without a bias (the epilogue has a copy for each)."""
     need_gpu()
     M, N, K = 4096, 9216, 1024
     x = torch.from_numpy(RNG.laplace(size=(M, K)).astype(np.float32)).to(torch.bfloat16).cuda()
     w = (torch.from_numpy(RNG.standard_normal((N, K)).astype(np.float32)) * 0.02).to(torch.bfloat16).cuda()
-    bias = torch.from_numpy(RNG.standard_normal(N).astype(np.float32)).cuda()
+    bias = torch.from_numpy(RNG.standard_normal(N).astype(np.float32)).cuda() if with_bias else None
     a = V.hadamard_quantize(x, 64, fmt)
     wd = V.hadamard_quantize(w, 64, "mxfp4")
     yb = V.qgemm_mx(a, wd, bias, "bf16")

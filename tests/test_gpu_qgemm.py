@@ -190,16 +190,18 @@ def test_split_k_repeatable(M, N, K):
         assert all(torch.equal(ys[0], y) for y in ys[1:])
 
 
+@pytest.mark.parametrize("with_bias", [True, False])
 @pytest.mark.parametrize("fmt", ["nvfp4", "int8"])
-def test_bf16_output_is_rounded_f32(fmt):
+def test_bf16_output_is_rounded_f32(fmt, with_bias):
     """The bf16 output (staged through LDS) is the fp32 output (stored
     directly, same accumulation) rounded to nearest even, bit for bit, with
-    a bias, ragged M and a split tail."""
+    and without a bias (the NVFP4 epilogue has a copy for each), ragged M
+    and a split tail."""
     need_gpu()
     M, N, K = 4000, 9216, 1024
     x = torch.from_numpy(RNG.laplace(size=(M, K)).astype(np.float32)).to(torch.bfloat16).cuda()
     w = (torch.from_numpy(RNG.standard_normal((N, K)).astype(np.float32)) * 0.02).to(torch.bfloat16).cuda()
-    bias = torch.from_numpy(RNG.standard_normal(N).astype(np.float32)).cuda()
+    bias = torch.from_numpy(RNG.standard_normal(N).astype(np.float32)).cuda() if with_bias else None
     a = V.hadamard_quantize(x, 64, fmt)
     wd = V.hadamard_quantize(w, 64, "nvfp4")
     fn = V.qgemm_w4a4 if fmt == "nvfp4" else V.qgemm_w4a8
