@@ -472,6 +472,8 @@ void qgemm_pipe_kernel(GemmParams p) {
   // reads stage ke-1's addresses into this wave's landing area, and the
   // scale-pair loads go out every stage, to the landing area unless the
   // stage is even or the segment's first (the pair (kt & ~1, kt | 1)).
+  // Such a load reads the same 16 bytes in every lane (offset 0 from the
+  // stage's base), one memory request instead of one per row.
   const uint32_t dummy = lds0 + P::DUMMY + wvu * 1024;
   // (the destination is chosen by masks, not branches: the step stays one
   // basic block, so its schedule holds)
@@ -482,22 +484,22 @@ void qgemm_pipe_kernel(GemmParams p) {
     const uint32_t st = lds0 + (uint32_t)ring(kt) * P::STAGE;
     const int k0 = ks * BK;
     if (u < P::NA) {
-      dma16(aq + (A8 ? k0 : k0 / 2), offA[u], pick(live, st + (wvu * P::NA + u) * 1024));
+      dma16(aq + (A8 ? k0 : k0 / 2), offA[u] & live, pick(live, st + (wvu * P::NA + u) * 1024));
     } else if (u < P::NA + P::NAS) {
       const int v = u - P::NA;
-      dma4(as + k0 / 16, offAS[v], pick(live, st + P::A_CODES + (wvu * P::NAS + v) * 256));
+      dma4(as + k0 / 16, offAS[v] & live, pick(live, st + P::A_CODES + (wvu * P::NAS + v) * 256));
     } else if (u < P::NA + P::NAS + P::NW) {
       const int v = u - P::NA - P::NAS;
-      dma16(p.w_q + k0 / 2, offW[v], pick(live, st + P::A_CODES + P::A_SC + (wvu * P::NW + v) * 1024));
+      dma16(p.w_q + k0 / 2, offW[v] & live, pick(live, st + P::A_CODES + P::A_SC + (wvu * P::NW + v) * 1024));
     } else if (u < P::LPS) {
       const int v = u - P::NA - P::NAS - P::NW;
-      dma4(p.w_s + k0 / 16, offWS[v], pick(live, st + P::A_CODES + P::A_SC + P::W_CODES + (wvu * P::NWS + v) * 256));
+      dma4(p.w_s + k0 / 16, offWS[v] & live, pick(live, st + P::A_CODES + P::A_SC + P::W_CODES + (wvu * P::NWS + v) * 256));
     } else if (PAIRS) {
       const uint32_t real = live & (0u - (uint32_t)(((kt & 1) == 0) | (kt == kbase)));
       const int pr = ks >> 1;
       const uint32_t ps = lds0 + P::PAIR_BASE + (uint32_t)(pr & 1) * P::PAIR_SLOT + wvu * 64 * 16;
-      if (P::PAIR_A && u == P::LPS) dma16(as + 16 * pr, offAP, pick(real, ps));
-      else dma16(p.w_s + 16 * pr, offWP, pick(real, ps + P::PAIR_A));
+      if (P::PAIR_A && u == P::LPS) dma16(as + 16 * pr, offAP & real, pick(real, ps));
+      else dma16(p.w_s + 16 * pr, offWP & real, pick(real, ps + P::PAIR_A));
     }
   };
   auto issue_stage = [&](int kt) {

@@ -117,7 +117,8 @@ void qgemm_a16_kernel(GemmParams p) {
   const uint32_t wvu = __builtin_amdgcn_readfirstlane(wv);
   auto ring = [&](int kt) { return (kt - kb) % A16_NS; };
   // Load u (0 .. NLOAD-1) of stage kt, branch-free: a stage past the last
-  // reads stage ke-1's addresses into this wave's landing area.  The scale
+  // reads the same 16 bytes (stage ke-1's base) in every lane into this
+  // wave's landing area, one memory request instead of one per row.  The scale
   // slot with QUADS loads the 16 bytes of stages 4g .. 4g+3 per row into
   // buffer g % 2 on stage 4g (and on a slice's first stage), else nothing.
   const uint32_t dummy = lds0 + P::DUMMY + wvu * 1024;
@@ -127,14 +128,14 @@ void qgemm_a16_kernel(GemmParams p) {
     const uint32_t st = lds0 + (uint32_t)ring(kt) * P::STAGE;
     auto pick = [&](uint32_t target) { return dummy + ((target - dummy) & live); };
     if (u < 8) {
-      dma16(a_bf + 2 * k0, offA[u], pick(st + (wvu * 8 + u) * 1024));
+      dma16(a_bf + 2 * k0, offA[u] & live, pick(st + (wvu * 8 + u) * 1024));
     } else if (u < 10) {
-      dma16(p.w_q + k0 / 2, offW[u - 8], pick(st + A16_A + (wvu * 2 + (u - 8)) * 1024));
+      dma16(p.w_q + k0 / 2, offW[u - 8] & live, pick(st + A16_A + (wvu * 2 + (u - 8)) * 1024));
     } else if constexpr (QUADS) {
       if (kt < ke && ((kt & 3) == 0 || kt == kb))
         dma16(p.w_s + (kt >> 2) * 16, offWS, lds0 + P::SQ + (uint32_t)((kt >> 2) & 1) * 4096u + wvu * 1024u);
     } else {
-      dma4(p.w_s + k0 / 16, offWS, pick(st + A16_A + A16_W + wvu * 256));
+      dma4(p.w_s + k0 / 16, offWS & live, pick(st + A16_A + A16_W + wvu * 256));
     }
   };
   auto issue_stage = [&](int kt) {
